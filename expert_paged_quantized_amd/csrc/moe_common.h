@@ -1,0 +1,67 @@
+// Definitions shared by the HIP kernels and the host runtime of the MoE layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace strata {
+
+enum QFormat : int { Q_INT4 = 1, Q_MXFP4 = 2 };
+enum RouterKind : int { R_SOFTMAX = 1, R_SIGMOID = 2 };
+
+// Token tile of the prefill grouped GEMM (rows of one expert segment).
+constexpr int kPrefillTM = 128;
+// Largest T that takes the decode (split-K GEMV-style) kernels.
+constexpr int kDecodeMaxT = 8;
+// Weight tile: 32 output rows x 64 inputs; one lane owns 16 bytes of codes.
+constexpr int kTileRows = 32;
+constexpr int kTileK = 64;
+constexpr int kTileCodeBytes = 1024;
+
+// One unit of grouped-GEMM work: up to kPrefillTM (prefill) or all (decode)
+// rows [row_begin, row_begin + nrows) of the permuted row space, all routed to
+// `expert`, whose packed record lives at slot_ptr[slot].
+struct Tile {
+  int32_t expert;
+  int32_t slot;
+  int32_t row_begin;
+  int32_t nrows;
+};
+
+// Byte offsets of the regions of one prepacked expert record.
+//   w1 = gate and up interleaved per 32-row tile (16 gate rows, then the same
+//   16 rows of up), [F/16 tiles][H/64 k-blocks]; w2 = down, [H/32][F/64].
+//   codes: 1024 B per tile, lane l holds tile row l%32, inputs 32*(l/32)..+31;
+//   scales: int4 128 B per tile (u32 per row: bf16 scale | bf16 bias << 16),
+//           MXFP4 64 B per tile (E8M0 byte per (half, row)).
+struct RecordLayout {
+  int64_t w1_codes, w1_scales, w2_codes, w2_scales, bytes;
+  static RecordLayout make(int H, int F, int quant) {
+    RecordLayout r;
+    const int64_t sb = (quant == Q_INT4) ? 128 : 64;
+    const int64_t w1_tiles = int64_t(F / 16) * (H / kTileK);
+    const int64_t w2_tiles = int64_t(H / 32) * (F / kTileK);
+    r.w1_codes = 0;
+    r.w1_scales = r.w1_codes + w1_tiles * kTileCodeBytes;
+    r.w2_codes = r.w1_scales + w1_tiles * sb;
+    r.w2_scales = r.w2_codes + w2_tiles * kTileCodeBytes;
+    r.bytes = r.w2_scales + w2_tiles * sb;
+    return r;
+  }
+};
+
+// Arguments of one grouped-GEMM launch (gate+up or down).
+struct GemmArgs {
+  const void* act;           // gate+up: x bf16 [T, H]; down: h [R, F] (f16 int4, bf16 MXFP4)
+  const int32_t* gather;     // gate+up: perm (row -> token); down: nullptr (row -> row)
+  const Tile* tiles;
+  const int32_t* n_tiles_dev;  // device-side tile count, or nullptr to use n_tiles
+  int32_t n_tiles;
+  const uint8_t* const* slot_ptr;  // device array: slot -> record base
+  int64_t off_codes, off_scales;   // region offsets inside a record
+  int32_t N;                 // weight output rows (2F for gate+up, H for down)
+  int32_t K;                 // reduction length (H or F)
+  void* out;                 // gate+up: h [R, F]; down: o fp32 [R, H]
+  int32_t out_ld;            // F or H
+};
+
+}  // namespace strata

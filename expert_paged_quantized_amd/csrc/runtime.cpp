@@ -1,0 +1,795 @@
+// Host runtime and C ABI of the routed 4-bit MoE layer (see include/strata_moe.h).
+//
+// Create validates and admits the checkpoint, prepacks every routed expert
+// once into a pinned host store (a byte permutation into the kernels' tile
+// order: same byte count, no wider copy; ro99/strata README, SM86 kernel and
+// precision paragraphs), allocates the HBM slot pool for the budget
+// ("Documentation" page, Signature) plus the resident shared expert and router
+// ("Strata, Explained", section 2: routers and shared experts live in GPU
+// memory next to a cache of routed experts), and preloads slots.
+//
+// Forward enqueues router -> top-k -> permute, then the expert GEMMs and the
+// combine.  With every expert resident the whole forward stays on the device.
+// With a smaller budget the per-expert counts come back to the host once, the
+// residency manager decides hits, misses and waves, misses are copied from the
+// pinned store into their slots on a side stream, and each wave runs its hit
+// experts while its misses are still in flight.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/strata_moe.h"
+#include "moe_common.h"
+#include "residency.h"
+
+namespace strata {
+hipError_t launch_router(const uint16_t*, const uint16_t*, const float*, float*, int, int, int,
+                         hipStream_t);
+hipError_t launch_topk(const float*, int, int, int, int, int32_t*, float*, hipStream_t);
+hipError_t launch_permute(const int32_t*, int, int, int, int, int, int, int32_t*, int32_t*,
+                          int32_t*, int32_t*, Tile*, int32_t*, unsigned long long*, hipStream_t);
+hipError_t launch_expert_gemm(const GemmArgs&, int, bool, bool, int, hipStream_t);
+hipError_t launch_combine(const float*, const int32_t*, const float*, int, int, int, int,
+                          uint16_t*, hipStream_t);
+}  // namespace strata
+
+using namespace strata;
+
+// ---------------------------------------------------------------------------
+// error state
+// ---------------------------------------------------------------------------
+static thread_local std::string g_err;
+
+static strata_status fail(strata_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+static const char* fault_env() {
+  const char* f = getenv("STRATA_FAULT");
+  return f ? f : "";
+}
+static bool fault(const char* what) { return strcmp(fault_env(), what) == 0; }
+
+#define HIP_CHECK(expr)                                                                      \
+  do {                                                                                       \
+    hipError_t _e = (expr);                                                                  \
+    if (_e != hipSuccess) return fail(STRATA_E_HIP, std::string(#expr) + ": " + hipGetErrorString(_e)); \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// handle
+// ---------------------------------------------------------------------------
+struct TimingRec {
+  int cls;
+  hipEvent_t a, b;
+};
+
+struct strata_moe {
+  int H = 0, F = 0, E = 0, k = 0, S = 0, quant = 0, router = 0, policy = 0, budget = 0;
+  int max_tokens = 0, device = 0;
+  RecordLayout lay{};
+  size_t slot_stride = 0;
+  size_t max_rows = 0, max_tiles = 0;
+
+  uint8_t* host_store = nullptr;  // pinned, E * lay.bytes
+  uint8_t* d_pool = nullptr;      // budget * slot_stride
+  uint8_t* d_shared = nullptr;    // slot_stride
+  uint16_t* d_router_w = nullptr;
+  float* d_router_bias = nullptr;
+  uint8_t** d_slot_ptr = nullptr;  // budget + 1 entries
+  std::vector<uint8_t*> h_slot_ptr;
+
+  float* d_logits = nullptr;
+  int32_t* d_idx = nullptr;
+  float* d_w = nullptr;
+  int32_t* d_counts = nullptr;
+  int32_t* d_offsets = nullptr;
+  int32_t* d_perm = nullptr;
+  int32_t* d_pos = nullptr;
+  Tile* d_tiles_dev = nullptr;
+  Tile* d_tiles_host = nullptr;
+  int32_t* d_ntiles = nullptr;
+  unsigned long long* d_distinct = nullptr;
+  void* d_h = nullptr;
+  float* d_o = nullptr;
+  uint64_t ws_bytes = 0;
+
+  int32_t* h_counts = nullptr;  // pinned
+  Tile* h_tiles = nullptr;      // pinned
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t ev_fwd_done = nullptr;
+  bool fwd_recorded = false;
+  std::vector<hipEvent_t> ev_copied, ev_wave_done;
+
+  ResidencyManager rm;
+  uint64_t forwards = 0;
+  bool poisoned = false;
+
+  bool timing = false;
+  std::vector<TimingRec> trecs;
+  std::vector<hipEvent_t> ev_pool;
+  double t_ms[STRATA_K_COUNT] = {};
+  uint64_t t_launch[STRATA_K_COUNT] = {};
+};
+
+// ---------------------------------------------------------------------------
+// validation / admission (pure host; runs before any HIP call)
+// ---------------------------------------------------------------------------
+static bool fp16_exact(uint16_t bf) {
+  const uint32_t u = uint32_t(bf) << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  if (!(f == f) || f == __builtin_inff() || f == -__builtin_inff()) return false;
+  const _Float16 h = (_Float16)f;
+  return (float)h == f;
+}
+
+static strata_status validate(const strata_moe_desc* d) {
+  if (!d) return fail(STRATA_E_INVALID, "desc is NULL");
+  if (d->hidden <= 0 || d->ffn <= 0 || d->num_experts <= 0 || d->top_k <= 0 || d->max_tokens <= 0)
+    return fail(STRATA_E_INVALID, "sizes must be positive");
+  if (d->num_experts > 1024) return fail(STRATA_E_UNSUPPORTED, "num_experts > 1024");
+  if (d->top_k > d->num_experts) return fail(STRATA_E_INVALID, "top_k > num_experts");
+  if (d->top_k > 32) return fail(STRATA_E_UNSUPPORTED, "top_k > 32");
+  if (d->num_shared != 0 && d->num_shared != 1) return fail(STRATA_E_UNSUPPORTED, "num_shared must be 0 or 1");
+  if (d->quant != STRATA_Q_INT4_G64_AFFINE_BF16 && d->quant != STRATA_Q_MXFP4_E2M1_E8M0_G32)
+    return fail(STRATA_E_INVALID, "unknown quant");
+  if (d->router != STRATA_R_SOFTMAX_TOPK_RENORM && d->router != STRATA_R_SIGMOID_TOPK_RENORM)
+    return fail(STRATA_E_INVALID, "unknown router");
+  if (d->policy != STRATA_P_LRU && d->policy != STRATA_P_LFU) return fail(STRATA_E_INVALID, "unknown policy");
+  if (d->expert_budget < 1 || d->expert_budget > d->num_experts)
+    return fail(STRATA_E_INVALID, "expert_budget must be in [1, num_experts]");
+  if (d->max_tokens > (1 << 20)) return fail(STRATA_E_UNSUPPORTED, "max_tokens > 2^20");
+  if (d->hidden % 512) return fail(STRATA_E_UNSUPPORTED, "hidden must be a multiple of 512");
+  if (d->ffn % 64) return fail(STRATA_E_UNSUPPORTED, "ffn must be a multiple of 64");
+  if (!d->router_w) return fail(STRATA_E_INVALID, "router_w is NULL");
+  const bool int4 = d->quant == STRATA_Q_INT4_G64_AFFINE_BF16;
+  auto chk = [&](const strata_qmat& m, const char* name) -> strata_status {
+    if (!m.codes || !m.scales) return fail(STRATA_E_INVALID, std::string(name) + ": codes/scales NULL");
+    if (int4 && !m.biases) return fail(STRATA_E_INVALID, std::string(name) + ": int4 needs biases");
+    if (!int4 && m.biases) return fail(STRATA_E_INVALID, std::string(name) + ": MXFP4 takes no biases");
+    return STRATA_OK;
+  };
+  strata_status st;
+  if ((st = chk(d->gate, "gate")) || (st = chk(d->up, "up")) || (st = chk(d->down, "down"))) return st;
+  if (d->num_shared) {
+    if ((st = chk(d->sh_gate, "sh_gate")) || (st = chk(d->sh_up, "sh_up")) || (st = chk(d->sh_down, "sh_down")))
+      return st;
+  } else if (d->sh_gate.codes || d->sh_up.codes || d->sh_down.codes) {
+    return fail(STRATA_E_INVALID, "shared expert weights given with num_shared = 0");
+  }
+  // admission of scales
+  const size_t H = d->hidden, F = d->ffn;
+  auto admit = [&](const strata_qmat& m, size_t n_exp, size_t rows, size_t cols, const char* name) -> strata_status {
+    if (int4) {
+      const size_t n = n_exp * rows * (cols / 64);
+      const uint16_t* s = (const uint16_t*)m.scales;
+      const uint16_t* b = (const uint16_t*)m.biases;
+      for (size_t i = 0; i < n; ++i)
+        if (!fp16_exact(s[i]) || !fp16_exact(b[i]))
+          return fail(STRATA_E_UNSUPPORTED, std::string(name) +
+                                                ": int4 scale/bias not exactly representable in fp16");
+    } else {
+      const size_t n = n_exp * rows * (cols / 32);
+      const uint8_t* s = (const uint8_t*)m.scales;
+      for (size_t i = 0; i < n; ++i)
+        if (s[i] == 0 || s[i] == 255)
+          return fail(STRATA_E_BAD_SCALE, std::string(name) + ": E8M0 scale byte 0 or 255 at index " +
+                                              std::to_string(i));
+    }
+    return STRATA_OK;
+  };
+  const size_t E = d->num_experts;
+  if ((st = admit(d->gate, E, F, H, "gate")) || (st = admit(d->up, E, F, H, "up")) ||
+      (st = admit(d->down, E, H, F, "down")))
+    return st;
+  if (d->num_shared) {
+    if ((st = admit(d->sh_gate, 1, F, H, "sh_gate")) || (st = admit(d->sh_up, 1, F, H, "sh_up")) ||
+        (st = admit(d->sh_down, 1, H, F, "sh_down")))
+      return st;
+  }
+  return STRATA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// prepack: one expert's gate/up/down into the tile-order record
+// ---------------------------------------------------------------------------
+// int4 word nibble order k0 k2 k4 k6 k1 k3 k5 k7 (low to high); see the kernel.
+static inline uint32_t int4_word_perm(uint32_t w) {
+  uint32_t r = 0;
+  for (int j = 0; j < 4; ++j) {
+    r |= ((w >> (8 * j)) & 0xFu) << (4 * j);            // k_2j  -> nibble j
+    r |= ((w >> (8 * j + 4)) & 0xFu) << (4 * (j + 4));  // k_2j+1 -> nibble j+4
+  }
+  return r;
+}
+
+struct MatView {
+  const uint8_t* codes;   // [rows, cols/2]
+  const uint8_t* scales;  // int4: bf16 [rows, cols/64]; MXFP4: u8 [rows, cols/32]
+  const uint8_t* biases;  // int4: bf16 [rows, cols/64]
+};
+
+static MatView view(const strata_qmat& m, size_t e, size_t rows, size_t cols, bool int4) {
+  MatView v;
+  v.codes = (const uint8_t*)m.codes + e * rows * (cols / 2);
+  if (int4) {
+    v.scales = (const uint8_t*)m.scales + e * rows * (cols / 64) * 2;
+    v.biases = (const uint8_t*)m.biases + e * rows * (cols / 64) * 2;
+  } else {
+    v.scales = (const uint8_t*)m.scales + e * rows * (cols / 32);
+    v.biases = nullptr;
+  }
+  return v;
+}
+
+// Packs the tiles of one matrix.  `row_of(rt, r)` maps tile row r of row tile
+// rt to a (source matrix, row) pair.
+template <class RowOf>
+static void pack_matrix(uint8_t* codes_dst, uint8_t* scales_dst, int n_rt, int K, bool int4,
+                        RowOf row_of) {
+  const int KB = K / 64;
+  for (int rt = 0; rt < n_rt; ++rt) {
+    for (int kb = 0; kb < KB; ++kb) {
+      uint8_t* cd = codes_dst + ((size_t)rt * KB + kb) * kTileCodeBytes;
+      for (int l = 0; l < 64; ++l) {
+        const int r = l & 31, h = l >> 5;
+        const MatView* mv;
+        int row;
+        row_of(rt, r, mv, row);
+        const uint8_t* src = mv->codes + (size_t)row * (K / 2) + (kb * 64 + h * 32) / 2;
+        uint8_t* dst = cd + l * 16;
+        if (int4) {
+          for (int wi = 0; wi < 4; ++wi) {
+            uint32_t w;
+            memcpy(&w, src + 4 * wi, 4);
+            w = int4_word_perm(w);
+            memcpy(dst + 4 * wi, &w, 4);
+          }
+        } else {
+          memcpy(dst, src, 16);
+        }
+      }
+      if (int4) {
+        uint8_t* sd = scales_dst + ((size_t)rt * KB + kb) * 128;
+        for (int r = 0; r < 32; ++r) {
+          const MatView* mv;
+          int row;
+          row_of(rt, r, mv, row);
+          const size_t gi = (size_t)row * KB + kb;
+          uint16_t s, b;
+          memcpy(&s, mv->scales + gi * 2, 2);
+          memcpy(&b, mv->biases + gi * 2, 2);
+          const uint32_t u = uint32_t(s) | (uint32_t(b) << 16);
+          memcpy(sd + r * 4, &u, 4);
+        }
+      } else {
+        uint8_t* sd = scales_dst + ((size_t)rt * KB + kb) * 64;
+        for (int l = 0; l < 64; ++l) {
+          const int r = l & 31, h = l >> 5;
+          const MatView* mv;
+          int row;
+          row_of(rt, r, mv, row);
+          sd[l] = mv->scales[(size_t)row * (K / 32) + kb * 2 + h];
+        }
+      }
+    }
+  }
+}
+
+static void pack_expert(uint8_t* rec, const RecordLayout& lay, const strata_qmat& g,
+                        const strata_qmat& u, const strata_qmat& d, size_t e, int H, int F, bool int4) {
+  const MatView vg = view(g, e, F, H, int4), vu = view(u, e, F, H, int4), vd = view(d, e, H, F, int4);
+  // w1: tile rt = gate rows 16rt..+15 then up rows 16rt..+15
+  pack_matrix(rec + lay.w1_codes, rec + lay.w1_scales, F / 16, H, int4,
+              [&](int rt, int r, const MatView*& mv, int& row) {
+                mv = (r < 16) ? &vg : &vu;
+                row = rt * 16 + (r & 15);
+              });
+  pack_matrix(rec + lay.w2_codes, rec + lay.w2_scales, H / 32, F, int4,
+              [&](int rt, int r, const MatView*& mv, int& row) {
+                mv = &vd;
+                row = rt * 32 + r;
+              });
+}
+
+// ---------------------------------------------------------------------------
+// create / destroy
+// ---------------------------------------------------------------------------
+static void release(strata_moe* h) {
+  if (!h) return;
+  if (h->device >= 0) (void)hipSetDevice(h->device);
+  if (h->copy_stream) (void)hipStreamSynchronize(h->copy_stream);
+  (void)hipDeviceSynchronize();
+  for (auto& r : h->trecs) {
+    h->ev_pool.push_back(r.a);
+    h->ev_pool.push_back(r.b);
+  }
+  for (auto e : h->ev_pool) (void)hipEventDestroy(e);
+  for (auto e : h->ev_copied) (void)hipEventDestroy(e);
+  for (auto e : h->ev_wave_done) (void)hipEventDestroy(e);
+  if (h->ev_fwd_done) (void)hipEventDestroy(h->ev_fwd_done);
+  if (h->copy_stream) (void)hipStreamDestroy(h->copy_stream);
+  void* dev[] = {h->d_pool, h->d_shared, h->d_router_w, h->d_router_bias, h->d_slot_ptr,
+                 h->d_logits, h->d_idx, h->d_w, h->d_counts, h->d_offsets, h->d_perm, h->d_pos,
+                 h->d_tiles_dev, h->d_tiles_host, h->d_ntiles, h->d_distinct, h->d_h, h->d_o};
+  for (void* p : dev)
+    if (p) (void)hipFree(p);
+  if (h->host_store) (void)hipHostFree(h->host_store);
+  if (h->h_counts) (void)hipHostFree(h->h_counts);
+  if (h->h_tiles) (void)hipHostFree(h->h_tiles);
+  delete h;
+}
+
+template <class T>
+static strata_status dev_alloc(strata_moe* h, T** p, size_t bytes) {
+  if (fault("devalloc")) return fail(STRATA_E_NOMEM, "hipMalloc failed (injected fault)");
+  bytes = std::max<size_t>(bytes, 256);
+  hipError_t e = hipMalloc((void**)p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    return fail(STRATA_E_NOMEM, std::string("hipMalloc(") + std::to_string(bytes) + "): " + hipGetErrorString(e));
+  }
+  return STRATA_OK;
+}
+
+template <class T>
+static strata_status host_alloc(T** p, size_t bytes) {
+  if (fault("hostalloc")) return fail(STRATA_E_NOMEM, "hipHostMalloc failed (injected fault)");
+  hipError_t e = hipHostMalloc((void**)p, std::max<size_t>(bytes, 64), hipHostMallocDefault);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    return fail(STRATA_E_NOMEM, std::string("hipHostMalloc(") + std::to_string(bytes) + "): " + hipGetErrorString(e));
+  }
+  return STRATA_OK;
+}
+
+static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
+  h->H = d->hidden;
+  h->F = d->ffn;
+  h->E = d->num_experts;
+  h->k = d->top_k;
+  h->S = d->num_shared;
+  h->quant = d->quant == STRATA_Q_INT4_G64_AFFINE_BF16 ? Q_INT4 : Q_MXFP4;
+  h->router = d->router == STRATA_R_SOFTMAX_TOPK_RENORM ? R_SOFTMAX : R_SIGMOID;
+  h->policy = d->policy;
+  h->budget = d->expert_budget;
+  h->max_tokens = d->max_tokens;
+  h->lay = RecordLayout::make(h->H, h->F, h->quant);
+  h->slot_stride = (size_t(h->lay.bytes) + 255) & ~size_t(255);
+  const bool int4 = h->quant == Q_INT4;
+
+  int dev = d->device;
+  if (dev < 0) HIP_CHECK(hipGetDevice(&dev));
+  h->device = dev;
+  HIP_CHECK(hipSetDevice(dev));
+
+  // pinned host store, prepacked in parallel over experts
+  strata_status st;
+  const size_t rec = h->lay.bytes;
+  if ((st = host_alloc(&h->host_store, rec * h->E))) return st;
+  {
+    unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    std::vector<std::thread> th;
+    for (unsigned t = 0; t < nth; ++t)
+      th.emplace_back([&, t]() {
+        for (int e = t; e < h->E; e += nth)
+          pack_expert(h->host_store + rec * e, h->lay, d->gate, d->up, d->down, e, h->H, h->F, int4);
+      });
+    for (auto& t : th) t.join();
+  }
+
+  // device: slot pool, shared expert, router, slot pointer table
+  if ((st = dev_alloc(h, &h->d_pool, h->slot_stride * h->budget))) return st;
+  if (h->S) {
+    if ((st = dev_alloc(h, &h->d_shared, h->slot_stride))) return st;
+    std::vector<uint8_t> tmp(rec);
+    pack_expert(tmp.data(), h->lay, d->sh_gate, d->sh_up, d->sh_down, 0, h->H, h->F, int4);
+    HIP_CHECK(hipMemcpy(h->d_shared, tmp.data(), rec, hipMemcpyHostToDevice));
+  }
+  if ((st = dev_alloc(h, &h->d_router_w, size_t(h->E) * h->H * 2))) return st;
+  HIP_CHECK(hipMemcpy(h->d_router_w, d->router_w, size_t(h->E) * h->H * 2, hipMemcpyHostToDevice));
+  if (d->router_bias) {
+    if ((st = dev_alloc(h, &h->d_router_bias, size_t(h->E) * 4))) return st;
+    HIP_CHECK(hipMemcpy(h->d_router_bias, d->router_bias, size_t(h->E) * 4, hipMemcpyHostToDevice));
+  }
+  h->h_slot_ptr.resize(h->budget + 1);
+  for (int s = 0; s < h->budget; ++s) h->h_slot_ptr[s] = h->d_pool + h->slot_stride * s;
+  h->h_slot_ptr[h->budget] = h->d_shared ? h->d_shared : h->d_pool;
+  if ((st = dev_alloc(h, &h->d_slot_ptr, sizeof(uint8_t*) * (h->budget + 1)))) return st;
+  HIP_CHECK(hipMemcpy(h->d_slot_ptr, h->h_slot_ptr.data(), sizeof(uint8_t*) * (h->budget + 1),
+                      hipMemcpyHostToDevice));
+
+  // workspace for max_tokens
+  const size_t T = h->max_tokens, TK = T * h->k;
+  h->max_rows = TK + (h->S ? T : 0);
+  h->max_tiles = TK / kPrefillTM + std::min<size_t>(h->E, TK) + (T + kPrefillTM - 1) / kPrefillTM + 4;
+  uint64_t ws = 0;
+  auto walloc = [&](auto** p, size_t bytes) -> strata_status {
+    ws += std::max<size_t>(bytes, 256);
+    return dev_alloc(h, p, bytes);
+  };
+  if ((st = walloc(&h->d_logits, T * h->E * 4)) || (st = walloc(&h->d_idx, TK * 4)) ||
+      (st = walloc(&h->d_w, TK * 4)) || (st = walloc(&h->d_counts, size_t(h->E) * 4)) ||
+      (st = walloc(&h->d_offsets, size_t(h->E + 1) * 4)) || (st = walloc(&h->d_perm, h->max_rows * 4)) ||
+      (st = walloc(&h->d_pos, TK * 4)) || (st = walloc(&h->d_tiles_dev, h->max_tiles * sizeof(Tile))) ||
+      (st = walloc(&h->d_tiles_host, h->max_tiles * sizeof(Tile))) || (st = walloc(&h->d_ntiles, 64)) ||
+      (st = walloc(&h->d_distinct, 64)) || (st = walloc(&h->d_h, h->max_rows * h->F * 2)) ||
+      (st = walloc(&h->d_o, h->max_rows * h->H * 4)))
+    return st;
+  h->ws_bytes = ws;
+  HIP_CHECK(hipMemset(h->d_distinct, 0, 64));
+  if ((st = host_alloc(&h->h_counts, size_t(h->E) * 4))) return st;
+  if ((st = host_alloc(&h->h_tiles, h->max_tiles * sizeof(Tile)))) return st;
+
+  HIP_CHECK(hipStreamCreateWithFlags(&h->copy_stream, hipStreamNonBlocking));
+  HIP_CHECK(hipEventCreateWithFlags(&h->ev_fwd_done, hipEventDisableTiming));
+
+  // preload experts 0..budget-1 into slots 0..budget-1
+  for (int s = 0; s < h->budget; ++s)
+    HIP_CHECK(hipMemcpy(h->h_slot_ptr[s], h->host_store + rec * s, rec, hipMemcpyHostToDevice));
+  HIP_CHECK(hipDeviceSynchronize());
+  h->rm.init(h->E, h->budget, h->policy == STRATA_P_LFU ? ResidencyManager::kLFU : ResidencyManager::kLRU,
+             rec);
+  return STRATA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+static hipEvent_t pool_event(strata_moe* h) {
+  if (!h->ev_pool.empty()) {
+    hipEvent_t e = h->ev_pool.back();
+    h->ev_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class Fn>
+static hipError_t timed(strata_moe* h, int cls, hipStream_t s, Fn&& fn) {
+  if (!h->timing) return fn();
+  hipEvent_t a = pool_event(h), b = pool_event(h);
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = fn();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  h->trecs.push_back({cls, a, b});
+  return e;
+}
+
+static GemmArgs gemm_args(strata_moe* h, bool gate_up, const void* x, const Tile* tiles,
+                          const int32_t* n_dev, int n_tiles) {
+  GemmArgs a;
+  a.act = gate_up ? x : h->d_h;
+  a.gather = gate_up ? h->d_perm : nullptr;
+  a.tiles = tiles;
+  a.n_tiles_dev = n_dev;
+  a.n_tiles = n_tiles;
+  a.slot_ptr = h->d_slot_ptr;
+  a.off_codes = gate_up ? h->lay.w1_codes : h->lay.w2_codes;
+  a.off_scales = gate_up ? h->lay.w1_scales : h->lay.w2_scales;
+  a.N = gate_up ? 2 * h->F : h->H;
+  a.K = gate_up ? h->H : h->F;
+  a.out = gate_up ? h->d_h : (void*)h->d_o;
+  a.out_ld = gate_up ? h->F : h->H;
+  return a;
+}
+
+static int prefill_grid(int items) { return std::max(1, std::min(items, 2048)); }
+
+// Runs gate+up then down over a tile range.  n_dev != nullptr: the count lives
+// on the device and `n_tiles` is only an upper bound.
+static hipError_t run_experts(strata_moe* h, const void* x, const Tile* tiles, const int32_t* n_dev,
+                              int n_tiles, bool decode, hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool gate_up = pass == 0;
+    GemmArgs a = gemm_args(h, gate_up, x, tiles, n_dev, n_tiles);
+    const int nrt = a.N / 32;
+    int grid;
+    if (decode)
+      grid = n_tiles * nrt;
+    else
+      grid = prefill_grid(n_tiles * ((nrt + 7) / 8));
+    const int cls = decode ? (gate_up ? STRATA_K_DEC_UP : STRATA_K_DEC_DOWN)
+                           : (gate_up ? STRATA_K_PRE_UP : STRATA_K_PRE_DOWN);
+    hipError_t e = timed(h, cls, s, [&]() { return launch_expert_gemm(a, h->quant, gate_up, decode, grid, s); });
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+static void add_tiles(strata_moe* h, int expert, int slot, int row_begin, int count, bool decode,
+                      int& n) {
+  const int tr = decode ? count : kPrefillTM;
+  for (int r = 0; r < count; r += tr) {
+    Tile t;
+    t.expert = expert;
+    t.slot = slot;
+    t.row_begin = row_begin + r;
+    t.nrows = std::min(tr, count - r);
+    h->h_tiles[n++] = t;
+  }
+}
+
+static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, hipStream_t s,
+                                  const strata_route_dbg* dbg) {
+  const bool decode = T <= kDecodeMaxT;
+  const int TK = T * h->k;
+  if (h->fwd_recorded) HIP_CHECK(hipStreamWaitEvent(s, h->ev_fwd_done, 0));
+
+  HIP_CHECK(timed(h, STRATA_K_ROUTER, s, [&]() {
+    return launch_router((const uint16_t*)x, h->d_router_w, h->d_router_bias, h->d_logits, T, h->E, h->H, s);
+  }));
+  HIP_CHECK(timed(h, STRATA_K_TOPK, s, [&]() {
+    return launch_topk(h->d_logits, T, h->E, h->k, h->router, h->d_idx, h->d_w, s);
+  }));
+  const int tile_rows = decode ? (1 << 30) : kPrefillTM;
+  HIP_CHECK(timed(h, STRATA_K_PERMUTE, s, [&]() {
+    return launch_permute(h->d_idx, T, h->k, h->E, h->S, tile_rows, h->budget, h->d_counts, h->d_offsets,
+                          h->d_perm, h->d_pos, h->d_tiles_dev, h->d_ntiles, h->d_distinct, s);
+  }));
+
+  if (h->budget == h->E) {
+    const int ub = decode ? std::min(h->E, TK) + h->S
+                          : TK / kPrefillTM + std::min(h->E, TK) + (h->S ? (T + kPrefillTM - 1) / kPrefillTM : 0);
+    HIP_CHECK(run_experts(h, x, h->d_tiles_dev, h->d_ntiles, ub, decode, s));
+    h->rm.forwards++;
+    h->rm.waves++;
+  } else {
+    HIP_CHECK(hipMemcpyAsync(h->h_counts, h->d_counts, size_t(h->E) * 4, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    std::vector<int32_t> needed;
+    std::vector<int32_t> off(h->E + 1, 0);
+    for (int e = 0; e < h->E; ++e) {
+      off[e + 1] = off[e] + h->h_counts[e];
+      if (h->h_counts[e] > 0) needed.push_back(e);
+    }
+    if (off[h->E] != TK) return fail(STRATA_E_HIP, "token counts do not add up to T*k");
+    std::vector<std::vector<PlanEntry>> plan;
+    h->rm.forward(needed, plan);
+    // tile lists: per wave [hits (+ shared in wave 0)] [paged]
+    const int nw = (int)plan.size();
+    std::vector<int> hb(nw), he(nw), pe(nw);
+    int n = 0;
+    for (int w = 0; w < nw; ++w) {
+      hb[w] = n;
+      for (const PlanEntry& p : plan[w])
+        if (!p.paged) add_tiles(h, p.expert, p.slot, off[p.expert], h->h_counts[p.expert], decode, n);
+      if (w == 0 && h->S) add_tiles(h, h->E, h->budget, TK, T, decode, n);
+      he[w] = n;
+      for (const PlanEntry& p : plan[w])
+        if (p.paged) add_tiles(h, p.expert, p.slot, off[p.expert], h->h_counts[p.expert], decode, n);
+      pe[w] = n;
+    }
+    if ((size_t)n > h->max_tiles) return fail(STRATA_E_HIP, "tile list overflow");
+    HIP_CHECK(hipMemcpyAsync(h->d_tiles_host, h->h_tiles, size_t(n) * sizeof(Tile), hipMemcpyHostToDevice, s));
+    while ((int)h->ev_copied.size() < nw) {
+      hipEvent_t a, b;
+      HIP_CHECK(hipEventCreateWithFlags(&a, hipEventDisableTiming));
+      HIP_CHECK(hipEventCreateWithFlags(&b, hipEventDisableTiming));
+      h->ev_copied.push_back(a);
+      h->ev_wave_done.push_back(b);
+    }
+    const size_t rec = h->lay.bytes;
+    for (int w = 0; w < nw; ++w) {
+      const bool any_paged = pe[w] > he[w];
+      if (any_paged) {
+        if (w > 0) HIP_CHECK(hipStreamWaitEvent(h->copy_stream, h->ev_wave_done[w - 1], 0));
+        for (const PlanEntry& p : plan[w]) {
+          if (!p.paged) continue;
+          if (fault("h2d")) return fail(STRATA_E_HIP, "hipMemcpyAsync H2D failed (injected fault)");
+          HIP_CHECK(hipMemcpyAsync(h->h_slot_ptr[p.slot], h->host_store + rec * p.expert, rec,
+                                   hipMemcpyHostToDevice, h->copy_stream));
+        }
+        HIP_CHECK(hipEventRecord(h->ev_copied[w], h->copy_stream));
+      }
+      HIP_CHECK(run_experts(h, x, h->d_tiles_host + hb[w], nullptr, he[w] - hb[w], decode, s));
+      if (any_paged) {
+        HIP_CHECK(hipStreamWaitEvent(s, h->ev_copied[w], 0));
+        HIP_CHECK(run_experts(h, x, h->d_tiles_host + he[w], nullptr, pe[w] - he[w], decode, s));
+      }
+      HIP_CHECK(hipEventRecord(h->ev_wave_done[w], s));
+    }
+  }
+
+  HIP_CHECK(timed(h, STRATA_K_COMBINE, s, [&]() {
+    return launch_combine(h->d_o, h->d_pos, h->d_w, T, h->k, h->H, h->S ? TK : -1, (uint16_t*)y, s);
+  }));
+
+  if (dbg) {
+    auto cp = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
+      return dst ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s) : hipSuccess;
+    };
+    HIP_CHECK(cp(dbg->logits, h->d_logits, size_t(T) * h->E * 4));
+    HIP_CHECK(cp(dbg->topk_idx, h->d_idx, size_t(TK) * 4));
+    HIP_CHECK(cp(dbg->topk_w, h->d_w, size_t(TK) * 4));
+    HIP_CHECK(cp(dbg->counts, h->d_counts, size_t(h->E) * 4));
+    HIP_CHECK(cp(dbg->offsets, h->d_offsets, size_t(h->E + 1) * 4));
+    HIP_CHECK(cp(dbg->perm, h->d_perm, size_t(TK) * 4));
+  }
+  HIP_CHECK(hipEventRecord(h->ev_fwd_done, s));
+  h->fwd_recorded = true;
+  if (getenv("STRATA_LOG")) {
+    fprintf(stderr, "[strata] T=%d forwards=%llu hits=%llu misses=%llu waves=%llu bytes_h2d=%llu\n", T,
+            (unsigned long long)h->rm.forwards, (unsigned long long)h->rm.hits,
+            (unsigned long long)h->rm.misses, (unsigned long long)h->rm.waves,
+            (unsigned long long)h->rm.bytes_h2d);
+  }
+  return STRATA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+strata_status strata_moe_create(const strata_moe_desc* desc, strata_moe** out) {
+  if (!out) return fail(STRATA_E_INVALID, "out is NULL");
+  *out = nullptr;
+  strata_status st = validate(desc);
+  if (st) return st;
+  strata_moe* h = new strata_moe();
+  h->device = -1;
+  st = create_impl(desc, h);
+  if (st) {
+    std::string msg = g_err;
+    release(h);
+    g_err = msg;
+    return st;
+  }
+  g_err.clear();
+  *out = h;
+  return STRATA_OK;
+}
+
+strata_status strata_moe_forward(strata_moe* h, const void* x, int32_t T, void* y, void* stream,
+                                 const strata_route_dbg* dbg) {
+  if (!h) return fail(STRATA_E_INVALID, "handle is NULL");
+  if (h->poisoned) return fail(STRATA_E_POISONED, "handle poisoned by an earlier HIP failure");
+  if (T < 0 || T > h->max_tokens) return fail(STRATA_E_INVALID, "T out of range [0, max_tokens]");
+  if (T == 0) return STRATA_OK;
+  if (!x || !y) return fail(STRATA_E_INVALID, "x or y is NULL");
+  const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y, nb = (uintptr_t)T * h->H * 2;
+  if (xa < ya + nb && ya < xa + nb) return fail(STRATA_E_INVALID, "x and y overlap");
+  if ((xa | ya) & 15) return fail(STRATA_E_INVALID, "x and y must be 16-byte aligned");
+  int cur = -1;
+  if (hipGetDevice(&cur) == hipSuccess && cur != h->device) (void)hipSetDevice(h->device);
+  strata_status st = forward_impl(h, x, T, y, (hipStream_t)stream, dbg);
+  if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
+  if (st == STRATA_E_HIP) h->poisoned = true;
+  return st;
+}
+
+strata_status strata_expert_cache_stats(const strata_moe* h, strata_cache_stats* out) {
+  if (!h || !out) return fail(STRATA_E_INVALID, "NULL argument");
+  memset(out, 0, sizeof(*out));
+  out->forwards = h->rm.forwards;
+  out->hits = h->rm.hits;
+  out->misses = h->rm.misses;
+  out->evictions = h->rm.evictions;
+  out->bytes_h2d = h->rm.bytes_h2d;
+  out->waves = h->rm.waves;
+  if (h->budget == h->E && h->rm.forwards > 0) {
+    unsigned long long d = 0;
+    HIP_CHECK(hipSetDevice(h->device));
+    HIP_CHECK(hipDeviceSynchronize());
+    HIP_CHECK(hipMemcpy(&d, h->d_distinct, 8, hipMemcpyDeviceToHost));
+    out->hits = d;
+  }
+  out->budget = h->budget;
+  out->resident = h->rm.resident();
+  out->policy = h->policy;
+  out->expert_bytes = h->lay.bytes;
+  out->resident_bytes = uint64_t(out->resident) * h->lay.bytes;
+  return STRATA_OK;
+}
+
+strata_status strata_moe_memory(const strata_moe* h, strata_memory_info* out) {
+  if (!h || !out) return fail(STRATA_E_INVALID, "NULL argument");
+  memset(out, 0, sizeof(*out));
+  out->slot_pool = uint64_t(h->slot_stride) * h->budget;
+  out->shared = h->S ? h->slot_stride : 0;
+  out->router = uint64_t(h->E) * h->H * 2 + (h->d_router_bias ? uint64_t(h->E) * 4 : 0) +
+                uint64_t(sizeof(uint8_t*)) * (h->budget + 1);
+  out->workspace = h->ws_bytes;
+  out->device_total = out->slot_pool + out->shared + out->router + out->workspace;
+  out->host_store = uint64_t(h->lay.bytes) * h->E;
+  return STRATA_OK;
+}
+
+strata_status strata_moe_set_timing(strata_moe* h, int32_t enable) {
+  if (!h) return fail(STRATA_E_INVALID, "handle is NULL");
+  h->timing = enable != 0;
+  return STRATA_OK;
+}
+
+strata_status strata_moe_timing(strata_moe* h, strata_timing* out) {
+  if (!h || !out) return fail(STRATA_E_INVALID, "NULL argument");
+  HIP_CHECK(hipSetDevice(h->device));
+  for (auto& r : h->trecs) {
+    HIP_CHECK(hipEventSynchronize(r.b));
+    float ms = 0.0f;
+    HIP_CHECK(hipEventElapsedTime(&ms, r.a, r.b));
+    h->t_ms[r.cls] += ms;
+    h->t_launch[r.cls] += 1;
+    h->ev_pool.push_back(r.a);
+    h->ev_pool.push_back(r.b);
+  }
+  h->trecs.clear();
+  memset(out, 0, sizeof(*out));
+  for (int c = 0; c < STRATA_K_COUNT; ++c) {
+    out->ms[c] = h->t_ms[c];
+    out->launches[c] = h->t_launch[c];
+    h->t_ms[c] = 0.0;
+    h->t_launch[c] = 0;
+  }
+  return STRATA_OK;
+}
+
+void strata_moe_destroy(strata_moe* h) { release(h); }
+
+const char* strata_last_error(void) { return g_err.c_str(); }
+
+strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32_t policy,
+                                      uint64_t expert_bytes, int32_t n_forwards,
+                                      const int32_t* needed_len, const int32_t* needed_flat,
+                                      int32_t* plan_slots, strata_cache_stats* out) {
+  if (!out || n_forwards < 0 || (n_forwards > 0 && (!needed_len || !needed_flat)))
+    return fail(STRATA_E_INVALID, "NULL argument or negative count");
+  if (num_experts < 1 || budget < 1 || budget > num_experts)
+    return fail(STRATA_E_INVALID, "budget must be in [1, num_experts]");
+  if (policy != STRATA_P_LRU && policy != STRATA_P_LFU) return fail(STRATA_E_INVALID, "unknown policy");
+  ResidencyManager rm;
+  rm.init(num_experts, budget, policy == STRATA_P_LFU ? ResidencyManager::kLFU : ResidencyManager::kLRU,
+          expert_bytes);
+  size_t pos = 0, out_pos = 0;
+  std::vector<std::vector<PlanEntry>> plan;
+  for (int32_t f = 0; f < n_forwards; ++f) {
+    if (needed_len[f] < 0) return fail(STRATA_E_INVALID, "negative needed_len");
+    std::vector<int32_t> nd(needed_flat + pos, needed_flat + pos + needed_len[f]);
+    pos += needed_len[f];
+    for (int32_t e : nd)
+      if (e < 0 || e >= num_experts) return fail(STRATA_E_INVALID, "expert id out of range");
+    std::sort(nd.begin(), nd.end());
+    nd.erase(std::unique(nd.begin(), nd.end()), nd.end());
+    rm.forward(nd, plan);
+    for (auto& w : plan)
+      for (auto& p : w) {
+        if (plan_slots) plan_slots[out_pos] = p.slot;
+        ++out_pos;
+      }
+    // duplicates collapse: keep the output aligned with needed_len
+    out_pos += (size_t)needed_len[f] - nd.size();
+  }
+  memset(out, 0, sizeof(*out));
+  out->forwards = rm.forwards;
+  out->hits = rm.hits;
+  out->misses = rm.misses;
+  out->evictions = rm.evictions;
+  out->bytes_h2d = rm.bytes_h2d;
+  out->waves = rm.waves;
+  out->budget = budget;
+  out->resident = rm.resident();
+  out->policy = policy;
+  out->expert_bytes = expert_bytes;
+  out->resident_bytes = uint64_t(rm.resident()) * expert_bytes;
+  return STRATA_OK;
+}
+
+}  // extern "C"

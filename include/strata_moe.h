@@ -1,0 +1,241 @@
+/*
+ * strata_moe.h — C ABI of one routed 4-bit Mixture-of-Experts FFN layer that
+ * runs under an expert budget on an AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes (the forward of one MoE FFN block):
+ *   router logits l = x Wr^T (+ b), top-k experts per token, routing weights
+ *   (softmax over the selected logits, or sigmoid renormalised over them),
+ *   tokens grouped by expert, per expert a SwiGLU FFN o = Wd (silu(Wg x) * Wu x)
+ *   computed straight from 4-bit packed weights, and y = sum_j w_j o_j (+ the
+ *   shared expert's output).
+ *
+ * Sources (page title, section):
+ *   - "Documentation" (strata.amperor.ai docs), Signature: a model loads with
+ *     a budget of resident experts per layer (or a RAM target that implies
+ *     one) and a paging policy; the rest of the experts are streamed.
+ *   - "Strata, Explained" (Medium tutorial), section 2: GPU memory holds the
+ *     router, the shared experts and a cache of the most-used experts that
+ *     adapts to the workload, host RAM holds every expert pinned; a 512-expert
+ *     layer activates 10 routed experts plus 1 shared expert per token.
+ *   - ro99/strata README (C++20/CUDA engine): list of enforced rules (never
+ *     below four bits; routing semantics, expert count and top-k come from the
+ *     checkpoint and never change silently; a predictor may only reorder work;
+ *     exact mode completes or fails); precision paragraph (MXFP4 = two E2M1
+ *     codes per byte and one E8M0 exponent per 32, read as stored with no
+ *     wider copy; E8M0 bytes 0 and 255 fail admission at load); SM86 kernel
+ *     paragraph (a prepack of the 4-bit weights into kernel operand order is a
+ *     pure permutation of the same byte count).
+ *
+ * Conventions of every entry point:
+ *   - Return a strata_status; on failure the thread-local message returned by
+ *     strata_last_error() says why.  Nothing falls back to a different
+ *     computation: an unsupported configuration is an error.
+ *   - "device pointer" means memory of the GPU the handle was created on;
+ *     "host pointer" means ordinary CPU memory.
+ *   - A handle is not thread-safe; one thread at a time may use it.
+ */
+#ifndef STRATA_MOE_H
+#define STRATA_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct strata_moe strata_moe; /* opaque; owned by the library */
+
+typedef enum {
+  STRATA_OK = 0,
+  STRATA_E_INVALID = 1,     /* null pointer, size out of range, bad enum       */
+  STRATA_E_UNSUPPORTED = 2, /* shape or value the kernels cannot take exactly  */
+  STRATA_E_BAD_SCALE = 3,   /* MXFP4 E8M0 scale byte 0 or 255 (admission)      */
+  STRATA_E_NOMEM = 4,       /* host-pinned or device allocation failed         */
+  STRATA_E_HIP = 5,         /* a HIP runtime call failed                       */
+  STRATA_E_POISONED = 6     /* an earlier HIP failure left the handle unusable */
+} strata_status;
+
+/* 4-bit expert weight formats. */
+typedef enum {
+  /* int4 codes, one bf16 scale s and one bf16 bias b per 64 consecutive inputs
+   * of a row: w = s * q + b, q in 0..15 (the MLX-style "4bit" affine form). */
+  STRATA_Q_INT4_G64_AFFINE_BF16 = 1,
+  /* OCP MXFP4: E2M1 codes (sign bit 3), one E8M0 exponent byte e per 32
+   * consecutive inputs of a row: w = e2m1(code) * 2^(e - 127), e in 1..254. */
+  STRATA_Q_MXFP4_E2M1_E8M0_G32 = 2
+} strata_quant;
+
+typedef enum {
+  /* softmax over the k selected logits (equals softmax over all experts
+   * renormalised to the top k) */
+  STRATA_R_SOFTMAX_TOPK_RENORM = 1,
+  /* sigmoid of each selected logit divided by the sum over the k selected */
+  STRATA_R_SIGMOID_TOPK_RENORM = 2
+} strata_router;
+
+typedef enum {
+  STRATA_P_LRU = 1, /* evict the least recently used, ties to the lower id */
+  STRATA_P_LFU = 2  /* evict the least often used, then least recent, then lower id */
+} strata_policy;
+
+/* One stacked packed matrix, host pointers, row-major [out, in] per expert and
+ * quantised along `in`.  Element 2i of a row is the low nibble of byte i.
+ *   codes  : u8   [n_exp, out, in/2]
+ *   scales : int4 -> bf16 bits [n_exp, out, in/64]; MXFP4 -> u8 E8M0 [n_exp, out, in/32]
+ *   biases : int4 -> bf16 bits [n_exp, out, in/64]; MXFP4 -> must be NULL
+ * Gate and up are [F, H] (out = F, in = H); down is [H, F]. */
+typedef struct {
+  const void* codes;
+  const void* scales;
+  const void* biases;
+} strata_qmat;
+
+typedef struct {
+  int32_t hidden;        /* H: multiple of 512                               */
+  int32_t ffn;           /* F: multiple of 64                                */
+  int32_t num_experts;   /* E: routed experts, 1..1024                       */
+  int32_t top_k;         /* k: 1..min(E, 32)                                 */
+  int32_t num_shared;    /* 0 or 1 shared expert (weight 1, always resident) */
+  int32_t quant;         /* strata_quant                                     */
+  int32_t router;        /* strata_router                                    */
+  int32_t policy;        /* strata_policy                                    */
+  int32_t expert_budget; /* resident routed experts (HBM slots), 1..E         */
+  int32_t max_tokens;    /* largest T a forward may take (sizes the workspace) */
+  int32_t device;        /* HIP device ordinal; -1 = the current device       */
+  const uint16_t* router_w;   /* host, bf16 bits [E, H]                        */
+  const float* router_bias;   /* host, fp32 [E], or NULL                       */
+  strata_qmat gate, up, down; /* routed experts, n_exp = E                     */
+  strata_qmat sh_gate, sh_up, sh_down; /* shared expert, n_exp = 1, or all NULL */
+} strata_moe_desc;
+
+/* Creates a layer.  Validates the descriptor, admits the weights (every MXFP4
+ * scale byte must be in 1..254, every int4 scale and bias must be exactly
+ * representable in fp16, which the kernels compute in), copies every routed
+ * expert once into a library-owned pinned host store (a byte permutation into
+ * kernel tile order: same byte count, no wider copy), allocates the HBM slot
+ * pool (expert_budget slots), the resident shared expert, the router and a
+ * workspace sized by max_tokens, and preloads routed experts 0..budget-1 into
+ * slots 0..budget-1.  The caller's buffers may be freed when this returns.
+ * Errors: E_INVALID, E_UNSUPPORTED, E_BAD_SCALE, E_NOMEM, E_HIP.  On error
+ * *out is NULL and nothing is leaked. */
+strata_status strata_moe_create(const strata_moe_desc* desc, strata_moe** out);
+
+/* Optional routing outputs of a forward, device pointers, each may be NULL.
+ *   logits  fp32 [T, E]       router logits
+ *   topk_idx int32 [T, k]     selected experts, rank order
+ *   topk_w  fp32 [T, k]       routing weights
+ *   counts  int32 [E]         tokens per expert
+ *   offsets int32 [E + 1]     exclusive prefix sum of counts
+ *   perm    int32 [T * k]     token ids grouped by expert, ascending inside one */
+typedef struct {
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+} strata_route_dbg;
+
+/* One forward of the layer on T tokens.
+ *   x      device, bf16 bits [T, H] row-major, caller-owned, read only
+ *   y      device, bf16 bits [T, H] row-major, caller-owned, written (RNE)
+ *   stream hipStream_t to enqueue on (NULL = the null stream)
+ *   dbg    optional routing outputs (NULL = none)
+ * x and y must not overlap.  The call enqueues its work on `stream`.  When the
+ * budget is smaller than E it waits once for the per-expert token counts to
+ * reach the host, decides hits and misses, and pages missing experts from the
+ * pinned store into slots with hipMemcpyAsync on an internal copy stream; if
+ * more distinct experts are needed than there are slots, the experts run in
+ * waves of at most `budget`.  Paging, waves and slot placement never change y
+ * (it is bitwise the same as with budget = E).  T == 0 is a no-op.
+ * Errors: E_INVALID (null handle or pointers, T < 0, T > max_tokens), E_HIP
+ * (after which the handle is poisoned), E_POISONED. */
+strata_status strata_moe_forward(strata_moe* h, const void* x, int32_t T, void* y, void* stream,
+                                 const strata_route_dbg* dbg);
+
+/* Cumulative counters since create ("/health" style live state: policy,
+ * budget, resident bytes). */
+typedef struct {
+  uint64_t forwards;       /* forwards with T > 0                              */
+  uint64_t hits;           /* needed experts already resident at call start    */
+  uint64_t misses;         /* needed experts paged in                          */
+  uint64_t evictions;      /* pages that overwrote a resident expert           */
+  uint64_t bytes_h2d;      /* expert bytes paged host -> device                */
+  uint64_t waves;          /* expert waves run                                 */
+  int32_t budget;          /* slots                                            */
+  int32_t resident;        /* slots holding an expert                          */
+  int32_t policy;          /* strata_policy                                    */
+  int32_t reserved;
+  uint64_t resident_bytes; /* resident * expert_bytes                          */
+  uint64_t expert_bytes;   /* packed bytes of one expert                       */
+} strata_cache_stats;
+
+/* Reads the counters.  Does no device work except, when budget == E, one
+ * blocking read of a device-side counter of distinct experts used.
+ * Errors: E_INVALID (null pointers), E_HIP. */
+strata_status strata_expert_cache_stats(const strata_moe* h, strata_cache_stats* out);
+
+/* Device and pinned-host bytes held by a handle.  None of the device terms
+ * grows with E * H * F except through the budget: no dequantised copy exists. */
+typedef struct {
+  uint64_t slot_pool;   /* expert_budget * slot stride                          */
+  uint64_t shared;      /* the resident shared expert (0 if none)               */
+  uint64_t router;      /* router weights and bias                              */
+  uint64_t workspace;   /* activations, routing buffers, outputs for max_tokens */
+  uint64_t device_total;
+  uint64_t host_store;  /* pinned host bytes of the routed expert store         */
+} strata_memory_info;
+
+strata_status strata_moe_memory(const strata_moe* h, strata_memory_info* out);
+
+/* Kernel timing.  While enabled, every kernel launch of a forward is bracketed
+ * by HIP events on the forward's stream; strata_moe_timing() waits for them
+ * and returns totals per kernel class, and resets them. */
+typedef enum {
+  STRATA_K_ROUTER = 0,   /* router logits                     */
+  STRATA_K_TOPK = 1,     /* top-k + weights                   */
+  STRATA_K_PERMUTE = 2,  /* counts, offsets, perm, tile list  */
+  STRATA_K_DEC_UP = 3,   /* decode gate+up GEMV + SwiGLU      */
+  STRATA_K_DEC_DOWN = 4, /* decode down GEMV                  */
+  STRATA_K_PRE_UP = 5,   /* prefill gate+up grouped GEMM      */
+  STRATA_K_PRE_DOWN = 6, /* prefill down grouped GEMM         */
+  STRATA_K_COMBINE = 7,  /* weighted top-k + shared combine   */
+  STRATA_K_COUNT = 8
+} strata_kernel_class;
+
+typedef struct {
+  double ms[STRATA_K_COUNT];        /* summed event time per class        */
+  uint64_t launches[STRATA_K_COUNT];
+  uint64_t rows[STRATA_K_COUNT];    /* real token rows through the class  */
+  uint64_t weight_bytes[STRATA_K_COUNT]; /* packed expert bytes the class streams */
+} strata_timing;
+
+strata_status strata_moe_set_timing(strata_moe* h, int32_t enable);
+strata_status strata_moe_timing(strata_moe* h, strata_timing* out);
+
+/* Frees everything the handle owns (waits for its outstanding work first).
+ * NULL is ignored. */
+void strata_moe_destroy(strata_moe* h);
+
+/* Message of the last failure on this thread ("" if none).  Owned by the
+ * library; valid until the next call on this thread. */
+const char* strata_last_error(void);
+
+/* Dry-run planner (host only, touches no GPU): replays the residency policy of
+ * a layer with E experts and `budget` slots over a trace of forwards and
+ * reports what a real run would page, the placement-plan side of the budget
+ * decision.  needed_flat holds the needed expert ids of every forward back to
+ * back, needed_len[i] of them for forward i (any order, duplicates ignored).
+ * If plan_slots is not NULL it receives, per forward and per needed expert in
+ * the order the forward runs them (hits ascending, then misses ascending), the
+ * slot used; its length must be sum(needed_len).  Errors: E_INVALID. */
+strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32_t policy,
+                                      uint64_t expert_bytes, int32_t n_forwards,
+                                      const int32_t* needed_len, const int32_t* needed_flat,
+                                      int32_t* plan_slots, strata_cache_stats* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STRATA_MOE_H */

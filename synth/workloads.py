@@ -29,8 +29,10 @@ codes u8 [rows, in/2] with element 2i in the low nibble of byte i.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -144,14 +146,11 @@ def _e2m1_encode(v: np.ndarray) -> np.ndarray:
     """Round-to-nearest-even onto the E2M1 grid, saturating at 6; returns 4-bit codes."""
     a = np.abs(v)
     # midpoints between consecutive grid values; at a tie the even code
-    # (mantissa bit 0) wins, i.e. codes 0, 2, 4, 6.
-    mids = (_E2M1_GRID[:-1] + _E2M1_GRID[1:]) / 2.0
+    # (mantissa bit 0: codes 0, 2, 4, 6) wins
+    mids = ((_E2M1_GRID[:-1] + _E2M1_GRID[1:]) / 2.0).astype(a.dtype)
     code = np.searchsorted(mids, a, side="left")  # a == mid -> lower code
-    # for ties, move to the even neighbour
-    tie = np.isin(a, mids)
-    lower = code
-    upper = np.minimum(code + 1, 7)
-    code = np.where(tie & (lower % 2 == 1), upper, lower)
+    tie = a == mids[np.minimum(code, 6)]
+    code = code + (tie & (code % 2 == 1))
     code = np.minimum(code, 7).astype(np.uint8)
     sign = (np.signbit(v) & (code != 0)).astype(np.uint8)
     return code | (sign << 3)
@@ -160,12 +159,13 @@ def _e2m1_encode(v: np.ndarray) -> np.ndarray:
 def quantize_mxfp4_g32(w: np.ndarray):
     """w float32 [N, K] -> (codes u8 [N,K/2], e8m0 scales u8 [N,K/32])."""
     N, K = w.shape
-    g = w.reshape(N, K // 32, 32).astype(np.float64)
-    amax = np.abs(g).max(axis=2)
+    g = w.reshape(N, K // 32, 32)
+    amax = np.abs(g).max(axis=2).astype(np.float64)
     with np.errstate(divide="ignore"):
         e = np.floor(np.log2(np.where(amax > 0, amax, 1e-300))) - 2 + 127
     e = np.clip(e, 1, 254).astype(np.int32)
-    scaled = g / np.exp2(e - 127.0)[..., None]
+    # division by a power of two is exact, in float32 as in float64 (normal range)
+    scaled = g.astype(np.float64) / np.exp2(e - 127.0)[..., None]
     codes = _e2m1_encode(scaled).reshape(N, K)
     return _pack_nibbles(codes), e.astype(np.uint8)
 
@@ -228,22 +228,47 @@ def _store(dst: QMat, e: int, src: QMat):
         dst.biases[e] = src.biases
 
 
-def _gen_experts(cfg: LayerConfig, rng, n_exp: int):
+def _gen_expert(cfg: LayerConfig, seed: int, e: int):
+    """One expert's (gate, up, down) from its own stream, so experts generate in parallel."""
+    H, F = cfg.hidden, cfg.ffn
+    rng = np.random.default_rng([seed, 104729, e])
+    sg, sd = np.float32(1.0 / math.sqrt(H)), np.float32(math.sqrt(0.25 / F))
+    g = _quant(cfg, rng.standard_normal((F, H), dtype=np.float32) * sg)
+    u = _quant(cfg, rng.standard_normal((F, H), dtype=np.float32) * sg)
+    d = _quant(cfg, rng.standard_normal((H, F), dtype=np.float32) * sd)
+    return g, u, d
+
+
+def _gen_experts(cfg: LayerConfig, seed: int, first: int, n_exp: int, threads: int):
     H, F = cfg.hidden, cfg.ffn
     gate = _alloc_stack(cfg, n_exp, F, H)
     up = _alloc_stack(cfg, n_exp, F, H)
     down = _alloc_stack(cfg, n_exp, H, F)
-    sg, sd = np.float32(1.0 / math.sqrt(H)), np.float32(math.sqrt(0.25 / F))
-    for e in range(n_exp):
-        _store(gate, e, _quant(cfg, rng.standard_normal((F, H), dtype=np.float32) * sg))
-        _store(up, e, _quant(cfg, rng.standard_normal((F, H), dtype=np.float32) * sg))
-        _store(down, e, _quant(cfg, rng.standard_normal((H, F), dtype=np.float32) * sd))
+
+    def one(i):
+        g, u, d = _gen_expert(cfg, seed, first + i)
+        _store(gate, i, g)
+        _store(up, i, u)
+        _store(down, i, d)
+
+    if threads > 1 and n_exp > 1:
+        with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, range(n_exp)))
+    else:
+        for i in range(n_exp):
+            one(i)
     return gate, up, down
 
 
-def make_layer(cfg: LayerConfig, seed: Optional[int] = None) -> LayerWeights:
-    """Seeded synthetic layer weights for `cfg` (deterministic in seed)."""
-    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+def make_layer(cfg: LayerConfig, seed: Optional[int] = None, threads: Optional[int] = None) -> LayerWeights:
+    """Seeded synthetic layer weights for `cfg` (deterministic in seed, whatever the thread count).
+
+    Routed expert e draws from the stream (seed, 104729, e); the shared expert
+    from (seed, 104729, E)."""
+    seed = cfg.seed if seed is None else seed
+    if threads is None:
+        threads = min(16, len(os.sched_getaffinity(0)))
+    rng = np.random.default_rng(seed)
     H, E = cfg.hidden, cfg.num_experts
     router_w = f32_to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32)
                                 * np.float32(1.0 / math.sqrt(H)))
@@ -251,10 +276,10 @@ def make_layer(cfg: LayerConfig, seed: Optional[int] = None) -> LayerWeights:
     if cfg.zipf_s is not None:
         rank = 1 + rng.permutation(E)
         bias = (-cfg.zipf_s * np.log(rank.astype(np.float64))).astype(np.float32)
-    gate, up, down = _gen_experts(cfg, rng, E)
+    gate, up, down = _gen_experts(cfg, seed, 0, E, threads)
     lw = LayerWeights(cfg, router_w, bias, gate, up, down)
     if cfg.num_shared:
-        lw.sh_gate, lw.sh_up, lw.sh_down = _gen_experts(cfg, rng, 1)
+        lw.sh_gate, lw.sh_up, lw.sh_down = _gen_experts(cfg, seed, E, 1, 1)
     return lw
 
 

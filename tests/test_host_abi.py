@@ -1,0 +1,186 @@
+"""Host-side checks of the C ABI library: symbols, descriptor validation and
+admission errors (all decided before any HIP call), and the residency manager
+through the dry-run planner against the residency model."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import expert_paged_quantized_amd as epq
+from expert_paged_quantized_amd import _capi
+from oracle.residency import LFU, LRU, ResidencyModel
+from synth import CONFIGS, make_layer
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "strata_moe.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(strata_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert "strata_moe_create" in names and "strata_moe_forward" in names
+    assert "strata_expert_cache_stats" in names
+    L = epq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_capi.EXPORTS)
+
+
+def _desc_from(lw, **over):
+    c = lw.cfg
+    keep = []
+    d = _capi.Desc()
+    d.hidden, d.ffn, d.num_experts, d.top_k, d.num_shared = c.hidden, c.ffn, c.num_experts, c.top_k, c.num_shared
+    d.quant = 1 if c.quant == "int4_g64" else 2
+    d.router = 1 if c.router == "softmax" else 2
+    d.policy, d.expert_budget, d.max_tokens, d.device = 1, c.budget, 16, -1
+    keep.append(lw.router_w)
+    d.router_w = lw.router_w.ctypes.data
+    d.router_bias = None
+    for name in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+        m = getattr(lw, name)
+        if m is None:
+            setattr(d, name, _capi.QMat(None, None, None))
+        else:
+            setattr(d, name, _capi.QMat(m.codes.ctypes.data, m.scales.ctypes.data,
+                                        None if m.biases is None else m.biases.ctypes.data))
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d, keep
+
+
+def _create_status(d):
+    h = ctypes.c_void_p()
+    st = epq.lib().strata_moe_create(ctypes.byref(d), ctypes.byref(h))
+    if st == 0:
+        epq.lib().strata_moe_destroy(h)
+    return st, epq.lib().strata_last_error().decode()
+
+
+@pytest.fixture(scope="module")
+def tiny_int4():
+    return make_layer(CONFIGS["tiny"].scaled(ffn=128, num_experts=4, top_k=2, budget_frac=0.5), seed=1)
+
+
+@pytest.fixture(scope="module")
+def tiny_fp4():
+    return make_layer(CONFIGS["tiny"].scaled(ffn=128, num_experts=4, top_k=2, quant="mxfp4_g32",
+                                             num_shared=1, budget_frac=0.5), seed=2)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("hidden", 0, _capi.E_INVALID),
+    ("hidden", 768, _capi.E_UNSUPPORTED),      # not a multiple of 512
+    ("ffn", 96, _capi.E_UNSUPPORTED),          # not a multiple of 64
+    ("top_k", 5, _capi.E_INVALID),             # k > E
+    ("top_k", 0, _capi.E_INVALID),
+    ("expert_budget", 0, _capi.E_INVALID),
+    ("expert_budget", 5, _capi.E_INVALID),     # budget > E
+    ("num_shared", 2, _capi.E_UNSUPPORTED),
+    ("quant", 7, _capi.E_INVALID),
+    ("router", 0, _capi.E_INVALID),
+    ("policy", 3, _capi.E_INVALID),
+    ("max_tokens", 0, _capi.E_INVALID),
+    ("num_experts", 2000, _capi.E_UNSUPPORTED),
+    ("router_w", None, _capi.E_INVALID),
+])
+def test_invalid_descriptors(tiny_int4, field, value, status):
+    d, keep = _desc_from(tiny_int4, **{field: value})
+    st, msg = _create_status(d)
+    assert st == status, msg
+    assert msg
+
+
+def test_null_arguments():
+    L = epq.lib()
+    h = ctypes.c_void_p()
+    assert L.strata_moe_create(None, ctypes.byref(h)) == _capi.E_INVALID
+    assert L.strata_moe_forward(None, None, 1, None, None, None) == _capi.E_INVALID
+    s = _capi.CacheStats()
+    assert L.strata_expert_cache_stats(None, ctypes.byref(s)) == _capi.E_INVALID
+    L.strata_moe_destroy(None)  # ignored
+
+
+def test_int4_requires_biases_and_mxfp4_refuses_them(tiny_int4, tiny_fp4):
+    d, keep = _desc_from(tiny_int4)
+    d.gate = _capi.QMat(d.gate.codes, d.gate.scales, None)
+    assert _create_status(d)[0] == _capi.E_INVALID
+    d, keep = _desc_from(tiny_fp4)
+    d.up = _capi.QMat(d.up.codes, d.up.scales, d.up.codes)
+    assert _create_status(d)[0] == _capi.E_INVALID
+
+
+def test_shared_weights_must_match_num_shared(tiny_fp4):
+    d, keep = _desc_from(tiny_fp4, num_shared=0)
+    assert _create_status(d)[0] == _capi.E_INVALID
+
+
+@pytest.mark.parametrize("bad", [0, 255])
+@pytest.mark.parametrize("which", ["gate", "down", "sh_up"])
+def test_e8m0_admission_refuses_0_and_255(tiny_fp4, bad, which):
+    lw = tiny_fp4
+    m = getattr(lw, which)
+    saved = m.scales.copy()
+    try:
+        m.scales.reshape(-1)[m.scales.size // 2] = bad
+        d, keep = _desc_from(lw)
+        st, msg = _create_status(d)
+        assert st == _capi.E_BAD_SCALE, msg
+        assert "E8M0" in msg
+    finally:
+        m.scales[...] = saved
+
+
+def test_int4_scales_must_be_exact_in_fp16(tiny_int4):
+    lw = tiny_int4
+    saved = lw.up.scales.copy()
+    try:
+        lw.up.scales.reshape(-1)[3] = 0x0081  # bf16 ~1.2e-38: no exact fp16 value
+        d, keep = _desc_from(lw)
+        st, msg = _create_status(d)
+        assert st == _capi.E_UNSUPPORTED and "fp16" in msg
+    finally:
+        lw.up.scales[...] = saved
+
+
+# ----------------------------------------------------------------------------
+# residency manager (C++) through the dry-run planner vs. the residency model
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("policy", [LRU, LFU])
+def test_residency_replay_matches_model(policy):
+    rng = np.random.default_rng(21)
+    for trial in range(40):
+        E = int(rng.integers(2, 64))
+        B = int(rng.integers(1, E + 1))
+        trace = []
+        for _ in range(int(rng.integers(1, 40))):
+            n = int(rng.integers(1, E + 1))
+            # Zipf-ish popularity so hits and waves both occur
+            p = 1.0 / np.arange(1, E + 1) ** 1.1
+            p = p[rng.permutation(E)]
+            trace.append(rng.choice(E, size=n, replace=False, p=p / p.sum()).tolist())
+        m = ResidencyModel(E, B, policy, expert_bytes=1000)
+        want_slots = []
+        for n in trace:
+            for wave in m.forward(n):
+                want_slots += [s for (_, s, _) in wave]
+        got = epq.replay_residency(E, B, trace, policy=policy, expert_bytes=1000, want_slots=True)
+        st = m.stats()
+        for k in ("forwards", "hits", "misses", "evictions", "bytes_h2d", "waves", "resident",
+                  "resident_bytes"):
+            assert got[k] == st[k], (trial, k)
+        assert got["slots"].tolist() == want_slots
+
+
+def test_residency_replay_rejects_bad_arguments():
+    with pytest.raises(epq.StrataError):
+        epq.replay_residency(4, 0, [[0]])
+    with pytest.raises(epq.StrataError):
+        epq.replay_residency(4, 2, [[7]])
