@@ -1,0 +1,258 @@
+"""Benchmark of the routed 4-bit MoE FFN layer on one MI355X.
+
+One step = the layer's work for a prompt and its first generated token: one
+prefill forward over the configuration's prompt length followed by one decode
+forward of a single token, as configured (expert budget, LRU paging from the
+pinned host store).  Inputs are synthetic and already resident in HBM when the
+timed region starts.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import faulthandler
+import gc
+import json
+import os
+import statistics
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s (decode B=1, prefill 1180) + expert-weight HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_30b_a3b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
+    return ap.parse_args()
+
+
+def flops_gate_up(cfg, rows):
+    return 2.0 * rows * cfg.hidden * 2 * cfg.ffn
+
+
+def flops_down(cfg, rows):
+    return 2.0 * rows * cfg.ffn * cfg.hidden
+
+
+def w1_bytes(cfg):
+    """Packed gate+up bytes of one expert."""
+    H, F = cfg.hidden, cfg.ffn
+    per = (H * F // 2 + 4 * F * (H // 64)) if cfg.quant == "int4_g64" else (H * F // 2 + F * (H // 32))
+    return 2 * per
+
+
+def w2_bytes(cfg):
+    return cfg.expert_bytes() - w1_bytes(cfg)
+
+
+def main():
+    args = parse()
+    if args.cpu_baseline_only:
+        from synth import CONFIGS, make_layer
+        cfg = CONFIGS[args.workload]
+        print(json.dumps(cpu_baseline(make_layer(cfg), cfg, args.cpu_steps)), flush=True)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer is not "
+              "sharded in this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import expert_paged_quantized_amd as epq
+    from synth import CONFIGS, make_layer, make_tokens
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    cfg = CONFIGS[args.workload]
+    Tp, Td = cfg.prefill_T, 1
+    K, W = args.steps, args.warmup
+    log(f"[bench] {cfg.name}: generating weights")
+    t0 = time.time()
+    lw = make_layer(cfg)
+    log(f"[bench] generated in {time.time() - t0:.1f}s; creating layers")
+    paged = epq.MoELayer.from_weights(lw, budget=cfg.budget, max_tokens=Tp)
+    resident = epq.MoELayer.from_weights(lw, budget=cfg.num_experts, max_tokens=Tp)
+
+    n = W + K
+    xs_p = [torch.from_numpy(make_tokens(cfg, Tp, step=2 * i).view(np.int16)).view(torch.bfloat16).to(dev)
+            for i in range(n)]
+    xs_d = [torch.from_numpy(make_tokens(cfg, Td, step=2 * i + 1).view(np.int16)).view(torch.bfloat16).to(dev)
+            for i in range(n)]
+    y_p = torch.empty((Tp, cfg.hidden), dtype=torch.bfloat16, device=dev)
+    y_d = torch.empty((Td, cfg.hidden), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def run(layer, i):
+        layer.forward(xs_p[i], y=y_p)
+        layer.forward(xs_d[i], y=y_d)
+
+    def timed_region(layer, events=False, per_step_sync=True):
+        for i in range(W):
+            run(layer, i)
+        torch.cuda.synchronize()
+        layer.set_timing(events)
+        layer.timing()  # reset
+        per = []
+        torch.cuda.synchronize()
+        t_all = time.perf_counter()
+        for i in range(W, n):
+            a = time.perf_counter()
+            run(layer, i)
+            if per_step_sync:
+                torch.cuda.synchronize()
+                per.append(time.perf_counter() - a)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t_all
+        tm = layer.timing()
+        layer.set_timing(False)
+        return dt, per, tm
+
+    # (1) headline: as configured, no instrumentation
+    log("[bench] timed region: as configured")
+    dt, per, _ = timed_region(paged)
+    # (2) the same inputs with HIP events around every kernel (kernel durations)
+    log("[bench] timed region: kernel events")
+    dt_ev, _, tm = timed_region(paged, events=True)
+    # (3) all experts resident: the GPU path alone
+    log("[bench] timed region: all resident")
+    dt_r, _, _ = timed_region(resident, per_step_sync=False)
+    _, per_r, tm_r = timed_region(resident, events=True)
+    st = paged.stats()
+
+    rows = Tp * cfg.top_k + cfg.num_shared * Tp
+    up_ms, up_n = tm["prefill_gate_up"]
+    dn_ms, dn_n = tm["prefill_down"]
+    up_fl = flops_gate_up(cfg, rows) * K
+    dn_fl = flops_down(cfg, rows) * K
+    mfma_dtype = "f16" if cfg.quant == "int4_g64" else "bf16"
+    peak = MFMA_PEAK_TFLOPS[mfma_dtype]
+    ach = up_fl / (up_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": "moe_prefill_kernel (gate+up, SwiGLU epilogue)",
+            "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+            "traffic": None, "launches": int(up_n), "avg_launch_us": round(up_ms / max(up_n, 1) * 1e3, 2),
+            "algorithmic_flops_per_step": flops_gate_up(cfg, rows)}
+
+    # decode kernels, cold MALL: all-resident layer, 1 GiB scratch written between forwards
+    log("[bench] decode cold-cache pass")
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    resident.set_timing(True)
+    resident.timing()
+    dec_bytes = 0
+    n_dec = 0
+    for i in range(W, n):
+        flush.fill_(float(i))
+        _, dbg = resident.forward(xs_d[i], y=y_d, dbg=True)
+        torch.cuda.synchronize()
+        dec_bytes += int((dbg["counts"] > 0).sum().item()) * cfg.expert_bytes() + cfg.num_shared * cfg.expert_bytes()
+        n_dec += 1
+    tmd = resident.timing()
+    resident.set_timing(False)
+    del flush
+    dec_ms = tmd["decode_gate_up"][0] + tmd["decode_down"][0]
+    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+    decode_roof = {"bound": "hbm", "kernel": "moe_decode_kernel (gate+up and down)",
+                   "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                   "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                   "expert_bytes_per_forward": dec_bytes / n_dec,
+                   "kernel_us_per_forward": round(dec_ms / n_dec * 1e3, 2), "mall": "cold (1 GiB written between forwards)"}
+
+    # pinned host -> device rate on this machine (the paging link), measured by the library
+    h2d_gbps = epq.measure_h2d(0, 256 << 20, 3)
+
+    tokens_per_step = Tp + Td
+    value = K * tokens_per_step / dt
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(dt / K * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": mfma_dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: one MoE FFN layer, H={cfg.hidden} F={cfg.ffn} "
+                               f"E={cfg.num_experts} top-{cfg.top_k} shared={cfg.num_shared} "
+                               f"{cfg.quant} {cfg.router} router"
+                               + (f" Zipf({cfg.zipf_s}) bias" if cfg.zipf_s else "")
+                               + f"; budget {cfg.budget}/{cfg.num_experts} slots, LRU; "
+                               f"step = prefill {Tp} tokens + decode {Td} token",
+                   "prefill_T": Tp, "decode_T": Td, "budget": cfg.budget,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "decode_roofline": decode_roof,
+        "step_ms_median": round(statistics.median(per) * 1e3, 3),
+        "step_ms_range": [round(min(per) * 1e3, 3), round(max(per) * 1e3, 3)],
+        "all_resident": {"value": round(K * tokens_per_step / dt_r, 1),
+                         "step_ms_median": round(statistics.median(per_r) * 1e3, 4),
+                         "kernel_ms_per_step": {k: round(v[0] / K, 4) for k, v in tm_r.items()}},
+        "kernel_ms_per_step": {k: round(v[0] / K, 4) for k, v in tm.items()},
+        "events_pass_ms_per_step": round(dt_ev / K * 1e3, 4),
+        "cache": st, "h2d_GBps": round(h2d_gbps, 2),
+        "gpu": {"name": props.name, "cus": props.multi_processor_count},
+    }
+
+    paged.close()
+    resident.close()
+    if not args.no_cpu_baseline:
+        # the oracle runs in a process of its own (no GPU runtime there)
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-only",
+                            "--workload", args.workload, "--cpu-steps", str(args.cpu_steps)],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"cpu baseline failed: {r.stderr[-2000:]}")
+        res["cpu_baseline"] = json.loads(r.stdout.strip().splitlines()[-1])
+    # release every GPU object while the runtime is fully up, so that nothing
+    # device-side is left for the interpreter's exit-time collection
+    del xs_p, xs_d, y_p, y_d, dbg, lw
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(lw, cfg, n_steps):
+    """The CPU oracle, untouched, timed on a bounded sample of the same workload:
+    the first `n_steps` steps (prefill + one decode token each) of the inputs."""
+    import threadpoolctl
+
+    from oracle import moe as om
+    from synth import make_tokens
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    with threadpoolctl.threadpool_limits(limits=cores):
+        xs = [(make_tokens(cfg, cfg.prefill_T, step=2 * i), make_tokens(cfg, 1, step=2 * i + 1))
+              for i in range(n_steps)]
+        log(f"[bench] cpu baseline: oracle on {n_steps} steps, {cores} threads")
+        a = time.perf_counter()
+        for xp, xd in xs:
+            om.moe_forward(lw, xp)
+            om.moe_forward(lw, xd)
+        dt = time.perf_counter() - a
+    tok = n_steps * (cfg.prefill_T + 1)
+    return {"value": round(tok / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_steps} whole steps (prefill {cfg.prefill_T} + decode 1 token each) of the "
+                      f"same inputs; {dt:.1f} s; fp64 oracle, dequantising per forward"}
+
+
+if __name__ == "__main__":
+    faulthandler.enable()
+    main()
+    gc.collect()
+    gc.freeze()

@@ -13,7 +13,7 @@ import numpy as np
 from . import _capi
 from ._capi import StrataError, check, lib
 
-__all__ = ["MoELayer", "StrataError", "replay_residency", "lib"]
+__all__ = ["MoELayer", "StrataError", "measure_h2d", "replay_residency", "lib"]
 
 _QUANT = {"int4_g64": _capi.Q_INT4_G64, "mxfp4_g32": _capi.Q_MXFP4_G32}
 _ROUTER = {"softmax": _capi.R_SOFTMAX, "sigmoid": _capi.R_SIGMOID}
@@ -137,6 +137,13 @@ class MoELayer:
             self.close()
         except Exception:
             pass
+
+
+def measure_h2d(device=-1, nbytes=256 << 20, iters=3) -> float:
+    """Pinned host -> device copy rate in GB/s (the paging link)."""
+    g = ctypes.c_double()
+    check(lib().strata_measure_h2d(device, nbytes, iters, ctypes.byref(g)))
+    return g.value
 
 
 def replay_residency(num_experts, budget, trace, policy="lru", expert_bytes=0, want_slots=False):

@@ -746,6 +746,44 @@ void strata_moe_destroy(strata_moe* h) { release(h); }
 
 const char* strata_last_error(void) { return g_err.c_str(); }
 
+strata_status strata_measure_h2d(int32_t device, uint64_t bytes, int32_t iters, double* gbps) {
+  if (!gbps || bytes == 0 || iters < 1) return fail(STRATA_E_INVALID, "bad arguments");
+  *gbps = 0.0;
+  if (device < 0) HIP_CHECK(hipGetDevice(&device));
+  HIP_CHECK(hipSetDevice(device));
+  void* hbuf = nullptr;
+  void* dbuf = nullptr;
+  strata_status st = host_alloc(&hbuf, bytes);
+  if (st) return st;
+  if (hipMalloc(&dbuf, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipHostFree(hbuf);
+    return fail(STRATA_E_NOMEM, "hipMalloc failed");
+  }
+  memset(hbuf, 1, bytes);
+  hipStream_t s = nullptr;
+  hipEvent_t a = nullptr, b = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreate(&a);
+  if (e == hipSuccess) e = hipEventCreate(&b);
+  if (e == hipSuccess) e = hipMemcpyAsync(dbuf, hbuf, bytes, hipMemcpyHostToDevice, s);  // warm
+  if (e == hipSuccess) e = hipEventRecord(a, s);
+  for (int i = 0; i < iters && e == hipSuccess; ++i)
+    e = hipMemcpyAsync(dbuf, hbuf, bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  if (e == hipSuccess) e = hipEventSynchronize(b);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+  if (a) (void)hipEventDestroy(a);
+  if (b) (void)hipEventDestroy(b);
+  if (s) (void)hipStreamDestroy(s);
+  (void)hipFree(dbuf);
+  (void)hipHostFree(hbuf);
+  if (e != hipSuccess) return fail(STRATA_E_HIP, std::string("h2d probe: ") + hipGetErrorString(e));
+  *gbps = double(bytes) * iters / (ms * 1e-3) / 1e9;
+  return STRATA_OK;
+}
+
 strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32_t policy,
                                       uint64_t expert_bytes, int32_t n_forwards,
                                       const int32_t* needed_len, const int32_t* needed_flat,

@@ -222,6 +222,12 @@ void strata_moe_destroy(strata_moe* h);
  * library; valid until the next call on this thread. */
 const char* strata_last_error(void);
 
+/* Measures the pinned host -> device copy rate of the paging link: allocates
+ * `bytes` of pinned host memory and of device memory on `device`, times `iters`
+ * hipMemcpyAsync copies with HIP events, frees both and writes GB/s (1e9 B/s).
+ * Errors: E_INVALID (bytes == 0, iters < 1, NULL out), E_NOMEM, E_HIP. */
+strata_status strata_measure_h2d(int32_t device, uint64_t bytes, int32_t iters, double* gbps);
+
 /* Dry-run planner (host only, touches no GPU): replays the residency policy of
  * a layer with E experts and `budget` slots over a trace of forwards and
  * reports what a real run would page, the placement-plan side of the budget

@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(strata_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(strata_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
