@@ -12,8 +12,6 @@ timed region starts.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import faulthandler
-import gc
 import json
 import os
 import statistics
@@ -219,12 +217,6 @@ def main():
         if r.returncode != 0:
             raise RuntimeError(f"cpu baseline failed: {r.stderr[-2000:]}")
         res["cpu_baseline"] = json.loads(r.stdout.strip().splitlines()[-1])
-    # release every GPU object while the runtime is fully up, so that nothing
-    # device-side is left for the interpreter's exit-time collection
-    del xs_p, xs_d, y_p, y_d, dbg, lw
-    gc.collect()
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
 
@@ -252,7 +244,4 @@ def cpu_baseline(lw, cfg, n_steps):
 
 
 if __name__ == "__main__":
-    faulthandler.enable()
     main()
-    gc.collect()
-    gc.freeze()

@@ -205,10 +205,8 @@ typedef enum {
 } strata_kernel_class;
 
 typedef struct {
-  double ms[STRATA_K_COUNT];        /* summed event time per class        */
-  uint64_t launches[STRATA_K_COUNT];
-  uint64_t rows[STRATA_K_COUNT];    /* real token rows through the class  */
-  uint64_t weight_bytes[STRATA_K_COUNT]; /* packed expert bytes the class streams */
+  double ms[STRATA_K_COUNT];         /* summed event time per class */
+  uint64_t launches[STRATA_K_COUNT]; /* launches per class          */
 } strata_timing;
 
 strata_status strata_moe_set_timing(strata_moe* h, int32_t enable);

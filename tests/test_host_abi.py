@@ -184,3 +184,31 @@ def test_residency_replay_rejects_bad_arguments():
         epq.replay_residency(4, 0, [[0]])
     with pytest.raises(epq.StrataError):
         epq.replay_residency(4, 2, [[7]])
+
+
+def test_ctypes_mirrors_match_the_c_struct_sizes(tmp_path):
+    """Compiles the header with gcc and compares sizeof/offsetof of every struct
+    the binding passes by pointer with the ctypes declarations."""
+    import shutil
+    import subprocess
+    if not shutil.which("gcc"):
+        pytest.skip("gcc missing")
+    structs = {"strata_moe_desc": _capi.Desc, "strata_qmat": _capi.QMat,
+               "strata_route_dbg": _capi.RouteDbg, "strata_cache_stats": _capi.CacheStats,
+               "strata_memory_info": _capi.MemoryInfo, "strata_timing": _capi.Timing}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname}.{fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("return 0;}")
+    src = tmp_path / "sizes.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "sizes"
+    subprocess.run(["gcc", "-o", str(exe), str(src)], check=True)
+    out = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.split("\n") if l)
+    for cname, py in structs.items():
+        assert int(out[cname]) == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert int(out[f"{cname}.{fname}"]) == getattr(py, fname).offset, (cname, fname)
