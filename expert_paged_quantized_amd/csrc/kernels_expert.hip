@@ -21,9 +21,9 @@
 //
 // int4 group-64 affine weights are decoded to fp16 (w = s*q + b, one fp16
 // rounding; s and b are admitted only if exact in fp16) and the activations
-// are converted bf16 -> fp16 (exact in range).  MXFP4 weights are decoded to
-// bf16 with the gfx950 scaled FP4 conversion (exact: an E2M1 value times a
-// power of two).  Accumulation is fp32 throughout; nothing uses float atomics,
+// arrive as fp16 (the router kernel writes that copy of x; exact in range).
+// MXFP4 weights are decoded to bf16 with the gfx950 scaled FP4 conversion
+// (exact: an E2M1 value times a power of two).  Accumulation is fp32 throughout; nothing uses float atomics,
 // so every expert's result depends only on its own rows and weights.
 #include "moe_common.h"
 
@@ -42,51 +42,86 @@ __device__ __forceinline__ To bitcast(const From& f) {
   return __builtin_bit_cast(To, f);
 }
 
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Loads through global-address-space pointers: the expert records are reached
+// through a pointer table, and a generic (flat) load would also count against
+// the LDS wait counter, serialising weight prefetches with LDS reads.
+typedef const __attribute__((address_space(1))) u32x4 g_u32x4;
+typedef const __attribute__((address_space(1))) uint32_t g_u32;
+typedef const __attribute__((address_space(1))) uint8_t g_u8;
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(g_u32x4*)(p); }
+__device__ __forceinline__ uint32_t ld4(const void* p) { return *(g_u32*)(p); }
+__device__ __forceinline__ uint32_t ld1(const void* p) { return *(g_u8*)(p); }
 
-// --- decode of one 16-byte code chunk into four MFMA A operands ------------
-// int4: the prepack stores each 32-bit word's nibbles as k0 k2 k4 k6 k1 k3 k5 k7
-// (low to high), so (w >> 4j) & 0x000F000F holds the pair (k_2j, k_2j+1) in the
-// two fp16 halves; OR-ing 0x6400 makes them 1024 + q exactly; subtracting 1024
-// gives q, and one fp16 fma gives s*q + b.
-__device__ __forceinline__ void dequant_int4(const u32x4& c, uint32_t sb, u32x4 (&a)[4]) {
-  const _Float16 s = (_Float16)__uint_as_float(sb << 16);
-  const _Float16 b = (_Float16)__uint_as_float(sb & 0xffff0000u);
-  const f16x2 s2 = {s, s}, b2 = {b, b};
+// (a & b) | c in one instruction (the compiler splits it when b, c are literals)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+// One MFMA step (8 inputs) of a decoded int4 chunk: word `st` of the 16-byte
+// chunk.  Nibble n of the word holds input k0 k2 k4 k6 k1 k3 k5 k7 (n = 0..7),
+// so the low nibbles of bytes 0 and 2 are (k0, k1) and their high nibbles
+// (k2, k3); after a shift by 8 the same masks give (k4, k5) and (k6, k7).  A
+// low nibble OR 0x6400 is the fp16 1024 + q, a high nibble (bits 4..7) OR
+// 0x5400 is the fp16 64 + q; subtracting 1024 or 64 gives q exactly and one
+// fp16 fma gives s*q + b.
+__device__ __forceinline__ u32x4 dequant_int4_step(uint32_t w, f16x2 s2, f16x2 b2) {
+  const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, mag_lo = 0x64006400u, mag_hi = 0x54005400u;
   const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const uint32_t w = c[st];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t v = ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-      f16x2 h = bitcast<f16x2>(v) - k1024;
-      h = __builtin_elementwise_fma(h, s2, b2);
-      a[st][j] = bitcast<uint32_t>(h);
+  const f16x2 k64 = {(_Float16)64.0f, (_Float16)64.0f};
+  const uint32_t w8 = w >> 8;
+  const f16x2 h0 = bitcast<f16x2>(and_or(w, m_lo, mag_lo)) - k1024;
+  const f16x2 h1 = bitcast<f16x2>(and_or(w, m_hi, mag_hi)) - k64;
+  const f16x2 h2 = bitcast<f16x2>(and_or(w8, m_lo, mag_lo)) - k1024;
+  const f16x2 h3 = bitcast<f16x2>(and_or(w8, m_hi, mag_hi)) - k64;
+  u32x4 a;
+  a[0] = bitcast<uint32_t>(__builtin_elementwise_fma(h0, s2, b2));
+  a[1] = bitcast<uint32_t>(__builtin_elementwise_fma(h1, s2, b2));
+  a[2] = bitcast<uint32_t>(__builtin_elementwise_fma(h2, s2, b2));
+  a[3] = bitcast<uint32_t>(__builtin_elementwise_fma(h3, s2, b2));
+  return a;
+}
+
+__device__ __forceinline__ u32x4 dequant_fp4_step(uint32_t w, float scale) {
+  u32x4 a;
+  a[0] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  a[1] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  a[2] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  a[3] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return a;
+}
+
+// Per-chunk decode parameters: fp16 (scale, bias) pairs for int4, the fp32
+// power of two for MXFP4.
+template <int QF>
+struct ChunkScale {
+  f16x2 s2, b2;
+  float scale;
+  __device__ __forceinline__ explicit ChunkScale(uint32_t sc) {
+    if constexpr (QF == Q_INT4) {
+      const _Float16 s = (_Float16)__uint_as_float(sc << 16);
+      const _Float16 b = (_Float16)__uint_as_float(sc & 0xffff0000u);
+      s2 = f16x2{s, s};
+      b2 = f16x2{b, b};
+      scale = 0.0f;
+    } else {
+      scale = __uint_as_float(sc << 23);
     }
   }
-}
-
-// MXFP4: byte i of a word holds elements 2i (low nibble) and 2i+1; the scale
-// is the E8M0 exponent as an fp32 power of two.
-__device__ __forceinline__ void dequant_fp4(const u32x4& c, uint32_t e8m0, u32x4 (&a)[4]) {
-  const float scale = __uint_as_float(e8m0 << 23);
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const uint32_t w = c[st];
-    a[st][0] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-    a[st][1] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-    a[st][2] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-    a[st][3] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  __device__ __forceinline__ u32x4 step(uint32_t w) const {
+    if constexpr (QF == Q_INT4)
+      return dequant_int4_step(w, s2, b2);
+    else
+      return dequant_fp4_step(w, scale);
   }
-}
+};
 
 template <int QF>
 __device__ __forceinline__ void dequant(const u32x4& c, uint32_t sc, u32x4 (&a)[4]) {
-  if constexpr (QF == Q_INT4)
-    dequant_int4(c, sc, a);
-  else
-    dequant_fp4(c, sc, a);
+  const ChunkScale<QF> cs(sc);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) a[st] = cs.step(c[st]);
 }
 
 template <int QF>
@@ -105,23 +140,11 @@ struct ScaleLayout {
   __device__ static int lane_off(int lane) { return (QF == Q_INT4) ? (lane & 31) * 4 : lane; }
   __device__ static uint32_t load(const uint8_t* p) {
     if constexpr (QF == Q_INT4)
-      return *reinterpret_cast<const uint32_t*>(p);
+      return ld4(p);
     else
-      return *p;
+      return ld1(p);
   }
 };
-
-// bf16x8 -> f16x8 (exact for |x| in the fp16 normal range)
-__device__ __forceinline__ u32x4 bf16_to_f16_8(const u32x4& v) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2 h = {(_Float16)__uint_as_float(v[i] << 16),
-                     (_Float16)__uint_as_float(v[i] & 0xffff0000u)};
-    r[i] = bitcast<uint32_t>(h);
-  }
-  return r;
-}
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -150,7 +173,6 @@ constexpr int kDecWaves = 8;
 template <int QF, bool GATE_UP>
 __global__ __launch_bounds__(512) void moe_decode_kernel(GemmArgs p) {
   using SL = ScaleLayout<QF>;
-  constexpr bool kCvt = (QF == Q_INT4) && GATE_UP;
   __shared__ float red[kDecWaves][kDecodeMaxT][32];
   const int nrt = p.N >> 5;
   const int tile_i = blockIdx.x / nrt, rt = blockIdx.x % nrt;
@@ -200,8 +222,7 @@ __global__ __launch_bounds__(512) void moe_decode_kernel(GemmArgs p) {
         dequant<QF>(wq[u], ws[u], a);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          const u32x4 b = kCvt ? bf16_to_f16_8(xa[u][st]) : xa[u][st];
-          acc = mfma<QF>(a[st], b, acc);
+          acc = mfma<QF>(a[st], xa[u][st], acc);
         }
       }
     }
@@ -238,158 +259,208 @@ __global__ __launch_bounds__(512) void moe_decode_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill kernel: persistent workgroups of 4 waves.  A work item is (tile of up
-// to 128 token rows of one expert, block of 8 weight row-tiles = 256 outputs).
-// Wave w owns row tiles 2w, 2w+1 of the block and all 128 tokens (4 column
-// tiles, skipped beyond the tile's rows).  Per K-block of 64 inputs the
-// workgroup stages the 128 x 64 activation tile in LDS (double buffered,
-// 16-byte chunks XOR-swizzled by row) while each wave decodes its weight
-// chunks straight from global memory into MFMA operands.
+// Prefill kernel: persistent workgroups of 4 waves, two per CU.  A work item is
+// (tile of up to 128 token rows of one expert, block of 8 weight row-tiles =
+// 256 outputs).  Wave w owns row tiles 2w, 2w+1 of the block (64 outputs) and
+// all of the tile's tokens (NCT column tiles of 32, a template parameter so the
+// K loop has no branches).  Per K-block of 64 inputs the workgroup stages
+// the activation tile in LDS (two buffers, rows padded to 144 bytes) while
+// each wave decodes its weight chunks straight from global memory into MFMA
+// operands.  Software pipeline: weights and activations are loaded two
+// K-blocks ahead into register rings; activations are written to the other
+// LDS buffer one K-block ahead.  Loads never branch: padding rows read a valid
+// row of the tile and row tiles past N re-read the last row tile; those
+// results are computed and not stored.
 // ---------------------------------------------------------------------------
 constexpr int kPreThreads = 256;
 constexpr int kPreRowTilesPerWave = 2;
 constexpr int kPreRowTilesPerItem = 8;
+// LDS row: 64 16-bit inputs (32 u32) padded to 36 u32 (144 B), so 16
+// consecutive rows start in 16 different 16-byte bank groups and both the
+// staging writes (one row per lane) and the MFMA operand reads (one row per
+// lane) are free of bank conflicts.
+constexpr int kRowU32 = 36;
+
+template <int QF, bool GATE_UP, int NCT>
+__device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, int nb,
+                                             uint32_t (*lds)[kPrefillTM * kRowU32]) {
+  using SL = ScaleLayout<QF>;
+  constexpr int RTW = kPreRowTilesPerWave;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nrt = p.N >> 5;
+  const int KB = p.K >> 6;
+  // staging: 8 consecutive lanes read one 128-byte activation row, so each
+  // load instruction covers 32 whole rows; chunk sc of rows q*32 + sr0
+  const int sc = threadIdx.x & 7, sr0 = threadIdx.x >> 3;
+  const int rt0 = nb * kPreRowTilesPerItem + wave * RTW;
+
+  // staging sources: rows past the tile's end re-read its first row
+  const uint16_t* s_src[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = q * 32 + sr0;
+    const int srow = (r < t.nrows) ? r : 0;
+    const int64_t gr = p.gather ? p.gather[t.row_begin + srow] : (t.row_begin + srow);
+    s_src[q] = reinterpret_cast<const uint16_t*>(p.act) + gr * p.K + sc * 8;
+  }
+
+  const uint8_t* rec = p.slot_ptr[t.slot];
+  const uint8_t* codes[RTW];
+  const uint8_t* scs[RTW];
+#pragma unroll
+  for (int r = 0; r < RTW; ++r) {
+    const int rtl = min(rt0 + r, nrt - 1);
+    codes[r] = rec + p.off_codes + (int64_t)rtl * KB * kTileCodeBytes + lane * 16;
+    scs[r] = rec + p.off_scales + (int64_t)rtl * KB * SL::kTileBytes + SL::lane_off(lane);
+  }
+
+  f32x16 acc[RTW][NCT];
+#pragma unroll
+  for (int a = 0; a < RTW; ++a)
+#pragma unroll
+    for (int b = 0; b < NCT; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+  u32x4 sv0[4], sv1[4];              // activation chunks of two K-blocks in flight
+  u32x4 wq0[RTW], wq1[RTW];          // weight ring: even / odd K-blocks
+  uint32_t ws0[RTW], ws1[RTW];
+
+  auto stage_load = [&](u32x4(&sv)[4], int kb) {
+    kb = min(kb, KB - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sv[q] = ld16(s_src[q] + kb * 64);
+  };
+  auto stage_store = [&](const u32x4(&sv)[4], int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<u32x4*>(&lds[buf][(q * 32 + sr0) * kRowU32 + sc * 4]) = sv[q];
+  };
+  auto w_load = [&](u32x4(&wq)[RTW], uint32_t(&ws)[RTW], int kb) {
+    kb = min(kb, KB - 1);
+#pragma unroll
+    for (int r = 0; r < RTW; ++r) {
+      wq[r] = ld16(codes[r] + (int64_t)kb * kTileCodeBytes);
+      ws[r] = SL::load(scs[r] + (int64_t)kb * SL::kTileBytes);
+    }
+  };
+  auto step = [&](int buf, const u32x4(&wq)[RTW], const uint32_t(&ws)[RTW]) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int c = 4 * (lane >> 5) + st;
+      u32x4 b[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int mrow = ct * 32 + (lane & 31);
+        b[ct] = *reinterpret_cast<const u32x4*>(&lds[buf][mrow * kRowU32 + c * 4]);
+      }
+#pragma unroll
+      for (int r = 0; r < RTW; ++r) {
+        const u32x4 a = ChunkScale<QF>(ws[r]).step(wq[r][st]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[r][ct] = mfma<QF>(a, b[ct], acc[r][ct]);
+      }
+    }
+  };
+
+  // prologue: activation 0 in LDS; activations 1, 2 and weights 0, 1 in flight
+  stage_load(sv0, 0);
+  stage_load(sv1, 1);
+  w_load(wq0, ws0, 0);
+  w_load(wq1, ws1, 1);
+  stage_store(sv0, 0);
+  stage_load(sv0, 2);
+  __syncthreads();
+
+  // step kb: store activation kb+1 into the other LDS buffer, load activation
+  // kb+3 into the freed registers and weights kb+2, compute K-block kb
+  auto even_step = [&](int kb) {  // LDS buffer 0, weight set 0
+    stage_store(sv1, 1);
+    stage_load(sv1, kb + 3);
+    u32x4 wq[RTW];
+    uint32_t ws[RTW];
+#pragma unroll
+    for (int r = 0; r < RTW; ++r) {
+      wq[r] = wq0[r];
+      ws[r] = ws0[r];
+    }
+    w_load(wq0, ws0, kb + 2);
+    step(0, wq, ws);
+    __syncthreads();
+  };
+  auto odd_step = [&](int kb) {  // LDS buffer 1, weight set 1
+    stage_store(sv0, 0);
+    stage_load(sv0, kb + 3);
+    u32x4 wq[RTW];
+    uint32_t ws[RTW];
+#pragma unroll
+    for (int r = 0; r < RTW; ++r) {
+      wq[r] = wq1[r];
+      ws[r] = ws1[r];
+    }
+    w_load(wq1, ws1, kb + 2);
+    step(1, wq, ws);
+    __syncthreads();
+  };
+  int kb = 0;
+  for (; kb + 1 < KB; kb += 2) {
+    even_step(kb);
+    odd_step(kb + 1);
+  }
+  if (kb < KB) even_step(kb);
+
+  // epilogue
+#pragma unroll
+  for (int r = 0; r < RTW; ++r) {
+    const int rt = rt0 + r;
+    if (rt >= nrt) continue;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int mm = ct * 32 + (lane & 31);
+      if (mm >= t.nrows) continue;
+      const int64_t row = t.row_begin + mm;
+      if constexpr (GATE_UP) {
+        uint16_t* h = reinterpret_cast<uint16_t*>(p.out) + row * p.out_ld + rt * 16;
+#pragma unroll
+        for (int g4 = 0; g4 < 2; ++g4) {
+          uint16_t v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = g4 * 4 + q;
+            v[q] = to_h_elem<QF>(silu(acc[r][ct][i]) * acc[r][ct][i + 8]);
+          }
+          const uint2 pk = {(uint32_t)v[0] | ((uint32_t)v[1] << 16),
+                            (uint32_t)v[2] | ((uint32_t)v[3] << 16)};
+          *reinterpret_cast<uint2*>(h + g4 * 8 + (lane >> 5) * 4) = pk;
+        }
+      } else {
+        float* o = reinterpret_cast<float*>(p.out) + row * p.out_ld + rt * 32;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 v = {acc[r][ct][g4 * 4 + 0], acc[r][ct][g4 * 4 + 1], acc[r][ct][g4 * 4 + 2],
+                            acc[r][ct][g4 * 4 + 3]};
+          *reinterpret_cast<float4*>(o + g4 * 8 + (lane >> 5) * 4) = v;
+        }
+      }
+    }
+  }
+}
 
 template <int QF, bool GATE_UP>
 __global__ __launch_bounds__(kPreThreads, 2) void moe_prefill_kernel(GemmArgs p) {
-  using SL = ScaleLayout<QF>;
-  constexpr bool kCvt = (QF == Q_INT4) && GATE_UP;
-  constexpr int kRowU32 = kTileK / 2;  // 64 16-bit elements = 32 u32 per LDS row
   __shared__ __attribute__((aligned(16))) uint32_t lds[2][kPrefillTM * kRowU32];
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nrt = p.N >> 5;
   const int n_nb = (nrt + kPreRowTilesPerItem - 1) / kPreRowTilesPerItem;
   const int n_tiles = p.n_tiles_dev ? p.n_tiles_dev[0] : p.n_tiles;
   const int n_items = n_tiles * n_nb;
-  const int KB = p.K >> 6;
-  const int sr = threadIdx.x >> 1, sh = threadIdx.x & 1;  // staging row / half
-
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const Tile t = p.tiles[item / n_nb];
     const int nb = item % n_nb;
-    const int n_ct = (t.nrows + 31) >> 5;
-    const int rtA = nb * kPreRowTilesPerItem + wave * kPreRowTilesPerWave;
-    const bool okA = rtA < nrt, okB = rtA + 1 < nrt;
-
-    const bool s_valid = sr < t.nrows;
-    int64_t s_row = 0;
-    if (s_valid) s_row = p.gather ? p.gather[t.row_begin + sr] : (t.row_begin + sr);
-    const uint16_t* s_src = reinterpret_cast<const uint16_t*>(p.act) + s_row * p.K + sh * 32;
-
-    const uint8_t* rec = p.slot_ptr[t.slot];
-    const uint8_t* codesA = rec + p.off_codes + (int64_t)rtA * KB * kTileCodeBytes + lane * 16;
-    const uint8_t* codesB = codesA + (int64_t)KB * kTileCodeBytes;
-    const uint8_t* scA = rec + p.off_scales + (int64_t)rtA * KB * SL::kTileBytes + SL::lane_off(lane);
-    const uint8_t* scB = scA + (int64_t)KB * SL::kTileBytes;
-
-    f32x16 acc[2][4];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-
-    u32x4 sv[4];
-    auto stage_load = [&](int kb) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (s_valid) v = ld16(s_src + kb * 64 + q * 8);
-        sv[q] = v;
-      }
-    };
-    auto stage_store = [&](int buf) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = sh * 4 + q;
-        const int pc = c ^ (sr & 7);
-        const u32x4 v = kCvt ? bf16_to_f16_8(sv[q]) : sv[q];
-        *reinterpret_cast<u32x4*>(&lds[buf][sr * kRowU32 + pc * 4]) = v;
-      }
-    };
-    u32x4 wA = {0u, 0u, 0u, 0u}, wB = {0u, 0u, 0u, 0u};
-    uint32_t sA = 0, sB = 0;
-    auto w_load = [&](int kb) {
-      if (okA) {
-        wA = ld16(codesA + (int64_t)kb * kTileCodeBytes);
-        sA = SL::load(scA + (int64_t)kb * SL::kTileBytes);
-      }
-      if (okB) {
-        wB = ld16(codesB + (int64_t)kb * kTileCodeBytes);
-        sB = SL::load(scB + (int64_t)kb * SL::kTileBytes);
-      }
-    };
-
-    stage_load(0);
-    w_load(0);
-    stage_store(0);
-    __syncthreads();
-
-    for (int kb = 0; kb < KB; ++kb) {
-      const int cur = kb & 1;
-      u32x4 aA[4], aB[4];
-      if (okA) dequant<QF>(wA, sA, aA);
-      if (okB) dequant<QF>(wB, sB, aB);
-      if (kb + 1 < KB) {
-        stage_load(kb + 1);
-        w_load(kb + 1);
-      }
-      if (okA) {
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          if (ct < n_ct) {
-            const int mrow = ct * 32 + (lane & 31);
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-              const int c = 4 * (lane >> 5) + st;
-              const u32x4 b =
-                  *reinterpret_cast<const u32x4*>(&lds[cur][mrow * kRowU32 + ((c ^ (mrow & 7)) * 4)]);
-              acc[0][ct] = mfma<QF>(aA[st], b, acc[0][ct]);
-              if (okB) acc[1][ct] = mfma<QF>(aB[st], b, acc[1][ct]);
-            }
-          }
-        }
-      }
-      if (kb + 1 < KB) stage_store(cur ^ 1);
-      __syncthreads();
-    }
-
-    // epilogue
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      const int rt = rtA + which;
-      if (rt >= nrt) continue;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int mm = ct * 32 + (lane & 31);
-        if (ct >= n_ct || mm >= t.nrows) continue;
-        const int64_t row = t.row_begin + mm;
-        if constexpr (GATE_UP) {
-          uint16_t* h = reinterpret_cast<uint16_t*>(p.out) + row * p.out_ld + rt * 16;
-#pragma unroll
-          for (int g4 = 0; g4 < 2; ++g4) {
-            uint16_t v[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int i = g4 * 4 + q;
-              v[q] = to_h_elem<QF>(silu(acc[which][ct][i]) * acc[which][ct][i + 8]);
-            }
-            const uint2 pk = {(uint32_t)v[0] | ((uint32_t)v[1] << 16),
-                              (uint32_t)v[2] | ((uint32_t)v[3] << 16)};
-            *reinterpret_cast<uint2*>(h + g4 * 8 + (lane >> 5) * 4) = pk;
-          }
-        } else {
-          float* o = reinterpret_cast<float*>(p.out) + row * p.out_ld + rt * 32;
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const float4 v = {acc[which][ct][g4 * 4 + 0], acc[which][ct][g4 * 4 + 1],
-                              acc[which][ct][g4 * 4 + 2], acc[which][ct][g4 * 4 + 3]};
-            *reinterpret_cast<float4*>(o + g4 * 8 + (lane >> 5) * 4) = v;
-          }
-        }
-      }
+    switch ((t.nrows + 31) >> 5) {
+      case 1: prefill_item<QF, GATE_UP, 1>(p, t, nb, lds); break;
+      case 2: prefill_item<QF, GATE_UP, 2>(p, t, nb, lds); break;
+      case 3: prefill_item<QF, GATE_UP, 3>(p, t, nb, lds); break;
+      default: prefill_item<QF, GATE_UP, 4>(p, t, nb, lds); break;
     }
     __syncthreads();
   }

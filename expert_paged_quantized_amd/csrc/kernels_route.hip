@@ -19,7 +19,9 @@ namespace strata {
 // from +0; the 64 lane partials are then folded with offsets 32, 16, 8, 4, 2,
 // 1 (p[L] += p[L + o]) and lane 0 holds the logit; the bias is added last.
 // That order is part of the layer's definition so that the top-k decision is
-// reproducible bit for bit.
+// reproducible bit for bit.  When x16 is given (int4 layers, whose expert
+// GEMMs run in fp16) the waves of the first expert block also write the fp16
+// copy of their token rows (bf16 -> fp16 is exact in the fp16 range).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -28,7 +30,8 @@ template <int TT, int TE>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ wr,
                                                             const float* __restrict__ bias,
-                                                            float* __restrict__ logits, int T, int E,
+                                                            float* __restrict__ logits,
+                                                            uint16_t* __restrict__ x16, int T, int E,
                                                             int H) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -53,6 +56,22 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     for (int b = 0; b < TE; ++b) {
       const int e = min(e0 + b, E - 1);
       wv[b] = *reinterpret_cast<const uint4*>(wr + (size_t)e * H + off);
+    }
+    if (x16 && e0 == 0) {
+#pragma unroll
+      for (int a = 0; a < TT; ++a) {
+        if (t0 + a < T) {
+          uint4 hv;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t w = (&xv[a].x)[q];
+            const _Float16 lo = (_Float16)bf16_lo(w), hi = (_Float16)bf16_hi(w);
+            (&hv.x)[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          }
+          *reinterpret_cast<uint4*>(x16 + (size_t)(t0 + a) * H + off) = hv;
+        }
+      }
     }
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
@@ -282,6 +301,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
       tl.slot = tid;
       tl.row_begin = o + i * tile_rows;
       tl.nrows = min(tile_rows, c - i * tile_rows);
+      tl.group_first = to;
+      tl.group_count = nt;
       tiles[to + i] = tl;
     }
   }
@@ -292,6 +313,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     tl.slot = shared_slot;
     tl.row_begin = TK + i * tile_rows;
     tl.nrows = min(tile_rows, T - i * tile_rows);
+    tl.group_first = ntot;
+    tl.group_count = nsh;
     tiles[ntot + i] = tl;
   }
   if (tid == 0) {
@@ -304,13 +327,13 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
-                         int T, int E, int H, hipStream_t s) {
+                         uint16_t* x16, int T, int E, int H, hipStream_t s) {
   if (T <= 8) {
     const int waves = T * E;
-    router_logits_kernel<1, 1><<<(waves + 3) / 4, 256, 0, s>>>(x, wr, bias, logits, T, E, H);
+    router_logits_kernel<1, 1><<<(waves + 3) / 4, 256, 0, s>>>(x, wr, bias, logits, x16, T, E, H);
   } else {
     const int waves = ((T + 3) / 4) * ((E + 3) / 4);
-    router_logits_kernel<4, 4><<<(waves + 3) / 4, 256, 0, s>>>(x, wr, bias, logits, T, E, H);
+    router_logits_kernel<4, 4><<<(waves + 3) / 4, 256, 0, s>>>(x, wr, bias, logits, x16, T, E, H);
   }
   return hipGetLastError();
 }

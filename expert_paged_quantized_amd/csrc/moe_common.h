@@ -19,12 +19,15 @@ constexpr int kTileCodeBytes = 1024;
 
 // One unit of grouped-GEMM work: up to kPrefillTM (prefill) or all (decode)
 // rows [row_begin, row_begin + nrows) of the permuted row space, all routed to
-// `expert`, whose packed record lives at slot_ptr[slot].
+// `expert`, whose packed record lives at slot_ptr[slot].  The tiles of one
+// expert are consecutive in a list: [group_first, group_first + group_count).
 struct Tile {
   int32_t expert;
   int32_t slot;
   int32_t row_begin;
   int32_t nrows;
+  int32_t group_first;
+  int32_t group_count;
 };
 
 // Byte offsets of the regions of one prepacked expert record.

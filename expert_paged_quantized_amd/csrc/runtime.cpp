@@ -30,8 +30,8 @@
 #include "residency.h"
 
 namespace strata {
-hipError_t launch_router(const uint16_t*, const uint16_t*, const float*, float*, int, int, int,
-                         hipStream_t);
+hipError_t launch_router(const uint16_t*, const uint16_t*, const float*, float*, uint16_t*, int, int,
+                         int, hipStream_t);
 hipError_t launch_topk(const float*, int, int, int, int, int32_t*, float*, hipStream_t);
 hipError_t launch_permute(const int32_t*, int, int, int, int, int, int, int32_t*, int32_t*,
                           int32_t*, int32_t*, Tile*, int32_t*, unsigned long long*, hipStream_t);
@@ -100,6 +100,7 @@ struct strata_moe {
   unsigned long long* d_distinct = nullptr;
   void* d_h = nullptr;
   float* d_o = nullptr;
+  uint16_t* d_x16 = nullptr;  // fp16 copy of x (int4 layers)
   uint64_t ws_bytes = 0;
 
   int32_t* h_counts = nullptr;  // pinned
@@ -320,7 +321,8 @@ static void release(strata_moe* h) {
   if (h->copy_stream) (void)hipStreamDestroy(h->copy_stream);
   void* dev[] = {h->d_pool, h->d_shared, h->d_router_w, h->d_router_bias, h->d_slot_ptr,
                  h->d_logits, h->d_idx, h->d_w, h->d_counts, h->d_offsets, h->d_perm, h->d_pos,
-                 h->d_tiles_dev, h->d_tiles_host, h->d_ntiles, h->d_distinct, h->d_h, h->d_o};
+                 h->d_tiles_dev, h->d_tiles_host, h->d_ntiles, h->d_distinct, h->d_h, h->d_o,
+                 h->d_x16};
   for (void* p : dev)
     if (p) (void)hipFree(p);
   if (h->host_store) (void)hipHostFree(h->host_store);
@@ -427,6 +429,7 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
       (st = walloc(&h->d_distinct, 64)) || (st = walloc(&h->d_h, h->max_rows * h->F * 2)) ||
       (st = walloc(&h->d_o, h->max_rows * h->H * 4)))
     return st;
+  if (int4 && (st = walloc(&h->d_x16, T * h->H * 2))) return st;
   h->ws_bytes = ws;
   HIP_CHECK(hipMemset(h->d_distinct, 0, 64));
   if ((st = host_alloc(&h->h_counts, size_t(h->E) * 4))) return st;
@@ -475,7 +478,7 @@ static hipError_t timed(strata_moe* h, int cls, hipStream_t s, Fn&& fn) {
 static GemmArgs gemm_args(strata_moe* h, bool gate_up, const void* x, const Tile* tiles,
                           const int32_t* n_dev, int n_tiles) {
   GemmArgs a;
-  a.act = gate_up ? x : h->d_h;
+  a.act = gate_up ? (h->d_x16 ? (const void*)h->d_x16 : x) : h->d_h;
   a.gather = gate_up ? h->d_perm : nullptr;
   a.tiles = tiles;
   a.n_tiles_dev = n_dev;
@@ -490,7 +493,8 @@ static GemmArgs gemm_args(strata_moe* h, bool gate_up, const void* x, const Tile
   return a;
 }
 
-static int prefill_grid(int items) { return std::max(1, std::min(items, 2048)); }
+// Persistent prefill grid: at most two workgroups per CU.
+static int prefill_grid(int items) { return std::max(1, std::min(items, 512)); }
 
 // Runs gate+up then down over a tile range.  n_dev != nullptr: the count lives
 // on the device and `n_tiles` is only an upper bound.
@@ -517,12 +521,15 @@ static hipError_t run_experts(strata_moe* h, const void* x, const Tile* tiles, c
 static void add_tiles(strata_moe* h, int expert, int slot, int row_begin, int count, bool decode,
                       int& n) {
   const int tr = decode ? count : kPrefillTM;
+  const int first = n, nt = (count + tr - 1) / tr;
   for (int r = 0; r < count; r += tr) {
     Tile t;
     t.expert = expert;
     t.slot = slot;
     t.row_begin = row_begin + r;
     t.nrows = std::min(tr, count - r);
+    t.group_first = first;
+    t.group_count = nt;
     h->h_tiles[n++] = t;
   }
 }
@@ -534,7 +541,8 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
   if (h->fwd_recorded) HIP_CHECK(hipStreamWaitEvent(s, h->ev_fwd_done, 0));
 
   HIP_CHECK(timed(h, STRATA_K_ROUTER, s, [&]() {
-    return launch_router((const uint16_t*)x, h->d_router_w, h->d_router_bias, h->d_logits, T, h->E, h->H, s);
+    return launch_router((const uint16_t*)x, h->d_router_w, h->d_router_bias, h->d_logits, h->d_x16, T,
+                         h->E, h->H, s);
   }));
   HIP_CHECK(timed(h, STRATA_K_TOPK, s, [&]() {
     return launch_topk(h->d_logits, T, h->E, h->k, h->router, h->d_idx, h->d_w, s);
@@ -578,6 +586,11 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
       pe[w] = n;
     }
     if ((size_t)n > h->max_tiles) return fail(STRATA_E_HIP, "tile list overflow");
+    // group indices are relative to the first tile of each launch's range
+    for (int w = 0; w < nw; ++w) {
+      for (int i = hb[w]; i < he[w]; ++i) h->h_tiles[i].group_first -= hb[w];
+      for (int i = he[w]; i < pe[w]; ++i) h->h_tiles[i].group_first -= he[w];
+    }
     HIP_CHECK(hipMemcpyAsync(h->d_tiles_host, h->h_tiles, size_t(n) * sizeof(Tile), hipMemcpyHostToDevice, s));
     while ((int)h->ev_copied.size() < nw) {
       hipEvent_t a, b;
