@@ -25,6 +25,8 @@
 // MXFP4 weights are decoded to bf16 with the gfx950 scaled FP4 conversion
 // (exact: an E2M1 value times a power of two).  Accumulation is fp32 throughout; nothing uses float atomics,
 // so every expert's result depends only on its own rows and weights.
+#include <type_traits>
+
 #include "moe_common.h"
 
 namespace strata {
@@ -281,7 +283,7 @@ constexpr int kPreRowTilesPerItem = 8;
 // lane) are free of bank conflicts.
 constexpr int kRowU32 = 36;
 
-template <int QF, bool GATE_UP, int NCT>
+template <int QF, bool GATE_UP, int NCT, int WD>
 __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, int nb,
                                              uint32_t (*lds)[kPrefillTM * kRowU32]) {
   using SL = ScaleLayout<QF>;
@@ -290,14 +292,15 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
   const int nrt = p.N >> 5;
   const int KB = p.K >> 6;
   // staging: 8 consecutive lanes read one 128-byte activation row, so each
-  // load instruction covers 32 whole rows; chunk sc of rows q*32 + sr0
+  // load instruction covers 32 whole rows; chunk sc of rows q*32 + sr0, only
+  // for the NCT*32 rows the tile uses
   const int sc = threadIdx.x & 7, sr0 = threadIdx.x >> 3;
   const int rt0 = nb * kPreRowTilesPerItem + wave * RTW;
 
   // staging sources: rows past the tile's end re-read its first row
-  const uint16_t* s_src[4];
+  const uint16_t* s_src[NCT];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NCT; ++q) {
     const int r = q * 32 + sr0;
     const int srow = (r < t.nrows) ? r : 0;
     const int64_t gr = p.gather ? p.gather[t.row_begin + srow] : (t.row_begin + srow);
@@ -322,29 +325,29 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-  u32x4 sv0[4], sv1[4];              // activation chunks of two K-blocks in flight
-  u32x4 wq0[RTW], wq1[RTW];          // weight ring: even / odd K-blocks
-  uint32_t ws0[RTW], ws1[RTW];
+  u32x4 sv[2][NCT];        // activation chunks of two K-blocks in flight
+  u32x4 wq[WD][RTW];       // weight ring: K-block kb lives in slot kb % WD
+  uint32_t ws[WD][RTW];
 
-  auto stage_load = [&](u32x4(&sv)[4], int kb) {
+  auto stage_load = [&](u32x4(&v)[NCT], int kb) {
     kb = min(kb, KB - 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sv[q] = ld16(s_src[q] + kb * 64);
+    for (int q = 0; q < NCT; ++q) v[q] = ld16(s_src[q] + kb * 64);
   };
-  auto stage_store = [&](const u32x4(&sv)[4], int buf) {
+  auto stage_store = [&](const u32x4(&v)[NCT], int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<u32x4*>(&lds[buf][(q * 32 + sr0) * kRowU32 + sc * 4]) = sv[q];
+    for (int q = 0; q < NCT; ++q)
+      *reinterpret_cast<u32x4*>(&lds[buf][(q * 32 + sr0) * kRowU32 + sc * 4]) = v[q];
   };
-  auto w_load = [&](u32x4(&wq)[RTW], uint32_t(&ws)[RTW], int kb) {
+  auto w_load = [&](u32x4(&q4)[RTW], uint32_t(&s4)[RTW], int kb) {
     kb = min(kb, KB - 1);
 #pragma unroll
     for (int r = 0; r < RTW; ++r) {
-      wq[r] = ld16(codes[r] + (int64_t)kb * kTileCodeBytes);
-      ws[r] = SL::load(scs[r] + (int64_t)kb * SL::kTileBytes);
+      q4[r] = ld16(codes[r] + (int64_t)kb * kTileCodeBytes);
+      s4[r] = SL::load(scs[r] + (int64_t)kb * SL::kTileBytes);
     }
   };
-  auto step = [&](int buf, const u32x4(&wq)[RTW], const uint32_t(&ws)[RTW]) {
+  auto compute = [&](int buf, const u32x4(&q4)[RTW], const uint32_t(&s4)[RTW]) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int c = 4 * (lane >> 5) + st;
@@ -356,58 +359,57 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
       }
 #pragma unroll
       for (int r = 0; r < RTW; ++r) {
-        const u32x4 a = ChunkScale<QF>(ws[r]).step(wq[r][st]);
+        const u32x4 a = ChunkScale<QF>(s4[r]).step(q4[r][st]);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) acc[r][ct] = mfma<QF>(a, b[ct], acc[r][ct]);
       }
     }
   };
+  // One K-block: store activation kb+1 into the other LDS buffer, load
+  // activation kb+3 into the freed registers and weights kb+WD into the freed
+  // ring slot, compute K-block kb.  D = kb % WD and the buffer parity are
+  // compile-time, so every register index is static.
+  auto one_step = [&](int kb, auto dc) {
+    constexpr int D = decltype(dc)::value;
+    constexpr int BUF = D & 1;
+    stage_store(sv[BUF ^ 1], BUF ^ 1);
+    stage_load(sv[BUF ^ 1], kb + 3);
+    u32x4 q4[RTW];
+    uint32_t s4[RTW];
+#pragma unroll
+    for (int r = 0; r < RTW; ++r) {
+      q4[r] = wq[D][r];
+      s4[r] = ws[D][r];
+    }
+    w_load(wq[D], ws[D], kb + WD);
+    compute(BUF, q4, s4);
+    __syncthreads();
+  };
 
-  // prologue: activation 0 in LDS; activations 1, 2 and weights 0, 1 in flight
-  stage_load(sv0, 0);
-  stage_load(sv1, 1);
-  w_load(wq0, ws0, 0);
-  w_load(wq1, ws1, 1);
-  stage_store(sv0, 0);
-  stage_load(sv0, 2);
+  // prologue: activation 0 in LDS, activations 1 and 2 and weights 0..WD-1 in flight
+  stage_load(sv[0], 0);
+  stage_load(sv[1], 1);
+#pragma unroll
+  for (int d = 0; d < WD; ++d) w_load(wq[d], ws[d], d);
+  stage_store(sv[0], 0);
+  stage_load(sv[0], 2);
   __syncthreads();
 
-  // step kb: store activation kb+1 into the other LDS buffer, load activation
-  // kb+3 into the freed registers and weights kb+2, compute K-block kb
-  auto even_step = [&](int kb) {  // LDS buffer 0, weight set 0
-    stage_store(sv1, 1);
-    stage_load(sv1, kb + 3);
-    u32x4 wq[RTW];
-    uint32_t ws[RTW];
-#pragma unroll
-    for (int r = 0; r < RTW; ++r) {
-      wq[r] = wq0[r];
-      ws[r] = ws0[r];
-    }
-    w_load(wq0, ws0, kb + 2);
-    step(0, wq, ws);
-    __syncthreads();
-  };
-  auto odd_step = [&](int kb) {  // LDS buffer 1, weight set 1
-    stage_store(sv0, 0);
-    stage_load(sv0, kb + 3);
-    u32x4 wq[RTW];
-    uint32_t ws[RTW];
-#pragma unroll
-    for (int r = 0; r < RTW; ++r) {
-      wq[r] = wq1[r];
-      ws[r] = ws1[r];
-    }
-    w_load(wq1, ws1, kb + 2);
-    step(1, wq, ws);
-    __syncthreads();
-  };
   int kb = 0;
-  for (; kb + 1 < KB; kb += 2) {
-    even_step(kb);
-    odd_step(kb + 1);
+  for (; kb + WD <= KB; kb += WD) {
+    one_step(kb + 0, std::integral_constant<int, 0>{});
+    one_step(kb + 1, std::integral_constant<int, 1>{});
+    if constexpr (WD == 4) {
+      one_step(kb + 2, std::integral_constant<int, 2>{});
+      one_step(kb + 3, std::integral_constant<int, 3>{});
+    }
   }
-  if (kb < KB) even_step(kb);
+  // tail (KB not a multiple of WD): slots 0.. hold K-blocks kb..
+  if (kb + 0 < KB) one_step(kb + 0, std::integral_constant<int, 0>{});
+  if (kb + 1 < KB) one_step(kb + 1, std::integral_constant<int, 1>{});
+  if constexpr (WD == 4) {
+    if (kb + 2 < KB) one_step(kb + 2, std::integral_constant<int, 2>{});
+  }
 
   // epilogue
 #pragma unroll
@@ -457,10 +459,10 @@ __global__ __launch_bounds__(kPreThreads, 2) void moe_prefill_kernel(GemmArgs p)
     const Tile t = p.tiles[item / n_nb];
     const int nb = item % n_nb;
     switch ((t.nrows + 31) >> 5) {
-      case 1: prefill_item<QF, GATE_UP, 1>(p, t, nb, lds); break;
-      case 2: prefill_item<QF, GATE_UP, 2>(p, t, nb, lds); break;
-      case 3: prefill_item<QF, GATE_UP, 3>(p, t, nb, lds); break;
-      default: prefill_item<QF, GATE_UP, 4>(p, t, nb, lds); break;
+      case 1: prefill_item<QF, GATE_UP, 1, 4>(p, t, nb, lds); break;
+      case 2: prefill_item<QF, GATE_UP, 2, 4>(p, t, nb, lds); break;
+      case 3: prefill_item<QF, GATE_UP, 3, 2>(p, t, nb, lds); break;
+      default: prefill_item<QF, GATE_UP, 4, 2>(p, t, nb, lds); break;
     }
     __syncthreads();
   }
