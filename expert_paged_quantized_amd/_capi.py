@@ -13,7 +13,7 @@ STATUS_NAMES = ["OK", "E_INVALID", "E_UNSUPPORTED", "E_BAD_SCALE", "E_NOMEM", "E
 Q_INT4_G64, Q_MXFP4_G32 = 1, 2
 R_SOFTMAX, R_SIGMOID = 1, 2
 P_LRU, P_LFU = 1, 2
-KERNEL_CLASSES = ["router", "topk", "permute", "decode_gate_up", "decode_down", "prefill_gate_up",
+KERNEL_CLASSES = ["router", "group", "decode_gate_up", "decode_down", "prefill_gate_up",
                   "prefill_down", "combine"]
 
 
@@ -54,7 +54,7 @@ class MemoryInfo(ctypes.Structure):
 
 
 class Timing(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 8), ("launches", c_u64 * 8)]
+    _fields_ = [("ms", ctypes.c_double * 7), ("launches", c_u64 * 7)]
 
 
 EXPORTS = {

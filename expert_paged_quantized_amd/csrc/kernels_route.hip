@@ -1,6 +1,7 @@
 // Routing kernels of the MoE layer for gfx950: router logits in one fixed fp32
 // summation order, top-k selection with routing weights, and the grouping of
-// tokens by expert (counts, offsets, permutation, inverse positions, tile list).
+// tokens by expert (counts, offsets, permutation, inverse positions, tile list)
+// in two multi-block passes.
 //
 // The routing semantics (top-k, softmax or sigmoid renormalised over the
 // selected experts) come from the checkpoint and are never altered (ro99/strata
@@ -25,6 +26,23 @@ namespace strata {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// p[L] += p[L + o] for o = 32, 16 (cross-row lane permutes) then 8, 4, 2, 1
+// (DPP row shifts inside 16-lane rows); lane 0 ends with the canonical sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_shl(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf,
+                                                               0xf, true));
+}
+__device__ __forceinline__ float fold_to_lane0(float p) {
+  p = p + __shfl_down(p, 32, 64);
+  p = p + __shfl_down(p, 16, 64);
+  p = p + dpp_row_shl<0x108>(p);
+  p = p + dpp_row_shl<0x104>(p);
+  p = p + dpp_row_shl<0x102>(p);
+  p = p + dpp_row_shl<0x101>(p);
+  return p;
+}
 
 template <int TT, int TE>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
@@ -89,12 +107,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     }
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
+  for (int a = 0; a < TT; ++a)
 #pragma unroll
-    for (int a = 0; a < TT; ++a)
-#pragma unroll
-      for (int b = 0; b < TE; ++b) acc[a][b] = acc[a][b] + __shfl_down(acc[a][b], o, 64);
-  }
+    for (int b = 0; b < TE; ++b) acc[a][b] = fold_to_lane0(acc[a][b]);
   if (lane == 0) {
 #pragma unroll
     for (int a = 0; a < TT; ++a)
@@ -106,89 +121,216 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
-// ---------------------------------------------------------------------------
-// Top-k + routing weights: one wave per token.  Selection is by (logit
-// descending, expert id ascending) with IEEE comparison, so -0 and +0 tie.
-// Weights: softmax over the selected logits, exp(l_j - l_0) / sum, or
-// sigmoid(l_j) / sum of the selected sigmoids; the sum runs j = 0..k-1.
-// ---------------------------------------------------------------------------
-constexpr int kTopkMaxPerLane = 16;  // E <= 1024
 
+// ---------------------------------------------------------------------------
+// Router logits for many tokens: one wave computes an 8 x 8 block (64 logits).
+// Each lane accumulates its inputs exactly as above; the 64 lane partials of
+// every logit are then transposed through LDS so that lane j holds the 64
+// partials of logit j and folds them in registers with the same pairing
+// (q[i] += q[i + o] for o = 32..1), which costs 63 adds per lane for all 64
+// logits instead of 64 cross-lane folds.
+// ---------------------------------------------------------------------------
+constexpr int kRbTT = 8, kRbTE = 8, kRbPitch = 68;
+
+__global__ __launch_bounds__(256) void router_block_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr,
+                                                          const float* __restrict__ bias,
+                                                          float* __restrict__ logits,
+                                                          uint16_t* __restrict__ x16, int T, int E,
+                                                          int H) {
+  __shared__ __attribute__((aligned(16))) float red[4][64 * kRbPitch];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wave = blockIdx.x * 4 + w;
+  const int neb = (E + kRbTE - 1) / kRbTE;
+  const int t0 = (wave / neb) * kRbTT, e0 = (wave % neb) * kRbTE;
+  const bool active = t0 < T;
+  float acc[kRbTT][kRbTE];
+#pragma unroll
+  for (int a = 0; a < kRbTT; ++a)
+#pragma unroll
+    for (int b = 0; b < kRbTE; ++b) acc[a][b] = 0.0f;
+  const int C = H >> 9;
+  for (int c = 0; c < C && active; ++c) {
+    const int off = (c * 64 + lane) * 8;
+    uint4 xv[kRbTT], wv[kRbTE];
+#pragma unroll
+    for (int a = 0; a < kRbTT; ++a)
+      xv[a] = *reinterpret_cast<const uint4*>(x + (size_t)min(t0 + a, T - 1) * H + off);
+#pragma unroll
+    for (int b = 0; b < kRbTE; ++b)
+      wv[b] = *reinterpret_cast<const uint4*>(wr + (size_t)min(e0 + b, E - 1) * H + off);
+    if (x16 && e0 == 0) {
+#pragma unroll
+      for (int a = 0; a < kRbTT; ++a) {
+        if (t0 + a < T) {
+          uint4 hv;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t wd = (&xv[a].x)[q];
+            const _Float16 lo = (_Float16)bf16_lo(wd), hi = (_Float16)bf16_hi(wd);
+            (&hv.x)[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          }
+          *reinterpret_cast<uint4*>(x16 + (size_t)(t0 + a) * H + off) = hv;
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      float xf[kRbTT];
+#pragma unroll
+      for (int a = 0; a < kRbTT; ++a) {
+        const uint32_t xw = (&xv[a].x)[v >> 1];
+        xf[a] = (v & 1) ? bf16_hi(xw) : bf16_lo(xw);
+      }
+#pragma unroll
+      for (int b = 0; b < kRbTE; ++b) {
+        const uint32_t ww = (&wv[b].x)[v >> 1];
+        const float wf = (v & 1) ? bf16_hi(ww) : bf16_lo(ww);
+#pragma unroll
+        for (int a = 0; a < kRbTT; ++a) acc[a][b] = __builtin_fmaf(xf[a], wf, acc[a][b]);
+      }
+    }
+  }
+  // transpose: partial of logit j = a*8 + b from lane L goes to red[j][L]
+  float* rw = red[w];
+#pragma unroll
+  for (int a = 0; a < kRbTT; ++a)
+#pragma unroll
+    for (int b = 0; b < kRbTE; ++b) rw[(a * kRbTE + b) * kRbPitch + lane] = acc[a][b];
+  __syncthreads();
+  float q[64];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 v = *reinterpret_cast<const float4*>(&rw[lane * kRbPitch + 4 * i]);
+    q[4 * i + 0] = v.x;
+    q[4 * i + 1] = v.y;
+    q[4 * i + 2] = v.z;
+    q[4 * i + 3] = v.w;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+    for (int i = 0; i < o; ++i) q[i] = q[i] + q[i + o];
+  const int t = t0 + lane / kRbTE, e = e0 + lane % kRbTE;
+  if (active && t < T && e < E) logits[(size_t)t * E + e] = bias ? q[0] + bias[e] : q[0];
+}
+
+// ---------------------------------------------------------------------------
+// Top-k + routing weights (one wave per token), and the first half of the
+// grouping by expert.  Selection is by (logit descending, expert id ascending)
+// with IEEE comparison, so -0 and +0 tie.  Weights: softmax over the selected
+// logits, exp(l_j - l_0) / sum, or sigmoid(l_j) / sum of the selected
+// sigmoids; the sum runs j = 0..k-1.  The rank pass takes tokens in blocks of
+// 64: each selected (token, expert) sets the token's bit in a 64-bit LDS mask
+// of that expert; the block writes its per-expert histogram and, for every
+// entry, the number of earlier tokens of the block that chose the same expert
+// (its rank inside the block).  Integer work only: independent of ordering.
+// ---------------------------------------------------------------------------
+constexpr int kPermMaxE = 1024;
+constexpr int kRouteBlock = 64;      // tokens per routing block
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+// keep the better of (v, e) and its partner lane's under the DPP pattern CTRL
+__device__ __forceinline__ void best_of_impl(float& v, int& e, float ov, int oe) {
+  if (ov > v || (ov == v && oe < e)) {
+    v = ov;
+    e = oe;
+  }
+}
+#define best_of(v, e, CTRL)                                                               \
+  best_of_impl(v, e, __builtin_bit_cast(float, dpp_mov<CTRL>(__builtin_bit_cast(int, v))), \
+               dpp_mov<CTRL>(e))
+
+// Lanes r < k end with the r-th selected (logit, expert) of token t.  JPL =
+// logits per lane (E <= 64 * JPL); the per-round scan is branch-free.
+template <int JPL>
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
+                                           int lane, float& my_v, int& my_e) {
+  float vals[JPL];
+#pragma unroll
+  for (int j = 0; j < JPL; ++j) {
+    const int e = lane + 64 * j;
+    const float v = logits[(size_t)t * E + min(e, E - 1)];
+    vals[j] = (e < E) ? v : -INFINITY;
+  }
+  uint32_t taken = 0;
+  my_v = 0.0f;
+  my_e = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < JPL; ++j) {
+      const int e = lane + 64 * j;
+      const bool ok = (e < E) && !((taken >> j) & 1u);
+      const float v = ok ? vals[j] : -INFINITY;
+      const int ee = ok ? e : 0x7fffffff;
+      const bool better = v > bv || (v == bv && ee < be);
+      bv = better ? v : bv;
+      be = better ? ee : be;
+    }
+    // (value desc, id asc) is a strict total order, so any reduction tree
+    // finds the same winner: quad swaps, half-row and row mirrors (DPP) give
+    // every lane its row's best, then the four rows are compared.
+    best_of(bv, be, 0xB1);   // lanes xor 1
+    best_of(bv, be, 0x4E);   // lanes xor 2
+    best_of(bv, be, 0x141);  // half-row mirror
+    best_of(bv, be, 0x140);  // row mirror
+    float cv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 0));
+    int ce = __builtin_amdgcn_readlane(be, 0);
+#pragma unroll
+    for (int row = 1; row < 4; ++row) {
+      const float ov =
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), row * 16));
+      const int oe = __builtin_amdgcn_readlane(be, row * 16);
+      if (ov > cv || (ov == cv && oe < ce)) {
+        cv = ov;
+        ce = oe;
+      }
+    }
+    if ((ce & 63) == lane) taken |= 1u << (ce >> 6);
+    if (lane == r) {
+      my_v = cv;
+      my_e = ce;
+    }
+  }
+}
+
+// Weights of one token from its selected logits (lanes r < k hold pick r).
+__device__ __forceinline__ float topk_weight(float my_v, int k, int router, int lane) {
+  const float v0 = __shfl(my_v, 0, 64);
+  float z = 0.0f;
+  if (lane < k) z = (router == R_SOFTMAX) ? __expf(my_v - v0) : 1.0f / (1.0f + __expf(-my_v));
+  float sum = 0.0f;
+  for (int j = 0; j < k; ++j) sum += __shfl(z, j, 64);
+  return z / sum;
+}
+
+// one wave per token, 4 tokens per workgroup
+template <int JPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int router, int32_t* __restrict__ idx,
                                                    float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  float vals[kTopkMaxPerLane];
-#pragma unroll
-  for (int j = 0; j < kTopkMaxPerLane; ++j) {
-    const int e = lane + 64 * j;
-    vals[j] = (e < E) ? logits[(size_t)t * E + e] : -INFINITY;
-  }
-  uint32_t taken = 0;
-  float my_v = 0.0f;
-  int my_e = 0;
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < kTopkMaxPerLane; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && !((taken >> j) & 1u)) {
-        const float v = vals[j];
-        if (v > bv || (v == bv && e < be)) {
-          bv = v;
-          be = e;
-        }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == r) {
-      my_v = bv;
-      my_e = be;
-    }
-  }
-  const float v0 = __shfl(my_v, 0, 64);
-  float z = 0.0f;
-  if (lane < k) z = (router == R_SOFTMAX) ? __expf(my_v - v0) : 1.0f / (1.0f + __expf(-my_v));
-  float sum = 0.0f;
-  for (int j = 0; j < k; ++j) sum += __shfl(z, j, 64);
+  float my_v;
+  int my_e;
+  topk_token<JPL>(logits, t, E, k, lane, my_v, my_e);
+  const float wt = topk_weight(my_v, k, router, lane);
   if (lane < k) {
     idx[(size_t)t * k + lane] = my_e;
-    w[(size_t)t * k + lane] = z / sum;
+    w[(size_t)t * k + lane] = wt;
   }
 }
 
-// ---------------------------------------------------------------------------
-// Permute: a single 1024-thread workgroup.
-//   counts[e]    LDS histogram of idx (integer atomics: order-free)
-//   offsets      exclusive prefix sum over experts
-//   perm, pos    stable ranks: token t's entry for expert e lands at
-//                offsets[e] + #{t' < t : e in idx[t']}.  Tokens are swept in
-//                chunks of NW*64; in a chunk every wave sets bit `lane` of a
-//                64-bit LDS mask per expert, and the rank is the running count
-//                of earlier chunks + popcounts of earlier waves' masks + the
-//                popcount of lower lanes in the own mask.
-//   shared rows  perm[T*k + t] = t for the shared expert
-//   tiles        per expert ceil(count / tile_rows) tiles in ascending expert
-//                id, then the shared expert's tiles; slot = expert id (this
-//                list serves the all-resident case).
-// ---------------------------------------------------------------------------
-constexpr int kPermThreads = 1024;
-constexpr int kPermMaxE = 1024;
-constexpr int kPermMaskWords = 4096;  // NW * E <= 4096 64-bit masks (32 KB)
-
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
+// exclusive scan over up to 1024 values held one per thread of a 1024-thread
+// workgroup; returns the thread's prefix and the total
+__device__ __forceinline__ int block_scan1024(int v, int* wave_tot, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int inc = v;
 #pragma unroll
@@ -198,116 +340,51 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& t
   }
   if (lane == 63) wave_tot[wave] = inc;
   __syncthreads();
-  if (wave == 0) {
-    const int nw = kPermThreads / 64;
-    int s = (lane < nw) ? wave_tot[lane] : 0;
-    int si = s;
+  int wbase = 0, tot = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int n = __shfl_up(si, o, 64);
-      if (lane >= o) si += n;
-    }
-    if (lane < nw) wave_tot[lane] = si - s;  // exclusive per wave
-    if (lane == nw - 1) wave_tot[nw] = si;   // grand total
+  for (int w2 = 0; w2 < 16; ++w2) {
+    const int x = wave_tot[w2];
+    if (w2 < wave) wbase += x;
+    tot += x;
   }
+  total = tot;
   __syncthreads();
-  const int r = inc - v + wave_tot[wave];
-  total = wave_tot[kPermThreads / 64];
-  __syncthreads();
-  return r;
+  return wbase + inc - v;
 }
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const int32_t* __restrict__ idx, int T, int k, int E, int S, int tile_rows, int shared_slot,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ pos, Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
-    unsigned long long* __restrict__ distinct_total) {
-  __shared__ int cnt[kPermMaxE];
-  __shared__ int off[kPermMaxE + 1];
-  __shared__ int run[kPermMaxE];
-  __shared__ int toff[kPermMaxE + 1];
-  __shared__ int wave_tot[kPermThreads / 64 + 1];
-  __shared__ unsigned long long masks[kPermMaskWords];
-  __shared__ int n_distinct;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < E) {
-    cnt[tid] = 0;
-    run[tid] = 0;
-  }
-  if (tid == 0) n_distinct = 0;
-  __syncthreads();
-  const int TK = T * k;
-  for (int i = tid; i < TK; i += kPermThreads) atomicAdd(&cnt[idx[i]], 1);
-  __syncthreads();
-  const int c = (tid < E) ? cnt[tid] : 0;
-  int total;
-  const int o = block_exclusive_scan(c, wave_tot, total);
-  const int nt = (c > 0) ? (c + tile_rows - 1) / tile_rows : 0;
+// Writes counts, offsets, the tile list (ascending expert, then the shared
+// expert) and the distinct-expert counter from per-expert totals held one per
+// thread of a 1024-thread workgroup (E <= 1024).
+__device__ __forceinline__ void emit_counts_and_tiles(int c, int o, int total, int T, int k, int E,
+                                                      int S, int tile_rows, int shared_slot,
+                                                      int* wave_tot, int32_t* counts,
+                                                      int32_t* offsets, Tile* tiles,
+                                                      int32_t* n_tiles,
+                                                      unsigned long long* distinct_total) {
+  const int e = threadIdx.x;
+  const bool used = e < E && c > 0;
+  const int nt = used ? (c + tile_rows - 1) / tile_rows : 0;
   int ntot;
-  const int to = block_exclusive_scan(nt, wave_tot, ntot);
-  if (tid < E) {
-    off[tid] = o;
-    toff[tid] = to;
-    counts[tid] = c;
-    offsets[tid] = o;
-    if (c > 0) atomicAdd(&n_distinct, 1);
-  }
-  if (tid == 0) {
-    off[E] = total;
-    toff[E] = ntot;
-    offsets[E] = total;
-  }
-  __syncthreads();
-
-  // stable ranks
-  int nw = kPermMaskWords / E;
-  nw = nw < 1 ? 1 : (nw > kPermThreads / 64 ? kPermThreads / 64 : nw);
-  for (int base = 0; base < T; base += nw * 64) {
-    for (int i = tid; i < nw * E; i += kPermThreads) masks[i] = 0ull;
-    __syncthreads();
-    const int t = base + wave * 64 + lane;
-    const bool act = wave < nw && t < T;
-    if (act)
-      for (int j = 0; j < k; ++j) atomicOr(&masks[wave * E + idx[(size_t)t * k + j]], 1ull << lane);
-    __syncthreads();
-    if (act) {
-      const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      for (int j = 0; j < k; ++j) {
-        const int e = idx[(size_t)t * k + j];
-        int r = run[e];
-        for (int w2 = 0; w2 < wave; ++w2) r += __popcll(masks[w2 * E + e]);
-        r += __popcll(masks[wave * E + e] & below);
-        const int p = off[e] + r;
-        perm[p] = t;
-        pos[(size_t)t * k + j] = p;
-      }
-    }
-    __syncthreads();
-    if (tid < E) {
-      int add = 0;
-      for (int w2 = 0; w2 < nw; ++w2) add += __popcll(masks[w2 * E + tid]);
-      run[tid] += add;
-    }
-    __syncthreads();
-  }
-
-  if (S)
-    for (int t = tid; t < T; t += kPermThreads) perm[TK + t] = t;
-
-  if (tid < E && c > 0) {
-    for (int i = 0; i < nt; ++i) {
+  const int to = block_scan1024(nt, wave_tot, ntot);
+  int nd_tot;
+  (void)block_scan1024(used ? 1 : 0, wave_tot, nd_tot);
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = o;
+    for (int j = 0; j < nt; ++j) {
       Tile tl;
-      tl.expert = tid;
-      tl.slot = tid;
-      tl.row_begin = o + i * tile_rows;
-      tl.nrows = min(tile_rows, c - i * tile_rows);
+      tl.expert = e;
+      tl.slot = e;
+      tl.row_begin = o + j * tile_rows;
+      tl.nrows = min(tile_rows, c - j * tile_rows);
       tl.group_first = to;
       tl.group_count = nt;
-      tiles[to + i] = tl;
+      tiles[to + j] = tl;
     }
   }
+  const int TK = T * k;
   const int nsh = S ? (T + tile_rows - 1) / tile_rows : 0;
-  for (int i = tid; i < nsh; i += kPermThreads) {
+  for (int i = e; i < nsh; i += 1024) {
     Tile tl;
     tl.expert = E;
     tl.slot = shared_slot;
@@ -317,10 +394,149 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     tl.group_count = nsh;
     tiles[ntot + i] = tl;
   }
-  if (tid == 0) {
+  if (e == 0) {
+    offsets[E] = total;
     n_tiles[0] = ntot + nsh;
-    distinct_total[0] += (unsigned long long)n_distinct;
+    distinct_total[0] += (unsigned long long)nd_tot;
   }
+}
+
+// Per 64-token block: histogram over experts and each entry's rank inside the
+// block, from 64-bit LDS masks (bit = token of the block).  The last block to
+// finish (an atomic ticket taken after a device-scope fence) turns the
+// histograms into per-block prefixes (entries of e in earlier blocks), writes
+// counts, offsets and the tile list, and resets the ticket.
+__global__ __launch_bounds__(1024) void rank_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                    int S, int tile_rows, int shared_slot,
+                                                    int32_t* __restrict__ rank_in_block,
+                                                    int32_t* __restrict__ hist,
+                                                    unsigned int* __restrict__ ticket,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    Tile* __restrict__ tiles,
+                                                    int32_t* __restrict__ n_tiles,
+                                                    unsigned long long* __restrict__ distinct_total) {
+  __shared__ unsigned long long mask[kPermMaxE];
+  __shared__ int wave_tot[16];
+  __shared__ int last;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) mask[e] = 0ull;
+  __syncthreads();
+  const int tb = blockIdx.x * kRouteBlock;
+  const int n = min(kRouteBlock, T - tb) * k;
+  for (int i = tid; i < n; i += 1024) atomicOr(&mask[idx[(size_t)tb * k + i]], 1ull << (i / k));
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) hist[(size_t)blockIdx.x * E + e] = __popcll(mask[e]);
+  for (int i = tid; i < n; i += 1024) {
+    const int tl = i / k;
+    const unsigned long long below = (tl == 0) ? 0ull : (~0ull >> (64 - tl));
+    rank_in_block[(size_t)tb * k + i] = __popcll(mask[idx[(size_t)tb * k + i]] & below);
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last = (atomicAdd(ticket, 1u) == gridDim.x - 1) ? 1 : 0;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  // last block: per expert, exclusive prefix over blocks (in place); the
+  // permute pass adds the expert's offset
+  const int nb = gridDim.x;
+  int run = 0;
+  if (tid < E) {
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      int h[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) h[u] = (b0 + u < nb) ? hist[(size_t)(b0 + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (b0 + u < nb) hist[(size_t)(b0 + u) * E + tid] = run;
+        run += h[u];
+      }
+    }
+  }
+  int total;
+  const int o = block_scan1024(tid < E ? run : 0, wave_tot, total);
+  emit_counts_and_tiles(run, o, total, T, k, E, S, tile_rows, shared_slot, wave_tot, counts, offsets,
+                        tiles, n_tiles, distinct_total);
+  if (tid == 0) *ticket = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Permute (one 256-thread workgroup per block of 64 tokens): token t's entry
+// for expert e lands at offsets[e] + prefix[block][e] + rank inside the
+// block, i.e. tokens
+// ascending inside each expert segment; pos is the inverse map.  Shared-expert
+// rows are the identity after the routed rows.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict__ idx,
+                                                      const int32_t* __restrict__ rank_in_block,
+                                                      const int32_t* __restrict__ prefix,
+                                                      const int32_t* __restrict__ offsets, int T, int k,
+                                                      int E, int S, int32_t* __restrict__ perm,
+                                                      int32_t* __restrict__ pos) {
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const int tb = b * kRouteBlock;
+  const int n = min(kRouteBlock, T - tb) * k;
+  for (int i = tid; i < n; i += 256) {
+    const size_t q = (size_t)tb * k + i;
+    const int e = idx[q];
+    const int p = offsets[e] + prefix[(size_t)b * E + e] + rank_in_block[q];
+    perm[p] = tb + i / k;
+    pos[q] = p;
+  }
+  if (S)
+    for (int t = tb + tid; t < min(T, tb + kRouteBlock); t += 256) perm[T * k + t] = t;
+}
+
+// ---------------------------------------------------------------------------
+// Whole routing of a small batch (T <= 16) in one 1024-thread workgroup: top-k
+// (wave w takes token w), then the same masks, offsets, permutation and tile
+// list as the multi-block passes.
+// ---------------------------------------------------------------------------
+constexpr int kSmallT = 16;
+
+template <int JPL>
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int router, int S, int tile_rows,
+    int shared_slot, int32_t* __restrict__ idx, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ pos,
+    Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+    unsigned long long* __restrict__ distinct_total) {
+  __shared__ unsigned int mask[kPermMaxE];  // bit = token (T <= 16)
+  __shared__ int off[kPermMaxE];
+  __shared__ int sel[kSmallT * 32];
+  __shared__ int wave_tot[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += 1024) mask[e] = 0u;
+  __syncthreads();
+  if (wave < T) {
+    float my_v;
+    int my_e;
+    topk_token<JPL>(logits, wave, E, k, lane, my_v, my_e);
+    const float wt = topk_weight(my_v, k, router, lane);
+    if (lane < k) {
+      idx[wave * k + lane] = my_e;
+      w[wave * k + lane] = wt;
+      sel[wave * k + lane] = my_e;
+      atomicOr(&mask[my_e], 1u << wave);
+    }
+  }
+  __syncthreads();
+  const int c = (tid < E) ? __popc(mask[tid]) : 0;
+  int total;
+  const int o = block_scan1024(c, wave_tot, total);
+  if (tid < E) off[tid] = o;
+  __syncthreads();
+  const int TK = T * k;
+  for (int i = tid; i < TK; i += 1024) {
+    const int t = i / k, e = sel[i];
+    const int p = off[e] + __popc(mask[e] & ((1u << t) - 1u));
+    perm[p] = t;
+    pos[i] = p;
+  }
+  if (S && tid < T) perm[TK + tid] = tid;
+  emit_counts_and_tiles(c, o, total, T, k, E, S, tile_rows, shared_slot, wave_tot, counts, offsets,
+                        tiles, n_tiles, distinct_total);
 }
 
 // ---------------------------------------------------------------------------
@@ -328,28 +544,56 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 // ---------------------------------------------------------------------------
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
                          uint16_t* x16, int T, int E, int H, hipStream_t s) {
-  if (T <= 8) {
+  // 8 x 8 blocks when they still give the GPU thousands of waves, else one
+  // logit per wave (small T or few experts)
+  const int blocked_waves = ((T + kRbTT - 1) / kRbTT) * ((E + kRbTE - 1) / kRbTE);
+  if (blocked_waves >= 2048) {
+    router_block_kernel<<<(blocked_waves + 3) / 4, 256, 0, s>>>(x, wr, bias, logits, x16, T, E, H);
+  } else {
     const int waves = T * E;
     router_logits_kernel<1, 1><<<(waves + 3) / 4, 256, 0, s>>>(x, wr, bias, logits, x16, T, E, H);
-  } else {
-    const int waves = ((T + 3) / 4) * ((E + 3) / 4);
-    router_logits_kernel<4, 4><<<(waves + 3) / 4, 256, 0, s>>>(x, wr, bias, logits, x16, T, E, H);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, int T, int E, int k, int router, int32_t* idx,
-                       float* w, hipStream_t s) {
-  topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, router, idx, w);
-  return hipGetLastError();
+template <int JPL>
+static void launch_route_jpl(const float* logits, int T, int E, int k, int router, int S, int tile_rows,
+                             int shared_slot, int32_t* idx, float* w, int32_t* rank_in_block,
+                             int32_t* hist, unsigned int* ticket, int32_t* counts, int32_t* offsets,
+                             int32_t* perm, int32_t* pos, Tile* tiles, int32_t* n_tiles,
+                             unsigned long long* distinct_total, hipStream_t s) {
+  if (T <= kSmallT) {
+    route_small_kernel<JPL><<<1, 1024, 0, s>>>(logits, T, E, k, router, S, tile_rows, shared_slot, idx,
+                                               w, counts, offsets, perm, pos, tiles, n_tiles,
+                                               distinct_total);
+    return;
+  }
+  const int nblk = (T + kRouteBlock - 1) / kRouteBlock;
+  topk_kernel<JPL><<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, router, idx, w);
+  rank_kernel<<<nblk, 1024, 0, s>>>(idx, T, E, k, S, tile_rows, shared_slot, rank_in_block, hist, ticket,
+                                    counts, offsets, tiles, n_tiles, distinct_total);
+  permute_kernel<<<nblk, 256, 0, s>>>(idx, rank_in_block, hist, offsets, T, k, E, S, perm, pos);
 }
 
-hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int S, int tile_rows,
-                          int shared_slot, int32_t* counts, int32_t* offsets, int32_t* perm,
-                          int32_t* pos, Tile* tiles, int32_t* n_tiles,
-                          unsigned long long* distinct_total, hipStream_t s) {
-  permute_kernel<<<1, kPermThreads, 0, s>>>(idx, T, k, E, S, tile_rows, shared_slot, counts,
-                                            offsets, perm, pos, tiles, n_tiles, distinct_total);
+hipError_t launch_route(const float* logits, int T, int E, int k, int router, int S, int tile_rows,
+                        int shared_slot, int32_t* idx, float* w, int32_t* rank_in_block, int32_t* hist,
+                        unsigned int* ticket, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* pos, Tile* tiles, int32_t* n_tiles, unsigned long long* distinct_total,
+                        hipStream_t s) {
+#define STRATA_ROUTE(J)                                                                             \
+  launch_route_jpl<J>(logits, T, E, k, router, S, tile_rows, shared_slot, idx, w, rank_in_block, hist, \
+                      ticket, counts, offsets, perm, pos, tiles, n_tiles, distinct_total, s)
+  if (E <= 64)
+    STRATA_ROUTE(1);
+  else if (E <= 128)
+    STRATA_ROUTE(2);
+  else if (E <= 256)
+    STRATA_ROUTE(4);
+  else if (E <= 512)
+    STRATA_ROUTE(8);
+  else
+    STRATA_ROUTE(16);
+#undef STRATA_ROUTE
   return hipGetLastError();
 }
 

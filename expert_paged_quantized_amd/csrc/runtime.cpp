@@ -32,9 +32,9 @@
 namespace strata {
 hipError_t launch_router(const uint16_t*, const uint16_t*, const float*, float*, uint16_t*, int, int,
                          int, hipStream_t);
-hipError_t launch_topk(const float*, int, int, int, int, int32_t*, float*, hipStream_t);
-hipError_t launch_permute(const int32_t*, int, int, int, int, int, int, int32_t*, int32_t*,
-                          int32_t*, int32_t*, Tile*, int32_t*, unsigned long long*, hipStream_t);
+hipError_t launch_route(const float*, int, int, int, int, int, int, int, int32_t*, float*, int32_t*,
+                        int32_t*, unsigned int*, int32_t*, int32_t*, int32_t*, int32_t*, Tile*, int32_t*,
+                        unsigned long long*, hipStream_t);
 hipError_t launch_expert_gemm(const GemmArgs&, int, bool, bool, int, hipStream_t);
 hipError_t launch_combine(const float*, const int32_t*, const float*, int, int, int, int,
                           uint16_t*, hipStream_t);
@@ -94,9 +94,12 @@ struct strata_moe {
   int32_t* d_offsets = nullptr;
   int32_t* d_perm = nullptr;
   int32_t* d_pos = nullptr;
+  int32_t* d_rank = nullptr;  // rank of each (token, choice) inside its 64-token block
+  int32_t* d_hist = nullptr;  // per 64-token block, per expert token counts
   Tile* d_tiles_dev = nullptr;
   Tile* d_tiles_host = nullptr;
   int32_t* d_ntiles = nullptr;
+  unsigned int* d_ticket = nullptr;  // completion ticket of the rank pass (reset by its last block)
   unsigned long long* d_distinct = nullptr;
   void* d_h = nullptr;
   float* d_o = nullptr;
@@ -322,7 +325,7 @@ static void release(strata_moe* h) {
   void* dev[] = {h->d_pool, h->d_shared, h->d_router_w, h->d_router_bias, h->d_slot_ptr,
                  h->d_logits, h->d_idx, h->d_w, h->d_counts, h->d_offsets, h->d_perm, h->d_pos,
                  h->d_tiles_dev, h->d_tiles_host, h->d_ntiles, h->d_distinct, h->d_h, h->d_o,
-                 h->d_x16};
+                 h->d_x16, h->d_rank, h->d_hist, h->d_ticket};
   for (void* p : dev)
     if (p) (void)hipFree(p);
   if (h->host_store) (void)hipHostFree(h->host_store);
@@ -424,14 +427,16 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   if ((st = walloc(&h->d_logits, T * h->E * 4)) || (st = walloc(&h->d_idx, TK * 4)) ||
       (st = walloc(&h->d_w, TK * 4)) || (st = walloc(&h->d_counts, size_t(h->E) * 4)) ||
       (st = walloc(&h->d_offsets, size_t(h->E + 1) * 4)) || (st = walloc(&h->d_perm, h->max_rows * 4)) ||
-      (st = walloc(&h->d_pos, TK * 4)) || (st = walloc(&h->d_tiles_dev, h->max_tiles * sizeof(Tile))) ||
+      (st = walloc(&h->d_pos, TK * 4)) || (st = walloc(&h->d_rank, TK * 4)) ||
+      (st = walloc(&h->d_hist, ((T + 63) / 64) * size_t(h->E) * 4)) || (st = walloc(&h->d_tiles_dev, h->max_tiles * sizeof(Tile))) ||
       (st = walloc(&h->d_tiles_host, h->max_tiles * sizeof(Tile))) || (st = walloc(&h->d_ntiles, 64)) ||
-      (st = walloc(&h->d_distinct, 64)) || (st = walloc(&h->d_h, h->max_rows * h->F * 2)) ||
+      (st = walloc(&h->d_distinct, 64)) || (st = walloc(&h->d_ticket, 64)) || (st = walloc(&h->d_h, h->max_rows * h->F * 2)) ||
       (st = walloc(&h->d_o, h->max_rows * h->H * 4)))
     return st;
   if (int4 && (st = walloc(&h->d_x16, T * h->H * 2))) return st;
   h->ws_bytes = ws;
   HIP_CHECK(hipMemset(h->d_distinct, 0, 64));
+  HIP_CHECK(hipMemset(h->d_ticket, 0, 64));
   if ((st = host_alloc(&h->h_counts, size_t(h->E) * 4))) return st;
   if ((st = host_alloc(&h->h_tiles, h->max_tiles * sizeof(Tile)))) return st;
 
@@ -544,13 +549,11 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
     return launch_router((const uint16_t*)x, h->d_router_w, h->d_router_bias, h->d_logits, h->d_x16, T,
                          h->E, h->H, s);
   }));
-  HIP_CHECK(timed(h, STRATA_K_TOPK, s, [&]() {
-    return launch_topk(h->d_logits, T, h->E, h->k, h->router, h->d_idx, h->d_w, s);
-  }));
   const int tile_rows = decode ? (1 << 30) : kPrefillTM;
-  HIP_CHECK(timed(h, STRATA_K_PERMUTE, s, [&]() {
-    return launch_permute(h->d_idx, T, h->k, h->E, h->S, tile_rows, h->budget, h->d_counts, h->d_offsets,
-                          h->d_perm, h->d_pos, h->d_tiles_dev, h->d_ntiles, h->d_distinct, s);
+  HIP_CHECK(timed(h, STRATA_K_GROUP, s, [&]() {
+    return launch_route(h->d_logits, T, h->E, h->k, h->router, h->S, tile_rows, h->budget, h->d_idx,
+                        h->d_w, h->d_rank, h->d_hist, h->d_ticket, h->d_counts, h->d_offsets,
+                        h->d_perm, h->d_pos, h->d_tiles_dev, h->d_ntiles, h->d_distinct, s);
   }));
 
   if (h->budget == h->E) {

@@ -193,15 +193,14 @@ strata_status strata_moe_memory(const strata_moe* h, strata_memory_info* out);
  * by HIP events on the forward's stream; strata_moe_timing() waits for them
  * and returns totals per kernel class, and resets them. */
 typedef enum {
-  STRATA_K_ROUTER = 0,   /* router logits                     */
-  STRATA_K_TOPK = 1,     /* top-k + weights                   */
-  STRATA_K_PERMUTE = 2,  /* counts, offsets, perm, tile list  */
-  STRATA_K_DEC_UP = 3,   /* decode gate+up GEMV + SwiGLU      */
-  STRATA_K_DEC_DOWN = 4, /* decode down GEMV                  */
-  STRATA_K_PRE_UP = 5,   /* prefill gate+up grouped GEMM      */
-  STRATA_K_PRE_DOWN = 6, /* prefill down grouped GEMM         */
-  STRATA_K_COMBINE = 7,  /* weighted top-k + shared combine   */
-  STRATA_K_COUNT = 8
+  STRATA_K_ROUTER = 0,   /* router logits                                          */
+  STRATA_K_GROUP = 1,    /* top-k, weights, counts, offsets, perm, tile list       */
+  STRATA_K_DEC_UP = 2,   /* decode gate+up GEMV + SwiGLU                           */
+  STRATA_K_DEC_DOWN = 3, /* decode down GEMV                                       */
+  STRATA_K_PRE_UP = 4,   /* prefill gate+up grouped GEMM                           */
+  STRATA_K_PRE_DOWN = 5, /* prefill down grouped GEMM                              */
+  STRATA_K_COMBINE = 6,  /* weighted top-k + shared combine                        */
+  STRATA_K_COUNT = 7
 } strata_kernel_class;
 
 typedef struct {
