@@ -7,8 +7,8 @@
 // and the SM86 kernel paragraph, whose register-fed decode into matrix-core
 // operands is the prior art here; its prepack into operand order is a pure
 // byte permutation, as is the tile order used below).  One weight layout
-// serves both the decode kernel (T <= 8 tokens, split-K over a workgroup's
-// waves) and the prefill kernel (token tiles of 128 rows staged in LDS), as
+// serves both the decode kernel (T <= 8 tokens, one row tile per wave, split-K
+// across workgroups) and the prefill kernel (token tiles of 128 rows staged in LDS), as
 // the same README does with one layout for M=1 decode and M=128 pages.
 //
 // MFMA used: v_mfma_f32_32x32x16_{f16,bf16}.  The weight tile is the A
@@ -25,6 +25,7 @@
 // MXFP4 weights are decoded to bf16 with the gfx950 scaled FP4 conversion
 // (exact: an E2M1 value times a power of two).  Accumulation is fp32 throughout; nothing uses float atomics,
 // so every expert's result depends only on its own rows and weights.
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_common.h"
@@ -53,6 +54,12 @@ typedef const __attribute__((address_space(1))) uint8_t g_u8;
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(g_u32x4*)(p); }
 __device__ __forceinline__ uint32_t ld4(const void* p) { return *(g_u32*)(p); }
 __device__ __forceinline__ uint32_t ld1(const void* p) { return *(g_u8*)(p); }
+// Streaming (non-temporal) variants for weights read once per launch: they
+// do not displace cached data, and measured streaming reads reach about 7 TB/s
+// this way against about 5 TB/s with ordinary loads.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) { return __builtin_nontemporal_load((g_u32x4*)(p)); }
+__device__ __forceinline__ uint32_t ld4_nt(const void* p) { return __builtin_nontemporal_load((g_u32*)(p)); }
+__device__ __forceinline__ uint32_t ld1_nt(const void* p) { return __builtin_nontemporal_load((g_u8*)(p)); }
 
 // (a & b) | c in one instruction (the compiler splits it when b, c are literals)
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
@@ -146,6 +153,12 @@ struct ScaleLayout {
     else
       return ld1(p);
   }
+  __device__ static uint32_t load_nt(const uint8_t* p) {
+    if constexpr (QF == Q_INT4)
+      return ld4_nt(p);
+    else
+      return ld1_nt(p);
+  }
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -164,98 +177,374 @@ __device__ __forceinline__ uint16_t to_h_elem(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel: one workgroup of 8 waves per (tile, 32-row weight tile).  The
-// waves split the K-blocks of the row tile in contiguous ranges, each streams
-// its 1 KB code chunks (plus scales) with up to 4 blocks in flight, the tokens
-// (<= 8) read their activations straight from global memory, and the partial
-// sums are added in LDS in wave order 0..7 before the epilogue.
+// Decode kernel (T <= 8 tokens).  Workgroup = 8 waves = R row tiles (32
+// weight rows each) of one expert x S K-splits, R*S = 8.  K is walked in
+// chunks of S*8 K-blocks; in a chunk, wave (r, s) takes the 8 consecutive
+// blocks s*8..s*8+7 of row tile r.  The token rows of a chunk are staged in
+// LDS once for all eight waves, their loads issued a whole chunk ahead.  Each
+// wave streams its 1 KB code chunks (and scales) through an 8-deep register
+// ring: a slot is decoded, then refilled with the block of the next chunk, so
+// eight blocks stay in flight.  Every load address is clamped rather than
+// branched around, keeping the loop straight-line so the wait counters track
+// each slot (and the activation loads, issued a chunk before their use)
+// exactly.  At the end the S partial sums of a row tile are added in LDS in
+// split order 0..S-1, then the epilogue runs.  S is fixed per layer shape
+// (capped by LDS at 8 tokens), never by the tiles of a launch.
 // ---------------------------------------------------------------------------
 constexpr int kDecWaves = 8;
+constexpr int kDecDepth = 8;
 
+// Epilogue of one wave's 32-row tile rt for the token columns n < nrows.
 template <int QF, bool GATE_UP>
-__global__ __launch_bounds__(512) void moe_decode_kernel(GemmArgs p) {
+__device__ __forceinline__ void decode_store(const GemmArgs& p, const Tile& t, int rt, int lane,
+                                             const f32x16& acc) {
+  const int n = lane & 31;
+  if (n >= t.nrows) return;
+  const int64_t row = t.row_begin + n;
+  if constexpr (GATE_UP) {
+    uint16_t* h = reinterpret_cast<uint16_t*>(p.out) + row * p.out_ld + rt * 16;
+#pragma unroll
+    for (int g4 = 0; g4 < 2; ++g4) {
+      uint16_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = g4 * 4 + q;
+        v[q] = to_h_elem<QF>(silu(acc[i]) * acc[i + 8]);
+      }
+      const uint2 pk = {(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16)};
+      *reinterpret_cast<uint2*>(h + g4 * 8 + (lane >> 5) * 4) = pk;
+    }
+  } else {
+    float* o = reinterpret_cast<float*>(p.out) + row * p.out_ld + rt * 32;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float4 v = {acc[g4 * 4 + 0], acc[g4 * 4 + 1], acc[g4 * 4 + 2], acc[g4 * 4 + 3]};
+      *reinterpret_cast<float4*>(o + g4 * 8 + (lane >> 5) * 4) = v;
+    }
+  }
+}
+
+// NP = 16-byte activation pieces each thread stages per chunk:
+// ceil(T * S * 64 / 512) for the launch's token count T (>= every tile's
+// rows), with T * S <= 32.
+template <int QF, bool GATE_UP, int NP>
+__global__ __launch_bounds__(kDecWaves * 64) void moe_decode_kernel(GemmArgs p, int log2S) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t xs[];
   using SL = ScaleLayout<QF>;
-  __shared__ float red[kDecWaves][kDecodeMaxT][32];
+  const int S = 1 << log2S, R = kDecWaves >> log2S;
   const int nrt = p.N >> 5;
-  const int tile_i = blockIdx.x / nrt, rt = blockIdx.x % nrt;
+  const int nrg = (nrt + R - 1) / R;
+  const int rg = blockIdx.x % nrg, tile_i = blockIdx.x / nrg;
   const int n_tiles = p.n_tiles_dev ? p.n_tiles_dev[0] : p.n_tiles;
-  if (tile_i >= n_tiles) return;
+  if (tile_i >= n_tiles) return;  // the whole workgroup leaves together
   const Tile t = p.tiles[tile_i];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sw = wave & (S - 1);           // this wave's split
+  const int rt = rg * R + (wave >> log2S);
+  const int rtc = min(rt, nrt - 1);
   const int KB = p.K >> 6;
-  const int kb0 = wave * KB / kDecWaves, kb1 = (wave + 1) * KB / kDecWaves;
+  const int cb = S * kDecDepth;             // K-blocks per chunk
+  const int nc = (KB + cb - 1) / cb;
+  const int row_u32 = cb * 32 + 4;          // staged row: cb*64 16-bit inputs + 16 B pad
+
   const uint8_t* rec = p.slot_ptr[t.slot];
-  const uint8_t* codes = rec + p.off_codes + (int64_t)rt * KB * kTileCodeBytes + lane * 16;
-  const uint8_t* scales = rec + p.off_scales + (int64_t)rt * KB * SL::kTileBytes + SL::lane_off(lane);
-  const int m = lane & 31;
-  const bool valid = m < t.nrows;
-  int64_t arow = 0;
-  if (valid) arow = p.gather ? p.gather[t.row_begin + m] : (t.row_begin + m);
-  const uint16_t* act = reinterpret_cast<const uint16_t*>(p.act) + arow * p.K + 32 * (lane >> 5);
+  const uint8_t* codes = rec + p.off_codes + (int64_t)rtc * KB * kTileCodeBytes + lane * 16;
+  const uint8_t* scales = rec + p.off_scales + (int64_t)rtc * KB * SL::kTileBytes + SL::lane_off(lane);
+
+  // staging pieces (the tile's own rows only): piece pc = tid + 512*j ->
+  // token row pc >> (log2S + 6), 16-byte column pc & (S*64 - 1) of the
+  // chunk; columns past K re-read the row's last piece (staged, never used)
+  const int pieces = t.nrows << (log2S + 6);
+  const uint16_t* xrow[NP];
+  int xcol[NP], xdst[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int q = tid + j * kDecWaves * 64;
+    const int pc = min(q, pieces - 1);
+    const int r = pc >> (log2S + 6), c = pc & ((S << 6) - 1);
+    const int64_t ar = p.gather ? p.gather[t.row_begin + r] : (t.row_begin + r);
+    xrow[j] = reinterpret_cast<const uint16_t*>(p.act) + ar * p.K;
+    xcol[j] = c * 8;
+    xdst[j] = (q < pieces) ? r * row_u32 + c * 4 : -1;
+  }
+  auto x_load = [&](u32x4(&v)[NP], int cc) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) v[j] = ld16(xrow[j] + min(cc * cb * 64 + xcol[j], p.K - 8));
+  };
+  auto x_store = [&](const u32x4(&v)[NP]) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+      if (xdst[j] >= 0) *reinterpret_cast<u32x4*>(&xs[xdst[j]]) = v[j];
+  };
+
+  // weight ring prologue: slot j holds block sw*8 + j of chunk 0
+  u32x4 wq[kDecDepth];
+  uint32_t ws[kDecDepth];
+#pragma unroll
+  for (int j = 0; j < kDecDepth; ++j) {
+    const int kb = min(sw * kDecDepth + j, KB - 1);
+    wq[j] = ld16_nt(codes + (int64_t)kb * kTileCodeBytes);
+    ws[j] = SL::load_nt(scales + (int64_t)kb * SL::kTileBytes);
+  }
+  u32x4 xv[NP];
+  x_load(xv, 0);
+  x_store(xv);
+  x_load(xv, 1);  // chunk 1 in flight during chunk 0
+  __syncthreads();
 
   f32x16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  const uint32_t* brow = xs + min(lane & 31, t.nrows - 1) * row_u32 + sw * (kDecDepth * 32) + (lane >> 5) * 16;
 
-  for (int kb = kb0; kb < kb1; kb += 4) {
-    const int nb = min(4, kb1 - kb);
-    u32x4 wq[4], xa[4][4];
-    uint32_t ws[4];
+  for (int cc = 0; cc < nc; ++cc) {
+    const int kbase = cc * cb + sw * kDecDepth;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (u < nb) {
-        wq[u] = ld16(codes + (int64_t)(kb + u) * kTileCodeBytes);
-        ws[u] = SL::load(scales + (int64_t)(kb + u) * SL::kTileBytes);
+    for (int j = 0; j < kDecDepth; ++j) {
+      // decode slot j first so its registers are free for the refill (the
+      // refill then reuses them in place and nothing is copied at the loop
+      // edge, which would wait for every load in flight)
+      u32x4 a[4];
+      dequant<QF>(wq[j], ws[j], a);
+      asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])::"memory");
+      const int kn = min(kbase + cb + j, KB - 1);
+      wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
+      ws[j] = SL::load_nt(scales + (int64_t)kn * SL::kTileBytes);
+      if (kbase + j < KB) {
+        const uint32_t* bp = brow + j * 32;
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          acc = mfma<QF>(a[st], *reinterpret_cast<const u32x4*>(bp + st * 4), acc);
       }
     }
+    __syncthreads();  // chunk cc fully read
+    x_store(xv);      // chunk cc+1 (past the end: unused)
+    x_load(xv, cc + 2);
+    __syncthreads();
+  }
+
+  // add the S partial sums of each row tile in split order (LDS reused)
+  float* red = reinterpret_cast<float*>(xs);
+  const int n = lane & 31;
+  if (sw > 0 && n < t.nrows) {
+    float* d = red + ((wave * kDecodeMaxT + n) * 32) + (lane >> 5) * 4;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int g4 = 0; g4 < 4; ++g4)
+      *reinterpret_cast<float4*>(d + g4 * 8) =
+          float4{acc[g4 * 4 + 0], acc[g4 * 4 + 1], acc[g4 * 4 + 2], acc[g4 * 4 + 3]};
+  }
+  __syncthreads();
+  if (sw == 0 && rt < nrt) {
+    if (n < t.nrows) {
+      for (int s2 = 1; s2 < S; ++s2) {
+        const float* d = red + (((wave + s2) * kDecodeMaxT + n) * 32) + (lane >> 5) * 4;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (u < nb && valid) v = ld16(act + (kb + u) * 64 + 8 * st);
-        xa[u][st] = v;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 v = *reinterpret_cast<const float4*>(d + g4 * 8);
+          acc[g4 * 4 + 0] += v.x;
+          acc[g4 * 4 + 1] += v.y;
+          acc[g4 * 4 + 2] += v.z;
+          acc[g4 * 4 + 3] += v.w;
+        }
       }
     }
+    decode_store<QF, GATE_UP>(p, t, rt, lane, acc);
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Dot-product decode kernel (T <= 4 tokens).  At a handful of tokens the
+// 32-column MFMA wastes most of its work and its issue time adds to the
+// decode time, so the contraction runs on the VALU dot units instead:
+//   int4:  an AND leaves a code pair as fp16 denormals (q * 2^-24 for the low
+//          nibbles, q * 2^-20 for the high ones, exact), v_dot2_f32_f16
+//          multiplies them with the fp16 activations, and the group's affine
+//          parameters are applied once per 32 inputs: s * sum(x q) + b * sum(x),
+//          with sum(x) staged alongside the activations.  No weight is rounded
+//          to 16 bits on this path.
+//   MXFP4: the gfx950 FP4 conversion (unit scale) gives exact bf16 pairs,
+//          v_dot2_f32_bf16 contracts them, and the E8M0 power of two scales
+//          the 32-input group sum.
+// Workgroup = S waves on one 32-row weight tile, wave s streaming the
+// contiguous K-blocks [s*KB/S, (s+1)*KB/S) of it; lane l owns tile row l%32
+// and inputs 32*(l/32)..+31 of each block (the prepacked layout: one 16-byte
+// code chunk, one affine or E8M0 group).  The token rows (all of K) are
+// staged in LDS once; weights stream through a register ring (16, 12 or 8 deep),
+// each slot unpacked before it is refilled in place.  The halves of a row are
+// added lane l + lane l+32, then the S partial sums in wave order, then the
+// epilogue.
+// ---------------------------------------------------------------------------
+// weight ring depth: registers at 1024 threads per workgroup are capped at
+// 128 per lane, and every token adds accumulators and activation operands
+constexpr int dot_depth(int tt) { return tt == 1 ? 16 : (tt == 2 ? 12 : 8); }
+
+template <int QF, bool GATE_UP, int TT, int NPR>
+__global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t xs[];
+  using SL = ScaleLayout<QF>;
+  constexpr int DEPTH = dot_depth(TT);
+  const int S = blockDim.x >> 6;
+  const int nrt = p.N >> 5;
+  const int rt = blockIdx.x % nrt, tile_i = blockIdx.x / nrt;
+  const int n_tiles = p.n_tiles_dev ? p.n_tiles_dev[0] : p.n_tiles;
+  if (tile_i >= n_tiles) return;  // the whole workgroup leaves together
+  const Tile t = p.tiles[tile_i];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = p.K, KB = K >> 6;
+  const int kb0 = wave * KB / S, kb1 = (wave + 1) * KB / S, nkb = kb1 - kb0;
+  const int row_u32 = K / 2 + 4;                  // staged row: K 16-bit inputs + 16 B pad
+  float* xsum = reinterpret_cast<float*>(xs + TT * row_u32);  // [TT][K/32] (int4)
+
+  const uint8_t* rec = p.slot_ptr[t.slot];
+  const uint8_t* codes = rec + p.off_codes + ((int64_t)rt * KB + kb0) * kTileCodeBytes + lane * 16;
+  const uint8_t* scales = rec + p.off_scales + ((int64_t)rt * KB + kb0) * SL::kTileBytes + SL::lane_off(lane);
+
+  // activation loads first: waiting for them later leaves the weight loads
+  // issued after them in flight
+  const int pr = K >> 3;  // 16-byte pieces per row
+  u32x4 v[TT][NPR];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (u < nb) {
-        u32x4 a[4];
-        dequant<QF>(wq[u], ws[u], a);
+  for (int r = 0; r < TT; ++r) {
+    const int rr = min(r, t.nrows - 1);  // rows past nrows re-read the last row
+    const int64_t ar = p.gather ? p.gather[t.row_begin + rr] : (t.row_begin + rr);
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.act) + ar * K;
+#pragma unroll
+    for (int j = 0; j < NPR; ++j) v[r][j] = ld16(src + min(tid + j * (int)blockDim.x, pr - 1) * 8);
+  }
+  asm volatile("" ::: "memory");
+  // weight ring prologue (clamped inside the range)
+  u32x4 wq[DEPTH];
+  uint32_t ws[DEPTH];
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) {
+    const int kb = min(j, nkb - 1);
+    wq[j] = ld16_nt(codes + (int64_t)kb * kTileCodeBytes);
+    ws[j] = SL::load_nt(scales + (int64_t)kb * SL::kTileBytes);
+  }
+  // stage the token rows; for int4 also the sums of each 32 inputs, four
+  // consecutive 8-input pieces per quad
+#pragma unroll
+  for (int r = 0; r < TT; ++r) {
+#pragma unroll
+    for (int j = 0; j < NPR; ++j) {
+      const int c = tid + j * (int)blockDim.x;
+      if (c < pr) *reinterpret_cast<u32x4*>(&xs[r * row_u32 + c * 4]) = v[r][j];
+      if constexpr (QF == Q_INT4) {
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum = __builtin_amdgcn_fdot2(bitcast<f16x2>(v[r][j][q]), one, sum, false);
+        // quad (xor 1, then xor 2) sum in a fixed tree; blockDim is a
+        // multiple of 64 and pr of 8, so a quad never straddles rows
+        sum += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, false));
+        sum += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF, false));
+        if (c < pr && (c & 3) == 0) xsum[r * (K >> 5) + (c >> 2)] = sum;
+      }
+    }
+  }
+  __syncthreads();
+
+  float acc[TT];
+#pragma unroll
+  for (int r = 0; r < TT; ++r) acc[r] = 0.0f;
+  const int h = lane >> 5;
+  const uint32_t* xl = xs + (kb0 * 32 + h * 16);  // this lane's 32 inputs of block kb0, row 0
+  const float* xsl = xsum + kb0 * 2 + h;
+
+  for (int i = 0; i < nkb; i += DEPTH) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      // unpack slot j, refill it in place, then contract
+      const int kbl = i + j;
+      const int kn = min(kbl + DEPTH, nkb - 1);
+      if constexpr (QF == Q_INT4) {
+        uint32_t m[4][4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          acc = mfma<QF>(a[st], xa[u][st], acc);
+          const uint32_t w = wq[j][st], w8 = w >> 8;
+          m[st][0] = w & 0x000F000Fu;   // (k0, k1) * 2^-24
+          m[st][1] = w & 0x00F000F0u;   // (k2, k3) * 2^-20
+          m[st][2] = w8 & 0x000F000Fu;  // (k4, k5) * 2^-24
+          m[st][3] = w8 & 0x00F000F0u;  // (k6, k7) * 2^-20
+        }
+        float s = __uint_as_float(ws[j] << 16), b = __uint_as_float(ws[j] & 0xffff0000u);
+        asm volatile("" : "+v"(m[0][0]), "+v"(m[0][1]), "+v"(m[0][2]), "+v"(m[0][3]), "+v"(m[1][0]),
+                     "+v"(m[1][1]), "+v"(m[1][2]), "+v"(m[1][3]), "+v"(m[2][0]), "+v"(m[2][1]),
+                     "+v"(m[2][2]), "+v"(m[2][3]), "+v"(m[3][0]), "+v"(m[3][1]), "+v"(m[3][2]),
+                     "+v"(m[3][3]), "+v"(s), "+v"(b)::"memory");
+        wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
+        ws[j] = SL::load_nt(scales + (int64_t)kn * SL::kTileBytes);
+        if (kbl < nkb) {
+#pragma unroll
+          for (int r = 0; r < TT; ++r) {
+            const uint32_t* xr = xl + r * row_u32 + kbl * 32;
+            float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+              const u32x4 x = *reinterpret_cast<const u32x4*>(xr + st * 4);
+              lo = __builtin_amdgcn_fdot2(bitcast<f16x2>(m[st][0]), bitcast<f16x2>(x[0]), lo, false);
+              hi = __builtin_amdgcn_fdot2(bitcast<f16x2>(m[st][1]), bitcast<f16x2>(x[1]), hi, false);
+              lo = __builtin_amdgcn_fdot2(bitcast<f16x2>(m[st][2]), bitcast<f16x2>(x[2]), lo, false);
+              hi = __builtin_amdgcn_fdot2(bitcast<f16x2>(m[st][3]), bitcast<f16x2>(x[3]), hi, false);
+            }
+            const float xq = __builtin_fmaf(lo, 16.0f, hi) * 1048576.0f;  // sum(x q)
+            acc[r] = __builtin_fmaf(s, xq, acc[r]);
+            acc[r] = __builtin_fmaf(b, xsl[r * (K >> 5) + kbl * 2], acc[r]);
+          }
+        }
+      } else {
+        u32x4 m[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) m[st] = dequant_fp4_step(wq[j][st], 1.0f);
+        float scale = __uint_as_float(ws[j] << 23);
+        asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(scale)::"memory");
+        wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
+        ws[j] = SL::load_nt(scales + (int64_t)kn * SL::kTileBytes);
+        if (kbl < nkb) {
+#pragma unroll
+          for (int r = 0; r < TT; ++r) {
+            const uint32_t* xr = xl + r * row_u32 + kbl * 32;
+            float d = 0.0f;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+              const u32x4 x = *reinterpret_cast<const u32x4*>(xr + st * 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                d = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(m[st][e]), bitcast<bf16x2>(x[e]), d, false);
+            }
+            acc[r] = __builtin_fmaf(scale, d, acc[r]);
+          }
         }
       }
     }
   }
 
-  if (valid && m < kDecodeMaxT) {
+  // halves: lane l (< 32) adds lane l+32; then the S waves in order
+  __syncthreads();  // staging area reused below
+  float* red = reinterpret_cast<float*>(xs);  // [S][TT][32]
 #pragma unroll
-    for (int i = 0; i < 16; ++i) red[wave][m][(i >> 2) * 8 + (lane >> 5) * 4 + (i & 3)] = acc[i];
+  for (int r = 0; r < TT; ++r) {
+    const float other = __shfl_down(acc[r], 32);
+    if (lane < 32) red[(wave * TT + r) * 32 + lane] = acc[r] + other;
   }
   __syncthreads();
-  const int tid = threadIdx.x;
-  if constexpr (GATE_UP) {
-    const int mm = tid >> 4, n = tid & 15;
-    if (mm < t.nrows) {
-      float g = 0.0f, u = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) {
-        g += red[w][mm][n];
-        u += red[w][mm][n + 16];
+  for (int q = tid; q < TT * 32; q += blockDim.x) {
+    const int n = q >> 5, row = q & 31;  // (token, row)
+    if (n >= t.nrows) continue;
+    if constexpr (GATE_UP) {
+      if (row >= 16) continue;
+      float g = red[n * 32 + row], u = red[n * 32 + row + 16];
+      for (int w = 1; w < S; ++w) {
+        g += red[(w * TT + n) * 32 + row];
+        u += red[(w * TT + n) * 32 + row + 16];
       }
-      uint16_t* h = reinterpret_cast<uint16_t*>(p.out);
-      h[(int64_t)(t.row_begin + mm) * p.out_ld + rt * 16 + n] = to_h_elem<QF>(silu(g) * u);
-    }
-  } else {
-    const int mm = tid >> 5, r = tid & 31;
-    if (mm < t.nrows) {
-      float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) s += red[w][mm][r];
-      float* o = reinterpret_cast<float*>(p.out);
-      o[(int64_t)(t.row_begin + mm) * p.out_ld + rt * 32 + r] = s;
+      uint16_t* hp = reinterpret_cast<uint16_t*>(p.out);
+      hp[(int64_t)(t.row_begin + n) * p.out_ld + rt * 16 + row] = to_h_elem<QF>(silu(g) * u);
+    } else {
+      float o = red[n * 32 + row];
+      for (int w = 1; w < S; ++w) o += red[(w * TT + n) * 32 + row];
+      reinterpret_cast<float*>(p.out)[(int64_t)(t.row_begin + n) * p.out_ld + rt * 32 + row] = o;
     }
   }
 }
@@ -503,20 +792,111 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_expert_gemm(const GemmArgs& a, int quant, bool gate_up, bool decode, int grid,
-                              hipStream_t s) {
+template <int QF, bool GATE_UP>
+static void launch_decode(const GemmArgs& a, int T, int log2S, int grid, hipStream_t s) {
+  const int S = 1 << log2S;
+  const size_t lds = std::max<size_t>((size_t)T * (S * kDecDepth * 128 + 16),
+                                      (size_t)kDecWaves * kDecodeMaxT * 32 * 4);
+  const int np = (T * S * 64 + kDecWaves * 64 - 1) / (kDecWaves * 64);
+  if (np <= 1)
+    moe_decode_kernel<QF, GATE_UP, 1><<<grid, kDecWaves * 64, lds, s>>>(a, log2S);
+  else if (np <= 2)
+    moe_decode_kernel<QF, GATE_UP, 2><<<grid, kDecWaves * 64, lds, s>>>(a, log2S);
+  else
+    moe_decode_kernel<QF, GATE_UP, 4><<<grid, kDecWaves * 64, lds, s>>>(a, log2S);
+}
+
+// Decode split: waves per row tile, log2.  Enough waves for about 16 per CU
+// at one token (k + S expert tiles), at least 4 K-blocks per wave, and at
+// most 8 splits; 8 tokens allow at most 4 (LDS and staging registers).
+// Depends only on the layer shape and the token count.
+int decode_log2_splits(int N, int K, int tiles_per_token, int T) {
+  const int KB = K / 64, units = tiles_per_token * (N / 32);
+  int l = 0;
+  while (l < 3 && (units << (l + 1)) <= 4096 && KB / (2 << l) >= 4) ++l;
+  while (T * (1 << l) > 32) --l;
+  return l;
+}
+
+int decode_grid(int N, int log2S, int n_tiles) {
+  const int R = kDecWaves >> log2S;
+  return n_tiles * ((N / 32 + R - 1) / R);
+}
+
+// Dot decode eligibility and split for an N x K weight at T tokens: waves per
+// row tile (1..16, enough for about 16 waves per CU at one token, at least a
+// full ring of 16 K-blocks each), 16-byte staging pieces per thread per row (<= 4), and the
+// LDS the staged rows need (<= 64 KB).  Returns 0 if the MFMA kernel is to be
+// used instead.  Depends only on the layer shape and T.
+int decode_dot_waves(int N, int K, int quant, int tiles_per_token, int T) {
+  if (T > 4) return 0;
+  const int TT = T <= 1 ? 1 : (T <= 2 ? 2 : 4);
+  const int KB = K / 64, units = tiles_per_token * (N / 32);
+  int S = 1;
+  while (S < 16 && units * 2 * S <= 4096 && KB / (2 * S) >= 16) S *= 2;
+  while (S < 16 && (K / 8 + 64 * S - 1) / (64 * S) > 4) S *= 2;
+  if ((K / 8 + 64 * S - 1) / (64 * S) > 4) return 0;
+  const size_t lds = (size_t)TT * (K * 2 + 16) + (quant == Q_INT4 ? (size_t)TT * (K / 32) * 4 : 0);
+  if (lds > 64 * 1024) return 0;
+  return S;
+}
+
+template <int QF, bool GATE_UP, int TT>
+static void launch_dot_tt(const GemmArgs& a, int S, int grid, size_t lds, hipStream_t s) {
+  const int npr = (a.K / 8 + 64 * S - 1) / (64 * S);
+  if (npr <= 1)
+    moe_decode_dot_kernel<QF, GATE_UP, TT, 1><<<grid, 64 * S, lds, s>>>(a);
+  else if (npr <= 2)
+    moe_decode_dot_kernel<QF, GATE_UP, TT, 2><<<grid, 64 * S, lds, s>>>(a);
+  else
+    moe_decode_dot_kernel<QF, GATE_UP, TT, 4><<<grid, 64 * S, lds, s>>>(a);
+}
+
+template <int QF, bool GATE_UP>
+static void launch_dot(const GemmArgs& a, int T, int S, int n_tiles, hipStream_t s) {
+  const int TT = T <= 1 ? 1 : (T <= 2 ? 2 : 4);
+  size_t lds = (size_t)TT * (a.K * 2 + 16) + (QF == Q_INT4 ? (size_t)TT * (a.K / 32) * 4 : 0);
+  lds = std::max(lds, (size_t)S * TT * 32 * 4);
+  const int grid = n_tiles * (a.N / 32);
+  if (TT == 1)
+    launch_dot_tt<QF, GATE_UP, 1>(a, S, grid, lds, s);
+  else if (TT == 2)
+    launch_dot_tt<QF, GATE_UP, 2>(a, S, grid, lds, s);
+  else
+    launch_dot_tt<QF, GATE_UP, 4>(a, S, grid, lds, s);
+}
+
+hipError_t launch_decode_dot(const GemmArgs& a, int quant, bool gate_up, int T, int S, int n_tiles,
+                             hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  if (quant == Q_INT4) {
+    if (gate_up)
+      launch_dot<Q_INT4, true>(a, T, S, n_tiles, s);
+    else
+      launch_dot<Q_INT4, false>(a, T, S, n_tiles, s);
+  } else {
+    if (gate_up)
+      launch_dot<Q_MXFP4, true>(a, T, S, n_tiles, s);
+    else
+      launch_dot<Q_MXFP4, false>(a, T, S, n_tiles, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_gemm(const GemmArgs& a, int quant, bool gate_up, bool decode, int T, int log2S,
+                              int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (decode) {
     if (quant == Q_INT4) {
       if (gate_up)
-        moe_decode_kernel<Q_INT4, true><<<grid, 512, 0, s>>>(a);
+        launch_decode<Q_INT4, true>(a, T, log2S, grid, s);
       else
-        moe_decode_kernel<Q_INT4, false><<<grid, 512, 0, s>>>(a);
+        launch_decode<Q_INT4, false>(a, T, log2S, grid, s);
     } else {
       if (gate_up)
-        moe_decode_kernel<Q_MXFP4, true><<<grid, 512, 0, s>>>(a);
+        launch_decode<Q_MXFP4, true>(a, T, log2S, grid, s);
       else
-        moe_decode_kernel<Q_MXFP4, false><<<grid, 512, 0, s>>>(a);
+        launch_decode<Q_MXFP4, false>(a, T, log2S, grid, s);
     }
   } else {
     if (quant == Q_INT4) {

@@ -35,7 +35,11 @@ hipError_t launch_router(const uint16_t*, const uint16_t*, const float*, float*,
 hipError_t launch_route(const float*, int, int, int, int, int, int, int, int32_t*, float*, int32_t*,
                         int32_t*, unsigned int*, int32_t*, int32_t*, int32_t*, int32_t*, Tile*, int32_t*,
                         unsigned long long*, hipStream_t);
-hipError_t launch_expert_gemm(const GemmArgs&, int, bool, bool, int, hipStream_t);
+hipError_t launch_expert_gemm(const GemmArgs&, int, bool, bool, int, int, int, hipStream_t);
+int decode_log2_splits(int N, int K, int tiles_per_token, int T);
+int decode_grid(int N, int log2S, int n_tiles);
+int decode_dot_waves(int N, int K, int quant, int tiles_per_token, int T);
+hipError_t launch_decode_dot(const GemmArgs& a, int quant, bool gate_up, int T, int S, int n_tiles, hipStream_t s);
 hipError_t launch_combine(const float*, const int32_t*, const float*, int, int, int, int,
                           uint16_t*, hipStream_t);
 }  // namespace strata
@@ -504,20 +508,29 @@ static int prefill_grid(int items) { return std::max(1, std::min(items, 512)); }
 // Runs gate+up then down over a tile range.  n_dev != nullptr: the count lives
 // on the device and `n_tiles` is only an upper bound.
 static hipError_t run_experts(strata_moe* h, const void* x, const Tile* tiles, const int32_t* n_dev,
-                              int n_tiles, bool decode, hipStream_t s) {
+                              int n_tiles, bool decode, int T, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
   for (int pass = 0; pass < 2; ++pass) {
     const bool gate_up = pass == 0;
     GemmArgs a = gemm_args(h, gate_up, x, tiles, n_dev, n_tiles);
     const int nrt = a.N / 32;
     int grid;
-    if (decode)
-      grid = n_tiles * nrt;
-    else
+    int log2S = 0;
+    const int dot_s = decode ? decode_dot_waves(a.N, a.K, h->quant, h->k + h->S, T) : 0;
+    if (dot_s > 0) {
+      const int cls = gate_up ? STRATA_K_DEC_UP : STRATA_K_DEC_DOWN;
+      hipError_t e = timed(h, cls, s, [&]() { return launch_decode_dot(a, h->quant, gate_up, T, dot_s, n_tiles, s); });
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    if (decode) {
+      log2S = decode_log2_splits(a.N, a.K, h->k + h->S, T);
+      grid = decode_grid(a.N, log2S, n_tiles);
+    } else
       grid = prefill_grid(n_tiles * ((nrt + 7) / 8));
     const int cls = decode ? (gate_up ? STRATA_K_DEC_UP : STRATA_K_DEC_DOWN)
                            : (gate_up ? STRATA_K_PRE_UP : STRATA_K_PRE_DOWN);
-    hipError_t e = timed(h, cls, s, [&]() { return launch_expert_gemm(a, h->quant, gate_up, decode, grid, s); });
+    hipError_t e = timed(h, cls, s, [&]() { return launch_expert_gemm(a, h->quant, gate_up, decode, T, log2S, grid, s); });
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -559,7 +572,7 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
   if (h->budget == h->E) {
     const int ub = decode ? std::min(h->E, TK) + h->S
                           : TK / kPrefillTM + std::min(h->E, TK) + (h->S ? (T + kPrefillTM - 1) / kPrefillTM : 0);
-    HIP_CHECK(run_experts(h, x, h->d_tiles_dev, h->d_ntiles, ub, decode, s));
+    HIP_CHECK(run_experts(h, x, h->d_tiles_dev, h->d_ntiles, ub, decode, T, s));
     h->rm.forwards++;
     h->rm.waves++;
   } else {
@@ -615,10 +628,10 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
         }
         HIP_CHECK(hipEventRecord(h->ev_copied[w], h->copy_stream));
       }
-      HIP_CHECK(run_experts(h, x, h->d_tiles_host + hb[w], nullptr, he[w] - hb[w], decode, s));
+      HIP_CHECK(run_experts(h, x, h->d_tiles_host + hb[w], nullptr, he[w] - hb[w], decode, T, s));
       if (any_paged) {
         HIP_CHECK(hipStreamWaitEvent(s, h->ev_copied[w], 0));
-        HIP_CHECK(run_experts(h, x, h->d_tiles_host + he[w], nullptr, pe[w] - he[w], decode, s));
+        HIP_CHECK(run_experts(h, x, h->d_tiles_host + he[w], nullptr, pe[w] - he[w], decode, T, s));
       }
       HIP_CHECK(hipEventRecord(h->ev_wave_done[w], s));
     }

@@ -21,13 +21,13 @@ pytestmark = pytest.mark.gpu
 
 SMALL = {
     # name: (config, Ts)
-    "tiny": (CONFIGS["tiny"], (1, 5, 8, 16)),
+    "tiny": (CONFIGS["tiny"], (1, 2, 5, 8, 16)),
     "mixtral_s": (CONFIGS["mixtral"].scaled(hidden=1024, ffn=512), (1, 3, 257)),
     "qwen_s": (CONFIGS["qwen3_30b_a3b"].scaled(hidden=1024, ffn=256, num_experts=32), (1, 8, 300)),
     "glm_s": (CONFIGS["glm45_air"].scaled(hidden=1024, ffn=320, num_experts=16, top_k=4, budget_frac=0.2),
               (1, 2, 4, 8, 300)),
     "e512_s": (CONFIGS["e512_mxfp4"].scaled(hidden=1024, ffn=256, num_experts=64, budget_frac=0.18),
-               (1, 8, 333)),
+               (1, 2, 3, 8, 333)),
 }
 
 
@@ -80,7 +80,7 @@ def test_paged_output_is_bitwise_the_resident_output(torch_cuda, name, policy):
     import expert_paged_quantized_amd as epq
     paged = epq.MoELayer.from_weights(lw, budget=cfg.budget, policy=policy, max_tokens=512)
     model = ResidencyModel(cfg.num_experts, cfg.budget, policy, cfg.expert_bytes())
-    Ts = [1, 300, 1, 2, 8, 1, 257, 1, 1, 5]
+    Ts = [1, 300, 1, 2, 8, 1, 257, 4, 1, 1, 5, 3]
     for i, T in enumerate(Ts):
         print(f"[paged] {name} {policy} step={i} T={T}", flush=True)
         x = make_tokens(cfg, T, step=100 + i, seed=cfg.seed + 50)
