@@ -8,10 +8,17 @@ timed region starts.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline]
+  python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload NAME]
+      turns two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+      WRITE_SIZE) into profiles/traffic_<workload>.json, which later runs use
+      for the roofline's `traffic` while the kernel source is unchanged.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import statistics
@@ -42,7 +49,52 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=2)
     ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     return ap.parse_args()
+
+
+KERNEL_SRC = os.path.join(ROOT, "expert_paged_quantized_amd", "csrc", "kernels_expert.hip")
+CALIB_BYTES = 256 << 20                        # plain device copy timed in the same run
+
+
+def kernel_source_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def pmc_summary(fetch_dir, write_dir, workload):
+    """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the prefill gate+up
+    kernel, each scaled by what the counter reads for the calibration copy
+    (CALIB_BYTES read and written by one copy kernel in the same process)."""
+    def read(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        assert f, f"no counter_collection.csv under {d}"
+        per = {}
+        for r in csv.DictReader(open(f[0])):
+            if r["Counter_Name"] != counter:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return per
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = read(d, counter)
+        up = [v for k, vs in per.items() if "moe_prefill_kernel" in k and ", true>" in k for v in vs]
+        # the calibration copy (a same-dtype device copy, run by the HIP
+        # runtime's copy kernel) is by far the largest copyBuffer dispatch
+        cal = max(max(vs) for k, vs in per.items() if "copyBuffer" in k)
+        factor = CALIB_BYTES / (cal * 1024.0)
+        out[counter] = {"kib_per_dispatch": sum(up) / len(up), "dispatches": len(up),
+                        "calibration_kib": cal, "factor": round(factor, 4)}
+    tb = sum(v["kib_per_dispatch"] * 1024.0 * v["factor"] for v in out.values())
+    res = {"workload": workload, "kernel": "moe_prefill_kernel (gate+up)",
+           "kernel_source_sha256_16": kernel_source_hash(), "counters": out,
+           "traffic_bytes_per_launch": round(tb)}
+    with open(traffic_path(workload), "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
 
 
 def flops_gate_up(cfg, rows):
@@ -66,6 +118,9 @@ def w2_bytes(cfg):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
+        return
     if args.cpu_baseline_only:
         from synth import CONFIGS, make_layer
         cfg = CONFIGS[args.workload]
@@ -131,9 +186,14 @@ def main():
     # (1) headline: as configured, no instrumentation
     log("[bench] timed region: as configured")
     dt, per, _ = timed_region(paged)
-    # (2) the same inputs with HIP events around every kernel (kernel durations)
+    # (2) the same inputs with HIP events around every kernel (kernel durations);
+    # a one-element cumsum before and after marks this region in a kernel trace
     log("[bench] timed region: kernel events")
+    mark = torch.ones(4, device=dev)
+    mark.cumsum(0)
     dt_ev, _, tm = timed_region(paged, events=True)
+    mark.cumsum(0)
+    torch.cuda.synchronize()
     # (3) all experts resident: the GPU path alone
     log("[bench] timed region: all resident")
     dt_r, _, _ = timed_region(resident, per_step_sync=False)
@@ -152,30 +212,59 @@ def main():
             "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
             "traffic": None, "launches": int(up_n), "avg_launch_us": round(up_ms / max(up_n, 1) * 1e3, 2),
             "algorithmic_flops_per_step": flops_gate_up(cfg, rows)}
+    tp = traffic_path(cfg.name)
+    if os.path.exists(tp):
+        tr = json.load(open(tp))
+        if tr.get("kernel_source_sha256_16") == kernel_source_hash():
+            roof["traffic"] = tr["traffic_bytes_per_launch"]
+            roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
 
-    # decode kernels, cold MALL: all-resident layer, 1 GiB scratch written between forwards
-    log("[bench] decode cold-cache pass")
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    resident.set_timing(True)
-    resident.timing()
-    dec_bytes = 0
-    n_dec = 0
-    for i in range(W, n):
-        flush.fill_(float(i))
-        _, dbg = resident.forward(xs_d[i], y=y_d, dbg=True)
-        torch.cuda.synchronize()
-        dec_bytes += int((dbg["counts"] > 0).sum().item()) * cfg.expert_bytes() + cfg.num_shared * cfg.expert_bytes()
-        n_dec += 1
-    tmd = resident.timing()
-    resident.set_timing(False)
+    # decode kernels: all-resident layer; cold = 1 GiB streamed (read) between
+    # forwards, so the last-level cache holds other, clean data; warm = the
+    # same forward repeated back to back
+    log("[bench] decode cold/warm passes")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+
+    def decode_pass(cold):
+        resident.set_timing(True)
+        resident.timing()
+        nbytes, cnt = 0, 0
+        for i in range(W, n):
+            if cold:
+                flush.sum()
+            else:
+                resident.forward(xs_d[i], y=y_d)
+            _, dbg = resident.forward(xs_d[i], y=y_d, dbg=True)
+            torch.cuda.synchronize()
+            nbytes += int((dbg["counts"] > 0).sum().item()) * cfg.expert_bytes() + cfg.num_shared * cfg.expert_bytes()
+            cnt += 1
+        t = resident.timing()
+        resident.set_timing(False)
+        runs = cnt if cold else 2 * cnt
+        ms = (t["decode_gate_up"][0] + t["decode_down"][0]) * (cnt / runs)
+        return nbytes / (ms * 1e-3) / 1e9, nbytes / cnt, ms / cnt
+
+    dec_gbps, dec_bytes, dec_ms = decode_pass(cold=True)
+    warm_gbps, _, warm_ms = decode_pass(cold=False)
     del flush
-    dec_ms = tmd["decode_gate_up"][0] + tmd["decode_down"][0]
-    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
-    decode_roof = {"bound": "hbm", "kernel": "moe_decode_kernel (gate+up and down)",
+    read_ceiling = epq.measure_hbm_read(0, 1 << 30, 5)
+    decode_roof = {"bound": "hbm", "kernel": "decode gate+up and down (expert-weight bytes)",
                    "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                    "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                   "expert_bytes_per_forward": dec_bytes / n_dec,
-                   "kernel_us_per_forward": round(dec_ms / n_dec * 1e3, 2), "mall": "cold (1 GiB written between forwards)"}
+                   "measured_read_ceiling": round(read_ceiling, 1),
+                   "frac_of_measured_ceiling": round(dec_gbps / read_ceiling, 4),
+                   "expert_bytes_per_forward": dec_bytes,
+                   "kernel_us_per_forward": round(dec_ms * 1e3, 2),
+                   "mall": "cold (1 GiB streamed between forwards)",
+                   "warm": {"achieved": round(warm_gbps, 1), "kernel_us_per_forward": round(warm_ms * 1e3, 2)}}
+
+    # calibration copy for the HBM byte counters (FETCH_SIZE / WRITE_SIZE):
+    # CALIB_BYTES read and written by one device-to-device copy
+    cal_src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
 
     # pinned host -> device rate on this machine (the paging link), measured by the library
     h2d_gbps = epq.measure_h2d(0, 256 << 20, 3)

@@ -13,7 +13,7 @@ import numpy as np
 from . import _capi
 from ._capi import StrataError, check, lib
 
-__all__ = ["MoELayer", "StrataError", "measure_h2d", "replay_residency", "lib"]
+__all__ = ["MoELayer", "StrataError", "measure_h2d", "measure_hbm_read", "replay_residency", "lib"]
 
 _QUANT = {"int4_g64": _capi.Q_INT4_G64, "mxfp4_g32": _capi.Q_MXFP4_G32}
 _ROUTER = {"softmax": _capi.R_SOFTMAX, "sigmoid": _capi.R_SIGMOID}
@@ -143,6 +143,13 @@ def measure_h2d(device=-1, nbytes=256 << 20, iters=3) -> float:
     """Pinned host -> device copy rate in GB/s (the paging link)."""
     g = ctypes.c_double()
     check(lib().strata_measure_h2d(device, nbytes, iters, ctypes.byref(g)))
+    return g.value
+
+
+def measure_hbm_read(device=-1, nbytes=1 << 30, iters=5) -> float:
+    """HBM read ceiling in GB/s: best of `iters` streaming-read passes over `nbytes`."""
+    g = ctypes.c_double()
+    check(lib().strata_measure_hbm_read(device, nbytes, iters, ctypes.byref(g)))
     return g.value
 
 

@@ -67,6 +67,7 @@ EXPORTS = {
     "strata_moe_destroy": (None, [c_vp]),
     "strata_last_error": (ctypes.c_char_p, []),
     "strata_measure_h2d": (c_i32, [c_i32, c_u64, c_i32, ctypes.POINTER(ctypes.c_double)]),
+    "strata_measure_hbm_read": (c_i32, [c_i32, c_u64, c_i32, ctypes.POINTER(ctypes.c_double)]),
     "strata_residency_replay": (c_i32, [c_i32, c_i32, c_i32, c_u64, c_i32, c_vp, c_vp, c_vp,
                                         ctypes.POINTER(CacheStats)]),
 }

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libstrata_moe.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["kernels_route.hip", "kernels_expert.hip", "residency.cpp", "runtime.cpp"]
+SOURCES = ["kernels_route.hip", "kernels_expert.hip", "kernels_probe.hip", "residency.cpp", "runtime.cpp"]
 ARCH = "gfx950"
 
 

@@ -38,6 +38,8 @@ hipError_t launch_route(const float*, int, int, int, int, int, int, int, int32_t
 hipError_t launch_expert_gemm(const GemmArgs&, int, bool, bool, int, int, int, hipStream_t);
 int decode_log2_splits(int N, int K, int tiles_per_token, int T);
 int decode_grid(int N, int log2S, int n_tiles);
+uint64_t read_probe_bytes(uint64_t bytes);
+hipError_t launch_read_probe(const void* p, uint64_t bytes, uint32_t* out, hipStream_t s);
 int decode_dot_waves(int N, int K, int quant, int tiles_per_token, int T);
 hipError_t launch_decode_dot(const GemmArgs& a, int quant, bool gate_up, int T, int S, int n_tiles, hipStream_t s);
 hipError_t launch_combine(const float*, const int32_t*, const float*, int, int, int, int,
@@ -76,6 +78,12 @@ struct TimingRec {
   hipEvent_t a, b;
 };
 
+#ifndef STRATA_COPY_STREAMS
+#define STRATA_COPY_STREAMS 4
+#endif
+// Side streams the expert pages are copied on (all at the default priority).
+constexpr int kCopyStreams = STRATA_COPY_STREAMS;
+
 struct strata_moe {
   int H = 0, F = 0, E = 0, k = 0, S = 0, quant = 0, router = 0, policy = 0, budget = 0;
   int max_tokens = 0, device = 0;
@@ -112,10 +120,11 @@ struct strata_moe {
 
   int32_t* h_counts = nullptr;  // pinned
   Tile* h_tiles = nullptr;      // pinned
-  hipStream_t copy_stream = nullptr;
+  hipStream_t copy_streams[kCopyStreams] = {};
   hipEvent_t ev_fwd_done = nullptr;
   bool fwd_recorded = false;
-  std::vector<hipEvent_t> ev_copied, ev_wave_done;
+  std::vector<hipEvent_t> ev_copied;  // [wave][copy stream]
+  std::vector<hipEvent_t> ev_wave_done;
 
   ResidencyManager rm;
   uint64_t forwards = 0;
@@ -315,7 +324,8 @@ static void pack_expert(uint8_t* rec, const RecordLayout& lay, const strata_qmat
 static void release(strata_moe* h) {
   if (!h) return;
   if (h->device >= 0) (void)hipSetDevice(h->device);
-  if (h->copy_stream) (void)hipStreamSynchronize(h->copy_stream);
+  for (auto cs : h->copy_streams)
+    if (cs) (void)hipStreamSynchronize(cs);
   (void)hipDeviceSynchronize();
   for (auto& r : h->trecs) {
     h->ev_pool.push_back(r.a);
@@ -325,7 +335,8 @@ static void release(strata_moe* h) {
   for (auto e : h->ev_copied) (void)hipEventDestroy(e);
   for (auto e : h->ev_wave_done) (void)hipEventDestroy(e);
   if (h->ev_fwd_done) (void)hipEventDestroy(h->ev_fwd_done);
-  if (h->copy_stream) (void)hipStreamDestroy(h->copy_stream);
+  for (auto cs : h->copy_streams)
+    if (cs) (void)hipStreamDestroy(cs);
   void* dev[] = {h->d_pool, h->d_shared, h->d_router_w, h->d_router_bias, h->d_slot_ptr,
                  h->d_logits, h->d_idx, h->d_w, h->d_counts, h->d_offsets, h->d_perm, h->d_pos,
                  h->d_tiles_dev, h->d_tiles_host, h->d_ntiles, h->d_distinct, h->d_h, h->d_o,
@@ -444,7 +455,7 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   if ((st = host_alloc(&h->h_counts, size_t(h->E) * 4))) return st;
   if ((st = host_alloc(&h->h_tiles, h->max_tiles * sizeof(Tile)))) return st;
 
-  HIP_CHECK(hipStreamCreateWithFlags(&h->copy_stream, hipStreamNonBlocking));
+  for (auto& cs : h->copy_streams) HIP_CHECK(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
   HIP_CHECK(hipEventCreateWithFlags(&h->ev_fwd_done, hipEventDisableTiming));
 
   // preload experts 0..budget-1 into slots 0..budget-1
@@ -608,29 +619,42 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
       for (int i = he[w]; i < pe[w]; ++i) h->h_tiles[i].group_first -= he[w];
     }
     HIP_CHECK(hipMemcpyAsync(h->d_tiles_host, h->h_tiles, size_t(n) * sizeof(Tile), hipMemcpyHostToDevice, s));
-    while ((int)h->ev_copied.size() < nw) {
-      hipEvent_t a, b;
-      HIP_CHECK(hipEventCreateWithFlags(&a, hipEventDisableTiming));
+    while ((int)h->ev_wave_done.size() < nw) {
+      hipEvent_t b;
       HIP_CHECK(hipEventCreateWithFlags(&b, hipEventDisableTiming));
-      h->ev_copied.push_back(a);
       h->ev_wave_done.push_back(b);
+      for (int c = 0; c < kCopyStreams; ++c) {
+        hipEvent_t a;
+        HIP_CHECK(hipEventCreateWithFlags(&a, hipEventDisableTiming));
+        h->ev_copied.push_back(a);
+      }
     }
+    // A wave's misses are dealt round-robin over the copy streams, so the
+    // per-copy setup of one record overlaps the transfer of another; each
+    // stream first waits until the previous wave no longer reads its slots.
     const size_t rec = h->lay.bytes;
     for (int w = 0; w < nw; ++w) {
       const bool any_paged = pe[w] > he[w];
+      int used = 0;
       if (any_paged) {
-        if (w > 0) HIP_CHECK(hipStreamWaitEvent(h->copy_stream, h->ev_wave_done[w - 1], 0));
+        int c = 0;
         for (const PlanEntry& p : plan[w]) {
           if (!p.paged) continue;
           if (fault("h2d")) return fail(STRATA_E_HIP, "hipMemcpyAsync H2D failed (injected fault)");
+          if (c == used) {
+            if (w > 0) HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_wave_done[w - 1], 0));
+            ++used;
+          }
           HIP_CHECK(hipMemcpyAsync(h->h_slot_ptr[p.slot], h->host_store + rec * p.expert, rec,
-                                   hipMemcpyHostToDevice, h->copy_stream));
+                                   hipMemcpyHostToDevice, h->copy_streams[c]));
+          c = (c + 1) % kCopyStreams;
         }
-        HIP_CHECK(hipEventRecord(h->ev_copied[w], h->copy_stream));
+        for (int i = 0; i < used; ++i)
+          HIP_CHECK(hipEventRecord(h->ev_copied[w * kCopyStreams + i], h->copy_streams[i]));
       }
       HIP_CHECK(run_experts(h, x, h->d_tiles_host + hb[w], nullptr, he[w] - hb[w], decode, T, s));
       if (any_paged) {
-        HIP_CHECK(hipStreamWaitEvent(s, h->ev_copied[w], 0));
+        for (int i = 0; i < used; ++i) HIP_CHECK(hipStreamWaitEvent(s, h->ev_copied[w * kCopyStreams + i], 0));
         HIP_CHECK(run_experts(h, x, h->d_tiles_host + he[w], nullptr, pe[w] - he[w], decode, T, s));
       }
       HIP_CHECK(hipEventRecord(h->ev_wave_done[w], s));
@@ -810,6 +834,44 @@ strata_status strata_measure_h2d(int32_t device, uint64_t bytes, int32_t iters, 
   (void)hipHostFree(hbuf);
   if (e != hipSuccess) return fail(STRATA_E_HIP, std::string("h2d probe: ") + hipGetErrorString(e));
   *gbps = double(bytes) * iters / (ms * 1e-3) / 1e9;
+  return STRATA_OK;
+}
+
+strata_status strata_measure_hbm_read(int32_t device, uint64_t bytes, int32_t iters, double* gbps) {
+  if (!gbps || bytes < (uint64_t(64) << 20) || iters < 1) return fail(STRATA_E_INVALID, "bad arguments");
+  *gbps = 0.0;
+  if (device < 0) HIP_CHECK(hipGetDevice(&device));
+  HIP_CHECK(hipSetDevice(device));
+  void* dbuf = nullptr;
+  const uint64_t flag_off = (bytes + 255) & ~uint64_t(255);
+  if (hipMalloc(&dbuf, flag_off + 256) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(STRATA_E_NOMEM, "hipMalloc failed");
+  }
+  uint32_t* flag = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(dbuf) + flag_off);
+  hipStream_t s = nullptr;
+  hipEvent_t a = nullptr, b = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreate(&a);
+  if (e == hipSuccess) e = hipEventCreate(&b);
+  if (e == hipSuccess) e = hipMemsetAsync(dbuf, 0x11, flag_off + 256, s);
+  if (e == hipSuccess) e = launch_read_probe(dbuf, bytes, flag, s);  // warm-up pass
+  float best = 0.0f;
+  for (int i = 0; i < iters && e == hipSuccess; ++i) {
+    e = hipEventRecord(a, s);
+    if (e == hipSuccess) e = launch_read_probe(dbuf, bytes, flag, s);
+    if (e == hipSuccess) e = hipEventRecord(b, s);
+    if (e == hipSuccess) e = hipEventSynchronize(b);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+    if (e == hipSuccess && (best == 0.0f || ms < best)) best = ms;
+  }
+  if (a) (void)hipEventDestroy(a);
+  if (b) (void)hipEventDestroy(b);
+  if (s) (void)hipStreamDestroy(s);
+  (void)hipFree(dbuf);
+  if (e != hipSuccess) return fail(STRATA_E_HIP, std::string("read probe: ") + hipGetErrorString(e));
+  *gbps = double(read_probe_bytes(bytes)) / (best * 1e-3) / 1e9;
   return STRATA_OK;
 }
 

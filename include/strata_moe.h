@@ -225,6 +225,16 @@ const char* strata_last_error(void);
  * Errors: E_INVALID (bytes == 0, iters < 1, NULL out), E_NOMEM, E_HIP. */
 strata_status strata_measure_h2d(int32_t device, uint64_t bytes, int32_t iters, double* gbps);
 
+/* Measures the HBM read ceiling that decode bandwidth is compared with (the
+ * "measured read ceiling" of the SM86 kernel paragraph of the ro99/strata
+ * README): allocates `bytes` of device memory on `device` (at least 64 MiB;
+ * use well over the 256 MB last-level cache so every pass streams from HBM),
+ * fills it, then times `iters` passes of a streaming-read kernel (each
+ * workgroup reads its own contiguous share with non-temporal 16-byte loads)
+ * with HIP events, frees it and writes the best pass in GB/s (1e9 B/s).
+ * Errors: E_INVALID (bytes < 64 MiB, iters < 1, NULL out), E_NOMEM, E_HIP. */
+strata_status strata_measure_hbm_read(int32_t device, uint64_t bytes, int32_t iters, double* gbps);
+
 /* Dry-run planner (host only, touches no GPU): replays the residency policy of
  * a layer with E experts and `budget` slots over a trace of forwards and
  * reports what a real run would page, the placement-plan side of the budget
