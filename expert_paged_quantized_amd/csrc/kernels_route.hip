@@ -355,6 +355,12 @@ __device__ __forceinline__ int block_scan1024(int v, int* wave_tot, int& total) 
 // Writes counts, offsets, the tile list (ascending expert, then the shared
 // expert) and the distinct-expert counter from per-expert totals held one per
 // thread of a 1024-thread workgroup (E <= 1024).
+// Tiles are emitted heaviest first so that persistent workgroups, which take
+// items in list order, finish together: the shared expert's tiles (all T rows,
+// mostly full), then the routed tiles grouped by their number of 32-row column
+// tiles (4, 3, 2, 1), experts ascending inside a group.  Tiles cover disjoint
+// rows, so their order changes no result.  With one tile per expert (decode)
+// the order is simply by expert.
 __device__ __forceinline__ void emit_counts_and_tiles(int c, int o, int total, int T, int k, int E,
                                                       int S, int tile_rows, int shared_slot,
                                                       int* wave_tot, int32_t* counts,
@@ -364,35 +370,49 @@ __device__ __forceinline__ void emit_counts_and_tiles(int c, int o, int total, i
   const int e = threadIdx.x;
   const bool used = e < E && c > 0;
   const int nt = used ? (c + tile_rows - 1) / tile_rows : 0;
+  const int TK = T * k;
+  const int nsh = S ? (T + tile_rows - 1) / tile_rows : 0;
   int ntot;
   const int to = block_scan1024(nt, wave_tot, ntot);
   int nd_tot;
   (void)block_scan1024(used ? 1 : 0, wave_tot, nd_tot);
+  auto put = [&](int at, int ex, int slot, int row_begin, int nrows, int first, int count) {
+    Tile tl;
+    tl.expert = ex;
+    tl.slot = slot;
+    tl.row_begin = row_begin;
+    tl.nrows = nrows;
+    tl.group_first = first;
+    tl.group_count = count;
+    tiles[at] = tl;
+  };
+  for (int i = e; i < nsh; i += 1024)
+    put(i, E, shared_slot, TK + i * tile_rows, min(tile_rows, T - i * tile_rows), 0, nsh);
+  if (tile_rows > kPrefillTM) {  // one tile per expert
+    if (used) put(nsh + to, e, e, o, c, nsh + to, 1);
+  } else {
+    // column tiles of each tile: full tiles have tile_rows / 32, the last one
+    // ceil(rem / 32); group g = column tiles, g = 4 first
+    const int full = c / tile_rows, rem = c - full * tile_rows;
+    const int last_g = rem ? (rem + 31) / 32 : 0;
+    const int gfull = tile_rows / 32;
+    int base = nsh;
+    for (int g = gfull; g >= 1; --g) {
+      const int mine = (g == gfull ? full : 0) + (last_g == g ? 1 : 0);
+      int tot;
+      const int at = block_scan1024(used ? mine : 0, wave_tot, tot);
+      if (used && mine > 0) {
+        int j = 0;
+        if (g == gfull)
+          for (; j < full; ++j) put(base + at + j, e, e, o + j * tile_rows, tile_rows, base + at, mine);
+        if (last_g == g) put(base + at + j, e, e, o + full * tile_rows, rem, base + at, mine);
+      }
+      base += tot;
+    }
+  }
   if (e < E) {
     counts[e] = c;
     offsets[e] = o;
-    for (int j = 0; j < nt; ++j) {
-      Tile tl;
-      tl.expert = e;
-      tl.slot = e;
-      tl.row_begin = o + j * tile_rows;
-      tl.nrows = min(tile_rows, c - j * tile_rows);
-      tl.group_first = to;
-      tl.group_count = nt;
-      tiles[to + j] = tl;
-    }
-  }
-  const int TK = T * k;
-  const int nsh = S ? (T + tile_rows - 1) / tile_rows : 0;
-  for (int i = e; i < nsh; i += 1024) {
-    Tile tl;
-    tl.expert = E;
-    tl.slot = shared_slot;
-    tl.row_begin = TK + i * tile_rows;
-    tl.nrows = min(tile_rows, T - i * tile_rows);
-    tl.group_first = ntot;
-    tl.group_count = nsh;
-    tiles[ntot + i] = tl;
   }
   if (e == 0) {
     offsets[E] = total;

@@ -613,10 +613,17 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
       pe[w] = n;
     }
     if ((size_t)n > h->max_tiles) return fail(STRATA_E_HIP, "tile list overflow");
-    // group indices are relative to the first tile of each launch's range
+    // group indices are relative to the first tile of each launch's range;
+    // prefill ranges then run heaviest tiles first (more 32-row column tiles
+    // first, list order otherwise), as the device-built list does
     for (int w = 0; w < nw; ++w) {
       for (int i = hb[w]; i < he[w]; ++i) h->h_tiles[i].group_first -= hb[w];
       for (int i = he[w]; i < pe[w]; ++i) h->h_tiles[i].group_first -= he[w];
+      if (!decode) {
+        auto heavier = [](const Tile& a, const Tile& b) { return (a.nrows + 31) / 32 > (b.nrows + 31) / 32; };
+        std::stable_sort(h->h_tiles + hb[w], h->h_tiles + he[w], heavier);
+        std::stable_sort(h->h_tiles + he[w], h->h_tiles + pe[w], heavier);
+      }
     }
     HIP_CHECK(hipMemcpyAsync(h->d_tiles_host, h->h_tiles, size_t(n) * sizeof(Tile), hipMemcpyHostToDevice, s));
     while ((int)h->ev_wave_done.size() < nw) {
