@@ -97,6 +97,19 @@ CONFIGS = {
 }
 CONFIG_ORDER = ["tiny", "mixtral", "qwen3_30b_a3b", "glm45_air", "e512_mxfp4"]
 
+# Wider routing (the ro99/strata README model table lists an 896-expert top-16
+# MXFP4 model and 256-expert top-6 FP4 models; it gives no hidden or expert
+# sizes, so those, the router kind and the budgets here are choices of this
+# recipe, not the pages').
+WIDE_CONFIGS = {
+    "e896_top16_mxfp4": LayerConfig("e896_top16_mxfp4", 5, 2048, 512, 896, 16, 0, MXFP4, SOFTMAX, 1.1,
+                                    0.18, (1,), 2048),
+    "e256_top6_fp4": LayerConfig("e256_top6_fp4", 6, 4096, 1024, 256, 6, 0, MXFP4, SIGMOID, None, 0.25,
+                                 (1,), 1180),
+}
+WIDE_ORDER = ["e896_top16_mxfp4", "e256_top6_fp4"]
+CONFIGS.update(WIDE_CONFIGS)
+
 
 # ----------------------------------------------------------------------------
 # bf16 helpers (encoding only)
