@@ -8,6 +8,11 @@ timed region starts.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline]
+  python bench.py --trace-summary TRACE_DIR
+      per-kernel duration table (markdown) of a rocprofv3 --kernel-trace run of
+      this script: the events-timed paged region, the events-timed all-resident
+      region (both delimited by the one-element cumsum markers recorded around
+      them) and the whole run.
   python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload NAME]
       turns two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
       WRITE_SIZE) into profiles/traffic_<workload>.json, which later runs use
@@ -50,6 +55,7 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=2)
     ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR")
     return ap.parse_args()
 
 
@@ -63,6 +69,36 @@ def kernel_source_hash():
 
 def traffic_path(workload):
     return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def trace_summary(trace_dir):
+    """Markdown tables of kernel durations from a rocprofv3 kernel trace of this
+    script, per marked region (see the module docstring)."""
+    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    assert f, f"no kernel_trace.csv under {trace_dir}"
+    rows = sorted(csv.DictReader(open(f[0])), key=lambda r: int(r["Start_Timestamp"]))
+
+    def short(n):
+        return n[n.find("strata::") + 8:].split("(")[0] if "strata::" in n else n[:60]
+    marks = [i for i, r in enumerate(rows) if "scan" in r["Kernel_Name"].lower()]
+
+    def table(sel, title):
+        agg = {}
+        for r in sel:
+            agg.setdefault(short(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        out = [f"### {title}", "", "| kernel | calls | total us | avg us | min us | max us |",
+               "|---|---|---|---|---|---|"]
+        for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"| `{k}` | {len(v)} | {sum(v):.1f} | {statistics.mean(v):.2f} | {min(v):.2f} | "
+                       f"{max(v):.2f} |")
+        return "\n".join(out) + "\n"
+    parts = []
+    if len(marks) >= 4:
+        parts.append(table(rows[marks[0] + 1:marks[1]], "Events-timed paged region (as configured)"))
+        parts.append(table(rows[marks[2] + 1:marks[3]], "Events-timed all-resident region"))
+    parts.append(table(rows, "Whole run"))
+    print("\n".join(parts))
 
 
 def pmc_summary(fetch_dir, write_dir, workload):
@@ -121,6 +157,9 @@ def main():
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
         return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.cpu_baseline_only:
         from synth import CONFIGS, make_layer
         cfg = CONFIGS[args.workload]
@@ -162,6 +201,8 @@ def main():
         layer.forward(xs_p[i], y=y_p)
         layer.forward(xs_d[i], y=y_d)
 
+    mark = torch.ones(4, device=dev)
+
     def timed_region(layer, events=False, per_step_sync=True):
         for i in range(W):
             run(layer, i)
@@ -169,6 +210,8 @@ def main():
         layer.set_timing(events)
         layer.timing()  # reset
         per = []
+        if events:  # a one-element cumsum marks the timed steps in a kernel trace
+            mark.cumsum(0)
         torch.cuda.synchronize()
         t_all = time.perf_counter()
         for i in range(W, n):
@@ -179,6 +222,8 @@ def main():
                 per.append(time.perf_counter() - a)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t_all
+        if events:
+            mark.cumsum(0)
         tm = layer.timing()
         layer.set_timing(False)
         return dt, per, tm
@@ -186,14 +231,9 @@ def main():
     # (1) headline: as configured, no instrumentation
     log("[bench] timed region: as configured")
     dt, per, _ = timed_region(paged)
-    # (2) the same inputs with HIP events around every kernel (kernel durations);
-    # a one-element cumsum before and after marks this region in a kernel trace
+    # (2) the same inputs with HIP events on every kernel (kernel durations)
     log("[bench] timed region: kernel events")
-    mark = torch.ones(4, device=dev)
-    mark.cumsum(0)
     dt_ev, _, tm = timed_region(paged, events=True)
-    mark.cumsum(0)
-    torch.cuda.synchronize()
     # (3) all experts resident: the GPU path alone
     log("[bench] timed region: all resident")
     dt_r, _, _ = timed_region(resident, per_step_sync=False)

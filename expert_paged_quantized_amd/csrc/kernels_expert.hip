@@ -799,11 +799,11 @@ static void launch_decode(const GemmArgs& a, int T, int log2S, int grid, hipStre
                                       (size_t)kDecWaves * kDecodeMaxT * 32 * 4);
   const int np = (T * S * 64 + kDecWaves * 64 - 1) / (kDecWaves * 64);
   if (np <= 1)
-    moe_decode_kernel<QF, GATE_UP, 1><<<grid, kDecWaves * 64, lds, s>>>(a, log2S);
+    launch_k(moe_decode_kernel<QF, GATE_UP, 1>, dim3(grid), dim3(kDecWaves * 64), lds, s, a, log2S);
   else if (np <= 2)
-    moe_decode_kernel<QF, GATE_UP, 2><<<grid, kDecWaves * 64, lds, s>>>(a, log2S);
+    launch_k(moe_decode_kernel<QF, GATE_UP, 2>, dim3(grid), dim3(kDecWaves * 64), lds, s, a, log2S);
   else
-    moe_decode_kernel<QF, GATE_UP, 4><<<grid, kDecWaves * 64, lds, s>>>(a, log2S);
+    launch_k(moe_decode_kernel<QF, GATE_UP, 4>, dim3(grid), dim3(kDecWaves * 64), lds, s, a, log2S);
 }
 
 // Decode split: waves per row tile, log2.  Enough waves for about 16 per CU
@@ -845,11 +845,11 @@ template <int QF, bool GATE_UP, int TT>
 static void launch_dot_tt(const GemmArgs& a, int S, int grid, size_t lds, hipStream_t s) {
   const int npr = (a.K / 8 + 64 * S - 1) / (64 * S);
   if (npr <= 1)
-    moe_decode_dot_kernel<QF, GATE_UP, TT, 1><<<grid, 64 * S, lds, s>>>(a);
+    launch_k(moe_decode_dot_kernel<QF, GATE_UP, TT, 1>, dim3(grid), dim3(64 * S), lds, s, a);
   else if (npr <= 2)
-    moe_decode_dot_kernel<QF, GATE_UP, TT, 2><<<grid, 64 * S, lds, s>>>(a);
+    launch_k(moe_decode_dot_kernel<QF, GATE_UP, TT, 2>, dim3(grid), dim3(64 * S), lds, s, a);
   else
-    moe_decode_dot_kernel<QF, GATE_UP, TT, 4><<<grid, 64 * S, lds, s>>>(a);
+    launch_k(moe_decode_dot_kernel<QF, GATE_UP, TT, 4>, dim3(grid), dim3(64 * S), lds, s, a);
 }
 
 template <int QF, bool GATE_UP>
@@ -901,14 +901,14 @@ hipError_t launch_expert_gemm(const GemmArgs& a, int quant, bool gate_up, bool d
   } else {
     if (quant == Q_INT4) {
       if (gate_up)
-        moe_prefill_kernel<Q_INT4, true><<<grid, kPreThreads, 0, s>>>(a);
+        launch_k(moe_prefill_kernel<Q_INT4, true>, dim3(grid), dim3(kPreThreads), 0, s, a);
       else
-        moe_prefill_kernel<Q_INT4, false><<<grid, kPreThreads, 0, s>>>(a);
+        launch_k(moe_prefill_kernel<Q_INT4, false>, dim3(grid), dim3(kPreThreads), 0, s, a);
     } else {
       if (gate_up)
-        moe_prefill_kernel<Q_MXFP4, true><<<grid, kPreThreads, 0, s>>>(a);
+        launch_k(moe_prefill_kernel<Q_MXFP4, true>, dim3(grid), dim3(kPreThreads), 0, s, a);
       else
-        moe_prefill_kernel<Q_MXFP4, false><<<grid, kPreThreads, 0, s>>>(a);
+        launch_k(moe_prefill_kernel<Q_MXFP4, false>, dim3(grid), dim3(kPreThreads), 0, s, a);
     }
   }
   return hipGetLastError();
@@ -916,7 +916,7 @@ hipError_t launch_expert_gemm(const GemmArgs& a, int quant, bool gate_up, bool d
 
 hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, int T, int k, int H,
                           int shared_row0, uint16_t* y, hipStream_t s) {
-  combine_kernel<<<T, 256, 0, s>>>(o, pos, w, k, H, shared_row0, y);
+  launch_k(combine_kernel, dim3(T), dim3(256), 0, s, o, pos, w, k, H, shared_row0, y);
   return hipGetLastError();
 }
 

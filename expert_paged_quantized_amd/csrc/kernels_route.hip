@@ -568,10 +568,10 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
   // logit per wave (small T or few experts)
   const int blocked_waves = ((T + kRbTT - 1) / kRbTT) * ((E + kRbTE - 1) / kRbTE);
   if (blocked_waves >= 2048) {
-    router_block_kernel<<<(blocked_waves + 3) / 4, 256, 0, s>>>(x, wr, bias, logits, x16, T, E, H);
+    launch_k(router_block_kernel, dim3((blocked_waves + 3) / 4), dim3(256), 0, s, x, wr, bias, logits, x16, T, E, H);
   } else {
     const int waves = T * E;
-    router_logits_kernel<1, 1><<<(waves + 3) / 4, 256, 0, s>>>(x, wr, bias, logits, x16, T, E, H);
+    launch_k(router_logits_kernel<1, 1>, dim3((waves + 3) / 4), dim3(256), 0, s, x, wr, bias, logits, x16, T, E, H);
   }
   return hipGetLastError();
 }

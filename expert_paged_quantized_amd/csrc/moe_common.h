@@ -1,5 +1,6 @@
 // Definitions shared by the HIP kernels and the host runtime of the MoE layer.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -66,5 +67,25 @@ struct GemmArgs {
   void* out;                 // gate+up: h [R, F]; down: o fp32 [R, H]
   int32_t out_ld;            // F or H
 };
+
+// Kernel timing: when the runtime times a single-kernel step it sets this
+// per-thread pair, and that kernel is launched with the events attached to the
+// dispatch itself (hipExtLaunchKernel), which timestamps the kernel's own
+// start and end rather than the queue around it.
+struct KernelTimer {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;  // set by the launch that took the events
+};
+extern thread_local KernelTimer g_ktimer;
+
+// Launches `kernel` on `s`, timed by g_ktimer if set.
+template <typename K, typename... Args>
+inline void launch_k(K kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args... args) {
+  if (g_ktimer.start && g_ktimer.stop && !g_ktimer.used) {
+    g_ktimer.used = true;
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, g_ktimer.start, g_ktimer.stop, 0u, args...);
+  } else
+    kernel<<<grid, block, shmem, s>>>(args...);
+}
 
 }  // namespace strata

@@ -78,6 +78,10 @@ struct TimingRec {
   hipEvent_t a, b;
 };
 
+namespace strata {
+thread_local KernelTimer g_ktimer;
+}  // namespace strata
+
 #ifndef STRATA_COPY_STREAMS
 #define STRATA_COPY_STREAMS 4
 #endif
@@ -481,16 +485,32 @@ static hipEvent_t pool_event(strata_moe* h) {
   return e;
 }
 
+// Times one step of a forward.  Single-kernel steps get the events attached to
+// the kernel's own dispatch (its start and end); the routing group, several
+// kernels, is bracketed by events recorded on the stream around it.
 template <class Fn>
 static hipError_t timed(strata_moe* h, int cls, hipStream_t s, Fn&& fn) {
   if (!h->timing) return fn();
   hipEvent_t a = pool_event(h), b = pool_event(h);
   if (!a || !b) return hipErrorOutOfMemory;
-  hipError_t e = hipEventRecord(a, s);
-  if (e != hipSuccess) return e;
-  e = fn();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(b, s);
+  hipError_t e;
+  if (cls == STRATA_K_GROUP) {
+    e = hipEventRecord(a, s);
+    if (e != hipSuccess) return e;
+    e = fn();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(b, s);
+  } else {
+    strata::g_ktimer = {a, b, false};
+    e = fn();
+    const bool used = strata::g_ktimer.used;
+    strata::g_ktimer = {};
+    if (!used) {  // nothing was launched (empty range): no record
+      h->ev_pool.push_back(a);
+      h->ev_pool.push_back(b);
+      return e;
+    }
+  }
   h->trecs.push_back({cls, a, b});
   return e;
 }
