@@ -30,7 +30,11 @@ R4  weights: softmax restricted to the selected logits, or sigmoid of each
     selected logit divided by their sum; no epsilon, no scaling.
 R5  tokens grouped by expert, ascending expert id, ascending token within one.
 R6  nibble 2i of a row is the low nibble of byte i.  int4: w = s*q + b with
-    bf16 s, b per 64 along the input dim.  MXFP4: E2M1 value times 2^(e-127).
+    bf16 s, b per 64 (or 128) along the input dim.  MXFP4: E2M1 value times
+    2^(e-127).  NVFP4 (named, not defined, in the ro99/strata README model
+    table; taken as the published format): E2M1 value times an E4M3 (OCP FP8,
+    bias 7) scale per 16 inputs times one fp32 scale per matrix; E4M3 NaN
+    bytes (0x7F, 0xFF) are refused like E8M0 0/255.
 R7  expert: g = Wg x, u = Wu x, a = silu(g)*u, o = Wd a; the shared expert is
     the same FFN with weight 1 and no gate.
 R8  y[t] = sum_j w[t,j] o_j + shared(x[t]), j ascending, shared last.
@@ -63,14 +67,22 @@ def _unpack_nibbles(codes: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequant_int4_g64(codes, scales, biases) -> np.ndarray:
-    """int4 group-64 affine: w[n,k] = s[n,k//64] * q[n,k] + b[n,k//64] (R6), fp64 [N, K]."""
+def dequant_int4_affine(codes, scales, biases, group) -> np.ndarray:
+    """int4 affine: w[n,k] = s[n,k//G] * q[n,k] + b[n,k//G] (R6), fp64 [N, K]."""
     q = _unpack_nibbles(codes).astype(np.float64)
     N, K = q.shape
     s = bf16_to_f64(scales)
     b = bf16_to_f64(biases)
-    assert s.shape == (N, K // 64) and b.shape == (N, K // 64)
-    return (q.reshape(N, K // 64, 64) * s[..., None] + b[..., None]).reshape(N, K)
+    assert s.shape == (N, K // group) and b.shape == (N, K // group)
+    return (q.reshape(N, K // group, group) * s[..., None] + b[..., None]).reshape(N, K)
+
+
+def dequant_int4_g64(codes, scales, biases) -> np.ndarray:
+    return dequant_int4_affine(codes, scales, biases, 64)
+
+
+def dequant_int4_g128(codes, scales, biases) -> np.ndarray:
+    return dequant_int4_affine(codes, scales, biases, 128)
 
 
 def e2m1_value(code) -> np.ndarray:
@@ -101,12 +113,43 @@ def dequant_mxfp4_g32(codes, scales) -> np.ndarray:
     return (v.reshape(N, K // 32, 32) * sc[..., None]).reshape(N, K)
 
 
+def e4m3_value(b) -> np.ndarray:
+    """OCP FP8 E4M3 from its bits: sign bit 7, exponent bits 6..3 (bias 7),
+    mantissa bits 2..0; exponent 0 is subnormal (m * 2^-9); S.1111.111 is NaN
+    and is refused (a scale must be a number), there is no infinity."""
+    b = np.asarray(b, dtype=np.int64)
+    if np.any((b & 0x7F) == 0x7F):
+        raise ValueError("E4M3 scale byte is NaN: checkpoint fails admission")
+    sign = np.where((b >> 7) & 1, -1.0, 1.0)
+    ex = (b >> 3) & 15
+    man = b & 7
+    mag = np.where(ex == 0, man * 2.0 ** -9, np.exp2(ex - 7.0) * (1.0 + man / 8.0))
+    return sign * mag
+
+
+def dequant_nvfp4_g16(codes, scales, global_scale) -> np.ndarray:
+    """NVFP4: w[n,k] = e2m1(code[n,k]) * e4m3(s[n,k//16]) * g, fp64 [N, K]."""
+    v = e2m1_value(_unpack_nibbles(codes))
+    N, K = v.shape
+    sc = e4m3_value(scales)
+    assert sc.shape == (N, K // 16)
+    g = float(np.float32(global_scale))
+    if not np.isfinite(g) or g <= 0:
+        raise ValueError("NVFP4 matrix scale must be finite and positive")
+    return (v.reshape(N, K // 16, 16) * sc[..., None]).reshape(N, K) * g
+
+
 def dequant_qmat(quant: str, m) -> np.ndarray:
-    """Dequantise one packed matrix object with .codes/.scales/.biases."""
+    """Dequantise one packed matrix object with .codes/.scales/.biases
+    (and .global_scale for NVFP4)."""
     if quant == "int4_g64":
         return dequant_int4_g64(m.codes, m.scales, m.biases)
+    if quant == "int4_g128":
+        return dequant_int4_g128(m.codes, m.scales, m.biases)
     if quant == "mxfp4_g32":
         return dequant_mxfp4_g32(m.codes, m.scales)
+    if quant == "nvfp4_g16":
+        return dequant_nvfp4_g16(m.codes, m.scales, m.global_scale)
     raise ValueError(f"unknown quant {quant!r}")
 
 

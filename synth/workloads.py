@@ -22,7 +22,10 @@ a stated recipe, not data:
   bias = min, both rounded to bf16, code = clamp(rint((w - bias)/scale), 0, 15);
 * MXFP4 encoding (OCP MX v1.0 recommended conversion): E8M0 exponent
   floor(log2(amax)) - 2 + 127 clamped to [1, 254], E2M1 round-to-nearest-even
-  with saturation at +-6.
+  with saturation at +-6;
+* int4 group-128: as group-64 with groups of 128;
+* NVFP4 encoding (the published two-level recipe): fp32 matrix scale
+  amax / (6 * 448), E4M3 block scale per 16 rounded to nearest, E2M1 codes.
 
 Packing (the layout the C ABI takes, row-major [out, in], quantised along in):
 codes u8 [rows, in/2] with element 2i in the low nibble of byte i.
@@ -38,7 +41,10 @@ from typing import Optional
 import numpy as np
 
 INT4 = "int4_g64"
+INT4_G128 = "int4_g128"
 MXFP4 = "mxfp4_g32"
+NVFP4 = "nvfp4_g16"
+AFFINE = (INT4, INT4_G128)
 SOFTMAX = "softmax"
 SIGMOID = "sigmoid"
 
@@ -61,7 +67,7 @@ class LayerConfig:
 
     @property
     def group(self) -> int:
-        return 64 if self.quant == INT4 else 32
+        return {INT4: 64, INT4_G128: 128, MXFP4: 32, NVFP4: 16}[self.quant]
 
     @property
     def budget(self) -> int:
@@ -75,11 +81,12 @@ class LayerConfig:
     def expert_bytes(self) -> int:
         """Packed bytes of one expert (gate + up + down: codes, scales, biases)."""
         H, F, G = self.hidden, self.ffn, self.group
-        if self.quant == INT4:
+        if self.quant in AFFINE:
             per = lambda n, k: n * k // 2 + 2 * (n * (k // G)) * 2
         else:
             per = lambda n, k: n * k // 2 + n * (k // G)
-        return 2 * per(F, H) + per(H, F)
+        extra = 3 * 4 if self.quant == NVFP4 else 0  # one fp32 scale per matrix
+        return 2 * per(F, H) + per(H, F) + extra
 
     def scaled(self, **kw) -> "LayerConfig":
         return dataclasses.replace(self, **kw)
@@ -110,6 +117,18 @@ WIDE_CONFIGS = {
 WIDE_ORDER = ["e896_top16_mxfp4", "e256_top6_fp4"]
 CONFIGS.update(WIDE_CONFIGS)
 
+# More 4-bit formats (the same table: a 256-expert top-8 model in INT4
+# group-128 W4A16, and a 256-expert + 1 shared top-10 model in NVFP4 or
+# MXFP4).  Again H, F, router kind, bias and budgets are this recipe's choices.
+FORMAT_CONFIGS = {
+    "e256_int4g128": LayerConfig("e256_int4g128", 7, 2048, 1024, 256, 8, 0, INT4_G128, SIGMOID, None,
+                                 0.1, (1,), 1180),
+    "e256_nvfp4": LayerConfig("e256_nvfp4", 8, 2048, 512, 256, 10, 1, NVFP4, SOFTMAX, 1.1, 0.18,
+                              (1,), 2048),
+}
+FORMAT_ORDER = ["e256_int4g128", "e256_nvfp4"]
+CONFIGS.update(FORMAT_CONFIGS)
+
 
 # ----------------------------------------------------------------------------
 # bf16 helpers (encoding only)
@@ -135,10 +154,10 @@ def _pack_nibbles(q: np.ndarray) -> np.ndarray:
     return (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
 
 
-def quantize_int4_g64(w: np.ndarray):
-    """w float32 [N, K] -> (codes u8 [N,K/2], scales bf16 bits [N,K/64], biases bf16 bits [N,K/64])."""
+def quantize_int4(w: np.ndarray, group: int):
+    """w float32 [N, K] -> (codes u8 [N,K/2], scales bf16 bits [N,K/G], biases bf16 bits [N,K/G])."""
     N, K = w.shape
-    g = w.reshape(N, K // 64, 64).astype(np.float32)
+    g = w.reshape(N, K // group, group).astype(np.float32)
     mn = g.min(axis=2)
     mx = g.max(axis=2)
     s_bits = f32_to_bf16_bits((mx - mn) / np.float32(15.0))
@@ -149,6 +168,10 @@ def quantize_int4_g64(w: np.ndarray):
         q = np.where(s > 0, np.rint((g - b) / np.where(s > 0, s, 1)), 0)
     q = np.clip(q, 0, 15).astype(np.uint8).reshape(N, K)
     return _pack_nibbles(q), s_bits, b_bits
+
+
+def quantize_int4_g64(w: np.ndarray):
+    return quantize_int4(w, 64)
 
 
 # E2M1 magnitudes in code order (sign is bit 3); used here only to encode.
@@ -183,6 +206,40 @@ def quantize_mxfp4_g32(w: np.ndarray):
     return _pack_nibbles(codes), e.astype(np.uint8)
 
 
+# E4M3 (OCP FP8, bias 7) magnitudes of the 127 non-NaN non-negative codes, in
+# code order; used here only to encode scales.
+_E4M3_GRID = np.array([(m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+                       for e in range(16) for m in range(8)][:127], dtype=np.float64)
+
+
+def _e4m3_encode_pos(v: np.ndarray) -> np.ndarray:
+    """Non-negative values -> E4M3 codes, round to nearest (ties to even code),
+    saturating at 448 (code 0x7E)."""
+    mids = (_E4M3_GRID[:-1] + _E4M3_GRID[1:]) / 2.0
+    code = np.searchsorted(mids, v, side="left")
+    tie = v == mids[np.minimum(code, 125)]
+    code = code + (tie & (code % 2 == 1))
+    return np.minimum(code, 126).astype(np.uint8)
+
+
+def quantize_nvfp4_g16(w: np.ndarray):
+    """w float32 [N, K] -> (codes u8 [N,K/2], E4M3 scales u8 [N,K/16], fp32 matrix scale).
+
+    The usual two-level recipe: matrix scale g = amax / (6 * 448); block scale =
+    E4M3(amax_block / (6 * g)); codes = E2M1(w / (block scale * g)), RNE."""
+    N, K = w.shape
+    amax = float(np.abs(w).max())
+    g = np.float32(amax / (6.0 * 448.0)) if amax > 0 else np.float32(1.0)
+    blk = w.reshape(N, K // 16, 16).astype(np.float64)
+    bmax = np.abs(blk).max(axis=2)
+    sc = _e4m3_encode_pos(bmax / (6.0 * float(g)))
+    sval = _E4M3_GRID[sc]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        scaled = np.where(sval[..., None] > 0, blk / (sval[..., None] * float(g)), 0.0)
+    codes = _e2m1_encode(scaled).reshape(N, K)
+    return _pack_nibbles(codes), sc, g
+
+
 # ----------------------------------------------------------------------------
 # layer weights
 # ----------------------------------------------------------------------------
@@ -191,6 +248,7 @@ class QMat:
     codes: np.ndarray
     scales: np.ndarray
     biases: Optional[np.ndarray]
+    global_scale: Optional[np.ndarray] = None  # NVFP4: fp32 per matrix ([E] for a stack)
 
 
 @dataclasses.dataclass
@@ -208,19 +266,24 @@ class LayerWeights:
     def expert(self, e: int):
         """(gate, up, down) QMats of routed expert e (views)."""
         def sl(m):
-            return QMat(m.codes[e], m.scales[e], None if m.biases is None else m.biases[e])
+            return QMat(m.codes[e], m.scales[e], None if m.biases is None else m.biases[e],
+                        None if m.global_scale is None else m.global_scale[e])
         return sl(self.gate), sl(self.up), sl(self.down)
 
     def shared(self):
         def sl(m):
-            return QMat(m.codes[0], m.scales[0], None if m.biases is None else m.biases[0])
+            return QMat(m.codes[0], m.scales[0], None if m.biases is None else m.biases[0],
+                        None if m.global_scale is None else m.global_scale[0])
         return sl(self.sh_gate), sl(self.sh_up), sl(self.sh_down)
 
 
 def _quant(cfg: LayerConfig, w: np.ndarray) -> QMat:
-    if cfg.quant == INT4:
-        c, s, b = quantize_int4_g64(w)
+    if cfg.quant in AFFINE:
+        c, s, b = quantize_int4(w, cfg.group)
         return QMat(c, s, b)
+    if cfg.quant == NVFP4:
+        c, s, g = quantize_nvfp4_g16(w)
+        return QMat(c, s, None, np.float32(g))
     c, s = quantize_mxfp4_g32(w)
     return QMat(c, s, None)
 
@@ -228,9 +291,12 @@ def _quant(cfg: LayerConfig, w: np.ndarray) -> QMat:
 def _alloc_stack(cfg: LayerConfig, n_exp: int, rows: int, cols: int) -> QMat:
     G = cfg.group
     codes = np.empty((n_exp, rows, cols // 2), np.uint8)
-    if cfg.quant == INT4:
+    if cfg.quant in AFFINE:
         return QMat(codes, np.empty((n_exp, rows, cols // G), np.uint16),
                     np.empty((n_exp, rows, cols // G), np.uint16))
+    if cfg.quant == NVFP4:
+        return QMat(codes, np.empty((n_exp, rows, cols // G), np.uint8), None,
+                    np.empty((n_exp,), np.float32))
     return QMat(codes, np.empty((n_exp, rows, cols // G), np.uint8), None)
 
 
@@ -239,6 +305,8 @@ def _store(dst: QMat, e: int, src: QMat):
     dst.scales[e] = src.scales
     if dst.biases is not None:
         dst.biases[e] = src.biases
+    if dst.global_scale is not None:
+        dst.global_scale[e] = src.global_scale
 
 
 def _gen_expert(cfg: LayerConfig, seed: int, e: int):

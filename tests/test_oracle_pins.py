@@ -14,7 +14,8 @@ import pytest
 import oracle
 from oracle import moe as om
 from oracle.residency import LFU, LRU, ResidencyModel
-from synth import (CONFIGS, f32_to_bf16_bits, make_layer, make_tokens, quantize_int4_g64,
+from synth import (CONFIGS, f32_to_bf16_bits, make_layer, make_tokens, quantize_int4, quantize_int4_g64,
+                   quantize_nvfp4_g16,
                    quantize_mxfp4_g32)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -46,6 +47,67 @@ def test_p1_int4_hand_packed_block():
     assert np.array_equal(w[0], expect)
     # the low nibble is the even element
     assert w[0, 0] == -4.0 and w[0, 1] == -3.5
+
+
+def test_p1_int4_group128_hand_packed_block():
+    # one row, two groups of 128: the scale/bias index is k // 128
+    q = np.array([(i * 7) % 16 for i in range(256)])
+    codes = np.zeros((1, 128), np.uint8)
+    for i in range(128):
+        codes[0, i] = q[2 * i] + 16 * q[2 * i + 1]
+    scales = np.array([[0x3E80, 0x4040]], np.uint16)   # bf16 0.25 and 3.0
+    biases = np.array([[0xBF80, 0x4100]], np.uint16)   # bf16 -1.0 and 8.0
+    w = om.dequant_int4_g128(codes, scales, biases)
+    expect = np.concatenate([0.25 * q[:128] - 1.0, 3.0 * q[128:] + 8.0])
+    assert np.array_equal(w[0], expect)
+    # a group-64 reading of the same bytes would differ at element 64
+    assert w[0, 64] == 0.25 * q[64] - 1.0
+
+
+# ----------------------------------------------------------------------------
+# P-2b NVFP4: E4M3 value table (OCP FP8), NaN refused, a hand-packed block
+# ----------------------------------------------------------------------------
+def _golden_e4m3():
+    vals = {}
+    with open(os.path.join(GOLDEN, "e4m3_values.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            c, v = line.split()
+            vals[int(c, 16)] = float(v)
+    return vals
+
+
+def test_p2_e4m3_table():
+    g = _golden_e4m3()
+    assert len(g) >= 15
+    for b, v in g.items():
+        got = float(om.e4m3_value(b))
+        assert got == v and np.signbit(got) == np.signbit(v), (hex(b), got, v)
+
+
+@pytest.mark.parametrize("bad", [0x7F, 0xFF])
+def test_p2_e4m3_nan_is_refused(bad):
+    with pytest.raises(ValueError):
+        om.e4m3_value(np.array([0x38, bad]))
+    codes = np.zeros((1, 16), np.uint8)
+    with pytest.raises(ValueError):
+        om.dequant_nvfp4_g16(codes, np.array([[0x38, bad]], np.uint8), 1.0)
+
+
+def test_p2_nvfp4_hand_packed_block():
+    # one row, two blocks of 16: codes 0..15 in both; block scales 1.0 (0x38)
+    # and 0.015625 (0x08, the smallest normal); matrix scale 0.5
+    e2m1 = {c: float(v) for c, v in _golden_e2m1().items()}
+    q = np.array([i % 16 for i in range(32)])
+    codes = np.zeros((1, 16), np.uint8)
+    for i in range(16):
+        codes[0, i] = q[2 * i] + 16 * q[2 * i + 1]
+    w = om.dequant_nvfp4_g16(codes, np.array([[0x38, 0x08]], np.uint8), np.float32(0.5))
+    expect = np.array([e2m1[c] * (1.0 if i < 16 else 0.015625) * 0.5 for i, c in enumerate(q)])
+    assert np.array_equal(w[0], expect)
+    with pytest.raises(ValueError):
+        om.dequant_nvfp4_g16(codes, np.array([[0x38, 0x08]], np.uint8), 0.0)
 
 
 # ----------------------------------------------------------------------------
@@ -110,6 +172,38 @@ def test_p3_int4_round_trip():
     w = (q.reshape(N, K // 64, 64) * s[..., None] + b[..., None]).reshape(N, K).astype(np.float32)
     codes, sb, bb = quantize_int4_g64(w)
     assert np.array_equal(om.dequant_int4_g64(codes, sb, bb), w.astype(np.float64))
+
+
+def test_p3_int4_group128_round_trip():
+    rng = np.random.default_rng(31)
+    N, K = 6, 512
+    s = np.float32(2.0) ** rng.integers(-8, -2, size=(N, K // 128)).astype(np.float32)
+    b = -np.float32(4.0) * s
+    q = rng.integers(0, 16, size=(N, K))
+    q[:, ::128] = 0
+    q[:, 1::128] = 15
+    w = (q.reshape(N, K // 128, 128) * s[..., None] + b[..., None]).reshape(N, K).astype(np.float32)
+    codes, sb, bb = quantize_int4(w, 128)
+    assert sb.shape == (N, K // 128)
+    assert np.array_equal(om.dequant_int4_g128(codes, sb, bb), w.astype(np.float64))
+
+
+def test_p3_nvfp4_round_trip():
+    # values on the NVFP4 grid whose matrix amax is 6 * 448 * g and whose every
+    # block holds a +-6 code, so the recipe recovers scales and codes exactly
+    rng = np.random.default_rng(32)
+    e2m1 = np.array([_golden_e2m1()[c] for c in range(16)])
+    g = np.float32(2.0 ** -10)
+    N, K = 4, 64
+    c = rng.integers(0, 16, size=(N, K))
+    c[:, ::16] = 7
+    sc = rng.integers(0x20, 0x7E, size=(N, K // 16))
+    sc[0, 0] = 0x7E   # 448: sets the matrix amax
+    sval = om.e4m3_value(sc)
+    w = (e2m1[c].reshape(N, K // 16, 16) * sval[..., None]).reshape(N, K) * float(g)
+    codes, s2, g2 = quantize_nvfp4_g16(w.astype(np.float32))
+    assert g2 == g and np.array_equal(s2, sc.astype(np.uint8))
+    assert np.array_equal(om.dequant_nvfp4_g16(codes, s2, g2), w)
 
 
 def test_p3_mxfp4_round_trip():
@@ -309,7 +403,9 @@ def _loop_ffn(x, wg, wu, wd):
 
 @pytest.mark.parametrize("router,shared,quant", [("softmax", 0, "int4_g64"),
                                                   ("sigmoid", 1, "int4_g64"),
-                                                  ("softmax", 1, "mxfp4_g32")])
+                                                  ("softmax", 1, "mxfp4_g32"),
+                                                  ("sigmoid", 0, "int4_g128"),
+                                                  ("softmax", 1, "nvfp4_g16")])
 def test_p8_isolation_per_expert(router, shared, quant):
     cfg = _tiny(router=router, num_shared=shared, quant=quant)
     layer = make_layer(cfg, seed=11)
