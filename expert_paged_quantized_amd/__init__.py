@@ -15,7 +15,8 @@ from ._capi import StrataError, check, lib
 
 __all__ = ["MoELayer", "StrataError", "measure_h2d", "measure_hbm_read", "replay_residency", "lib"]
 
-_QUANT = {"int4_g64": _capi.Q_INT4_G64, "mxfp4_g32": _capi.Q_MXFP4_G32}
+_QUANT = {"int4_g64": _capi.Q_INT4_G64, "mxfp4_g32": _capi.Q_MXFP4_G32,
+          "int4_g128": _capi.Q_INT4_G128, "nvfp4_g16": _capi.Q_NVFP4_G16}
 _ROUTER = {"softmax": _capi.R_SOFTMAX, "sigmoid": _capi.R_SIGMOID}
 _POLICY = {"lru": _capi.P_LRU, "lfu": _capi.P_LFU}
 
@@ -26,9 +27,11 @@ def _ptr(a):
 
 def _qmat(m, keep):
     if m is None:
-        return _capi.QMat(None, None, None)
+        return _capi.QMat(None, None, None, None)
+    gs = getattr(m, "global_scale", None)
     arrs = [np.ascontiguousarray(m.codes), np.ascontiguousarray(m.scales),
-            None if m.biases is None else np.ascontiguousarray(m.biases)]
+            None if m.biases is None else np.ascontiguousarray(m.biases),
+            None if gs is None else np.ascontiguousarray(np.atleast_1d(gs), dtype=np.float32)]
     keep.extend(a for a in arrs if a is not None)
     return _capi.QMat(*[None if a is None else a.ctypes.data for a in arrs])
 

@@ -10,7 +10,7 @@ c_i32, c_u64, c_vp = ctypes.c_int32, ctypes.c_uint64, ctypes.c_void_p
 
 OK, E_INVALID, E_UNSUPPORTED, E_BAD_SCALE, E_NOMEM, E_HIP, E_POISONED = range(7)
 STATUS_NAMES = ["OK", "E_INVALID", "E_UNSUPPORTED", "E_BAD_SCALE", "E_NOMEM", "E_HIP", "E_POISONED"]
-Q_INT4_G64, Q_MXFP4_G32 = 1, 2
+Q_INT4_G64, Q_MXFP4_G32, Q_INT4_G128, Q_NVFP4_G16 = 1, 2, 3, 4
 R_SOFTMAX, R_SIGMOID = 1, 2
 P_LRU, P_LFU = 1, 2
 KERNEL_CLASSES = ["router", "group", "decode_gate_up", "decode_down", "prefill_gate_up",
@@ -18,7 +18,7 @@ KERNEL_CLASSES = ["router", "group", "decode_gate_up", "decode_down", "prefill_g
 
 
 class QMat(ctypes.Structure):
-    _fields_ = [("codes", c_vp), ("scales", c_vp), ("biases", c_vp)]
+    _fields_ = [("codes", c_vp), ("scales", c_vp), ("biases", c_vp), ("global_scale", c_vp)]
 
 
 class Desc(ctypes.Structure):

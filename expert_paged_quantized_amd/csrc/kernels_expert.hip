@@ -51,15 +51,19 @@ __device__ __forceinline__ To bitcast(const From& f) {
 typedef const __attribute__((address_space(1))) u32x4 g_u32x4;
 typedef const __attribute__((address_space(1))) uint32_t g_u32;
 typedef const __attribute__((address_space(1))) uint8_t g_u8;
+typedef const __attribute__((address_space(1))) uint16_t g_u16;
+typedef const __attribute__((address_space(1))) float g_f32;
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(g_u32x4*)(p); }
 __device__ __forceinline__ uint32_t ld4(const void* p) { return *(g_u32*)(p); }
 __device__ __forceinline__ uint32_t ld1(const void* p) { return *(g_u8*)(p); }
+__device__ __forceinline__ uint32_t ld2(const void* p) { return *(g_u16*)(p); }
 // Streaming (non-temporal) variants for weights read once per launch: they
 // do not displace cached data, and measured streaming reads reach about 7 TB/s
 // this way against about 5 TB/s with ordinary loads.
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) { return __builtin_nontemporal_load((g_u32x4*)(p)); }
 __device__ __forceinline__ uint32_t ld4_nt(const void* p) { return __builtin_nontemporal_load((g_u32*)(p)); }
 __device__ __forceinline__ uint32_t ld1_nt(const void* p) { return __builtin_nontemporal_load((g_u8*)(p)); }
+__device__ __forceinline__ uint32_t ld2_nt(const void* p) { return __builtin_nontemporal_load((g_u16*)(p)); }
 
 // (a & b) | c in one instruction (the compiler splits it when b, c are literals)
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
@@ -101,8 +105,31 @@ __device__ __forceinline__ u32x4 dequant_fp4_step(uint32_t w, float scale) {
   return a;
 }
 
+// OCP FP8 E4M3 byte -> fp32 (exact): sign bit 7, exponent bits 6..3 (bias 7),
+// mantissa bits 2..0, exponent 0 subnormal (m * 2^-9).  NaN bytes never reach
+// a kernel (admission refuses them).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u, sgn = (b & 0x80u) << 24;
+  const float nrm = __uint_as_float(sgn | ((e + 120u) << 23) | (m << 20));
+  const float sub = __uint_as_float(__float_as_uint((float)m * 0.001953125f) | sgn);
+  return e ? nrm : sub;
+}
+
+// One MFMA step (8 inputs) of an NVFP4 chunk: the E2M1 codes converted with a
+// unit scale (exact in fp16), times the fp16 E4M3 block scale (exact: at most
+// 6 significant bits, magnitudes 2^-10 .. 2688).
+__device__ __forceinline__ u32x4 dequant_nvfp4_step(uint32_t w, f16x2 sc) {
+  u32x4 a;
+  a[0] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc);
+  a[1] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc);
+  a[2] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc);
+  a[3] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc);
+  return a;
+}
+
 // Per-chunk decode parameters: fp16 (scale, bias) pairs for int4, the fp32
-// power of two for MXFP4.
+// power of two for MXFP4, the fp16 scales of the chunk's two 16-input blocks
+// for NVFP4 (words 0-1 and 2-3 of the chunk).
 template <int QF>
 struct ChunkScale {
   f16x2 s2, b2;
@@ -114,13 +141,21 @@ struct ChunkScale {
       s2 = f16x2{s, s};
       b2 = f16x2{b, b};
       scale = 0.0f;
+    } else if constexpr (QF == Q_NVFP4) {
+      // both block scales in one register: (first 16 inputs, second 16)
+      s2 = f16x2{(_Float16)e4m3_to_f32(sc & 0xffu), (_Float16)e4m3_to_f32(sc >> 8)};
+      b2 = s2;
+      scale = 0.0f;
     } else {
       scale = __uint_as_float(sc << 23);
     }
   }
-  __device__ __forceinline__ u32x4 step(uint32_t w) const {
+  __device__ __forceinline__ u32x4 step(uint32_t w, int st) const {
     if constexpr (QF == Q_INT4)
       return dequant_int4_step(w, s2, b2);
+    else if constexpr (QF == Q_NVFP4)
+      return dequant_nvfp4_step(w, st < 2 ? __builtin_shufflevector(s2, s2, 0, 0)
+                                          : __builtin_shufflevector(s2, s2, 1, 1));
     else
       return dequant_fp4_step(w, scale);
   }
@@ -130,34 +165,47 @@ template <int QF>
 __device__ __forceinline__ void dequant(const u32x4& c, uint32_t sc, u32x4 (&a)[4]) {
   const ChunkScale<QF> cs(sc);
 #pragma unroll
-  for (int st = 0; st < 4; ++st) a[st] = cs.step(c[st]);
+  for (int st = 0; st < 4; ++st) a[st] = cs.step(c[st], st);
+}
+
+// fp32 matrix scales of this GEMM (NVFP4: gate and up, or down in .x), else 1.
+template <int QF>
+__device__ __forceinline__ float2 matrix_scales(const GemmArgs& p, const uint8_t* rec) {
+  if constexpr (QF == Q_NVFP4) {
+    const g_f32* g = (const g_f32*)(rec + p.off_gscale);
+    return float2{g[0], g[1]};
+  } else {
+    return float2{1.0f, 1.0f};
+  }
 }
 
 template <int QF>
 __device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
-  if constexpr (QF == Q_INT4)
+  if constexpr (QF != Q_MXFP4)
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<f16x8>(a), bitcast<f16x8>(b), c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(a), bitcast<bf16x8>(b), c, 0, 0,
                                                    0);
 }
 
-// scale bytes per weight tile and the lane's offset inside it
+// scale bytes per scale block and the lane's offset inside it
 template <int QF>
 struct ScaleLayout {
-  static constexpr int kTileBytes = (QF == Q_INT4) ? 128 : 64;
-  __device__ static int lane_off(int lane) { return (QF == Q_INT4) ? (lane & 31) * 4 : lane; }
+  static constexpr int kTileBytes = (QF == Q_MXFP4) ? 64 : 128;
+  __device__ static int lane_off(int lane) {
+    if constexpr (QF == Q_INT4) return (lane & 31) * 4;
+    else if constexpr (QF == Q_NVFP4) return lane * 2;
+    else return lane;
+  }
   __device__ static uint32_t load(const uint8_t* p) {
-    if constexpr (QF == Q_INT4)
-      return ld4(p);
-    else
-      return ld1(p);
+    if constexpr (QF == Q_INT4) return ld4(p);
+    else if constexpr (QF == Q_NVFP4) return ld2(p);
+    else return ld1(p);
   }
   __device__ static uint32_t load_nt(const uint8_t* p) {
-    if constexpr (QF == Q_INT4)
-      return ld4_nt(p);
-    else
-      return ld1_nt(p);
+    if constexpr (QF == Q_INT4) return ld4_nt(p);
+    else if constexpr (QF == Q_NVFP4) return ld2_nt(p);
+    else return ld1_nt(p);
   }
 };
 
@@ -170,7 +218,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 template <int QF>
 __device__ __forceinline__ uint16_t to_h_elem(float f) {
-  if constexpr (QF == Q_INT4)
+  if constexpr (QF != Q_MXFP4)
     return bitcast<uint16_t>((_Float16)f);
   else
     return f32_to_bf16_rne(f);
@@ -197,7 +245,7 @@ constexpr int kDecDepth = 8;
 // Epilogue of one wave's 32-row tile rt for the token columns n < nrows.
 template <int QF, bool GATE_UP>
 __device__ __forceinline__ void decode_store(const GemmArgs& p, const Tile& t, int rt, int lane,
-                                             const f32x16& acc) {
+                                             const f32x16& acc, float2 gs) {
   const int n = lane & 31;
   if (n >= t.nrows) return;
   const int64_t row = t.row_begin + n;
@@ -209,7 +257,7 @@ __device__ __forceinline__ void decode_store(const GemmArgs& p, const Tile& t, i
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = g4 * 4 + q;
-        v[q] = to_h_elem<QF>(silu(acc[i]) * acc[i + 8]);
+        v[q] = to_h_elem<QF>(silu(acc[i] * gs.x) * (acc[i + 8] * gs.y));
       }
       const uint2 pk = {(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16)};
       *reinterpret_cast<uint2*>(h + g4 * 8 + (lane >> 5) * 4) = pk;
@@ -218,7 +266,8 @@ __device__ __forceinline__ void decode_store(const GemmArgs& p, const Tile& t, i
     float* o = reinterpret_cast<float*>(p.out) + row * p.out_ld + rt * 32;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const float4 v = {acc[g4 * 4 + 0], acc[g4 * 4 + 1], acc[g4 * 4 + 2], acc[g4 * 4 + 3]};
+      const float4 v = {acc[g4 * 4 + 0] * gs.x, acc[g4 * 4 + 1] * gs.x, acc[g4 * 4 + 2] * gs.x,
+                        acc[g4 * 4 + 3] * gs.x};
       *reinterpret_cast<float4*>(o + g4 * 8 + (lane >> 5) * 4) = v;
     }
   }
@@ -249,7 +298,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void moe_decode_kernel(GemmArgs p, 
 
   const uint8_t* rec = p.slot_ptr[t.slot];
   const uint8_t* codes = rec + p.off_codes + (int64_t)rtc * KB * kTileCodeBytes + lane * 16;
-  const uint8_t* scales = rec + p.off_scales + (int64_t)rtc * KB * SL::kTileBytes + SL::lane_off(lane);
+  const uint8_t* scales =
+      rec + p.off_scales + (int64_t)rtc * (KB >> p.sshift) * SL::kTileBytes + SL::lane_off(lane);
 
   // staging pieces (the tile's own rows only): piece pc = tid + 512*j ->
   // token row pc >> (log2S + 6), 16-byte column pc & (S*64 - 1) of the
@@ -284,7 +334,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void moe_decode_kernel(GemmArgs p, 
   for (int j = 0; j < kDecDepth; ++j) {
     const int kb = min(sw * kDecDepth + j, KB - 1);
     wq[j] = ld16_nt(codes + (int64_t)kb * kTileCodeBytes);
-    ws[j] = SL::load_nt(scales + (int64_t)kb * SL::kTileBytes);
+    ws[j] = SL::load_nt(scales + (int64_t)(kb >> p.sshift) * SL::kTileBytes);
   }
   u32x4 xv[NP];
   x_load(xv, 0);
@@ -309,7 +359,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void moe_decode_kernel(GemmArgs p, 
       asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])::"memory");
       const int kn = min(kbase + cb + j, KB - 1);
       wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
-      ws[j] = SL::load_nt(scales + (int64_t)kn * SL::kTileBytes);
+      ws[j] = SL::load_nt(scales + (int64_t)(kn >> p.sshift) * SL::kTileBytes);
       if (kbase + j < KB) {
         const uint32_t* bp = brow + j * 32;
 #pragma unroll
@@ -348,7 +398,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void moe_decode_kernel(GemmArgs p, 
         }
       }
     }
-    decode_store<QF, GATE_UP>(p, t, rt, lane, acc);
+    decode_store<QF, GATE_UP>(p, t, rt, lane, acc, matrix_scales<QF>(p, rec));
   }
 }
 
@@ -366,6 +416,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void moe_decode_kernel(GemmArgs p, 
 //   MXFP4: the gfx950 FP4 conversion (unit scale) gives exact bf16 pairs,
 //          v_dot2_f32_bf16 contracts them, and the E8M0 power of two scales
 //          the 32-input group sum.
+//   NVFP4: the same conversion to fp16 pairs, v_dot2_f32_f16 against the fp16
+//          activations, each 16-input block sum times its E4M3 scale, the
+//          matrix scale applied to the final sums.
 // Workgroup = S waves on one 32-row weight tile, wave s streaming the
 // contiguous K-blocks [s*KB/S, (s+1)*KB/S) of it; lane l owns tile row l%32
 // and inputs 32*(l/32)..+31 of each block (the prepacked layout: one 16-byte
@@ -398,7 +451,9 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
 
   const uint8_t* rec = p.slot_ptr[t.slot];
   const uint8_t* codes = rec + p.off_codes + ((int64_t)rt * KB + kb0) * kTileCodeBytes + lane * 16;
-  const uint8_t* scales = rec + p.off_scales + ((int64_t)rt * KB + kb0) * SL::kTileBytes + SL::lane_off(lane);
+  // scale block of (absolute) k-block kb0 + kb is (kb0 + kb) >> sshift
+  const uint8_t* scales =
+      rec + p.off_scales + (int64_t)rt * (KB >> p.sshift) * SL::kTileBytes + SL::lane_off(lane);
 
   // activation loads first: waiting for them later leaves the weight loads
   // issued after them in flight
@@ -420,7 +475,7 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
   for (int j = 0; j < DEPTH; ++j) {
     const int kb = min(j, nkb - 1);
     wq[j] = ld16_nt(codes + (int64_t)kb * kTileCodeBytes);
-    ws[j] = SL::load_nt(scales + (int64_t)kb * SL::kTileBytes);
+    ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kb) >> p.sshift) * SL::kTileBytes);
   }
   // stage the token rows; for int4 also the sums of each 32 inputs, four
   // consecutive 8-input pieces per quad
@@ -474,7 +529,7 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
                      "+v"(m[2][2]), "+v"(m[2][3]), "+v"(m[3][0]), "+v"(m[3][1]), "+v"(m[3][2]),
                      "+v"(m[3][3]), "+v"(s), "+v"(b)::"memory");
         wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
-        ws[j] = SL::load_nt(scales + (int64_t)kn * SL::kTileBytes);
+        ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> p.sshift) * SL::kTileBytes);
         if (kbl < nkb) {
 #pragma unroll
           for (int r = 0; r < TT; ++r) {
@@ -493,6 +548,37 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
             acc[r] = __builtin_fmaf(b, xsl[r * (K >> 5) + kbl * 2], acc[r]);
           }
         }
+      } else if constexpr (QF == Q_NVFP4) {
+        // E2M1 codes converted with a unit scale (exact in fp16); the chunk's
+        // two 16-input blocks (words 0-1, 2-3) get their E4M3 scales in fp32
+        u32x4 m[4];
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) m[st] = dequant_nvfp4_step(wq[j][st], one);
+        float s0 = e4m3_to_f32(ws[j] & 0xffu), s1 = e4m3_to_f32(ws[j] >> 8);
+        asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(s0), "+v"(s1)::"memory");
+        wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
+        ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> p.sshift) * SL::kTileBytes);
+        if (kbl < nkb) {
+#pragma unroll
+          for (int r = 0; r < TT; ++r) {
+            const uint32_t* xr = xl + r * row_u32 + kbl * 32;
+            float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+              const u32x4 x = *reinterpret_cast<const u32x4*>(xr + st * 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (st < 2)
+                  d0 = __builtin_amdgcn_fdot2(bitcast<f16x2>(m[st][e]), bitcast<f16x2>(x[e]), d0, false);
+                else
+                  d1 = __builtin_amdgcn_fdot2(bitcast<f16x2>(m[st][e]), bitcast<f16x2>(x[e]), d1, false);
+              }
+            }
+            acc[r] = __builtin_fmaf(s0, d0, acc[r]);
+            acc[r] = __builtin_fmaf(s1, d1, acc[r]);
+          }
+        }
       } else {
         u32x4 m[4];
 #pragma unroll
@@ -500,7 +586,7 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
         float scale = __uint_as_float(ws[j] << 23);
         asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(scale)::"memory");
         wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
-        ws[j] = SL::load_nt(scales + (int64_t)kn * SL::kTileBytes);
+        ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> p.sshift) * SL::kTileBytes);
         if (kbl < nkb) {
 #pragma unroll
           for (int r = 0; r < TT; ++r) {
@@ -529,6 +615,7 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
     if (lane < 32) red[(wave * TT + r) * 32 + lane] = acc[r] + other;
   }
   __syncthreads();
+  const float2 gs = matrix_scales<QF>(p, rec);  // NVFP4 matrix scales, else 1
   for (int q = tid; q < TT * 32; q += blockDim.x) {
     const int n = q >> 5, row = q & 31;  // (token, row)
     if (n >= t.nrows) continue;
@@ -539,11 +626,14 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
         g += red[(w * TT + n) * 32 + row];
         u += red[(w * TT + n) * 32 + row + 16];
       }
+      g *= gs.x;
+      u *= gs.y;
       uint16_t* hp = reinterpret_cast<uint16_t*>(p.out);
       hp[(int64_t)(t.row_begin + n) * p.out_ld + rt * 16 + row] = to_h_elem<QF>(silu(g) * u);
     } else {
       float o = red[n * 32 + row];
       for (int w = 1; w < S; ++w) o += red[(w * TT + n) * 32 + row];
+      o *= gs.x;
       reinterpret_cast<float*>(p.out)[(int64_t)(t.row_begin + n) * p.out_ld + rt * 32 + row] = o;
     }
   }
@@ -603,7 +693,7 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
   for (int r = 0; r < RTW; ++r) {
     const int rtl = min(rt0 + r, nrt - 1);
     codes[r] = rec + p.off_codes + (int64_t)rtl * KB * kTileCodeBytes + lane * 16;
-    scs[r] = rec + p.off_scales + (int64_t)rtl * KB * SL::kTileBytes + SL::lane_off(lane);
+    scs[r] = rec + p.off_scales + (int64_t)rtl * (KB >> p.sshift) * SL::kTileBytes + SL::lane_off(lane);
   }
 
   f32x16 acc[RTW][NCT];
@@ -633,7 +723,7 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
 #pragma unroll
     for (int r = 0; r < RTW; ++r) {
       q4[r] = ld16(codes[r] + (int64_t)kb * kTileCodeBytes);
-      s4[r] = SL::load(scs[r] + (int64_t)kb * SL::kTileBytes);
+      s4[r] = SL::load(scs[r] + (int64_t)(kb >> p.sshift) * SL::kTileBytes);
     }
   };
   auto compute = [&](int buf, const u32x4(&q4)[RTW], const uint32_t(&s4)[RTW]) {
@@ -648,7 +738,7 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
       }
 #pragma unroll
       for (int r = 0; r < RTW; ++r) {
-        const u32x4 a = ChunkScale<QF>(s4[r]).step(q4[r][st]);
+        const u32x4 a = ChunkScale<QF>(s4[r]).step(q4[r][st], st);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) acc[r][ct] = mfma<QF>(a, b[ct], acc[r][ct]);
       }
@@ -700,7 +790,8 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
     if (kb + 2 < KB) one_step(kb + 2, std::integral_constant<int, 2>{});
   }
 
-  // epilogue
+  // epilogue (NVFP4: times the fp32 matrix scales)
+  const float2 gs = matrix_scales<QF>(p, rec);
 #pragma unroll
   for (int r = 0; r < RTW; ++r) {
     const int rt = rt0 + r;
@@ -718,7 +809,7 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int i = g4 * 4 + q;
-            v[q] = to_h_elem<QF>(silu(acc[r][ct][i]) * acc[r][ct][i + 8]);
+            v[q] = to_h_elem<QF>(silu(acc[r][ct][i] * gs.x) * (acc[r][ct][i + 8] * gs.y));
           }
           const uint2 pk = {(uint32_t)v[0] | ((uint32_t)v[1] << 16),
                             (uint32_t)v[2] | ((uint32_t)v[3] << 16)};
@@ -728,8 +819,8 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
         float* o = reinterpret_cast<float*>(p.out) + row * p.out_ld + rt * 32;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 v = {acc[r][ct][g4 * 4 + 0], acc[r][ct][g4 * 4 + 1], acc[r][ct][g4 * 4 + 2],
-                            acc[r][ct][g4 * 4 + 3]};
+          const float4 v = {acc[r][ct][g4 * 4 + 0] * gs.x, acc[r][ct][g4 * 4 + 1] * gs.x,
+                            acc[r][ct][g4 * 4 + 2] * gs.x, acc[r][ct][g4 * 4 + 3] * gs.x};
           *reinterpret_cast<float4*>(o + g4 * 8 + (lane >> 5) * 4) = v;
         }
       }
@@ -748,8 +839,9 @@ __global__ __launch_bounds__(kPreThreads, 2) void moe_prefill_kernel(GemmArgs p)
     const Tile t = p.tiles[item / n_nb];
     const int nb = item % n_nb;
     switch ((t.nrows + 31) >> 5) {
-      case 1: prefill_item<QF, GATE_UP, 1, 4>(p, t, nb, lds); break;
-      case 2: prefill_item<QF, GATE_UP, 2, 4>(p, t, nb, lds); break;
+      // (NVFP4 decodes need a few more registers: a shorter weight ring)
+      case 1: prefill_item<QF, GATE_UP, 1, (QF == Q_NVFP4 ? 2 : 4)>(p, t, nb, lds); break;
+      case 2: prefill_item<QF, GATE_UP, 2, (QF == Q_NVFP4 ? 2 : 4)>(p, t, nb, lds); break;
       case 3: prefill_item<QF, GATE_UP, 3, 2>(p, t, nb, lds); break;
       default: prefill_item<QF, GATE_UP, 4, 2>(p, t, nb, lds); break;
     }
@@ -866,51 +958,49 @@ static void launch_dot(const GemmArgs& a, int T, int S, int n_tiles, hipStream_t
     launch_dot_tt<QF, GATE_UP, 4>(a, S, grid, lds, s);
 }
 
+// Dispatch over the quant family and gate+up / down at run time.
+template <template <int, bool> class L, class... A>
+static void by_format(int quant, bool gate_up, A&&... args) {
+  if (quant == Q_INT4) {
+    if (gate_up) L<Q_INT4, true>::run(args...); else L<Q_INT4, false>::run(args...);
+  } else if (quant == Q_NVFP4) {
+    if (gate_up) L<Q_NVFP4, true>::run(args...); else L<Q_NVFP4, false>::run(args...);
+  } else {
+    if (gate_up) L<Q_MXFP4, true>::run(args...); else L<Q_MXFP4, false>::run(args...);
+  }
+}
+
+template <int QF, bool GU>
+struct DotL {
+  static void run(const GemmArgs& a, int T, int S, int n_tiles, hipStream_t s) { launch_dot<QF, GU>(a, T, S, n_tiles, s); }
+};
+template <int QF, bool GU>
+struct DecL {
+  static void run(const GemmArgs& a, int T, int log2S, int grid, hipStream_t s) {
+    launch_decode<QF, GU>(a, T, log2S, grid, s);
+  }
+};
+template <int QF, bool GU>
+struct PreL {
+  static void run(const GemmArgs& a, int grid, hipStream_t s) {
+    launch_k(moe_prefill_kernel<QF, GU>, dim3(grid), dim3(kPreThreads), 0, s, a);
+  }
+};
+
 hipError_t launch_decode_dot(const GemmArgs& a, int quant, bool gate_up, int T, int S, int n_tiles,
                              hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  if (quant == Q_INT4) {
-    if (gate_up)
-      launch_dot<Q_INT4, true>(a, T, S, n_tiles, s);
-    else
-      launch_dot<Q_INT4, false>(a, T, S, n_tiles, s);
-  } else {
-    if (gate_up)
-      launch_dot<Q_MXFP4, true>(a, T, S, n_tiles, s);
-    else
-      launch_dot<Q_MXFP4, false>(a, T, S, n_tiles, s);
-  }
+  by_format<DotL>(quant, gate_up, a, T, S, n_tiles, s);
   return hipGetLastError();
 }
 
 hipError_t launch_expert_gemm(const GemmArgs& a, int quant, bool gate_up, bool decode, int T, int log2S,
                               int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (decode) {
-    if (quant == Q_INT4) {
-      if (gate_up)
-        launch_decode<Q_INT4, true>(a, T, log2S, grid, s);
-      else
-        launch_decode<Q_INT4, false>(a, T, log2S, grid, s);
-    } else {
-      if (gate_up)
-        launch_decode<Q_MXFP4, true>(a, T, log2S, grid, s);
-      else
-        launch_decode<Q_MXFP4, false>(a, T, log2S, grid, s);
-    }
-  } else {
-    if (quant == Q_INT4) {
-      if (gate_up)
-        launch_k(moe_prefill_kernel<Q_INT4, true>, dim3(grid), dim3(kPreThreads), 0, s, a);
-      else
-        launch_k(moe_prefill_kernel<Q_INT4, false>, dim3(grid), dim3(kPreThreads), 0, s, a);
-    } else {
-      if (gate_up)
-        launch_k(moe_prefill_kernel<Q_MXFP4, true>, dim3(grid), dim3(kPreThreads), 0, s, a);
-      else
-        launch_k(moe_prefill_kernel<Q_MXFP4, false>, dim3(grid), dim3(kPreThreads), 0, s, a);
-    }
-  }
+  if (decode)
+    by_format<DecL>(quant, gate_up, a, T, log2S, grid, s);
+  else
+    by_format<PreL>(quant, gate_up, a, grid, s);
   return hipGetLastError();
 }
 

@@ -6,7 +6,10 @@
 
 namespace strata {
 
-enum QFormat : int { Q_INT4 = 1, Q_MXFP4 = 2 };
+// Kernel dequant families: int4 affine (group 64 or 128; fp16 compute), MXFP4
+// (E2M1 x E8M0; bf16 compute), NVFP4 (E2M1 x E4M3 per 16 x fp32 per matrix;
+// fp16 compute).
+enum QFormat : int { Q_INT4 = 1, Q_MXFP4 = 2, Q_NVFP4 = 4 };
 enum RouterKind : int { R_SOFTMAX = 1, R_SIGMOID = 2 };
 
 // Token tile of the prefill grouped GEMM (rows of one expert segment).
@@ -35,20 +38,26 @@ struct Tile {
 //   w1 = gate and up interleaved per 32-row tile (16 gate rows, then the same
 //   16 rows of up), [F/16 tiles][H/64 k-blocks]; w2 = down, [H/32][F/64].
 //   codes: 1024 B per tile, lane l holds tile row l%32, inputs 32*(l/32)..+31;
-//   scales: int4 128 B per tile (u32 per row: bf16 scale | bf16 bias << 16),
-//           MXFP4 64 B per tile (E8M0 byte per (half, row)).
+//   scales, per row tile and scale block (a k-block, or a pair of k-blocks for
+//   int4 group-128: block index kb >> sshift):
+//     int4  128 B (u32 per row: bf16 scale | bf16 bias << 16),
+//     MXFP4  64 B (E8M0 byte per (half, row)),
+//     NVFP4 128 B (two E4M3 bytes per (half, row): its two 16-input blocks);
+//   gscale (NVFP4 only): fp32 matrix scales of gate, up, down (12 B).
 struct RecordLayout {
-  int64_t w1_codes, w1_scales, w2_codes, w2_scales, bytes;
-  static RecordLayout make(int H, int F, int quant) {
+  int64_t w1_codes, w1_scales, w2_codes, w2_scales, gscale, bytes;
+  static int64_t scale_block_bytes(int qf) { return qf == Q_MXFP4 ? 64 : 128; }
+  static RecordLayout make(int H, int F, int qf, int sshift) {
     RecordLayout r;
-    const int64_t sb = (quant == Q_INT4) ? 128 : 64;
+    const int64_t sb = scale_block_bytes(qf);
     const int64_t w1_tiles = int64_t(F / 16) * (H / kTileK);
     const int64_t w2_tiles = int64_t(H / 32) * (F / kTileK);
     r.w1_codes = 0;
     r.w1_scales = r.w1_codes + w1_tiles * kTileCodeBytes;
-    r.w2_codes = r.w1_scales + w1_tiles * sb;
+    r.w2_codes = r.w1_scales + (w1_tiles >> sshift) * sb;
     r.w2_scales = r.w2_codes + w2_tiles * kTileCodeBytes;
-    r.bytes = r.w2_scales + w2_tiles * sb;
+    r.gscale = r.w2_scales + (w2_tiles >> sshift) * sb;
+    r.bytes = r.gscale + (qf == Q_NVFP4 ? 12 : 0);
     return r;
   }
 };
@@ -66,6 +75,9 @@ struct GemmArgs {
   int32_t K;                 // reduction length (H or F)
   void* out;                 // gate+up: h [R, F]; down: o fp32 [R, H]
   int32_t out_ld;            // F or H
+  int32_t sshift;            // scale block of k-block kb: kb >> sshift
+  int64_t off_gscale;        // NVFP4: record offset of this GEMM's fp32 matrix
+                             // scales (gate, up: two floats; down: one)
 };
 
 // Kernel timing: when the runtime times a single-kernel step it sets this

@@ -90,6 +90,7 @@ constexpr int kCopyStreams = STRATA_COPY_STREAMS;
 
 struct strata_moe {
   int H = 0, F = 0, E = 0, k = 0, S = 0, quant = 0, router = 0, policy = 0, budget = 0;
+  int sshift = 0;  // scale block of k-block kb is kb >> sshift (int4 group-128: 1)
   int max_tokens = 0, device = 0;
   RecordLayout lay{};
   size_t slot_stride = 0;
@@ -119,7 +120,7 @@ struct strata_moe {
   unsigned long long* d_distinct = nullptr;
   void* d_h = nullptr;
   float* d_o = nullptr;
-  uint16_t* d_x16 = nullptr;  // fp16 copy of x (int4 layers)
+  uint16_t* d_x16 = nullptr;  // fp16 copy of x (int4 and NVFP4 layers)
   uint64_t ws_bytes = 0;
 
   int32_t* h_counts = nullptr;  // pinned
@@ -153,6 +154,25 @@ static bool fp16_exact(uint16_t bf) {
   return (float)h == f;
 }
 
+// What the host needs to know about a weight format.
+struct FormatInfo {
+  int kq;       // kernel dequant family (QFormat)
+  int group;    // inputs per scale
+  bool affine;  // int4: bf16 scale and bias per group
+  bool f16;     // the kernels compute in fp16 (and read the fp16 copy of x)
+  int sshift;   // scale block of k-block kb is kb >> sshift
+};
+
+static bool format_of(int quant, FormatInfo& f) {
+  switch (quant) {
+    case STRATA_Q_INT4_G64_AFFINE_BF16: f = {Q_INT4, 64, true, true, 0}; return true;
+    case STRATA_Q_INT4_G128_AFFINE_BF16: f = {Q_INT4, 128, true, true, 1}; return true;
+    case STRATA_Q_MXFP4_E2M1_E8M0_G32: f = {Q_MXFP4, 32, false, false, 0}; return true;
+    case STRATA_Q_NVFP4_E2M1_E4M3_G16: f = {Q_NVFP4, 16, false, true, 0}; return true;
+    default: return false;
+  }
+}
+
 static strata_status validate(const strata_moe_desc* d) {
   if (!d) return fail(STRATA_E_INVALID, "desc is NULL");
   if (d->hidden <= 0 || d->ffn <= 0 || d->num_experts <= 0 || d->top_k <= 0 || d->max_tokens <= 0)
@@ -161,8 +181,8 @@ static strata_status validate(const strata_moe_desc* d) {
   if (d->top_k > d->num_experts) return fail(STRATA_E_INVALID, "top_k > num_experts");
   if (d->top_k > 32) return fail(STRATA_E_UNSUPPORTED, "top_k > 32");
   if (d->num_shared != 0 && d->num_shared != 1) return fail(STRATA_E_UNSUPPORTED, "num_shared must be 0 or 1");
-  if (d->quant != STRATA_Q_INT4_G64_AFFINE_BF16 && d->quant != STRATA_Q_MXFP4_E2M1_E8M0_G32)
-    return fail(STRATA_E_INVALID, "unknown quant");
+  FormatInfo fi;
+  if (!format_of(d->quant, fi)) return fail(STRATA_E_INVALID, "unknown quant");
   if (d->router != STRATA_R_SOFTMAX_TOPK_RENORM && d->router != STRATA_R_SIGMOID_TOPK_RENORM)
     return fail(STRATA_E_INVALID, "unknown router");
   if (d->policy != STRATA_P_LRU && d->policy != STRATA_P_LFU) return fail(STRATA_E_INVALID, "unknown policy");
@@ -171,12 +191,16 @@ static strata_status validate(const strata_moe_desc* d) {
   if (d->max_tokens > (1 << 20)) return fail(STRATA_E_UNSUPPORTED, "max_tokens > 2^20");
   if (d->hidden % 512) return fail(STRATA_E_UNSUPPORTED, "hidden must be a multiple of 512");
   if (d->ffn % 64) return fail(STRATA_E_UNSUPPORTED, "ffn must be a multiple of 64");
+  if (d->ffn % fi.group) return fail(STRATA_E_UNSUPPORTED, "ffn must be a multiple of the quant group");
   if (!d->router_w) return fail(STRATA_E_INVALID, "router_w is NULL");
-  const bool int4 = d->quant == STRATA_Q_INT4_G64_AFFINE_BF16;
+  const bool int4 = fi.affine, nvfp4 = fi.kq == Q_NVFP4;
   auto chk = [&](const strata_qmat& m, const char* name) -> strata_status {
     if (!m.codes || !m.scales) return fail(STRATA_E_INVALID, std::string(name) + ": codes/scales NULL");
     if (int4 && !m.biases) return fail(STRATA_E_INVALID, std::string(name) + ": int4 needs biases");
-    if (!int4 && m.biases) return fail(STRATA_E_INVALID, std::string(name) + ": MXFP4 takes no biases");
+    if (!int4 && m.biases) return fail(STRATA_E_INVALID, std::string(name) + ": MXFP4/NVFP4 take no biases");
+    if (nvfp4 && !m.global_scale) return fail(STRATA_E_INVALID, std::string(name) + ": NVFP4 needs global_scale");
+    if (!nvfp4 && m.global_scale)
+      return fail(STRATA_E_INVALID, std::string(name) + ": global_scale is for NVFP4 only");
     return STRATA_OK;
   };
   strata_status st;
@@ -191,13 +215,25 @@ static strata_status validate(const strata_moe_desc* d) {
   const size_t H = d->hidden, F = d->ffn;
   auto admit = [&](const strata_qmat& m, size_t n_exp, size_t rows, size_t cols, const char* name) -> strata_status {
     if (int4) {
-      const size_t n = n_exp * rows * (cols / 64);
+      const size_t n = n_exp * rows * (cols / fi.group);
       const uint16_t* s = (const uint16_t*)m.scales;
       const uint16_t* b = (const uint16_t*)m.biases;
       for (size_t i = 0; i < n; ++i)
         if (!fp16_exact(s[i]) || !fp16_exact(b[i]))
           return fail(STRATA_E_UNSUPPORTED, std::string(name) +
                                                 ": int4 scale/bias not exactly representable in fp16");
+    } else if (nvfp4) {
+      const size_t n = n_exp * rows * (cols / 16);
+      const uint8_t* s = (const uint8_t*)m.scales;
+      for (size_t i = 0; i < n; ++i)
+        if ((s[i] & 0x7F) == 0x7F)
+          return fail(STRATA_E_BAD_SCALE, std::string(name) + ": E4M3 scale byte is NaN at index " +
+                                              std::to_string(i));
+      for (size_t e = 0; e < n_exp; ++e) {
+        const float g = m.global_scale[e];
+        if (!(g > 0.0f) || g == __builtin_inff())
+          return fail(STRATA_E_BAD_SCALE, std::string(name) + ": NVFP4 matrix scale not finite and > 0");
+      }
     } else {
       const size_t n = n_exp * rows * (cols / 32);
       const uint8_t* s = (const uint8_t*)m.scales;
@@ -235,27 +271,25 @@ static inline uint32_t int4_word_perm(uint32_t w) {
 
 struct MatView {
   const uint8_t* codes;   // [rows, cols/2]
-  const uint8_t* scales;  // int4: bf16 [rows, cols/64]; MXFP4: u8 [rows, cols/32]
-  const uint8_t* biases;  // int4: bf16 [rows, cols/64]
+  const uint8_t* scales;  // int4: bf16 [rows, cols/G]; MXFP4: u8 [rows, cols/32]; NVFP4: u8 [rows, cols/16]
+  const uint8_t* biases;  // int4: bf16 [rows, cols/G]
+  float gscale;           // NVFP4 matrix scale
 };
 
-static MatView view(const strata_qmat& m, size_t e, size_t rows, size_t cols, bool int4) {
+static MatView view(const strata_qmat& m, size_t e, size_t rows, size_t cols, const FormatInfo& fi) {
   MatView v;
   v.codes = (const uint8_t*)m.codes + e * rows * (cols / 2);
-  if (int4) {
-    v.scales = (const uint8_t*)m.scales + e * rows * (cols / 64) * 2;
-    v.biases = (const uint8_t*)m.biases + e * rows * (cols / 64) * 2;
-  } else {
-    v.scales = (const uint8_t*)m.scales + e * rows * (cols / 32);
-    v.biases = nullptr;
-  }
+  const size_t per = rows * (cols / fi.group);
+  v.scales = (const uint8_t*)m.scales + e * per * (fi.affine ? 2 : 1);
+  v.biases = fi.affine ? (const uint8_t*)m.biases + e * per * 2 : nullptr;
+  v.gscale = m.global_scale ? m.global_scale[e] : 0.0f;
   return v;
 }
 
 // Packs the tiles of one matrix.  `row_of(rt, r)` maps tile row r of row tile
 // rt to a (source matrix, row) pair.
 template <class RowOf>
-static void pack_matrix(uint8_t* codes_dst, uint8_t* scales_dst, int n_rt, int K, bool int4,
+static void pack_matrix(uint8_t* codes_dst, uint8_t* scales_dst, int n_rt, int K, const FormatInfo& fi,
                         RowOf row_of) {
   const int KB = K / 64;
   for (int rt = 0; rt < n_rt; ++rt) {
@@ -268,7 +302,7 @@ static void pack_matrix(uint8_t* codes_dst, uint8_t* scales_dst, int n_rt, int K
         row_of(rt, r, mv, row);
         const uint8_t* src = mv->codes + (size_t)row * (K / 2) + (kb * 64 + h * 32) / 2;
         uint8_t* dst = cd + l * 16;
-        if (int4) {
+        if (fi.affine) {
           for (int wi = 0; wi < 4; ++wi) {
             uint32_t w;
             memcpy(&w, src + 4 * wi, 4);
@@ -279,18 +313,31 @@ static void pack_matrix(uint8_t* codes_dst, uint8_t* scales_dst, int n_rt, int K
           memcpy(dst, src, 16);
         }
       }
-      if (int4) {
-        uint8_t* sd = scales_dst + ((size_t)rt * KB + kb) * 128;
+      if (fi.affine) {
+        if (kb & ((1 << fi.sshift) - 1)) continue;  // one block per 2^sshift k-blocks
+        const int nsb = KB >> fi.sshift, sblk = kb >> fi.sshift;
+        uint8_t* sd = scales_dst + ((size_t)rt * nsb + sblk) * 128;
         for (int r = 0; r < 32; ++r) {
           const MatView* mv;
           int row;
           row_of(rt, r, mv, row);
-          const size_t gi = (size_t)row * KB + kb;
-          uint16_t s, b;
-          memcpy(&s, mv->scales + gi * 2, 2);
+          const size_t gi = (size_t)row * nsb + sblk;
+          uint16_t sc, b;
+          memcpy(&sc, mv->scales + gi * 2, 2);
           memcpy(&b, mv->biases + gi * 2, 2);
-          const uint32_t u = uint32_t(s) | (uint32_t(b) << 16);
+          const uint32_t u = uint32_t(sc) | (uint32_t(b) << 16);
           memcpy(sd + r * 4, &u, 4);
+        }
+      } else if (fi.kq == Q_NVFP4) {
+        uint8_t* sd = scales_dst + ((size_t)rt * KB + kb) * 128;
+        for (int l = 0; l < 64; ++l) {
+          const int r = l & 31, h = l >> 5;
+          const MatView* mv;
+          int row;
+          row_of(rt, r, mv, row);
+          const uint8_t* src = mv->scales + (size_t)row * (K / 16) + kb * 4 + h * 2;
+          sd[(h * 32 + r) * 2 + 0] = src[0];
+          sd[(h * 32 + r) * 2 + 1] = src[1];
         }
       } else {
         uint8_t* sd = scales_dst + ((size_t)rt * KB + kb) * 64;
@@ -307,19 +354,24 @@ static void pack_matrix(uint8_t* codes_dst, uint8_t* scales_dst, int n_rt, int K
 }
 
 static void pack_expert(uint8_t* rec, const RecordLayout& lay, const strata_qmat& g,
-                        const strata_qmat& u, const strata_qmat& d, size_t e, int H, int F, bool int4) {
-  const MatView vg = view(g, e, F, H, int4), vu = view(u, e, F, H, int4), vd = view(d, e, H, F, int4);
+                        const strata_qmat& u, const strata_qmat& d, size_t e, int H, int F,
+                        const FormatInfo& fi) {
+  const MatView vg = view(g, e, F, H, fi), vu = view(u, e, F, H, fi), vd = view(d, e, H, F, fi);
   // w1: tile rt = gate rows 16rt..+15 then up rows 16rt..+15
-  pack_matrix(rec + lay.w1_codes, rec + lay.w1_scales, F / 16, H, int4,
+  pack_matrix(rec + lay.w1_codes, rec + lay.w1_scales, F / 16, H, fi,
               [&](int rt, int r, const MatView*& mv, int& row) {
                 mv = (r < 16) ? &vg : &vu;
                 row = rt * 16 + (r & 15);
               });
-  pack_matrix(rec + lay.w2_codes, rec + lay.w2_scales, H / 32, F, int4,
+  pack_matrix(rec + lay.w2_codes, rec + lay.w2_scales, H / 32, F, fi,
               [&](int rt, int r, const MatView*& mv, int& row) {
                 mv = &vd;
                 row = rt * 32 + r;
               });
+  if (fi.kq == Q_NVFP4) {
+    const float gs[3] = {vg.gscale, vu.gscale, vd.gscale};
+    memcpy(rec + lay.gscale, gs, sizeof gs);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -384,14 +436,16 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   h->E = d->num_experts;
   h->k = d->top_k;
   h->S = d->num_shared;
-  h->quant = d->quant == STRATA_Q_INT4_G64_AFFINE_BF16 ? Q_INT4 : Q_MXFP4;
+  FormatInfo fi;
+  (void)format_of(d->quant, fi);  // validated
+  h->quant = fi.kq;
+  h->sshift = fi.sshift;
   h->router = d->router == STRATA_R_SOFTMAX_TOPK_RENORM ? R_SOFTMAX : R_SIGMOID;
   h->policy = d->policy;
   h->budget = d->expert_budget;
   h->max_tokens = d->max_tokens;
-  h->lay = RecordLayout::make(h->H, h->F, h->quant);
+  h->lay = RecordLayout::make(h->H, h->F, h->quant, h->sshift);
   h->slot_stride = (size_t(h->lay.bytes) + 255) & ~size_t(255);
-  const bool int4 = h->quant == Q_INT4;
 
   int dev = d->device;
   if (dev < 0) HIP_CHECK(hipGetDevice(&dev));
@@ -408,7 +462,7 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
     for (unsigned t = 0; t < nth; ++t)
       th.emplace_back([&, t]() {
         for (int e = t; e < h->E; e += nth)
-          pack_expert(h->host_store + rec * e, h->lay, d->gate, d->up, d->down, e, h->H, h->F, int4);
+          pack_expert(h->host_store + rec * e, h->lay, d->gate, d->up, d->down, e, h->H, h->F, fi);
       });
     for (auto& t : th) t.join();
   }
@@ -418,7 +472,7 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   if (h->S) {
     if ((st = dev_alloc(h, &h->d_shared, h->slot_stride))) return st;
     std::vector<uint8_t> tmp(rec);
-    pack_expert(tmp.data(), h->lay, d->sh_gate, d->sh_up, d->sh_down, 0, h->H, h->F, int4);
+    pack_expert(tmp.data(), h->lay, d->sh_gate, d->sh_up, d->sh_down, 0, h->H, h->F, fi);
     HIP_CHECK(hipMemcpy(h->d_shared, tmp.data(), rec, hipMemcpyHostToDevice));
   }
   if ((st = dev_alloc(h, &h->d_router_w, size_t(h->E) * h->H * 2))) return st;
@@ -452,7 +506,7 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
       (st = walloc(&h->d_distinct, 64)) || (st = walloc(&h->d_ticket, 64)) || (st = walloc(&h->d_h, h->max_rows * h->F * 2)) ||
       (st = walloc(&h->d_o, h->max_rows * h->H * 4)))
     return st;
-  if (int4 && (st = walloc(&h->d_x16, T * h->H * 2))) return st;
+  if (fi.f16 && (st = walloc(&h->d_x16, T * h->H * 2))) return st;
   h->ws_bytes = ws;
   HIP_CHECK(hipMemset(h->d_distinct, 0, 64));
   HIP_CHECK(hipMemset(h->d_ticket, 0, 64));
@@ -530,6 +584,8 @@ static GemmArgs gemm_args(strata_moe* h, bool gate_up, const void* x, const Tile
   a.K = gate_up ? h->H : h->F;
   a.out = gate_up ? h->d_h : (void*)h->d_o;
   a.out_ld = gate_up ? h->F : h->H;
+  a.sshift = h->sshift;
+  a.off_gscale = h->quant == Q_NVFP4 ? h->lay.gscale + (gate_up ? 0 : 8) : -1;
   return a;
 }
 

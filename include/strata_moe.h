@@ -50,7 +50,7 @@ typedef enum {
   STRATA_OK = 0,
   STRATA_E_INVALID = 1,     /* null pointer, size out of range, bad enum       */
   STRATA_E_UNSUPPORTED = 2, /* shape or value the kernels cannot take exactly  */
-  STRATA_E_BAD_SCALE = 3,   /* MXFP4 E8M0 scale byte 0 or 255 (admission)      */
+  STRATA_E_BAD_SCALE = 3,   /* admission: MXFP4 E8M0 byte 0 or 255, NVFP4 E4M3 NaN byte or matrix scale not finite and > 0 */
   STRATA_E_NOMEM = 4,       /* host-pinned or device allocation failed         */
   STRATA_E_HIP = 5,         /* a HIP runtime call failed                       */
   STRATA_E_POISONED = 6     /* an earlier HIP failure left the handle unusable */
@@ -63,7 +63,15 @@ typedef enum {
   STRATA_Q_INT4_G64_AFFINE_BF16 = 1,
   /* OCP MXFP4: E2M1 codes (sign bit 3), one E8M0 exponent byte e per 32
    * consecutive inputs of a row: w = e2m1(code) * 2^(e - 127), e in 1..254. */
-  STRATA_Q_MXFP4_E2M1_E8M0_G32 = 2
+  STRATA_Q_MXFP4_E2M1_E8M0_G32 = 2,
+  /* int4 affine as above with one (s, b) per 128 consecutive inputs (the
+   * "INT4 group-128, W4A16" of the ro99/strata README model table). */
+  STRATA_Q_INT4_G128_AFFINE_BF16 = 3,
+  /* NVFP4 (named in the same table; the published format): E2M1 codes, one
+   * OCP FP8 E4M3 scale byte per 16 consecutive inputs of a row and one fp32
+   * scale g per matrix: w = e2m1(code) * e4m3(byte) * g.  E4M3 NaN bytes
+   * (0x7F, 0xFF) fail admission. */
+  STRATA_Q_NVFP4_E2M1_E4M3_G16 = 4
 } strata_quant;
 
 typedef enum {
@@ -82,18 +90,21 @@ typedef enum {
 /* One stacked packed matrix, host pointers, row-major [out, in] per expert and
  * quantised along `in`.  Element 2i of a row is the low nibble of byte i.
  *   codes  : u8   [n_exp, out, in/2]
- *   scales : int4 -> bf16 bits [n_exp, out, in/64]; MXFP4 -> u8 E8M0 [n_exp, out, in/32]
- *   biases : int4 -> bf16 bits [n_exp, out, in/64]; MXFP4 -> must be NULL
+ *   scales : int4 -> bf16 bits [n_exp, out, in/G] (G = 64 or 128);
+ *            MXFP4 -> u8 E8M0 [n_exp, out, in/32]; NVFP4 -> u8 E4M3 [n_exp, out, in/16]
+ *   biases : int4 -> bf16 bits [n_exp, out, in/G]; MXFP4, NVFP4 -> must be NULL
+ *   global_scale : NVFP4 -> fp32 [n_exp], each finite and > 0; others -> must be NULL
  * Gate and up are [F, H] (out = F, in = H); down is [H, F]. */
 typedef struct {
   const void* codes;
   const void* scales;
   const void* biases;
+  const float* global_scale;
 } strata_qmat;
 
 typedef struct {
   int32_t hidden;        /* H: multiple of 512                               */
-  int32_t ffn;           /* F: multiple of 64                                */
+  int32_t ffn;           /* F: multiple of 64 (128 for int4 group-128)       */
   int32_t num_experts;   /* E: routed experts, 1..1024                       */
   int32_t top_k;         /* k: 1..min(E, 32)                                 */
   int32_t num_shared;    /* 0 or 1 shared expert (weight 1, always resident) */
@@ -110,7 +121,8 @@ typedef struct {
 } strata_moe_desc;
 
 /* Creates a layer.  Validates the descriptor, admits the weights (every MXFP4
- * scale byte must be in 1..254, every int4 scale and bias must be exactly
+ * scale byte must be in 1..254, every NVFP4 E4M3 byte a number and every
+ * NVFP4 matrix scale finite and > 0, every int4 scale and bias exactly
  * representable in fp16, which the kernels compute in), copies every routed
  * expert once into a library-owned pinned host store (a byte permutation into
  * kernel tile order: same byte count, no wider copy), allocates the HBM slot

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from oracle import moe as om
-from synth import CONFIG_ORDER, CONFIGS, WIDE_ORDER, make_layer, make_tokens
+from synth import CONFIG_ORDER, CONFIGS, FORMAT_ORDER, WIDE_ORDER, make_layer, make_tokens
 
 from gpu_util import W_ABS, assert_y_close, to_dev, y_bits, y_to_f64
 
@@ -43,7 +43,7 @@ def _check(lw, layer, x, sample, what):
     return y
 
 
-@pytest.mark.parametrize("name", CONFIG_ORDER + WIDE_ORDER)
+@pytest.mark.parametrize("name", CONFIG_ORDER + WIDE_ORDER + FORMAT_ORDER)
 def test_fullsize_config(name):
     import torch
     if not torch.cuda.is_available():

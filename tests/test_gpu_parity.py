@@ -31,6 +31,10 @@ SMALL = {
     # wider routing at the full expert counts (top-16 of 896, top-6 of 256)
     "e896_s": (CONFIGS["e896_top16_mxfp4"].scaled(hidden=512, ffn=128, budget_frac=0.1), (1, 3, 8, 300)),
     "e256_s": (CONFIGS["e256_top6_fp4"].scaled(hidden=1024, ffn=256), (1, 4, 333)),
+    # more 4-bit formats: int4 group-128, NVFP4 (with a shared expert)
+    "g128_s": (CONFIGS["e256_int4g128"].scaled(hidden=1024, ffn=256, num_experts=32, budget_frac=0.25),
+               (1, 2, 6, 300)),
+    "nvfp4_s": (CONFIGS["e256_nvfp4"].scaled(hidden=1024, ffn=256, num_experts=64), (1, 3, 8, 333)),
 }
 
 
@@ -72,7 +76,7 @@ def test_layer_matches_oracle_all_resident(torch_cuda, name):
     layer.close()
 
 
-@pytest.mark.parametrize("name", ["qwen_s", "glm_s", "e512_s", "mixtral_s", "e896_s"])
+@pytest.mark.parametrize("name", ["qwen_s", "glm_s", "e512_s", "mixtral_s", "e896_s", "g128_s", "nvfp4_s"])
 @pytest.mark.parametrize("policy", ["lru", "lfu"])
 def test_paged_output_is_bitwise_the_resident_output(torch_cuda, name, policy):
     """Budgeted (paged, waves) vs all-resident: identical y bits; counters equal

@@ -33,12 +33,15 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(_capi.EXPORTS)
 
 
+_QCODE = {"int4_g64": 1, "mxfp4_g32": 2, "int4_g128": 3, "nvfp4_g16": 4}
+
+
 def _desc_from(lw, **over):
     c = lw.cfg
     keep = []
     d = _capi.Desc()
     d.hidden, d.ffn, d.num_experts, d.top_k, d.num_shared = c.hidden, c.ffn, c.num_experts, c.top_k, c.num_shared
-    d.quant = 1 if c.quant == "int4_g64" else 2
+    d.quant = _QCODE[c.quant]
     d.router = 1 if c.router == "softmax" else 2
     d.policy, d.expert_budget, d.max_tokens, d.device = 1, c.budget, 16, -1
     keep.append(lw.router_w)
@@ -49,8 +52,13 @@ def _desc_from(lw, **over):
         if m is None:
             setattr(d, name, _capi.QMat(None, None, None))
         else:
+            gs = None
+            if m.global_scale is not None:
+                gs = np.ascontiguousarray(np.atleast_1d(m.global_scale), dtype=np.float32)
+                keep.append(gs)
             setattr(d, name, _capi.QMat(m.codes.ctypes.data, m.scales.ctypes.data,
-                                        None if m.biases is None else m.biases.ctypes.data))
+                                        None if m.biases is None else m.biases.ctypes.data,
+                                        None if gs is None else gs.ctypes.data))
     for k, v in over.items():
         setattr(d, k, v)
     return d, keep
@@ -212,3 +220,71 @@ def test_ctypes_mirrors_match_the_c_struct_sizes(tmp_path):
         assert int(out[cname]) == ctypes.sizeof(py), cname
         for fname, _ in py._fields_:
             assert int(out[f"{cname}.{fname}"]) == getattr(py, fname).offset, (cname, fname)
+
+
+# ----------------------------------------------------------------------------
+# more 4-bit formats: int4 group-128 and NVFP4 admission
+# ----------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def tiny_g128():
+    return make_layer(CONFIGS["tiny"].scaled(ffn=128, num_experts=4, top_k=2, quant="int4_g128",
+                                             budget_frac=0.5), seed=3)
+
+
+@pytest.fixture(scope="module")
+def tiny_nvfp4():
+    return make_layer(CONFIGS["tiny"].scaled(ffn=128, num_experts=4, top_k=2, quant="nvfp4_g16",
+                                             num_shared=1, budget_frac=0.5), seed=4)
+
+
+def test_int4_group128_ffn_must_be_a_multiple_of_128(tiny_g128):
+    d, keep = _desc_from(tiny_g128, ffn=192)
+    assert _create_status(d)[0] == _capi.E_UNSUPPORTED
+
+
+def test_int4_group128_needs_biases(tiny_g128):
+    d, keep = _desc_from(tiny_g128)
+    d.gate = _capi.QMat(d.gate.codes, d.gate.scales, None, None)
+    assert _create_status(d)[0] == _capi.E_INVALID
+
+
+def test_nvfp4_needs_matrix_scales_and_refuses_biases(tiny_nvfp4):
+    d, keep = _desc_from(tiny_nvfp4)
+    d.up = _capi.QMat(d.up.codes, d.up.scales, None, None)
+    assert _create_status(d)[0] == _capi.E_INVALID
+    d, keep = _desc_from(tiny_nvfp4)
+    d.down = _capi.QMat(d.down.codes, d.down.scales, d.down.codes, d.down.global_scale)
+    assert _create_status(d)[0] == _capi.E_INVALID
+
+
+def test_matrix_scale_is_refused_for_other_formats(tiny_int4):
+    d, keep = _desc_from(tiny_int4)
+    g = np.ones(4, np.float32)
+    d.gate = _capi.QMat(d.gate.codes, d.gate.scales, d.gate.biases, g.ctypes.data)
+    assert _create_status(d)[0] == _capi.E_INVALID
+
+
+@pytest.mark.parametrize("bad", [0x7F, 0xFF])
+@pytest.mark.parametrize("which", ["gate", "down", "sh_up"])
+def test_e4m3_nan_scale_is_refused(tiny_nvfp4, bad, which):
+    m = getattr(tiny_nvfp4, which)
+    saved = m.scales.copy()
+    try:
+        m.scales.reshape(-1)[m.scales.size // 3] = bad
+        d, keep = _desc_from(tiny_nvfp4)
+        st, msg = _create_status(d)
+        assert st == _capi.E_BAD_SCALE and "E4M3" in msg
+    finally:
+        m.scales[...] = saved
+
+
+@pytest.mark.parametrize("value", [0.0, -1.0, float("inf"), float("nan")])
+def test_nvfp4_matrix_scale_must_be_finite_and_positive(tiny_nvfp4, value):
+    m = tiny_nvfp4.up
+    saved = m.global_scale.copy()
+    try:
+        m.global_scale[1] = value
+        d, keep = _desc_from(tiny_nvfp4)
+        assert _create_status(d)[0] == _capi.E_BAD_SCALE
+    finally:
+        m.global_scale[...] = saved
