@@ -562,3 +562,131 @@ def test_p11_model_rejects_bad_budgets():
         ResidencyModel(4, 0)
     with pytest.raises(ValueError):
         ResidencyModel(4, 5)
+
+
+# ----------------------------------------------------------------------------
+# P-11b frequency decay, prefetch and expert profiles (hand-worked traces;
+# U = one use = 65536)
+# ----------------------------------------------------------------------------
+U = 65536
+
+
+def test_p11b_decay_changes_the_victim():
+    # E=3, B=2 (slots hold 0 and 1).  Expert 0 is used three times, expert 2
+    # twice later, then expert 1 is needed.  Scores under WARM d=1, by hand:
+    #   f1..f3 {0}: s0 = U, 1.5U, 1.75U          (decay halves, then +U)
+    #   f4 {2}: miss, evicts 1 (score 0);  s0 = 0.875U, s2 = U
+    #   f5 {2}: hit;                       s0 = 0.4375U = 28672, s2 = 1.5U = 98304
+    #   f6 {1}: miss; WARM evicts 0 (28672 < 98304), LFU evicts 2 (3U > 2U).
+    trace = [[0], [0], [0], [2], [2], [1]]
+    m = ResidencyModel(3, 2, "warm", decay_shift=1)
+    for n in trace[:5]:
+        m.forward(n)
+    assert m.profile() == [28672, 0, 98304]
+    assert m.forward([1]) == [[(1, 0, True)]]       # expert 0 sat in slot 0
+    m = ResidencyModel(3, 2, LFU)
+    for n in trace[:5]:
+        m.forward(n)
+    assert m.profile() == [3 * U, 0, 2 * U]
+    assert m.forward([1]) == [[(1, 1, True)]]       # expert 2 sat in slot 1
+    # decay rounds the loss down: 5 - (5 >> 2) = 4, 5 - (5 >> 1) = 3, and a
+    # score of 1 never decays (1 >> d = 0 for d >= 1)
+    m = ResidencyModel(3, 1, "warm", decay_shift=2, profile=[5, 1, 0])
+    m.forward([2])
+    assert m.profile() == [4, 1, U]
+    m = ResidencyModel(3, 1, "warm", decay_shift=1, profile=[5, 1, 0])
+    m.forward([2])
+    assert m.profile() == [3, 1, U]
+
+
+def test_p11b_prefetch_restores_the_hot_expert():
+    # E=3, B=2, LFU, prefetch 1.  {0,1} three times (s0 = s1 = 3U, last_use 3);
+    # f4 {2}: miss evicts 0 (key (3U,3,0) < (3U,3,1)) into slot 0; s2 = U.
+    # Prefetch: candidate 0 rank (3U,3) > smallest resident 2 rank (U,4):
+    # 0 is paged back into slot 0.  f5 {0} is then a hit from the prefetch.
+    m = ResidencyModel(3, 2, LFU, expert_bytes=10, prefetch=1)
+    for _ in range(3):
+        m.forward([0, 1])
+    assert m.forward([2]) == [[(2, 0, True)]]
+    assert m.resident() == {0: 0, 1: 1}
+    assert m.forward([0]) == [[(0, 0, False)]]
+    st = m.stats()
+    assert (st["hits"], st["misses"], st["evictions"], st["prefetched"], st["prefetch_hits"],
+            st["bytes_h2d"]) == (7, 1, 2, 1, 1, 20)
+    # without prefetch the same trace misses on f5
+    m = ResidencyModel(3, 2, LFU, expert_bytes=10)
+    for n in [[0, 1]] * 3 + [[2], [0]]:
+        m.forward(n)
+    st = m.stats()
+    assert (st["hits"], st["misses"], st["prefetched"]) == (6, 2, 0)
+    # equal ranks never swap: after f1 {2} (evicts 0) the non-residents 0 and
+    # 3 have rank (0, 0), the same as resident 1, so nothing is paged ahead
+    m = ResidencyModel(4, 2, LFU, prefetch=2)
+    m.forward([2])
+    assert m.resident() == {2: 0, 1: 1} and m.stats()["prefetched"] == 0
+
+
+def test_p11b_profile_warm_start_and_reload():
+    # profile [5, 0, 9U, 9U, 1], B=2: wanted = {2, 3}; slots 0,1 freed, 2 -> slot 0,
+    # 3 -> slot 1, nothing counted at create
+    prof = [5, 0, 9 * U, 9 * U, 1]
+    m = ResidencyModel(5, 2, "warm", expert_bytes=7, decay_shift=2, profile=prof)
+    assert m.resident() == {2: 0, 3: 1}
+    assert m.stats()["prefetched"] == 0 and m.stats()["bytes_h2d"] == 0
+    assert m.forward([2]) == [[(2, 0, False)]]
+    # d=2: s2 = 9U - 9U/4 + U = 507904; s3 = 442368; s0 = 5 - 1 = 4; s4 = 1
+    assert m.profile() == [4, 0, 507904, 442368, 1]
+    # run-time load [0,0,0,0,100]: wanted = {4, 0} (ties to the lower id);
+    # both residents leave, 0 -> slot 0, 4 -> slot 1; two prefetches, two evictions
+    m.load_profile([0, 0, 0, 0, 100])
+    assert m.resident() == {0: 0, 4: 1}
+    st = m.stats()
+    assert (st["prefetched"], st["evictions"], st["bytes_h2d"]) == (2, 2, 14)
+    m.forward([4])
+    assert m.stats()["prefetch_hits"] == 1
+    # a zero profile keeps the default slots; a wrong length or huge score is refused
+    assert ResidencyModel(5, 2, LFU, profile=[0] * 5).resident() == {0: 0, 1: 1}
+    with pytest.raises(ValueError):
+        ResidencyModel(5, 2, LFU, profile=[0] * 4)
+    with pytest.raises(ValueError):
+        ResidencyModel(5, 2, LFU, profile=[0, 0, 0, 0, 1 << 63])
+    with pytest.raises(ValueError):
+        ResidencyModel(5, 2, "warm")                 # warm needs a decay
+    with pytest.raises(ValueError):
+        ResidencyModel(5, 2, LRU, decay_shift=3)     # decay is warm only
+    with pytest.raises(ValueError):
+        ResidencyModel(5, 2, LRU, prefetch=3)        # prefetch above B
+
+
+def test_p11b_full_prefetch_keeps_the_top_ranked_set():
+    """With prefetch = B, after every forward no non-resident outranks a
+    resident (ranks compared without ids); brute force over random traces."""
+    rng = np.random.default_rng(33)
+    for policy, d in ((LFU, 0), ("warm", 1), ("warm", 5), (LRU, 0)):
+        for _ in range(20):
+            E = int(rng.integers(3, 24))
+            B = int(rng.integers(1, E))
+            m = ResidencyModel(E, B, policy, decay_shift=d, prefetch=B)
+            p = 1.0 / np.arange(1, E + 1) ** 1.2
+            for _ in range(40):
+                n = rng.choice(E, size=int(rng.integers(1, E + 1)), replace=False, p=p / p.sum())
+                m.forward(n.tolist())
+                res = m.resident()
+                rank = (lambda e: (m.last_use[e],)) if policy == LRU else \
+                    (lambda e: (m.score[e], m.last_use[e]))
+                inside = min(rank(e) for e in res)
+                outside = [rank(e) for e in range(E) if e not in res]
+                assert not outside or max(outside) <= inside
+
+
+def test_p11b_decay_is_exponential_forgetting():
+    """An expert used once and then never again follows
+    s_{n+1} = s_n - floor(s_n / 2**d): the loss is rounded down, so s_n lies
+    between U (1 - 2**-d)**n and that plus n."""
+    for d in (1, 3, 6):
+        m = ResidencyModel(2, 1, "warm", decay_shift=d)
+        m.forward([1])
+        for n in range(1, 60):
+            m.forward([0])
+            exact = U * (1 - 2.0 ** -d) ** n
+            assert exact - 1e-9 <= m.score[1] <= exact + n
