@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--workload", default="qwen3_30b_a3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--no-policies", action="store_true", help="skip the paged decode policy runs")
     ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--trace-summary", metavar="TRACE_DIR")
@@ -309,6 +310,9 @@ def main():
     # pinned host -> device rate on this machine (the paging link), measured by the library
     h2d_gbps = epq.measure_h2d(0, 256 << 20, 3)
 
+    # paged decode streams (B=1, fresh x per token) under each residency policy
+    policies = None if args.no_policies else decode_policies(epq, torch, lw, cfg, dev, make_tokens)
+
     tokens_per_step = Tp + Td
     value = K * tokens_per_step / dt
     res = {
@@ -333,6 +337,7 @@ def main():
         "kernel_ms_per_step": {k: round(v[0] / K, 4) for k, v in tm.items()},
         "events_pass_ms_per_step": round(dt_ev / K * 1e3, 4),
         "cache": st, "h2d_GBps": round(h2d_gbps, 2),
+        "paged_decode": policies,
         "gpu": {"name": props.name, "cus": props.multi_processor_count},
     }
 
@@ -347,6 +352,78 @@ def main():
             raise RuntimeError(f"cpu baseline failed: {r.stderr[-2000:]}")
         res["cpu_baseline"] = json.loads(r.stdout.strip().splitlines()[-1])
     print(json.dumps(res), flush=True)
+
+
+DECODE_WARM, DECODE_TIMED = 64, 256
+POLICY_RUNS = [("lru", dict(policy="lru")),
+               ("lfu", dict(policy="lfu")),
+               ("warm_d5", dict(policy="warm", decay_shift=5)),
+               ("warm_d5_prefetch2", dict(policy="warm", decay_shift=5, prefetch=2))]
+
+
+def decode_policies(epq, torch, lw, cfg, dev, make_tokens):
+    """Decode B=1 through the residency manager: DECODE_WARM untimed then
+    DECODE_TIMED timed forwards, each on a fresh token, per policy; the first
+    DECODE_WARM forwards of a new layer started cold and started from a
+    profile saved after another stream of the same workload; and a change of
+    work (DECODE_TIMED tokens of one topic, then DECODE_TIMED of another,
+    timed together after DECODE_WARM of the first)."""
+    log("[bench] paged decode policies")
+    n = DECODE_WARM + DECODE_TIMED
+    xs = [torch.from_numpy(make_tokens(cfg, 1, step=500000 + i).view(np.int16)).view(torch.bfloat16).to(dev)
+          for i in range(n)]
+    xs_prev = [torch.from_numpy(make_tokens(cfg, 1, step=600000 + i).view(np.int16)).view(torch.bfloat16)
+               .to(dev) for i in range(DECODE_TIMED)]
+    y = torch.empty((1, cfg.hidden), dtype=torch.bfloat16, device=dev)
+
+    def stream(layer, xs_run):
+        torch.cuda.synchronize()
+        s0 = layer.stats()
+        t0 = time.perf_counter()
+        for x in xs_run:
+            layer.forward(x, y=y)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        s1 = layer.stats()
+        d = {k: s1[k] - s0[k] for k in ("hits", "misses", "bytes_h2d", "prefetched", "prefetch_hits")}
+        return {"tokens_per_s": round(len(xs_run) / dt, 1), "us_per_token": round(dt / len(xs_run) * 1e6, 2),
+                "hit_rate": round(d["hits"] / max(1, d["hits"] + d["misses"]), 4),
+                "misses_per_token": round(d["misses"] / len(xs_run), 3),
+                "h2d_MB_per_token": round(d["bytes_h2d"] / len(xs_run) / 1e6, 3),
+                "prefetched": d["prefetched"], "prefetch_hits": d["prefetch_hits"]}
+
+    out = {"budget": cfg.budget, "experts": cfg.num_experts, "warmup_tokens": DECODE_WARM,
+           "timed_tokens": DECODE_TIMED, "runs": {}}
+    for name, kw in POLICY_RUNS:
+        layer = epq.MoELayer.from_weights(lw, budget=cfg.budget, max_tokens=1, **kw)
+        stream(layer, xs[:DECODE_WARM])
+        out["runs"][name] = stream(layer, xs[DECODE_WARM:])
+        layer.close()
+    # warm start: a profile learned on another stream of the same workload
+    src = epq.MoELayer.from_weights(lw, budget=cfg.budget, max_tokens=1, policy="warm", decay_shift=5)
+    stream(src, xs_prev)
+    prof = src.save_profile()
+    src.close()
+    ws = {}
+    for name, p in (("cold", None), ("profile", prof)):
+        layer = epq.MoELayer.from_weights(lw, budget=cfg.budget, max_tokens=1, policy="warm", decay_shift=5,
+                                          profile=p)
+        ws[name] = stream(layer, xs[:DECODE_WARM])
+        layer.close()
+    out["warm_start_first_tokens"] = ws
+    # a change of work: topic 1 then topic 2 (each adds a fixed direction to x)
+    xa = [torch.from_numpy(make_tokens(cfg, 1, step=700000 + i, topic=1).view(np.int16)).view(torch.bfloat16)
+          .to(dev) for i in range(DECODE_WARM + DECODE_TIMED)]
+    xb = [torch.from_numpy(make_tokens(cfg, 1, step=800000 + i, topic=2).view(np.int16)).view(torch.bfloat16)
+          .to(dev) for i in range(DECODE_TIMED)]
+    shift = {}
+    for name, kw in POLICY_RUNS[:3]:
+        layer = epq.MoELayer.from_weights(lw, budget=cfg.budget, max_tokens=1, **kw)
+        stream(layer, xa[:DECODE_WARM])
+        shift[name] = stream(layer, xa[DECODE_WARM:] + xb)
+        layer.close()
+    out["topic_shift"] = shift
+    return out
 
 
 def cpu_baseline(lw, cfg, n_steps):

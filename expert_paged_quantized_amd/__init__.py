@@ -18,7 +18,7 @@ __all__ = ["MoELayer", "StrataError", "measure_h2d", "measure_hbm_read", "replay
 _QUANT = {"int4_g64": _capi.Q_INT4_G64, "mxfp4_g32": _capi.Q_MXFP4_G32,
           "int4_g128": _capi.Q_INT4_G128, "nvfp4_g16": _capi.Q_NVFP4_G16}
 _ROUTER = {"softmax": _capi.R_SOFTMAX, "sigmoid": _capi.R_SIGMOID}
-_POLICY = {"lru": _capi.P_LRU, "lfu": _capi.P_LFU}
+_POLICY = {"lru": _capi.P_LRU, "lfu": _capi.P_LFU, "warm": _capi.P_WARM}
 
 
 def _ptr(a):
@@ -45,7 +45,7 @@ class MoELayer:
 
     def __init__(self, *, hidden, ffn, num_experts, top_k, num_shared, quant, router, budget,
                  max_tokens, router_w, router_bias, gate, up, down, sh_gate=None, sh_up=None,
-                 sh_down=None, policy="lru", device=-1):
+                 sh_down=None, policy="lru", decay_shift=0, prefetch=0, profile=None, device=-1):
         self.hidden, self.ffn, self.num_experts, self.top_k = hidden, ffn, num_experts, top_k
         self.num_shared, self.max_tokens = num_shared, max_tokens
         keep = []
@@ -58,6 +58,11 @@ class MoELayer:
         d.router = _ROUTER[router] if isinstance(router, str) else router
         d.policy = _POLICY[policy] if isinstance(policy, str) else policy
         d.expert_budget, d.max_tokens, d.device = budget, max_tokens, device
+        d.decay_shift, d.prefetch = decay_shift, prefetch
+        if profile is not None:
+            prof = _profile_array(profile, num_experts)
+            keep.append(prof)
+            d.expert_profile = prof.ctypes.data
         d.router_w, d.router_bias = rw.ctypes.data, (None if rb is None else rb.ctypes.data)
         d.gate, d.up, d.down = _qmat(gate, keep), _qmat(up, keep), _qmat(down, keep)
         d.sh_gate, d.sh_up, d.sh_down = _qmat(sh_gate, keep), _qmat(sh_up, keep), _qmat(sh_down, keep)
@@ -66,7 +71,8 @@ class MoELayer:
         self._h = h
 
     @classmethod
-    def from_weights(cls, lw, budget=None, policy="lru", max_tokens=None, device=-1):
+    def from_weights(cls, lw, budget=None, policy="lru", max_tokens=None, device=-1, decay_shift=0,
+                     prefetch=0, profile=None):
         """Builds a layer from a weights object with .cfg and the packed arrays."""
         c = lw.cfg
         return cls(hidden=c.hidden, ffn=c.ffn, num_experts=c.num_experts, top_k=c.top_k,
@@ -75,7 +81,8 @@ class MoELayer:
                    max_tokens=max(c.prefill_T, max(c.decode_T)) if max_tokens is None else max_tokens,
                    router_w=lw.router_w, router_bias=lw.router_bias, gate=lw.gate, up=lw.up,
                    down=lw.down, sh_gate=lw.sh_gate, sh_up=lw.sh_up, sh_down=lw.sh_down,
-                   policy=policy, device=device)
+                   policy=policy, decay_shift=decay_shift, prefetch=prefetch, profile=profile,
+                   device=device)
 
     # ------------------------------------------------------------------
     def forward(self, x, y=None, stream=None, dbg=False):
@@ -117,6 +124,17 @@ class MoELayer:
         check(lib().strata_expert_cache_stats(self._h, ctypes.byref(s)))
         return s.as_dict()
 
+    def save_profile(self) -> np.ndarray:
+        """The learned per-expert frequency scores, uint64 [E] (one use = 65536)."""
+        out = np.zeros(self.num_experts, dtype=np.uint64)
+        check(lib().strata_expert_profile_save(self._h, out.ctypes.data, self.num_experts))
+        return out
+
+    def load_profile(self, profile):
+        """Sets the scores and pages the profile's hottest experts in, ahead of need."""
+        prof = _profile_array(profile, self.num_experts)
+        check(lib().strata_expert_profile_load(self._h, prof.ctypes.data, self.num_experts))
+
     def memory(self) -> dict:
         m = _capi.MemoryInfo()
         check(lib().strata_moe_memory(self._h, ctypes.byref(m)))
@@ -156,16 +174,31 @@ def measure_hbm_read(device=-1, nbytes=1 << 30, iters=5) -> float:
     return g.value
 
 
-def replay_residency(num_experts, budget, trace, policy="lru", expert_bytes=0, want_slots=False):
-    """Dry-run of the residency policy on a trace of needed-expert lists (host only)."""
+def _profile_array(profile, num_experts):
+    prof = np.ascontiguousarray(profile, dtype=np.uint64)
+    if prof.shape != (num_experts,):
+        raise ValueError(f"profile must have shape ({num_experts},)")
+    return prof
+
+
+def replay_residency(num_experts, budget, trace, policy="lru", expert_bytes=0, want_slots=False,
+                     decay_shift=0, prefetch=0, profile=None):
+    """Dry-run of the residency policy on a trace of needed-expert lists (host
+    only).  Returns the counters, plus "slots" (want_slots) and the final
+    "scores"."""
     lens = np.array([len(n) for n in trace], dtype=np.int32)
     flat = np.array([e for n in trace for e in n], dtype=np.int32)
     slots = np.full(max(1, flat.size), -1, dtype=np.int32) if want_slots else None
+    scores = np.zeros(max(1, num_experts), dtype=np.uint64)
+    prof = None if profile is None else _profile_array(profile, num_experts)
     s = _capi.CacheStats()
-    check(lib().strata_residency_replay(num_experts, budget, _POLICY[policy], expert_bytes, len(trace),
-                                        _ptr(lens), _ptr(flat if flat.size else np.zeros(1, np.int32)),
-                                        _ptr(slots), ctypes.byref(s)))
+    check(lib().strata_residency_replay(num_experts, budget, _POLICY.get(policy, policy), decay_shift,
+                                        prefetch, None if prof is None else prof.ctypes.data,
+                                        expert_bytes, len(trace), _ptr(lens),
+                                        _ptr(flat if flat.size else np.zeros(1, np.int32)),
+                                        _ptr(slots), scores.ctypes.data, ctypes.byref(s)))
     res = s.as_dict()
     if want_slots:
         res["slots"] = slots[:flat.size]
+    res["scores"] = scores[:num_experts]
     return res

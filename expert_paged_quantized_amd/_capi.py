@@ -12,7 +12,7 @@ OK, E_INVALID, E_UNSUPPORTED, E_BAD_SCALE, E_NOMEM, E_HIP, E_POISONED = range(7)
 STATUS_NAMES = ["OK", "E_INVALID", "E_UNSUPPORTED", "E_BAD_SCALE", "E_NOMEM", "E_HIP", "E_POISONED"]
 Q_INT4_G64, Q_MXFP4_G32, Q_INT4_G128, Q_NVFP4_G16 = 1, 2, 3, 4
 R_SOFTMAX, R_SIGMOID = 1, 2
-P_LRU, P_LFU = 1, 2
+P_LRU, P_LFU, P_WARM = 1, 2, 3
 KERNEL_CLASSES = ["router", "group", "decode_gate_up", "decode_down", "prefill_gate_up",
                   "prefill_down", "combine"]
 
@@ -25,6 +25,7 @@ class Desc(ctypes.Structure):
     _fields_ = [("hidden", c_i32), ("ffn", c_i32), ("num_experts", c_i32), ("top_k", c_i32),
                 ("num_shared", c_i32), ("quant", c_i32), ("router", c_i32), ("policy", c_i32),
                 ("expert_budget", c_i32), ("max_tokens", c_i32), ("device", c_i32),
+                ("decay_shift", c_i32), ("prefetch", c_i32), ("expert_profile", c_vp),
                 ("router_w", c_vp), ("router_bias", c_vp),
                 ("gate", QMat), ("up", QMat), ("down", QMat),
                 ("sh_gate", QMat), ("sh_up", QMat), ("sh_down", QMat)]
@@ -38,8 +39,9 @@ class RouteDbg(ctypes.Structure):
 class CacheStats(ctypes.Structure):
     _fields_ = [("forwards", c_u64), ("hits", c_u64), ("misses", c_u64), ("evictions", c_u64),
                 ("bytes_h2d", c_u64), ("waves", c_u64), ("budget", c_i32), ("resident", c_i32),
-                ("policy", c_i32), ("reserved", c_i32), ("resident_bytes", c_u64),
-                ("expert_bytes", c_u64)]
+                ("policy", c_i32), ("decay_shift", c_i32), ("resident_bytes", c_u64),
+                ("expert_bytes", c_u64), ("prefetched", c_u64), ("prefetch_hits", c_u64),
+                ("prefetch", c_i32), ("reserved", c_i32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
@@ -68,8 +70,10 @@ EXPORTS = {
     "strata_last_error": (ctypes.c_char_p, []),
     "strata_measure_h2d": (c_i32, [c_i32, c_u64, c_i32, ctypes.POINTER(ctypes.c_double)]),
     "strata_measure_hbm_read": (c_i32, [c_i32, c_u64, c_i32, ctypes.POINTER(ctypes.c_double)]),
-    "strata_residency_replay": (c_i32, [c_i32, c_i32, c_i32, c_u64, c_i32, c_vp, c_vp, c_vp,
-                                        ctypes.POINTER(CacheStats)]),
+    "strata_expert_profile_save": (c_i32, [c_vp, c_vp, c_i32]),
+    "strata_expert_profile_load": (c_i32, [c_vp, c_vp, c_i32]),
+    "strata_residency_replay": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_u64, c_i32,
+                                        c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(CacheStats)]),
 }
 
 _lib = None

@@ -1,19 +1,26 @@
 #include "residency.h"
 
+#include <algorithm>
+
 namespace strata {
 
-void ResidencyManager::init(int num_experts, int budget, int policy, uint64_t expert_bytes) {
+void ResidencyManager::init(int num_experts, int budget, int policy, int decay_shift, int prefetch,
+                            uint64_t expert_bytes) {
   num_experts_ = num_experts;
   budget_ = budget;
   policy_ = policy;
+  decay_shift_ = policy == kWARM ? decay_shift : 0;
+  prefetch_ = prefetch;
   expert_bytes_ = expert_bytes;
   n_ = 0;
   forwards = hits = misses = evictions = bytes_h2d = waves = 0;
+  prefetched = prefetch_hits = 0;
   slot_expert_.assign(budget, -1);
   expert_slot_.assign(num_experts, -1);
   last_use_.assign(num_experts, 0);
-  use_count_.assign(num_experts, 0);
+  score_.assign(num_experts, 0);
   in_wave_.assign(num_experts, 0);
+  from_prefetch_.assign(num_experts, 0);
   for (int s = 0; s < budget; ++s) {
     slot_expert_[s] = s;
     expert_slot_[s] = s;
@@ -26,15 +33,54 @@ int ResidencyManager::resident() const {
   return r;
 }
 
+bool ResidencyManager::rank_less(int a, int b) const {
+  if (policy_ != kLRU && score_[a] != score_[b]) return score_[a] < score_[b];
+  return last_use_[a] < last_use_[b];
+}
+
 bool ResidencyManager::before(int a, int b) const {
-  if (policy_ == kLFU && use_count_[a] != use_count_[b]) return use_count_[a] < use_count_[b];
-  if (last_use_[a] != last_use_[b]) return last_use_[a] < last_use_[b];
+  if (rank_less(a, b)) return true;
+  if (rank_less(b, a)) return false;
   return a < b;
 }
 
+void ResidencyManager::page(int e, int slot, bool count, std::vector<PlanEntry>& pages) {
+  const int old = slot_expert_[slot];
+  if (old >= 0) {
+    expert_slot_[old] = -1;
+    from_prefetch_[old] = 0;
+  }
+  slot_expert_[slot] = e;
+  expert_slot_[e] = slot;
+  pages.push_back({e, slot, true});
+  if (count) {
+    if (old >= 0) ++evictions;
+    ++prefetched;
+    bytes_h2d += expert_bytes_;
+    from_prefetch_[e] = 1;
+  }
+}
+
+void ResidencyManager::load_profile(const uint64_t* scores, bool count, std::vector<PlanEntry>& pages) {
+  pages.clear();
+  score_.assign(scores, scores + num_experts_);
+  std::vector<int32_t> order(num_experts_);
+  for (int e = 0; e < num_experts_; ++e) order[e] = e;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return score_[a] > score_[b]; });
+  std::vector<uint8_t> wanted(num_experts_, 0);
+  for (int i = 0; i < budget_; ++i) wanted[order[i]] = 1;
+  std::vector<int32_t> freed, newcomers;
+  for (int s = 0; s < budget_; ++s)
+    if (slot_expert_[s] < 0 || !wanted[slot_expert_[s]]) freed.push_back(s);
+  for (int e = 0; e < num_experts_; ++e)
+    if (wanted[e] && expert_slot_[e] < 0) newcomers.push_back(e);
+  for (size_t i = 0; i < newcomers.size(); ++i) page(newcomers[i], freed[i], count, pages);
+}
+
 void ResidencyManager::forward(const std::vector<int32_t>& needed,
-                               std::vector<std::vector<PlanEntry>>& plan) {
+                               std::vector<std::vector<PlanEntry>>& plan, std::vector<PlanEntry>& ahead) {
   plan.clear();
+  ahead.clear();
   if (needed.empty()) return;
   ++n_;
   ++forwards;
@@ -45,6 +91,10 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
     if (expert_slot_[e] >= 0) {
       order.push_back(e);
       ++nh;
+      if (from_prefetch_[e]) {
+        ++prefetch_hits;
+        from_prefetch_[e] = 0;
+      }
     }
   for (int32_t e : needed)
     if (expert_slot_[e] < 0) order.push_back(e);
@@ -76,6 +126,7 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
         }
         slot = expert_slot_[victim];
         expert_slot_[victim] = -1;
+        from_prefetch_[victim] = 0;
         ++evictions;
       }
       slot_expert_[slot] = e;
@@ -85,14 +136,29 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
     for (size_t i = w0; i < w1; ++i) in_wave_[order[i]] = 0;
     plan.push_back(std::move(wave));
   }
+  if (decay_shift_ > 0)
+    for (int e = 0; e < num_experts_; ++e) score_[e] -= score_[e] >> decay_shift_;
   for (int32_t e : needed) {
     last_use_[e] = n_;
-    ++use_count_[e];
+    score_[e] += kUnit;
   }
   hits += nh;
   misses += nm;
   bytes_h2d += nm * expert_bytes_;
   waves += plan.size();
+
+  if (prefetch_ > 0) {
+    std::vector<int32_t> out, in;
+    for (int e = 0; e < num_experts_; ++e) (expert_slot_[e] < 0 ? out : in).push_back(e);
+    // candidates: decreasing rank, ties to the lower id; victims: increasing key
+    std::stable_sort(out.begin(), out.end(), [&](int a, int b) { return rank_less(b, a); });
+    std::sort(in.begin(), in.end(), [&](int a, int b) { return before(a, b); });
+    const size_t np = std::min({out.size(), in.size(), (size_t)prefetch_});
+    for (size_t i = 0; i < np; ++i) {
+      if (!rank_less(in[i], out[i])) break;
+      page(out[i], expert_slot_[in[i]], true, ahead);
+    }
+  }
 }
 
 }  // namespace strata

@@ -4,16 +4,29 @@
 // experts with the rest streamed ("Documentation" page, Signature: budget and
 // policy arguments), a GPU cache of the most-used experts that adapts to the
 // workload over an all-experts copy pinned in host RAM ("Strata, Explained",
-// section 2).  The rules below are the reading this library implements:
-//   * create fills slots 0..B-1 with experts 0..B-1 (last_use 0, use_count 0);
+// section 2), a learned cache that can be saved across restarts and a tunable
+// adaptation rate (same page, section 8), and predictors that may reorder
+// work but not change it (ro99/strata README, rules).  The rules below are the
+// reading this library implements:
+//   * each expert has last_use (forward number) and a frequency score
+//     (unsigned, one use = kUnit); create fills slots 0..B-1 with experts
+//     0..B-1 and, given a profile, sets the scores and rebalances (below);
 //   * a forward needs the experts with at least one token, N ascending;
 //     hits are those resident when it starts, misses the rest;
 //   * N is run as hits (ascending) then misses (ascending), in waves of at most
 //     B experts; a wave's compute finishes before any of its slots is reused;
 //   * a miss takes the lowest free slot, else evicts the resident outside the
-//     current wave with the smallest key: LRU (last_use, id), LFU (use_count,
-//     last_use, id);
-//   * then every expert of N gets last_use = forward number, use_count += 1.
+//     current wave with the smallest key: LRU (last_use, id), LFU and WARM
+//     (score, last_use, id);
+//   * then (WARM only) every score loses score >> decay_shift, and every
+//     expert of N gains kUnit and gets last_use = forward number;
+//   * with prefetch P > 0, non-residents by decreasing rank (the key without
+//     the id; ties to the lower id) are paired with residents by increasing
+//     key, and while fewer than P pairs are taken and the candidate outranks
+//     the resident strictly, the candidate is paged into that slot;
+//   * a profile load sets the scores, then the B experts with the largest
+//     score (ties to the lower id) take the slots of the residents outside
+//     that set, newcomers ascending by id into freed slots ascending.
 // None of this changes what a forward computes, only what it copies.
 #pragma once
 #include <stdint.h>
@@ -32,24 +45,38 @@ class ResidencyManager {
  public:
   static constexpr int kLRU = 1;
   static constexpr int kLFU = 2;
+  static constexpr int kWARM = 3;
+  static constexpr uint64_t kUnit = uint64_t(1) << 16;
+  static constexpr uint64_t kMaxScore = uint64_t(1) << 62;
 
-  void init(int num_experts, int budget, int policy, uint64_t expert_bytes);
-  // `needed` must be ascending and unique.  Fills `waves` with the plan.
-  void forward(const std::vector<int32_t>& needed, std::vector<std::vector<PlanEntry>>& waves);
+  void init(int num_experts, int budget, int policy, int decay_shift, int prefetch, uint64_t expert_bytes);
+  // `needed` must be ascending and unique.  Fills `waves` with the plan and
+  // `ahead` with the pages to make once the forward's compute is done.
+  void forward(const std::vector<int32_t>& needed, std::vector<std::vector<PlanEntry>>& waves,
+               std::vector<PlanEntry>& ahead);
+  // Sets the scores (E values, each <= kMaxScore; checked by the caller) and
+  // rebalances; `count` books the pages as prefetches (run time) or not
+  // (create).  Fills `pages` with the copies to make.
+  void load_profile(const uint64_t* scores, bool count, std::vector<PlanEntry>& pages);
+  const std::vector<uint64_t>& scores() const { return score_; }
 
   int budget() const { return budget_; }
   int resident() const;
   int slot_of(int e) const { return expert_slot_[e]; }
+  int expert_in(int slot) const { return slot_expert_[slot]; }
 
   uint64_t forwards = 0, hits = 0, misses = 0, evictions = 0, bytes_h2d = 0, waves = 0;
+  uint64_t prefetched = 0, prefetch_hits = 0;
 
  private:
-  bool before(int a, int b) const;  // a is a better victim than b
-  int num_experts_ = 0, budget_ = 0, policy_ = kLRU;
+  bool rank_less(int a, int b) const;  // rank of a < rank of b (ids ignored)
+  bool before(int a, int b) const;     // a is a better victim than b
+  void page(int e, int slot, bool count, std::vector<PlanEntry>& pages);
+  int num_experts_ = 0, budget_ = 0, policy_ = kLRU, decay_shift_ = 0, prefetch_ = 0;
   uint64_t expert_bytes_ = 0, n_ = 0;
   std::vector<int32_t> slot_expert_, expert_slot_;
-  std::vector<uint64_t> last_use_, use_count_;
-  std::vector<uint8_t> in_wave_;
+  std::vector<uint64_t> last_use_, score_;
+  std::vector<uint8_t> in_wave_, from_prefetch_;
 };
 
 }  // namespace strata

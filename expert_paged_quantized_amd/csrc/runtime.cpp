@@ -130,8 +130,14 @@ struct strata_moe {
   bool fwd_recorded = false;
   std::vector<hipEvent_t> ev_copied;  // [wave][copy stream]
   std::vector<hipEvent_t> ev_wave_done;
+  // pages made ahead of need (prefetch, profile loads): the last one on each
+  // copy stream; the next forward orders its copies and compute after them
+  hipEvent_t ev_ahead[kCopyStreams] = {};
+  bool ahead_used[kCopyStreams] = {};
+  bool ahead_pending = false;
 
   ResidencyManager rm;
+  int decay_shift = 0, prefetch = 0;
   uint64_t forwards = 0;
   bool poisoned = false;
 
@@ -173,6 +179,28 @@ static bool format_of(int quant, FormatInfo& f) {
   }
 }
 
+// Residency arguments shared by create and the dry-run planner.
+static strata_status check_residency(int E, int budget, int policy, int decay_shift, int prefetch,
+                                     const uint64_t* profile) {
+  if (policy != STRATA_P_LRU && policy != STRATA_P_LFU && policy != STRATA_P_WARM)
+    return fail(STRATA_E_INVALID, "unknown policy");
+  if (budget < 1 || budget > E) return fail(STRATA_E_INVALID, "expert_budget must be in [1, num_experts]");
+  if (policy == STRATA_P_WARM && (decay_shift < 1 || decay_shift > 24))
+    return fail(STRATA_E_INVALID, "WARM needs decay_shift in [1, 24]");
+  if (policy != STRATA_P_WARM && decay_shift != 0)
+    return fail(STRATA_E_INVALID, "decay_shift applies to WARM only");
+  if (prefetch < 0 || prefetch > budget) return fail(STRATA_E_INVALID, "prefetch must be in [0, budget]");
+  if (profile)
+    for (int e = 0; e < E; ++e)
+      if (profile[e] > ResidencyManager::kMaxScore) return fail(STRATA_E_INVALID, "profile score above 2^62");
+  return STRATA_OK;
+}
+
+static int rm_policy(int policy) {
+  return policy == STRATA_P_WARM ? ResidencyManager::kWARM
+                                 : policy == STRATA_P_LFU ? ResidencyManager::kLFU : ResidencyManager::kLRU;
+}
+
 static strata_status validate(const strata_moe_desc* d) {
   if (!d) return fail(STRATA_E_INVALID, "desc is NULL");
   if (d->hidden <= 0 || d->ffn <= 0 || d->num_experts <= 0 || d->top_k <= 0 || d->max_tokens <= 0)
@@ -185,9 +213,9 @@ static strata_status validate(const strata_moe_desc* d) {
   if (!format_of(d->quant, fi)) return fail(STRATA_E_INVALID, "unknown quant");
   if (d->router != STRATA_R_SOFTMAX_TOPK_RENORM && d->router != STRATA_R_SIGMOID_TOPK_RENORM)
     return fail(STRATA_E_INVALID, "unknown router");
-  if (d->policy != STRATA_P_LRU && d->policy != STRATA_P_LFU) return fail(STRATA_E_INVALID, "unknown policy");
-  if (d->expert_budget < 1 || d->expert_budget > d->num_experts)
-    return fail(STRATA_E_INVALID, "expert_budget must be in [1, num_experts]");
+  if (strata_status st = check_residency(d->num_experts, d->expert_budget, d->policy, d->decay_shift,
+                                         d->prefetch, d->expert_profile))
+    return st;
   if (d->max_tokens > (1 << 20)) return fail(STRATA_E_UNSUPPORTED, "max_tokens > 2^20");
   if (d->hidden % 512) return fail(STRATA_E_UNSUPPORTED, "hidden must be a multiple of 512");
   if (d->ffn % 64) return fail(STRATA_E_UNSUPPORTED, "ffn must be a multiple of 64");
@@ -390,6 +418,8 @@ static void release(strata_moe* h) {
   for (auto e : h->ev_pool) (void)hipEventDestroy(e);
   for (auto e : h->ev_copied) (void)hipEventDestroy(e);
   for (auto e : h->ev_wave_done) (void)hipEventDestroy(e);
+  for (auto e : h->ev_ahead)
+    if (e) (void)hipEventDestroy(e);
   if (h->ev_fwd_done) (void)hipEventDestroy(h->ev_fwd_done);
   for (auto cs : h->copy_streams)
     if (cs) (void)hipStreamDestroy(cs);
@@ -442,6 +472,8 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   h->sshift = fi.sshift;
   h->router = d->router == STRATA_R_SOFTMAX_TOPK_RENORM ? R_SOFTMAX : R_SIGMOID;
   h->policy = d->policy;
+  h->decay_shift = d->decay_shift;
+  h->prefetch = d->prefetch;
   h->budget = d->expert_budget;
   h->max_tokens = d->max_tokens;
   h->lay = RecordLayout::make(h->H, h->F, h->quant, h->sshift);
@@ -515,13 +547,19 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
 
   for (auto& cs : h->copy_streams) HIP_CHECK(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
   HIP_CHECK(hipEventCreateWithFlags(&h->ev_fwd_done, hipEventDisableTiming));
+  for (auto& e : h->ev_ahead) HIP_CHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
 
-  // preload experts 0..budget-1 into slots 0..budget-1
+  // preload: experts 0..budget-1 in slots 0..budget-1, or the profile's
+  // hottest experts
+  h->rm.init(h->E, h->budget, rm_policy(h->policy), d->decay_shift, d->prefetch, rec);
+  if (d->expert_profile) {
+    std::vector<PlanEntry> pages;
+    h->rm.load_profile(d->expert_profile, false, pages);
+  }
   for (int s = 0; s < h->budget; ++s)
-    HIP_CHECK(hipMemcpy(h->h_slot_ptr[s], h->host_store + rec * s, rec, hipMemcpyHostToDevice));
+    HIP_CHECK(hipMemcpy(h->h_slot_ptr[s], h->host_store + rec * h->rm.expert_in(s), rec,
+                        hipMemcpyHostToDevice));
   HIP_CHECK(hipDeviceSynchronize());
-  h->rm.init(h->E, h->budget, h->policy == STRATA_P_LFU ? ResidencyManager::kLFU : ResidencyManager::kLRU,
-             rec);
   return STRATA_OK;
 }
 
@@ -639,6 +677,38 @@ static void add_tiles(strata_moe* h, int expert, int slot, int row_begin, int co
   }
 }
 
+// Copies `pages` from the pinned store into their slots on the copy streams
+// (round-robin), after `after` (the compute that last read those slots), and
+// marks them pending for the next forward.
+static hipError_t page_ahead(strata_moe* h, const std::vector<PlanEntry>& pages, hipEvent_t after) {
+  const size_t rec = h->lay.bytes;
+  bool waited[kCopyStreams] = {};
+  int c = 0;
+  for (const PlanEntry& p : pages) {
+    hipStream_t cs = h->copy_streams[c];
+    if (!waited[c]) {
+      waited[c] = true;
+      hipError_t e = after ? hipStreamWaitEvent(cs, after, 0) : hipSuccess;
+      // an earlier batch of pages on another stream may target the same slot
+      for (int i = 0; i < kCopyStreams && e == hipSuccess; ++i)
+        if (i != c && h->ahead_used[i]) e = hipStreamWaitEvent(cs, h->ev_ahead[i], 0);
+      if (e != hipSuccess) return e;
+    }
+    hipError_t e = hipMemcpyAsync(h->h_slot_ptr[p.slot], h->host_store + rec * p.expert, rec,
+                                  hipMemcpyHostToDevice, cs);
+    if (e != hipSuccess) return e;
+    c = (c + 1) % kCopyStreams;
+  }
+  for (int i = 0; i < kCopyStreams; ++i) {
+    if (!waited[i]) continue;
+    hipError_t e = hipEventRecord(h->ev_ahead[i], h->copy_streams[i]);
+    if (e != hipSuccess) return e;
+    h->ahead_used[i] = true;
+  }
+  h->ahead_pending = true;
+  return hipSuccess;
+}
+
 static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, hipStream_t s,
                                   const strata_route_dbg* dbg) {
   const bool decode = T <= kDecodeMaxT;
@@ -673,7 +743,8 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
     }
     if (off[h->E] != TK) return fail(STRATA_E_HIP, "token counts do not add up to T*k");
     std::vector<std::vector<PlanEntry>> plan;
-    h->rm.forward(needed, plan);
+    std::vector<PlanEntry> ahead;
+    h->rm.forward(needed, plan, ahead);
     // tile lists: per wave [hits (+ shared in wave 0)] [paged]
     const int nw = (int)plan.size();
     std::vector<int> hb(nw), he(nw), pe(nw);
@@ -712,6 +783,18 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
         h->ev_copied.push_back(a);
       }
     }
+    // Pages made ahead of this forward (prefetch, profile load) land before
+    // its compute reads the slots and before any copy of it overwrites one.
+    if (h->ahead_pending) {
+      for (int i = 0; i < kCopyStreams; ++i) {
+        if (!h->ahead_used[i]) continue;
+        HIP_CHECK(hipStreamWaitEvent(s, h->ev_ahead[i], 0));
+        for (int c = 0; c < kCopyStreams; ++c)
+          if (c != i) HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_ahead[i], 0));
+        h->ahead_used[i] = false;
+      }
+      h->ahead_pending = false;
+    }
     // A wave's misses are dealt round-robin over the copy streams, so the
     // per-copy setup of one record overlaps the transfer of another; each
     // stream first waits until the previous wave no longer reads its slots.
@@ -742,6 +825,8 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
       }
       HIP_CHECK(hipEventRecord(h->ev_wave_done[w], s));
     }
+    // the policy's pages ahead of need, once this forward's experts are done
+    if (!ahead.empty()) HIP_CHECK(page_ahead(h, ahead, h->ev_wave_done[nw - 1]));
   }
 
   HIP_CHECK(timed(h, STRATA_K_COMBINE, s, [&]() {
@@ -831,8 +916,38 @@ strata_status strata_expert_cache_stats(const strata_moe* h, strata_cache_stats*
   out->budget = h->budget;
   out->resident = h->rm.resident();
   out->policy = h->policy;
+  out->decay_shift = h->decay_shift;
   out->expert_bytes = h->lay.bytes;
   out->resident_bytes = uint64_t(out->resident) * h->lay.bytes;
+  out->prefetched = h->rm.prefetched;
+  out->prefetch_hits = h->rm.prefetch_hits;
+  out->prefetch = h->prefetch;
+  return STRATA_OK;
+}
+
+strata_status strata_expert_profile_save(const strata_moe* h, uint64_t* scores, int32_t num_experts) {
+  if (!h || !scores) return fail(STRATA_E_INVALID, "NULL argument");
+  if (num_experts != h->E) return fail(STRATA_E_INVALID, "num_experts does not match the layer");
+  const std::vector<uint64_t>& sc = h->rm.scores();
+  std::copy(sc.begin(), sc.end(), scores);
+  return STRATA_OK;
+}
+
+strata_status strata_expert_profile_load(strata_moe* h, const uint64_t* scores, int32_t num_experts) {
+  if (!h || !scores) return fail(STRATA_E_INVALID, "NULL argument");
+  if (h->poisoned) return fail(STRATA_E_POISONED, "handle poisoned by an earlier HIP failure");
+  if (num_experts != h->E) return fail(STRATA_E_INVALID, "num_experts does not match the layer");
+  for (int e = 0; e < h->E; ++e)
+    if (scores[e] > ResidencyManager::kMaxScore) return fail(STRATA_E_INVALID, "profile score above 2^62");
+  hipError_t err = hipSetDevice(h->device);
+  std::vector<PlanEntry> pages;
+  h->rm.load_profile(scores, true, pages);
+  if (err == hipSuccess && !pages.empty())
+    err = page_ahead(h, pages, h->fwd_recorded ? h->ev_fwd_done : nullptr);
+  if (err != hipSuccess) {
+    h->poisoned = true;
+    return fail(STRATA_E_HIP, std::string("profile load: ") + hipGetErrorString(err));
+  }
   return STRATA_OK;
 }
 
@@ -959,17 +1074,19 @@ strata_status strata_measure_hbm_read(int32_t device, uint64_t bytes, int32_t it
 }
 
 strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32_t policy,
+                                      int32_t decay_shift, int32_t prefetch, const uint64_t* profile,
                                       uint64_t expert_bytes, int32_t n_forwards,
                                       const int32_t* needed_len, const int32_t* needed_flat,
-                                      int32_t* plan_slots, strata_cache_stats* out) {
+                                      int32_t* plan_slots, uint64_t* scores_out,
+                                      strata_cache_stats* out) {
   if (!out || n_forwards < 0 || (n_forwards > 0 && (!needed_len || !needed_flat)))
     return fail(STRATA_E_INVALID, "NULL argument or negative count");
-  if (num_experts < 1 || budget < 1 || budget > num_experts)
-    return fail(STRATA_E_INVALID, "budget must be in [1, num_experts]");
-  if (policy != STRATA_P_LRU && policy != STRATA_P_LFU) return fail(STRATA_E_INVALID, "unknown policy");
+  if (num_experts < 1 || num_experts > (1 << 20)) return fail(STRATA_E_INVALID, "num_experts out of range");
+  if (strata_status st = check_residency(num_experts, budget, policy, decay_shift, prefetch, profile)) return st;
   ResidencyManager rm;
-  rm.init(num_experts, budget, policy == STRATA_P_LFU ? ResidencyManager::kLFU : ResidencyManager::kLRU,
-          expert_bytes);
+  rm.init(num_experts, budget, rm_policy(policy), decay_shift, prefetch, expert_bytes);
+  std::vector<PlanEntry> ahead;
+  if (profile) rm.load_profile(profile, false, ahead);
   size_t pos = 0, out_pos = 0;
   std::vector<std::vector<PlanEntry>> plan;
   for (int32_t f = 0; f < n_forwards; ++f) {
@@ -980,7 +1097,7 @@ strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32
       if (e < 0 || e >= num_experts) return fail(STRATA_E_INVALID, "expert id out of range");
     std::sort(nd.begin(), nd.end());
     nd.erase(std::unique(nd.begin(), nd.end()), nd.end());
-    rm.forward(nd, plan);
+    rm.forward(nd, plan, ahead);
     for (auto& w : plan)
       for (auto& p : w) {
         if (plan_slots) plan_slots[out_pos] = p.slot;
@@ -999,8 +1116,13 @@ strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32
   out->budget = budget;
   out->resident = rm.resident();
   out->policy = policy;
+  out->decay_shift = decay_shift;
   out->expert_bytes = expert_bytes;
   out->resident_bytes = uint64_t(rm.resident()) * expert_bytes;
+  out->prefetched = rm.prefetched;
+  out->prefetch_hits = rm.prefetch_hits;
+  out->prefetch = prefetch;
+  if (scores_out) std::copy(rm.scores().begin(), rm.scores().end(), scores_out);
   return STRATA_OK;
 }
 

@@ -82,9 +82,20 @@ typedef enum {
   STRATA_R_SIGMOID_TOPK_RENORM = 2
 } strata_router;
 
+/* Residency policies.  The pages name policies (none, warm, cache, hybrid) on
+ * the "Documentation" page (Signature) without defining them, say the GPU
+ * cache adapts to the workload ("Strata, Explained", section 2) at a rate that
+ * is tuned per machine and that its learned state can be saved, one profile
+ * per kind of work (same page, section 8).  Every expert carries a frequency
+ * score (one use = 65536; see strata_expert_profile_save).  A policy only
+ * decides what is paged and when; it never changes y. */
 typedef enum {
   STRATA_P_LRU = 1, /* evict the least recently used, ties to the lower id */
-  STRATA_P_LFU = 2  /* evict the least often used, then least recent, then lower id */
+  STRATA_P_LFU = 2, /* evict the lowest score, then least recent, then lower id */
+  STRATA_P_WARM = 3 /* LFU order on a decaying score: after every forward each
+                     * score loses score >> decay_shift before the uses of that
+                     * forward are added, so old use fades at 1 - 2^-decay_shift
+                     * per forward (the cache's adaptation rate) */
 } strata_policy;
 
 /* One stacked packed matrix, host pointers, row-major [out, in] per expert and
@@ -114,6 +125,14 @@ typedef struct {
   int32_t expert_budget; /* resident routed experts (HBM slots), 1..E         */
   int32_t max_tokens;    /* largest T a forward may take (sizes the workspace) */
   int32_t device;        /* HIP device ordinal; -1 = the current device       */
+  int32_t decay_shift;   /* WARM: 1..24; other policies: must be 0            */
+  int32_t prefetch;      /* 0..budget: most experts paged ahead after a forward
+                          * (non-residents that outrank a resident under the
+                          * policy's order, hottest first, into the coldest
+                          * residents' slots); 0 = off                        */
+  const uint64_t* expert_profile; /* host [E] scores (each <= 2^62) to warm the
+                          * slots with at create, or NULL (see
+                          * strata_expert_profile_load)                       */
   const uint16_t* router_w;   /* host, bf16 bits [E, H]                        */
   const float* router_bias;   /* host, fp32 [E], or NULL                       */
   strata_qmat gate, up, down; /* routed experts, n_exp = E                     */
@@ -128,7 +147,10 @@ typedef struct {
  * kernel tile order: same byte count, no wider copy), allocates the HBM slot
  * pool (expert_budget slots), the resident shared expert, the router and a
  * workspace sized by max_tokens, and preloads routed experts 0..budget-1 into
- * slots 0..budget-1.  The caller's buffers may be freed when this returns.
+ * slots 0..budget-1, or, given expert_profile, the budget experts with the
+ * largest scores (ties to the lower id; those among 0..budget-1 keep their
+ * slots, the rest fill the freed slots in ascending id order).  The caller's
+ * buffers may be freed when this returns.
  * Errors: E_INVALID, E_UNSUPPORTED, E_BAD_SCALE, E_NOMEM, E_HIP.  On error
  * *out is NULL and nothing is leaked. */
 strata_status strata_moe_create(const strata_moe_desc* desc, strata_moe** out);
@@ -178,9 +200,15 @@ typedef struct {
   int32_t budget;          /* slots                                            */
   int32_t resident;        /* slots holding an expert                          */
   int32_t policy;          /* strata_policy                                    */
-  int32_t reserved;
+  int32_t decay_shift;     /* as created                                       */
   uint64_t resident_bytes; /* resident * expert_bytes                          */
   uint64_t expert_bytes;   /* packed bytes of one expert                       */
+  uint64_t prefetched;     /* experts paged ahead of need (prefetch, run-time
+                            * profile loads); included in bytes_h2d and, when
+                            * they overwrote an expert, in evictions           */
+  uint64_t prefetch_hits;  /* hits on an expert paged ahead, first use only    */
+  int32_t prefetch;        /* as created                                       */
+  int32_t reserved;
 } strata_cache_stats;
 
 /* Reads the counters.  Does no device work except, when budget == E, one
@@ -247,18 +275,40 @@ strata_status strata_measure_h2d(int32_t device, uint64_t bytes, int32_t iters, 
  * Errors: E_INVALID (bytes < 64 MiB, iters < 1, NULL out), E_NOMEM, E_HIP. */
 strata_status strata_measure_hbm_read(int32_t device, uint64_t bytes, int32_t iters, double* gbps);
 
+/* The learned cache state ("expert_profile_save", "Strata, Explained",
+ * section 8): writes the E frequency scores of the layer to `scores` (host,
+ * uint64 [num_experts]; one use = 65536, decayed under WARM).  Feeding them
+ * back at create (desc.expert_profile) or to strata_expert_profile_load
+ * starts a layer warm.  Host only.  Errors: E_INVALID (null pointers,
+ * num_experts != E). */
+strata_status strata_expert_profile_save(const strata_moe* h, uint64_t* scores, int32_t num_experts);
+
+/* Loads a saved profile into a live layer: sets the scores, then pages the B
+ * experts with the largest scores (ties to the lower id) that are not yet
+ * resident into the slots of the residents outside that set, on the copy
+ * streams, after the previous forward's compute; the next forward waits for
+ * them.  Returns without waiting.  Counted as prefetches.  With budget == E it
+ * only sets the scores.  Errors: E_INVALID (null pointers, num_experts != E,
+ * a score above 2^62), E_HIP (poisons the handle), E_POISONED. */
+strata_status strata_expert_profile_load(strata_moe* h, const uint64_t* scores, int32_t num_experts);
+
 /* Dry-run planner (host only, touches no GPU): replays the residency policy of
  * a layer with E experts and `budget` slots over a trace of forwards and
  * reports what a real run would page, the placement-plan side of the budget
- * decision.  needed_flat holds the needed expert ids of every forward back to
- * back, needed_len[i] of them for forward i (any order, duplicates ignored).
- * If plan_slots is not NULL it receives, per forward and per needed expert in
- * the order the forward runs them (hits ascending, then misses ascending), the
- * slot used; its length must be sum(needed_len).  Errors: E_INVALID. */
+ * decision.  policy, decay_shift, prefetch and profile (NULL or E scores
+ * applied at create) mean what they mean in strata_moe_desc.  needed_flat
+ * holds the needed expert ids of every forward back to back, needed_len[i] of
+ * them for forward i (any order, duplicates ignored).  If plan_slots is not
+ * NULL it receives, per forward and per needed expert in the order the
+ * forward runs them (hits ascending, then misses ascending), the slot used;
+ * its length must be sum(needed_len).  If scores_out is not NULL it receives
+ * the E final scores.  Errors: E_INVALID. */
 strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32_t policy,
+                                      int32_t decay_shift, int32_t prefetch, const uint64_t* profile,
                                       uint64_t expert_bytes, int32_t n_forwards,
                                       const int32_t* needed_len, const int32_t* needed_flat,
-                                      int32_t* plan_slots, strata_cache_stats* out);
+                                      int32_t* plan_slots, uint64_t* scores_out,
+                                      strata_cache_stats* out);
 
 #ifdef __cplusplus
 }

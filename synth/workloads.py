@@ -364,8 +364,18 @@ def make_layer(cfg: LayerConfig, seed: Optional[int] = None, threads: Optional[i
     return lw
 
 
-def make_tokens(cfg: LayerConfig, T: int, step: int = 0, seed: Optional[int] = None) -> np.ndarray:
-    """Activations x ~ N(0,1) in bf16 bits, uint16 [T, H]; one stream per step."""
+def make_tokens(cfg: LayerConfig, T: int, step: int = 0, seed: Optional[int] = None,
+                topic: Optional[int] = None, strength: float = 1.0) -> np.ndarray:
+    """Activations x ~ N(0,1) in bf16 bits, uint16 [T, H]; one stream per step.
+
+    With `topic`, every token also carries `strength` times a fixed N(0,1)
+    direction drawn from (seed, 31337, topic): a stand-in for one kind of
+    work, which moves the router's preferred experts (a topic shift moves the
+    hot set)."""
     base = cfg.seed if seed is None else seed
     rng = np.random.default_rng([base, 7919, step])
-    return f32_to_bf16_bits(rng.standard_normal((T, cfg.hidden), dtype=np.float32))
+    x = rng.standard_normal((T, cfg.hidden), dtype=np.float32)
+    if topic is not None:
+        v = np.random.default_rng([base, 31337, topic]).standard_normal(cfg.hidden, dtype=np.float32)
+        x = x + np.float32(strength) * v
+    return f32_to_bf16_bits(x)

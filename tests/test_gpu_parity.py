@@ -108,6 +108,47 @@ def test_paged_output_is_bitwise_the_resident_output(torch_cuda, name, policy):
     paged.close()
 
 
+@pytest.mark.parametrize("name", ["qwen_s", "glm_s", "e512_s", "nvfp4_s"])
+def test_warm_policy_prefetch_and_profiles_only_reorder_work(torch_cuda, name):
+    """WARM (decayed scores) with prefetch, a warm start from a profile and a
+    run-time profile load between forwards: y is bitwise the resident y, and
+    counters and scores equal the residency model's."""
+    lw = _get(name)
+    cfg = lw.cfg
+    E, B = cfg.num_experts, cfg.budget
+    P = max(1, B // 2)
+    rng = np.random.default_rng(cfg.seed + 90)
+    prof0 = rng.integers(0, 6 * 65536, size=E).astype(np.uint64)
+    prof1 = rng.integers(0, 6 * 65536, size=E).astype(np.uint64)
+    res = _mk(lw, budget=E)
+    import expert_paged_quantized_amd as epq
+    paged = epq.MoELayer.from_weights(lw, budget=B, policy="warm", decay_shift=2, prefetch=P,
+                                      profile=prof0, max_tokens=512)
+    model = ResidencyModel(E, B, "warm", cfg.expert_bytes(), decay_shift=2, prefetch=P,
+                           profile=prof0.tolist())
+    Ts = [1, 1, 300, 1, 2, 8, 1, 257, 4, 1, 1, 5, 3, 1, 1]
+    for i, T in enumerate(Ts):
+        if i == 6:
+            paged.load_profile(prof1)
+            model.load_profile(prof1.tolist())
+        print(f"[warm] {name} step={i} T={T}", flush=True)
+        x = make_tokens(cfg, T, step=400 + i, seed=cfg.seed + 50)
+        xd = to_dev(x)
+        y_r = res.forward(xd)
+        y_p, dbg = paged.forward(xd, dbg=True)
+        assert np.array_equal(y_bits(y_p), y_bits(y_r)), f"{name} step {i}: paged != resident"
+        model.forward(np.nonzero(dbg["counts"].cpu().numpy())[0].tolist())
+    st, want = paged.stats(), model.stats()
+    for k in ("forwards", "hits", "misses", "evictions", "bytes_h2d", "waves", "resident",
+              "resident_bytes", "prefetched", "prefetch_hits"):
+        assert st[k] == want[k], (k, st[k], want[k])
+    assert st["policy"] == 3 and st["decay_shift"] == 2 and st["prefetch"] == P
+    assert paged.save_profile().tolist() == model.profile()
+    assert st["prefetched"] > 0 and st["misses"] > 0
+    res.close()
+    paged.close()
+
+
 def test_budget_one_thrashes_but_matches(torch_cuda):
     lw = _get("glm_s")
     cfg = lw.cfg

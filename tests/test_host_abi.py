@@ -10,7 +10,7 @@ import pytest
 
 import expert_paged_quantized_amd as epq
 from expert_paged_quantized_amd import _capi
-from oracle.residency import LFU, LRU, ResidencyModel
+from oracle.residency import LFU, LRU, WARM, ResidencyModel
 from synth import CONFIGS, make_layer
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
@@ -94,7 +94,11 @@ def tiny_fp4():
     ("num_shared", 2, _capi.E_UNSUPPORTED),
     ("quant", 7, _capi.E_INVALID),
     ("router", 0, _capi.E_INVALID),
-    ("policy", 3, _capi.E_INVALID),
+    ("policy", 9, _capi.E_INVALID),
+    ("policy", 3, _capi.E_INVALID),            # WARM without a decay_shift
+    ("decay_shift", 2, _capi.E_INVALID),       # decay on LRU
+    ("prefetch", 3, _capi.E_INVALID),          # prefetch > budget (2)
+    ("prefetch", -1, _capi.E_INVALID),
     ("max_tokens", 0, _capi.E_INVALID),
     ("num_experts", 2000, _capi.E_UNSUPPORTED),
     ("router_w", None, _capi.E_INVALID),
@@ -192,6 +196,54 @@ def test_residency_replay_rejects_bad_arguments():
         epq.replay_residency(4, 0, [[0]])
     with pytest.raises(epq.StrataError):
         epq.replay_residency(4, 2, [[7]])
+    with pytest.raises(epq.StrataError):
+        epq.replay_residency(4, 2, [[0]], policy=WARM)               # no decay
+    with pytest.raises(epq.StrataError):
+        epq.replay_residency(4, 2, [[0]], policy=LFU, decay_shift=2)
+    with pytest.raises(epq.StrataError):
+        epq.replay_residency(4, 2, [[0]], policy=WARM, decay_shift=25)
+    with pytest.raises(epq.StrataError):
+        epq.replay_residency(4, 2, [[0]], prefetch=3)
+    with pytest.raises(epq.StrataError):
+        epq.replay_residency(4, 2, [[0]], profile=[0, 0, 0, (1 << 62) + 1])
+
+
+@pytest.mark.parametrize("policy,d", [(LRU, 0), (LFU, 0), (WARM, 1), (WARM, 4)])
+def test_residency_replay_with_decay_prefetch_and_profile_matches_model(policy, d):
+    """The C++ manager (decayed scores, prefetch pairing, warm start from a
+    profile) against the residency model: every counter, every slot and the
+    final scores agree."""
+    rng = np.random.default_rng(77 + d)
+    for trial in range(40):
+        E = int(rng.integers(2, 48))
+        B = int(rng.integers(1, E + 1))
+        P = int(rng.integers(0, B + 1))
+        prof = None
+        if trial % 3 == 0:
+            prof = rng.integers(0, 8 * 65536, size=E).astype(np.uint64)
+            prof[rng.integers(0, E)] = prof[0]           # a tie in the warm set
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p = p[rng.permutation(E)]
+        trace = []
+        for f in range(int(rng.integers(1, 50))):
+            if f == 25:                                   # the workload shifts
+                p = p[rng.permutation(E)]
+            n = int(rng.integers(1, E + 1))
+            trace.append(rng.choice(E, size=n, replace=False, p=p / p.sum()).tolist())
+        m = ResidencyModel(E, B, policy, expert_bytes=1000, decay_shift=d, prefetch=P,
+                           profile=None if prof is None else prof.tolist())
+        want_slots = []
+        for n in trace:
+            for wave in m.forward(n):
+                want_slots += [s for (_, s, _) in wave]
+        got = epq.replay_residency(E, B, trace, policy=policy, expert_bytes=1000, want_slots=True,
+                                   decay_shift=d, prefetch=P, profile=prof)
+        st = m.stats()
+        for k in ("forwards", "hits", "misses", "evictions", "bytes_h2d", "waves", "resident",
+                  "resident_bytes", "prefetched", "prefetch_hits"):
+            assert got[k] == st[k], (trial, k, got[k], st[k])
+        assert got["slots"].tolist() == want_slots, trial
+        assert got["scores"].tolist() == m.profile(), trial
 
 
 def test_ctypes_mirrors_match_the_c_struct_sizes(tmp_path):
