@@ -17,11 +17,18 @@ possible:
   given, the scores are set to it and the slots are then rebalanced (below);
 * forward n (n = 1, 2, ...): N = experts with at least one token, ascending;
   hits = N that are resident when the call starts, misses = the rest;
-* the needed list is hits (ascending) then misses (ascending), cut into waves
-  of B experts; a wave is computed before any of its slots is reused;
+* the needed list is hits (ascending) then misses (ascending).  If it holds
+  at most B experts it is one wave.  Otherwise (a forward that streams more
+  experts than there are slots) the P = floor(B/4) hits with the largest keys
+  are pinned for the whole forward, so a long prompt does not flush the hot
+  set; the other S = B - (pinned count) slots stream, and the list is cut into
+  waves of W = floor(S/2) experts (1 if S < 2): while one wave computes, the
+  next one's pages land in slots the computing wave does not read;
 * each miss, in list order, takes the lowest free slot, else evicts the
-  resident with the smallest key among residents that are not in the current
-  wave.  Keys: LRU (last_use, id); LFU and WARM (score, last_use, id);
+  resident with the smallest key among the residents that are not in the
+  current wave, not in the previous wave (multi-wave forwards with S >= 2)
+  and not pinned.  Keys: LRU (last_use, id); LFU and WARM (score, last_use,
+  id);
 * afterwards every expert loses score >> d (d = decay_shift; WARM only, LRU
   and LFU use d = 0), every expert of N gains UNIT and gets last_use = n;
   so a use's weight falls by 1 - 2**-d per later forward (the adaptation rate);
@@ -141,10 +148,19 @@ class ResidencyModel:
                 self.prefetch_hits += 1
                 self.from_prefetch[e] = False
         order = hits + misses
+        pinned, W, prev_too = set(), self.B, False
+        if len(order) > self.B:
+            pinned = set(sorted(hits, key=self._key, reverse=True)[:self.B // 4])
+            S = self.B - len(pinned)
+            W = S // 2 if S >= 2 else 1
+            prev_too = S >= 2
         plan = []
-        for w0 in range(0, len(order), self.B):
-            wave = order[w0:w0 + self.B]
+        prev = set()
+        for w0 in range(0, len(order), W):
+            wave = order[w0:w0 + W]
             in_wave = set(wave)
+            keep = in_wave | pinned | (prev if prev_too else set())
+            prev = in_wave
             entries = []
             for e in wave:
                 res = self.resident()
@@ -155,7 +171,7 @@ class ResidencyModel:
                 if free:
                     slot = free[0]
                 else:
-                    cands = [x for x in res if x not in in_wave]
+                    cands = [x for x in res if x not in keep]
                     victim = min(cands, key=self._key)
                     slot = res[victim]
                     self.from_prefetch[victim] = False

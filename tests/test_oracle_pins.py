@@ -541,13 +541,15 @@ def test_p11_lru_matches_ordered_dict():
 
 def test_p11_hand_worked_waves_and_lfu():
     # E=6, B=2; slots hold experts 0,1.  Need {0,3,4,5}: hit 0, misses 3,4,5.
+    # More than B experts: no pin (floor(2/4) = 0), S = 2 streaming slots,
+    # waves of 1; a miss may not evict the current or the previous wave.
     m = ResidencyModel(6, 2, LRU)
     plan = m.forward([5, 3, 0, 4])
-    # wave 1: [0 (hit, slot 0), 3 (evicts 1 from slot 1)];
-    # wave 2: [4, 5] evict by (last_use, id): 0 and 3 both last_use 0 -> 0 first
-    assert plan == [[(0, 0, False), (3, 1, True)], [(4, 0, True), (5, 1, True)]]
+    # [0] hit in slot 0; [3] may not take 0's slot -> evicts 1 (slot 1);
+    # [4] may not take 3's -> evicts 0 (slot 0); [5] may not take 4's -> evicts 3
+    assert plan == [[(0, 0, False)], [(3, 1, True)], [(4, 0, True)], [(5, 1, True)]]
     st = m.stats()
-    assert (st["hits"], st["misses"], st["evictions"], st["waves"]) == (1, 3, 3, 2)
+    assert (st["hits"], st["misses"], st["evictions"], st["waves"]) == (1, 3, 3, 4)
     # LFU keeps the frequently used expert 0 over the recently used expert 2
     m = ResidencyModel(4, 2, LFU)
     m.forward([0])
@@ -555,6 +557,26 @@ def test_p11_hand_worked_waves_and_lfu():
     m.forward([2])      # evicts 1 (use_count 0)
     m.forward([3])      # candidates 0 (count 2) and 2 (count 1): evicts 2
     assert set(m.resident()) == {0, 3}
+
+
+def test_p11_streaming_forward_keeps_the_pinned_hot_expert():
+    # E=10, B=4, LRU: slots hold 0..3; f1 {2} makes expert 2 the most recent.
+    # f2 needs 0..7 (> B): pin floor(4/4) = 1 hit with the largest key -> 2;
+    # S = 3 streaming slots, waves of 1, victims outside {current, previous, 2}
+    # (keys are the values before f2's update: 2 has last_use 1, others 0):
+    #   [4]: candidates 0, 1 -> 0 (slot 0)   [5]: candidates 1, 3 -> 1 (slot 1)
+    #   [6]: candidates 3, 4 -> 3 (slot 3)   [7]: candidates 4, 5 -> 4 (slot 0)
+    m = ResidencyModel(10, 4, LRU)
+    m.forward([2])
+    plan = m.forward(list(range(8)))
+    assert plan == [[(0, 0, False)], [(1, 1, False)], [(2, 2, False)], [(3, 3, False)],
+                    [(4, 0, True)], [(5, 1, True)], [(6, 3, True)], [(7, 0, True)]]
+    assert m.resident() == {7: 0, 5: 1, 2: 2, 6: 3}
+    st = m.stats()
+    assert (st["hits"], st["misses"], st["evictions"], st["waves"]) == (5, 4, 4, 9)
+    # a forward that fits (N <= B) is one wave with no pin: {2, 8} -> evicts the
+    # smallest key among 7, 5, 6 (all last_use 2) = 5
+    assert m.forward([2, 8]) == [[(2, 2, False), (8, 1, True)]]
 
 
 def test_p11_model_rejects_bad_budgets():
