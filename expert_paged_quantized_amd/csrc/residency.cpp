@@ -20,6 +20,7 @@ void ResidencyManager::init(int num_experts, int budget, int policy, int decay_s
   last_use_.assign(num_experts, 0);
   score_.assign(num_experts, 0);
   in_wave_.assign(num_experts, 0);
+  keep_.assign(num_experts, 0);
   from_prefetch_.assign(num_experts, 0);
   for (int s = 0; s < budget; ++s) {
     slot_expert_[s] = s;
@@ -100,9 +101,26 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
     if (expert_slot_[e] < 0) order.push_back(e);
   const uint64_t nm = needed.size() - nh;
 
-  for (size_t w0 = 0; w0 < order.size(); w0 += budget_) {
-    const size_t w1 = (w0 + budget_ < order.size()) ? w0 + budget_ : order.size();
+  // keep_: 1 = pinned for the forward; in_wave_: 1 = current wave, 2 = previous
+  size_t W = budget_;
+  bool prev_too = false;
+  std::vector<int32_t> pinned;
+  if (order.size() > (size_t)budget_) {
+    pinned.assign(order.begin(), order.begin() + nh);  // the hits
+    std::sort(pinned.begin(), pinned.end(), [&](int a, int b) { return before(b, a); });
+    pinned.resize(std::min(pinned.size(), (size_t)(budget_ / 4)));
+    for (int32_t e : pinned) keep_[e] = 1;
+    const int S = budget_ - (int)pinned.size();
+    W = S >= 2 ? S / 2 : 1;
+    prev_too = S >= 2;
+  }
+  wave_lag_ = prev_too ? 2 : 1;
+  size_t p0 = 0, p1 = 0;  // previous wave: order[p0, p1)
+  for (size_t w0 = 0; w0 < order.size(); w0 += W) {
+    const size_t w1 = (w0 + W < order.size()) ? w0 + W : order.size();
     for (size_t i = w0; i < w1; ++i) in_wave_[order[i]] = 1;
+    if (prev_too)
+      for (size_t i = p0; i < p1; ++i) in_wave_[order[i]] = 2;
     std::vector<PlanEntry> wave;
     wave.reserve(w1 - w0);
     for (size_t i = w0; i < w1; ++i) {
@@ -121,7 +139,7 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
         int victim = -1;
         for (int s = 0; s < budget_; ++s) {
           const int r = slot_expert_[s];
-          if (in_wave_[r]) continue;
+          if (in_wave_[r] || keep_[r]) continue;
           if (victim < 0 || before(r, victim)) victim = r;
         }
         slot = expert_slot_[victim];
@@ -133,9 +151,12 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
       expert_slot_[e] = slot;
       wave.push_back({e, slot, true});
     }
-    for (size_t i = w0; i < w1; ++i) in_wave_[order[i]] = 0;
+    for (size_t i = p0; i < w1; ++i) in_wave_[order[i]] = 0;
+    p0 = w0;
+    p1 = w1;
     plan.push_back(std::move(wave));
   }
+  for (int32_t e : pinned) keep_[e] = 0;
   if (decay_shift_ > 0)
     for (int e = 0; e < num_experts_; ++e) score_[e] -= score_[e] >> decay_shift_;
   for (int32_t e : needed) {

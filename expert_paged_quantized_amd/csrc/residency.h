@@ -13,11 +13,16 @@
 //     0..B-1 and, given a profile, sets the scores and rebalances (below);
 //   * a forward needs the experts with at least one token, N ascending;
 //     hits are those resident when it starts, misses the rest;
-//   * N is run as hits (ascending) then misses (ascending), in waves of at most
-//     B experts; a wave's compute finishes before any of its slots is reused;
-//   * a miss takes the lowest free slot, else evicts the resident outside the
-//     current wave with the smallest key: LRU (last_use, id), LFU and WARM
-//     (score, last_use, id);
+//   * N is run as hits (ascending) then misses (ascending); if N fits in B
+//     slots it is one wave; otherwise the floor(B/4) hits with the largest
+//     keys stay pinned for the whole forward (a long prompt does not flush the
+//     hot set) and the list runs in waves of W = floor(S/2) (1 if S < 2),
+//     S = B - pinned, so the next wave's pages land while a wave computes;
+//   * a miss takes the lowest free slot, else evicts, among residents outside
+//     the current wave, the previous wave (multi-wave, S >= 2) and the pinned
+//     set, the one with the smallest key: LRU (last_use, id), LFU and WARM
+//     (score, last_use, id); a wave's pages wait only for the compute of the
+//     wave that last read the slots (one or two waves back: wave_lag);
 //   * then (WARM only) every score loses score >> decay_shift, and every
 //     expert of N gains kUnit and gets last_use = forward number;
 //   * with prefetch P > 0, non-residents by decreasing rank (the key without
@@ -54,6 +59,9 @@ class ResidencyManager {
   // `ahead` with the pages to make once the forward's compute is done.
   void forward(const std::vector<int32_t>& needed, std::vector<std::vector<PlanEntry>>& waves,
                std::vector<PlanEntry>& ahead);
+  // Waves back whose compute the pages of a wave must wait for (1 or 2),
+  // for the last forward.
+  int wave_lag() const { return wave_lag_; }
   // Sets the scores (E values, each <= kMaxScore; checked by the caller) and
   // rebalances; `count` books the pages as prefetches (run time) or not
   // (create).  Fills `pages` with the copies to make.
@@ -72,11 +80,11 @@ class ResidencyManager {
   bool rank_less(int a, int b) const;  // rank of a < rank of b (ids ignored)
   bool before(int a, int b) const;     // a is a better victim than b
   void page(int e, int slot, bool count, std::vector<PlanEntry>& pages);
-  int num_experts_ = 0, budget_ = 0, policy_ = kLRU, decay_shift_ = 0, prefetch_ = 0;
+  int num_experts_ = 0, budget_ = 0, policy_ = kLRU, decay_shift_ = 0, prefetch_ = 0, wave_lag_ = 1;
   uint64_t expert_bytes_ = 0, n_ = 0;
   std::vector<int32_t> slot_expert_, expert_slot_;
   std::vector<uint64_t> last_use_, score_;
-  std::vector<uint8_t> in_wave_, from_prefetch_;
+  std::vector<uint8_t> in_wave_, keep_, from_prefetch_;
 };
 
 }  // namespace strata

@@ -797,8 +797,11 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
     }
     // A wave's misses are dealt round-robin over the copy streams, so the
     // per-copy setup of one record overlaps the transfer of another; each
-    // stream first waits until the previous wave no longer reads its slots.
+    // stream first waits for the compute of the wave that last read the slots
+    // it overwrites (the previous wave, or the one before it when the plan
+    // keeps the previous wave's slots: then pages overlap a wave's compute).
     const size_t rec = h->lay.bytes;
+    const int lag = h->rm.wave_lag();
     for (int w = 0; w < nw; ++w) {
       const bool any_paged = pe[w] > he[w];
       int used = 0;
@@ -808,7 +811,7 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
           if (!p.paged) continue;
           if (fault("h2d")) return fail(STRATA_E_HIP, "hipMemcpyAsync H2D failed (injected fault)");
           if (c == used) {
-            if (w > 0) HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_wave_done[w - 1], 0));
+            if (w >= lag) HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_wave_done[w - lag], 0));
             ++used;
           }
           HIP_CHECK(hipMemcpyAsync(h->h_slot_ptr[p.slot], h->host_store + rec * p.expert, rec,

@@ -179,10 +179,12 @@ typedef struct {
  * x and y must not overlap.  The call enqueues its work on `stream`.  When the
  * budget is smaller than E it waits once for the per-expert token counts to
  * reach the host, decides hits and misses, and pages missing experts from the
- * pinned store into slots with hipMemcpyAsync on an internal copy stream; if
- * more distinct experts are needed than there are slots, the experts run in
- * waves of at most `budget`.  Paging, waves and slot placement never change y
- * (it is bitwise the same as with budget = E).  T == 0 is a no-op.
+ * pinned store into slots with hipMemcpyAsync on internal copy streams; if
+ * more distinct experts are needed than there are slots, the policy's
+ * hottest quarter of the slots stays put and the experts stream through the
+ * rest in waves of half of it, so one wave's pages land while the previous
+ * wave computes.  Paging, waves and slot placement never change y (it is
+ * bitwise the same as with budget = E).  T == 0 is a no-op.
  * Errors: E_INVALID (null handle or pointers, T < 0, T > max_tokens), E_HIP
  * (after which the handle is poisoned), E_POISONED. */
 strata_status strata_moe_forward(strata_moe* h, const void* x, int32_t T, void* y, void* stream,
