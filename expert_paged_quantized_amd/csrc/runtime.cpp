@@ -20,6 +20,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cstdio>
 #include <string>
 #include <thread>
@@ -127,6 +128,7 @@ struct strata_moe {
   Tile* h_tiles = nullptr;      // pinned
   hipStream_t copy_streams[kCopyStreams] = {};
   hipEvent_t ev_fwd_done = nullptr;
+  hipEvent_t ev_counts = nullptr;  // the token counts have reached h_counts
   bool fwd_recorded = false;
   std::vector<hipEvent_t> ev_copied;  // [wave][copy stream]
   std::vector<hipEvent_t> ev_wave_done;
@@ -421,6 +423,7 @@ static void release(strata_moe* h) {
   for (auto e : h->ev_ahead)
     if (e) (void)hipEventDestroy(e);
   if (h->ev_fwd_done) (void)hipEventDestroy(h->ev_fwd_done);
+  if (h->ev_counts) (void)hipEventDestroy(h->ev_counts);
   for (auto cs : h->copy_streams)
     if (cs) (void)hipStreamDestroy(cs);
   void* dev[] = {h->d_pool, h->d_shared, h->d_router_w, h->d_router_bias, h->d_slot_ptr,
@@ -547,6 +550,7 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
 
   for (auto& cs : h->copy_streams) HIP_CHECK(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
   HIP_CHECK(hipEventCreateWithFlags(&h->ev_fwd_done, hipEventDisableTiming));
+  HIP_CHECK(hipEventCreateWithFlags(&h->ev_counts, hipEventDisableTiming));
   for (auto& e : h->ev_ahead) HIP_CHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
 
   // preload: experts 0..budget-1 in slots 0..budget-1, or the profile's
@@ -677,6 +681,18 @@ static void add_tiles(strata_moe* h, int expert, int slot, int row_begin, int co
   }
 }
 
+// Waits for `ev` on the host: polls for up to about 2 ms (the token counts
+// usually arrive within tens of microseconds, and a blocking wait adds its
+// own wake-up latency to every paged forward), then blocks.
+static hipError_t wait_spin(hipEvent_t ev) {
+  const auto t0 = std::chrono::steady_clock::now();
+  for (;;) {
+    const hipError_t e = hipEventQuery(ev);
+    if (e != hipErrorNotReady) return e;
+    if (std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(2000)) return hipEventSynchronize(ev);
+  }
+}
+
 // Copies `pages` from the pinned store into their slots on the copy streams
 // (round-robin), after `after` (the compute that last read those slots), and
 // marks them pending for the next forward.
@@ -734,7 +750,8 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
     h->rm.waves++;
   } else {
     HIP_CHECK(hipMemcpyAsync(h->h_counts, h->d_counts, size_t(h->E) * 4, hipMemcpyDeviceToHost, s));
-    HIP_CHECK(hipStreamSynchronize(s));
+    HIP_CHECK(hipEventRecord(h->ev_counts, s));
+    HIP_CHECK(wait_spin(h->ev_counts));
     std::vector<int32_t> needed;
     std::vector<int32_t> off(h->E + 1, 0);
     for (int e = 0; e < h->E; ++e) {
