@@ -17,6 +17,10 @@ timed region starts.  Prints one JSON line.
       turns two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
       WRITE_SIZE) into profiles/traffic_<workload>.json, which later runs use
       for the roofline's `traffic` while the kernel source is unchanged.
+  python bench.py --counter-summary DIR [DIR ...]
+      median per dispatch of every counter in rocprofv3 --pmc runs of this
+      script, for the prefill gate+up kernel in the all-resident region
+      (markdown table).
 """
 from __future__ import annotations
 
@@ -57,6 +61,7 @@ def parse():
     ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--trace-summary", metavar="TRACE_DIR")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR")
     return ap.parse_args()
 
 
@@ -102,23 +107,46 @@ def trace_summary(trace_dir):
     print("\n".join(parts))
 
 
+def region_rows(d, counter):
+    """Counter rows of one --pmc run, in dispatch order, and the slice of them
+    between the third and fourth region markers (the all-resident events-timed
+    steps)."""
+    f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    assert f, f"no counter_collection.csv under {d}"
+    rows = [r for r in csv.DictReader(open(f[0])) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    marks = [i for i, r in enumerate(rows) if "scan" in r["Kernel_Name"].lower()]
+    assert len(marks) >= 4, "expected the four region markers of the events-timed passes"
+    return rows, rows[marks[2] + 1:marks[3]]
+
+
+def is_gate_up_prefill(name):
+    return "moe_prefill_kernel" in name and ", true>" in name
+
+
+def counter_summary(dirs):
+    out = ["| counter | median per dispatch | dispatches |", "|---|---|---|"]
+    for d in dirs:
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        assert f, f"no counter_collection.csv under {d}"
+        names = sorted({r["Counter_Name"] for r in csv.DictReader(open(f[0]))})
+        for c in names:
+            _, region = region_rows(d, c)
+            v = [float(r["Counter_Value"]) for r in region if is_gate_up_prefill(r["Kernel_Name"])]
+            out.append(f"| {c} | {statistics.median(v):,.0f} | {len(v)} |")
+    print("\n".join(out))
+
+
 def pmc_summary(fetch_dir, write_dir, workload):
     """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the prefill gate+up
     kernel, each scaled by what the counter reads for the calibration copy
     (CALIB_BYTES read and written by one copy kernel in the same process)."""
     def read(d, counter):
-        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
-        assert f, f"no counter_collection.csv under {d}"
-        rows = [r for r in csv.DictReader(open(f[0])) if r["Counter_Name"] == counter]
-        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        rows, region = region_rows(d, counter)
         per = {}
         for r in rows:
             per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        marks = [i for i, r in enumerate(rows) if "scan" in r["Kernel_Name"].lower()]
-        assert len(marks) >= 4, "expected the four region markers of the events-timed passes"
-        region = rows[marks[2] + 1:marks[3]]          # the all-resident events-timed steps
-        up = [float(r["Counter_Value"]) for r in region
-              if "moe_prefill_kernel" in r["Kernel_Name"] and ", true>" in r["Kernel_Name"]]
+        up = [float(r["Counter_Value"]) for r in region if is_gate_up_prefill(r["Kernel_Name"])]
         return per, up
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -164,6 +192,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.cpu_baseline_only:
         from synth import CONFIGS, make_layer
