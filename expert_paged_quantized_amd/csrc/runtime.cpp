@@ -97,7 +97,7 @@ struct strata_moe {
   size_t slot_stride = 0;
   size_t max_rows = 0, max_tiles = 0;
 
-  uint8_t* host_store = nullptr;  // pinned, E * lay.bytes
+  uint8_t* host_store = nullptr;  // pinned, E records at slot_stride
   uint8_t* d_pool = nullptr;      // budget * slot_stride
   uint8_t* d_shared = nullptr;    // slot_stride
   uint16_t* d_router_w = nullptr;
@@ -490,14 +490,16 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   // pinned host store, prepacked in parallel over experts
   strata_status st;
   const size_t rec = h->lay.bytes;
-  if ((st = host_alloc(&h->host_store, rec * h->E))) return st;
+  // records sit at the slot stride (256-byte aligned) in the pinned store too,
+  // so every page is an aligned copy
+  if ((st = host_alloc(&h->host_store, h->slot_stride * h->E))) return st;
   {
     unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
     std::vector<std::thread> th;
     for (unsigned t = 0; t < nth; ++t)
       th.emplace_back([&, t]() {
         for (int e = t; e < h->E; e += nth)
-          pack_expert(h->host_store + rec * e, h->lay, d->gate, d->up, d->down, e, h->H, h->F, fi);
+          pack_expert(h->host_store + h->slot_stride * e, h->lay, d->gate, d->up, d->down, e, h->H, h->F, fi);
       });
     for (auto& t : th) t.join();
   }
@@ -561,7 +563,7 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
     h->rm.load_profile(d->expert_profile, false, pages);
   }
   for (int s = 0; s < h->budget; ++s)
-    HIP_CHECK(hipMemcpy(h->h_slot_ptr[s], h->host_store + rec * h->rm.expert_in(s), rec,
+    HIP_CHECK(hipMemcpy(h->h_slot_ptr[s], h->host_store + h->slot_stride * h->rm.expert_in(s), rec,
                         hipMemcpyHostToDevice));
   HIP_CHECK(hipDeviceSynchronize());
   return STRATA_OK;
@@ -710,7 +712,7 @@ static hipError_t page_ahead(strata_moe* h, const std::vector<PlanEntry>& pages,
         if (i != c && h->ahead_used[i]) e = hipStreamWaitEvent(cs, h->ev_ahead[i], 0);
       if (e != hipSuccess) return e;
     }
-    hipError_t e = hipMemcpyAsync(h->h_slot_ptr[p.slot], h->host_store + rec * p.expert, rec,
+    hipError_t e = hipMemcpyAsync(h->h_slot_ptr[p.slot], h->host_store + h->slot_stride * p.expert, rec,
                                   hipMemcpyHostToDevice, cs);
     if (e != hipSuccess) return e;
     c = (c + 1) % kCopyStreams;
@@ -819,28 +821,29 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
     // keeps the previous wave's slots: then pages overlap a wave's compute).
     const size_t rec = h->lay.bytes;
     const int lag = h->rm.wave_lag();
+    int rr = 0;  // the round-robin runs on across waves: small waves still spread
     for (int w = 0; w < nw; ++w) {
       const bool any_paged = pe[w] > he[w];
-      int used = 0;
+      bool used[kCopyStreams] = {};
       if (any_paged) {
-        int c = 0;
         for (const PlanEntry& p : plan[w]) {
           if (!p.paged) continue;
           if (fault("h2d")) return fail(STRATA_E_HIP, "hipMemcpyAsync H2D failed (injected fault)");
-          if (c == used) {
+          const int c = rr++ % kCopyStreams;
+          if (!used[c]) {
             if (w >= lag) HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_wave_done[w - lag], 0));
-            ++used;
+            used[c] = true;
           }
-          HIP_CHECK(hipMemcpyAsync(h->h_slot_ptr[p.slot], h->host_store + rec * p.expert, rec,
+          HIP_CHECK(hipMemcpyAsync(h->h_slot_ptr[p.slot], h->host_store + h->slot_stride * p.expert, rec,
                                    hipMemcpyHostToDevice, h->copy_streams[c]));
-          c = (c + 1) % kCopyStreams;
         }
-        for (int i = 0; i < used; ++i)
-          HIP_CHECK(hipEventRecord(h->ev_copied[w * kCopyStreams + i], h->copy_streams[i]));
+        for (int i = 0; i < kCopyStreams; ++i)
+          if (used[i]) HIP_CHECK(hipEventRecord(h->ev_copied[w * kCopyStreams + i], h->copy_streams[i]));
       }
       HIP_CHECK(run_experts(h, x, h->d_tiles_host + hb[w], nullptr, he[w] - hb[w], decode, T, s));
       if (any_paged) {
-        for (int i = 0; i < used; ++i) HIP_CHECK(hipStreamWaitEvent(s, h->ev_copied[w * kCopyStreams + i], 0));
+        for (int i = 0; i < kCopyStreams; ++i)
+          if (used[i]) HIP_CHECK(hipStreamWaitEvent(s, h->ev_copied[w * kCopyStreams + i], 0));
         HIP_CHECK(run_experts(h, x, h->d_tiles_host + he[w], nullptr, pe[w] - he[w], decode, T, s));
       }
       HIP_CHECK(hipEventRecord(h->ev_wave_done[w], s));
@@ -980,7 +983,7 @@ strata_status strata_moe_memory(const strata_moe* h, strata_memory_info* out) {
                 uint64_t(sizeof(uint8_t*)) * (h->budget + 1);
   out->workspace = h->ws_bytes;
   out->device_total = out->slot_pool + out->shared + out->router + out->workspace;
-  out->host_store = uint64_t(h->lay.bytes) * h->E;
+  out->host_store = uint64_t(h->slot_stride) * h->E;
   return STRATA_OK;
 }
 

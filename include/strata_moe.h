@@ -226,7 +226,8 @@ typedef struct {
   uint64_t router;      /* router weights and bias                              */
   uint64_t workspace;   /* activations, routing buffers, outputs for max_tokens */
   uint64_t device_total;
-  uint64_t host_store;  /* pinned host bytes of the routed expert store         */
+  uint64_t host_store;  /* pinned host bytes of the routed expert store: E
+                         * records, each at the 256-byte aligned slot stride */
 } strata_memory_info;
 
 strata_status strata_moe_memory(const strata_moe* h, strata_memory_info* out);

@@ -262,7 +262,8 @@ def test_device_memory_holds_no_widened_copy(torch_cuda):
     stride = (eb + 255) // 256 * 256
     assert m["slot_pool"] == cfg.budget * stride
     assert m["shared"] == stride
-    assert m["host_store"] == cfg.num_experts * eb     # prepack keeps the byte count
+    # prepack keeps the byte count; records sit at the 256-byte slot stride
+    assert m["host_store"] == cfg.num_experts * stride and stride - eb < 256
     assert m["device_total"] == m["slot_pool"] + m["shared"] + m["router"] + m["workspace"]
     widened = cfg.num_experts * 3 * cfg.hidden * cfg.ffn * 2
     assert m["device_total"] < widened / 2
