@@ -177,14 +177,18 @@ def flops_down(cfg, rows):
 
 
 def w1_bytes(cfg):
-    """Packed gate+up bytes of one expert."""
-    H, F = cfg.hidden, cfg.ffn
-    per = (H * F // 2 + 4 * F * (H // 64)) if cfg.quant == "int4_g64" else (H * F // 2 + F * (H // 32))
-    return 2 * per
+    """Packed gate+up bytes of one expert (codes, scales and biases; NVFP4
+    matrix scales)."""
+    H, F, G = cfg.hidden, cfg.ffn, cfg.group
+    per = H * F // 2 + (4 * F * (H // G) if cfg.quant.startswith("int4") else F * (H // G))
+    return 2 * per + (8 if cfg.quant == "nvfp4_g16" else 0)
 
 
-def w2_bytes(cfg):
-    return cfg.expert_bytes() - w1_bytes(cfg)
+def gate_up_bytes(cfg, distinct, rows):
+    """Algorithmic HBM bytes of one gate+up launch: the packed gate+up weights
+    of every expert it runs once (routed distinct + shared), each routed row's
+    activations once (16-bit), h written once (16-bit)."""
+    return (distinct + cfg.num_shared) * w1_bytes(cfg) + rows * cfg.hidden * 2 + rows * cfg.ffn * 2
 
 
 def main():
@@ -289,11 +293,22 @@ def main():
     ach = up_fl / (up_ms * 1e-3) / 1e12
     pg_ms, pg_n = tm["prefill_gate_up"]
     ach_pg = up_fl / (pg_ms * 1e-3) / 1e12
+    # arithmetic intensity of the launch against the ridge of the two peaks
+    _, dbg_p = resident.forward(xs_p[W], y=y_p, dbg=True)
+    distinct = int((dbg_p["counts"] > 0).sum().item())
+    gu_bytes = gate_up_bytes(cfg, distinct, rows)
+    ai = flops_gate_up(cfg, rows) / gu_bytes
+    ridge = peak * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    attainable = min(1.0, ai / ridge)
     roof = {"bound": "mfma", "kernel": "moe_prefill_kernel (gate+up, SwiGLU epilogue), one launch per "
                                        "prefill over all its experts (all-resident region)",
             "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
             "traffic": None, "launches": int(up_n), "avg_launch_us": round(up_ms / max(up_n, 1) * 1e3, 2),
             "algorithmic_flops_per_launch": flops_gate_up(cfg, rows),
+            "algorithmic_bytes_per_launch": gu_bytes, "distinct_experts": distinct,
+            "arithmetic_intensity": round(ai, 1), "ridge": round(ridge, 1),
+            "attainable_frac": round(attainable, 4), "frac_of_attainable": round(ach / peak / attainable, 4),
+            "hbm_GBps_on_algorithmic_bytes": round(gu_bytes / (up_ms / max(up_n, 1) * 1e-3) / 1e9, 1),
             "paged_region": {"launches": int(pg_n), "avg_launch_us": round(pg_ms / max(pg_n, 1) * 1e3, 2),
                              "achieved": round(ach_pg, 2), "frac": round(ach_pg / peak, 4),
                              "note": "the same kernel once per wave of the paged steps (same FLOPs in all)"}}
@@ -302,6 +317,7 @@ def main():
         tr = json.load(open(tp))
         if tr.get("kernel_source_sha256_16") == kernel_source_hash():
             roof["traffic"] = tr["traffic_bytes_per_launch"]
+            roof["traffic_over_algorithmic"] = round(tr["traffic_bytes_per_launch"] / gu_bytes, 3)
             roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
 
     # decode kernels: all-resident layer; cold = 1 GiB streamed (read) between
