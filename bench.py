@@ -58,7 +58,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=15)
     ap.add_argument("--workload", default="qwen3_30b_a3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--cpu-steps", type=int, default=6)
     ap.add_argument("--no-policies", action="store_true", help="skip the paged decode policy runs")
     ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
