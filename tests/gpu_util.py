@@ -45,3 +45,29 @@ def assert_routing_equal(dbg, ref, T, E, k, what=""):
     assert np.array_equal(dbg["perm"].cpu().numpy(), ref["perm"]), f"{what}: perm"
     dw = np.abs(dbg["w"].cpu().numpy().astype(np.float64) - ref["w"]).max()
     assert dw <= W_ABS, f"{what}: routing weights off by {dw}"
+
+
+def check_sampled(lw, layer, x, sample, what):
+    """One forward at any size: sampled logits bitwise, all routing against
+    the oracle's selection / grouping of the GPU logits, sampled y against
+    the oracle forward of those tokens.  Returns y."""
+    import torch
+    cfg = lw.cfg
+    T = x.shape[0]
+    y, dbg = layer.forward(to_dev(x), dbg=True)
+    torch.cuda.synchronize()
+    lg = dbg["logits"].cpu().numpy()
+    ref_l = om.router_logits_fp32(x[sample], lw.router_w, lw.router_bias)
+    assert np.array_equal(lg[sample].view(np.uint32), ref_l.view(np.uint32)), f"{what}: sampled logits"
+    idx = om.select_topk(lg, cfg.top_k)
+    assert np.array_equal(dbg["idx"].cpu().numpy(), idx), f"{what}: idx"
+    w = om.routing_weights(lg, idx, cfg.router)
+    assert np.abs(dbg["w"].cpu().numpy() - w).max() <= W_ABS, f"{what}: w"
+    counts, offsets, perm, pos = om.permute(idx, cfg.num_experts)
+    assert np.array_equal(dbg["counts"].cpu().numpy(), counts), f"{what}: counts"
+    assert np.array_equal(dbg["offsets"].cpu().numpy(), offsets), f"{what}: offsets"
+    assert np.array_equal(dbg["perm"].cpu().numpy(), perm), f"{what}: perm"
+    ref = om.moe_forward(lw, x, tokens=sample)
+    assert np.array_equal(ref["idx"], idx[sample])
+    assert_y_close(y_to_f64(y)[sample], ref["y"], what)
+    return y

@@ -15,32 +15,9 @@ import pytest
 from oracle import moe as om
 from synth import CONFIG_ORDER, CONFIGS, FORMAT_ORDER, WIDE_ORDER, make_layer, make_tokens
 
-from gpu_util import W_ABS, assert_y_close, to_dev, y_bits, y_to_f64
+from gpu_util import check_sampled as _check, to_dev, y_bits
 
 pytestmark = pytest.mark.gpu
-
-
-def _check(lw, layer, x, sample, what):
-    import torch
-    cfg = lw.cfg
-    T = x.shape[0]
-    y, dbg = layer.forward(to_dev(x), dbg=True)
-    torch.cuda.synchronize()
-    lg = dbg["logits"].cpu().numpy()
-    ref_l = om.router_logits_fp32(x[sample], lw.router_w, lw.router_bias)
-    assert np.array_equal(lg[sample].view(np.uint32), ref_l.view(np.uint32)), f"{what}: sampled logits"
-    idx = om.select_topk(lg, cfg.top_k)
-    assert np.array_equal(dbg["idx"].cpu().numpy(), idx), f"{what}: idx"
-    w = om.routing_weights(lg, idx, cfg.router)
-    assert np.abs(dbg["w"].cpu().numpy() - w).max() <= W_ABS, f"{what}: w"
-    counts, offsets, perm, pos = om.permute(idx, cfg.num_experts)
-    assert np.array_equal(dbg["counts"].cpu().numpy(), counts), f"{what}: counts"
-    assert np.array_equal(dbg["offsets"].cpu().numpy(), offsets), f"{what}: offsets"
-    assert np.array_equal(dbg["perm"].cpu().numpy(), perm), f"{what}: perm"
-    ref = om.moe_forward(lw, x, tokens=sample)
-    assert np.array_equal(ref["idx"], idx[sample])
-    assert_y_close(y_to_f64(y)[sample], ref["y"], what)
-    return y
 
 
 @pytest.mark.parametrize("name", CONFIG_ORDER + WIDE_ORDER + FORMAT_ORDER)
