@@ -642,7 +642,7 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------
 // Prefill kernel: persistent workgroups of 4 waves, two per CU.  A work item is
 // (tile of up to 128 token rows of one expert, block of 8 weight row-tiles =
-// 256 outputs).  Wave w owns row tiles 2w, 2w+1 of the block (64 outputs) and
+// 256 outputs, range of K when the down GEMM splits K).  Wave w owns row tiles 2w, 2w+1 of the block (64 outputs) and
 // all of the tile's tokens (NCT column tiles of 32, a template parameter so the
 // K loop has no branches).  Per K-block of 64 inputs the workgroup stages
 // the activation tile in LDS (two buffers, rows padded to 144 bytes) while
@@ -663,13 +663,15 @@ constexpr int kPreRowTilesPerItem = 8;
 constexpr int kRowU32 = 36;
 
 template <int QF, bool GATE_UP, int NCT, int WD>
-__device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, int nb,
+__device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, int nb, int ks,
                                              uint32_t (*lds)[kPrefillTM * kRowU32]) {
   using SL = ScaleLayout<QF>;
   constexpr int RTW = kPreRowTilesPerWave;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nrt = p.N >> 5;
-  const int KB = p.K >> 6;
+  // this item's K range: k-blocks [kb0, kb0 + KB) (the whole K unless split)
+  const int KB = (p.K >> 6) / p.ksplit;
+  const int kb0 = ks * KB;
   // staging: 8 consecutive lanes read one 128-byte activation row, so each
   // load instruction covers 32 whole rows; chunk sc of rows q*32 + sr0, only
   // for the NCT*32 rows the tile uses
@@ -683,7 +685,7 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
     const int r = q * 32 + sr0;
     const int srow = (r < t.nrows) ? r : 0;
     const int64_t gr = p.gather ? p.gather[t.row_begin + srow] : (t.row_begin + srow);
-    s_src[q] = reinterpret_cast<const uint16_t*>(p.act) + gr * p.K + sc * 8;
+    s_src[q] = reinterpret_cast<const uint16_t*>(p.act) + gr * p.K + kb0 * 64 + sc * 8;
   }
 
   const uint8_t* rec = p.slot_ptr[t.slot];
@@ -692,8 +694,11 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
 #pragma unroll
   for (int r = 0; r < RTW; ++r) {
     const int rtl = min(rt0 + r, nrt - 1);
-    codes[r] = rec + p.off_codes + (int64_t)rtl * KB * kTileCodeBytes + lane * 16;
-    scs[r] = rec + p.off_scales + (int64_t)rtl * (KB >> p.sshift) * SL::kTileBytes + SL::lane_off(lane);
+    const int kbt = p.K >> 6;  // k-blocks per row tile in the record
+    codes[r] = rec + p.off_codes + ((int64_t)rtl * kbt + kb0) * kTileCodeBytes + lane * 16;
+    // kb0 is a multiple of the scale block (1 << sshift k-blocks)
+    scs[r] = rec + p.off_scales + ((int64_t)rtl * (kbt >> p.sshift) + (kb0 >> p.sshift)) * SL::kTileBytes +
+             SL::lane_off(lane);
   }
 
   f32x16 acc[RTW][NCT];
@@ -816,7 +821,7 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
           *reinterpret_cast<uint2*>(h + g4 * 8 + (lane >> 5) * 4) = pk;
         }
       } else {
-        float* o = reinterpret_cast<float*>(p.out) + row * p.out_ld + rt * 32;
+        float* o = reinterpret_cast<float*>(p.out) + ks * p.split_stride + row * p.out_ld + rt * 32;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const float4 v = {acc[r][ct][g4 * 4 + 0] * gs.x, acc[r][ct][g4 * 4 + 1] * gs.x,
@@ -834,16 +839,18 @@ __global__ __launch_bounds__(kPreThreads, 2) void moe_prefill_kernel(GemmArgs p)
   const int nrt = p.N >> 5;
   const int n_nb = (nrt + kPreRowTilesPerItem - 1) / kPreRowTilesPerItem;
   const int n_tiles = p.n_tiles_dev ? p.n_tiles_dev[0] : p.n_tiles;
-  const int n_items = n_tiles * n_nb;
+  const int per_tile = n_nb * p.ksplit;
+  const int n_items = n_tiles * per_tile;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const Tile t = p.tiles[item / n_nb];
-    const int nb = item % n_nb;
+    const Tile t = p.tiles[item / per_tile];
+    const int rem = item % per_tile;
+    const int nb = rem / p.ksplit, ks = rem % p.ksplit;
     switch ((t.nrows + 31) >> 5) {
       // (NVFP4 decodes need a few more registers: a shorter weight ring)
-      case 1: prefill_item<QF, GATE_UP, 1, (QF == Q_NVFP4 ? 2 : 4)>(p, t, nb, lds); break;
-      case 2: prefill_item<QF, GATE_UP, 2, (QF == Q_NVFP4 ? 2 : 4)>(p, t, nb, lds); break;
-      case 3: prefill_item<QF, GATE_UP, 3, 2>(p, t, nb, lds); break;
-      default: prefill_item<QF, GATE_UP, 4, 2>(p, t, nb, lds); break;
+      case 1: prefill_item<QF, GATE_UP, 1, (QF == Q_NVFP4 ? 2 : 4)>(p, t, nb, ks, lds); break;
+      case 2: prefill_item<QF, GATE_UP, 2, (QF == Q_NVFP4 ? 2 : 4)>(p, t, nb, ks, lds); break;
+      case 3: prefill_item<QF, GATE_UP, 3, 2>(p, t, nb, ks, lds); break;
+      default: prefill_item<QF, GATE_UP, 4, 2>(p, t, nb, ks, lds); break;
     }
     __syncthreads();
   }
@@ -851,25 +858,41 @@ __global__ __launch_bounds__(kPreThreads, 2) void moe_prefill_kernel(GemmArgs p)
 
 // ---------------------------------------------------------------------------
 // Combine: y[t] = sum_j w[t,j] * o[pos[t,j]] (j ascending) + o[shared row of t],
-// fp32, rounded to bf16 (nearest-even).  One workgroup per token.
+// fp32, rounded to bf16 (nearest-even).  One workgroup per token.  With a
+// K-split prefill down GEMM each o row is the sum of its partial planes, in
+// plane order, before it is weighted.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float4 o_row(const float* __restrict__ o, size_t at, int ksplit,
+                                        int64_t stride) {
+  float4 v = *reinterpret_cast<const float4*>(o + at);
+  for (int s = 1; s < ksplit; ++s) {
+    const float4 q = *reinterpret_cast<const float4*>(o + s * stride + at);
+    v.x += q.x;
+    v.y += q.y;
+    v.z += q.z;
+    v.w += q.w;
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o,
                                                       const int32_t* __restrict__ pos,
                                                       const float* __restrict__ w, int k, int H,
-                                                      int shared_row0, uint16_t* __restrict__ y) {
+                                                      int shared_row0, int ksplit, int64_t stride,
+                                                      uint16_t* __restrict__ y) {
   const int t = blockIdx.x;
   for (int c = threadIdx.x * 4; c < H; c += 1024) {
     float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int j = 0; j < k; ++j) {
       const float wj = w[(size_t)t * k + j];
-      const float4 v = *reinterpret_cast<const float4*>(o + (size_t)pos[(size_t)t * k + j] * H + c);
+      const float4 v = o_row(o, (size_t)pos[(size_t)t * k + j] * H + c, ksplit, stride);
       acc.x = __builtin_fmaf(wj, v.x, acc.x);
       acc.y = __builtin_fmaf(wj, v.y, acc.y);
       acc.z = __builtin_fmaf(wj, v.z, acc.z);
       acc.w = __builtin_fmaf(wj, v.w, acc.w);
     }
     if (shared_row0 >= 0) {
-      const float4 v = *reinterpret_cast<const float4*>(o + (size_t)(shared_row0 + t) * H + c);
+      const float4 v = o_row(o, (size_t)(shared_row0 + t) * H + c, ksplit, stride);
       acc.x += v.x;
       acc.y += v.y;
       acc.z += v.z;
@@ -1005,8 +1028,8 @@ hipError_t launch_expert_gemm(const GemmArgs& a, int quant, bool gate_up, bool d
 }
 
 hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, int T, int k, int H,
-                          int shared_row0, uint16_t* y, hipStream_t s) {
-  launch_k(combine_kernel, dim3(T), dim3(256), 0, s, o, pos, w, k, H, shared_row0, y);
+                          int shared_row0, int ksplit, int64_t stride, uint16_t* y, hipStream_t s) {
+  launch_k(combine_kernel, dim3(T), dim3(256), 0, s, o, pos, w, k, H, shared_row0, ksplit, stride, y);
   return hipGetLastError();
 }
 

@@ -78,6 +78,9 @@ struct GemmArgs {
   int32_t sshift;            // scale block of k-block kb: kb >> sshift
   int64_t off_gscale;        // NVFP4: record offset of this GEMM's fp32 matrix
                              // scales (gate, up: two floats; down: one)
+  int32_t ksplit;            // prefill down: K is cut into ksplit equal ranges,
+                             // range ks writes its partial sums to out + ks * split_stride
+  int64_t split_stride;      // floats between partial-sum planes
 };
 
 // Kernel timing: when the runtime times a single-kernel step it sets this

@@ -43,7 +43,7 @@ uint64_t read_probe_bytes(uint64_t bytes);
 hipError_t launch_read_probe(const void* p, uint64_t bytes, uint32_t* out, hipStream_t s);
 int decode_dot_waves(int N, int K, int quant, int tiles_per_token, int T);
 hipError_t launch_decode_dot(const GemmArgs& a, int quant, bool gate_up, int T, int S, int n_tiles, hipStream_t s);
-hipError_t launch_combine(const float*, const int32_t*, const float*, int, int, int, int,
+hipError_t launch_combine(const float*, const int32_t*, const float*, int, int, int, int, int, int64_t,
                           uint16_t*, hipStream_t);
 }  // namespace strata
 
@@ -92,6 +92,7 @@ constexpr int kCopyStreams = STRATA_COPY_STREAMS;
 struct strata_moe {
   int H = 0, F = 0, E = 0, k = 0, S = 0, quant = 0, router = 0, policy = 0, budget = 0;
   int sshift = 0;  // scale block of k-block kb is kb >> sshift (int4 group-128: 1)
+  int ksplit = 1;  // prefill down: partial-sum planes of o
   int max_tokens = 0, device = 0;
   RecordLayout lay{};
   size_t slot_stride = 0;
@@ -463,6 +464,8 @@ static strata_status host_alloc(T** p, size_t bytes) {
   return STRATA_OK;
 }
 
+static int prefill_ksplit(int K, int sshift);
+
 static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   h->H = d->hidden;
   h->F = d->ffn;
@@ -473,6 +476,7 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   (void)format_of(d->quant, fi);  // validated
   h->quant = fi.kq;
   h->sshift = fi.sshift;
+  h->ksplit = prefill_ksplit(h->F, h->sshift);
   h->router = d->router == STRATA_R_SOFTMAX_TOPK_RENORM ? R_SOFTMAX : R_SIGMOID;
   h->policy = d->policy;
   h->decay_shift = d->decay_shift;
@@ -541,7 +545,7 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
       (st = walloc(&h->d_hist, ((T + 63) / 64) * size_t(h->E) * 4)) || (st = walloc(&h->d_tiles_dev, h->max_tiles * sizeof(Tile))) ||
       (st = walloc(&h->d_tiles_host, h->max_tiles * sizeof(Tile))) || (st = walloc(&h->d_ntiles, 64)) ||
       (st = walloc(&h->d_distinct, 64)) || (st = walloc(&h->d_ticket, 64)) || (st = walloc(&h->d_h, h->max_rows * h->F * 2)) ||
-      (st = walloc(&h->d_o, h->max_rows * h->H * 4)))
+      (st = walloc(&h->d_o, h->max_rows * h->H * 4 * h->ksplit)))
     return st;
   if (fi.f16 && (st = walloc(&h->d_x16, T * h->H * 2))) return st;
   h->ws_bytes = ws;
@@ -630,7 +634,22 @@ static GemmArgs gemm_args(strata_moe* h, bool gate_up, const void* x, const Tile
   a.out_ld = gate_up ? h->F : h->H;
   a.sshift = h->sshift;
   a.off_gscale = h->quant == Q_NVFP4 ? h->lay.gscale + (gate_up ? 0 : 8) : -1;
+  a.ksplit = 1;
+  a.split_stride = 0;
   return a;
+}
+
+// Prefill down GEMMs with a long reduction (K = F of many k-blocks) split K
+// into equal ranges, each its own work item writing a partial-sum plane; the
+// combine adds the planes in order.  Long-K experts then give the GPU
+// several times more work items (a handful of experts with F = 14336 would
+// otherwise leave most CUs idle).  Depends on the layer shape only, so every
+// forward of a layer (paged or not) sums in the same order.
+static int prefill_ksplit(int K, int sshift) {
+  const int KB = K >> 6;
+  for (int s : {4, 2})
+    if (KB >= 48 * s && KB % (s << sshift) == 0) return s;
+  return 1;
 }
 
 // Persistent prefill grid: at most two workgroups per CU.
@@ -657,8 +676,13 @@ static hipError_t run_experts(strata_moe* h, const void* x, const Tile* tiles, c
     if (decode) {
       log2S = decode_log2_splits(a.N, a.K, h->k + h->S, T);
       grid = decode_grid(a.N, log2S, n_tiles);
-    } else
-      grid = prefill_grid(n_tiles * ((nrt + 7) / 8));
+    } else {
+      if (!gate_up) {
+        a.ksplit = h->ksplit;
+        a.split_stride = int64_t(h->max_rows) * h->H;
+      }
+      grid = prefill_grid(n_tiles * ((nrt + 7) / 8) * a.ksplit);
+    }
     const int cls = decode ? (gate_up ? STRATA_K_DEC_UP : STRATA_K_DEC_DOWN)
                            : (gate_up ? STRATA_K_PRE_UP : STRATA_K_PRE_DOWN);
     hipError_t e = timed(h, cls, s, [&]() { return launch_expert_gemm(a, h->quant, gate_up, decode, T, log2S, grid, s); });
@@ -853,7 +877,8 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
   }
 
   HIP_CHECK(timed(h, STRATA_K_COMBINE, s, [&]() {
-    return launch_combine(h->d_o, h->d_pos, h->d_w, T, h->k, h->H, h->S ? TK : -1, (uint16_t*)y, s);
+    return launch_combine(h->d_o, h->d_pos, h->d_w, T, h->k, h->H, h->S ? TK : -1, decode ? 1 : h->ksplit,
+                          int64_t(h->max_rows) * h->H, (uint16_t*)y, s);
   }));
 
   if (dbg) {

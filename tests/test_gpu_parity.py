@@ -35,6 +35,11 @@ SMALL = {
     "g128_s": (CONFIGS["e256_int4g128"].scaled(hidden=1024, ffn=256, num_experts=32, budget_frac=0.25),
                (1, 2, 6, 300)),
     "nvfp4_s": (CONFIGS["e256_nvfp4"].scaled(hidden=1024, ffn=256, num_experts=64), (1, 3, 8, 333)),
+    # a long down-projection reduction (F = 8192: the prefill down GEMM splits
+    # K in two partial-sum planes), int4 group-64 and group-128
+    "longk_s": (CONFIGS["mixtral"].scaled(hidden=512, ffn=8192), (1, 3, 257)),
+    "longk_g128_s": (CONFIGS["e256_int4g128"].scaled(hidden=512, ffn=8192, num_experts=8, top_k=2,
+                                                       budget_frac=0.5), (1, 200)),
 }
 
 
@@ -76,7 +81,8 @@ def test_layer_matches_oracle_all_resident(torch_cuda, name):
     layer.close()
 
 
-@pytest.mark.parametrize("name", ["qwen_s", "glm_s", "e512_s", "mixtral_s", "e896_s", "g128_s", "nvfp4_s"])
+@pytest.mark.parametrize("name", ["qwen_s", "glm_s", "e512_s", "mixtral_s", "e896_s", "g128_s", "nvfp4_s",
+                                  "longk_s", "longk_g128_s"])
 @pytest.mark.parametrize("policy", ["lru", "lfu"])
 def test_paged_output_is_bitwise_the_resident_output(torch_cuda, name, policy):
     """Budgeted (paged, waves) vs all-resident: identical y bits; counters equal
