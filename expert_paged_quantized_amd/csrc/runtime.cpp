@@ -12,8 +12,11 @@
 // combine.  With every expert resident the whole forward stays on the device.
 // With a smaller budget the per-expert counts come back to the host once, the
 // residency manager decides hits, misses and waves, misses are copied from the
-// pinned store into their slots on a side stream, and each wave runs its hit
-// experts while its misses are still in flight.
+// pinned store into their slots over four copy streams, each wave runs its
+// hit experts while its misses are still in flight, and a wave's pages wait
+// only for the compute of the wave that last read their slots.  After a
+// forward the policy may page experts ahead of need (prefetch); the next
+// forward waits for those pages.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
