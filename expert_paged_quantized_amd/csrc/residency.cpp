@@ -21,6 +21,7 @@ void ResidencyManager::init(int num_experts, int budget, int policy, int decay_s
   score_.assign(num_experts, 0);
   in_wave_.assign(num_experts, 0);
   keep_.assign(num_experts, 0);
+  wave_of_.assign(num_experts, -1);
   from_prefetch_.assign(num_experts, 0);
   for (int s = 0; s < budget; ++s) {
     slot_expert_[s] = s;
@@ -114,11 +115,14 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
     W = S >= 2 ? S / 2 : 1;
     prev_too = S >= 2;
   }
-  wave_lag_ = prev_too ? 2 : 1;
   size_t p0 = 0, p1 = 0;  // previous wave: order[p0, p1)
   for (size_t w0 = 0; w0 < order.size(); w0 += W) {
     const size_t w1 = (w0 + W < order.size()) ? w0 + W : order.size();
-    for (size_t i = w0; i < w1; ++i) in_wave_[order[i]] = 1;
+    const int32_t wi = (int32_t)plan.size();
+    for (size_t i = w0; i < w1; ++i) {
+      in_wave_[order[i]] = 1;
+      wave_of_[order[i]] = wi;
+    }
     if (prev_too)
       for (size_t i = p0; i < p1; ++i) in_wave_[order[i]] = 2;
     std::vector<PlanEntry> wave;
@@ -129,7 +133,7 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
         wave.push_back({e, expert_slot_[e], false});
         continue;
       }
-      int slot = -1;
+      int slot = -1, after = -1;
       for (int s = 0; s < budget_; ++s)
         if (slot_expert_[s] < 0) {
           slot = s;
@@ -143,13 +147,14 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
           if (victim < 0 || before(r, victim)) victim = r;
         }
         slot = expert_slot_[victim];
+        after = wave_of_[victim];
         expert_slot_[victim] = -1;
         from_prefetch_[victim] = 0;
         ++evictions;
       }
       slot_expert_[slot] = e;
       expert_slot_[e] = slot;
-      wave.push_back({e, slot, true});
+      wave.push_back({e, slot, true, after});
     }
     for (size_t i = p0; i < w1; ++i) in_wave_[order[i]] = 0;
     p0 = w0;
@@ -157,6 +162,7 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
     plan.push_back(std::move(wave));
   }
   for (int32_t e : pinned) keep_[e] = 0;
+  for (int32_t e : needed) wave_of_[e] = -1;
   if (decay_shift_ > 0)
     for (int e = 0; e < num_experts_; ++e) score_[e] -= score_[e] >> decay_shift_;
   for (int32_t e : needed) {

@@ -21,8 +21,8 @@
 //   * a miss takes the lowest free slot, else evicts, among residents outside
 //     the current wave, the previous wave (multi-wave, S >= 2) and the pinned
 //     set, the one with the smallest key: LRU (last_use, id), LFU and WARM
-//     (score, last_use, id); a wave's pages wait only for the compute of the
-//     wave that last read the slots (one or two waves back: wave_lag);
+//     (score, last_use, id); each page records the wave of this forward that
+//     last read its slot (after_wave), the only compute it has to wait for;
 //   * then (WARM only) every score loses score >> decay_shift, and every
 //     expert of N gains kUnit and gets last_use = forward number;
 //   * with prefetch P > 0, non-residents by decreasing rank (the key without
@@ -44,6 +44,8 @@ struct PlanEntry {
   int32_t expert;
   int32_t slot;
   bool paged;
+  int32_t after_wave = -1;  // a page's slot was last read by this wave of the
+                            // same forward (-1: by no wave of it)
 };
 
 class ResidencyManager {
@@ -59,9 +61,6 @@ class ResidencyManager {
   // `ahead` with the pages to make once the forward's compute is done.
   void forward(const std::vector<int32_t>& needed, std::vector<std::vector<PlanEntry>>& waves,
                std::vector<PlanEntry>& ahead);
-  // Waves back whose compute the pages of a wave must wait for (1 or 2),
-  // for the last forward.
-  int wave_lag() const { return wave_lag_; }
   // Sets the scores (E values, each <= kMaxScore; checked by the caller) and
   // rebalances; `count` books the pages as prefetches (run time) or not
   // (create).  Fills `pages` with the copies to make.
@@ -80,11 +79,12 @@ class ResidencyManager {
   bool rank_less(int a, int b) const;  // rank of a < rank of b (ids ignored)
   bool before(int a, int b) const;     // a is a better victim than b
   void page(int e, int slot, bool count, std::vector<PlanEntry>& pages);
-  int num_experts_ = 0, budget_ = 0, policy_ = kLRU, decay_shift_ = 0, prefetch_ = 0, wave_lag_ = 1;
+  int num_experts_ = 0, budget_ = 0, policy_ = kLRU, decay_shift_ = 0, prefetch_ = 0;
   uint64_t expert_bytes_ = 0, n_ = 0;
   std::vector<int32_t> slot_expert_, expert_slot_;
   std::vector<uint64_t> last_use_, score_;
   std::vector<uint8_t> in_wave_, keep_, from_prefetch_;
+  std::vector<int32_t> wave_of_;  // wave of the current forward that runs the expert, or -1
 };
 
 }  // namespace strata

@@ -843,26 +843,36 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
     }
     // A wave's misses are dealt round-robin over the copy streams, so the
     // per-copy setup of one record overlaps the transfer of another; each
-    // stream first waits for the compute of the wave that last read the slots
-    // it overwrites (the previous wave, or the one before it when the plan
-    // keeps the previous wave's slots: then pages overlap a wave's compute).
+    // stream first waits for the compute of the latest wave of this forward
+    // that read a slot it overwrites (never the current or the previous wave:
+    // pages overlap a wave's compute), and not at all when the evicted
+    // experts are not run by this forward.
     const size_t rec = h->lay.bytes;
-    const int lag = h->rm.wave_lag();
     int rr = 0;  // the round-robin runs on across waves: small waves still spread
     for (int w = 0; w < nw; ++w) {
       const bool any_paged = pe[w] > he[w];
       bool used[kCopyStreams] = {};
       if (any_paged) {
+        // streams for this wave's pages, and on each stream the latest wave
+        // of this forward that read one of the slots it overwrites
+        int dep[kCopyStreams];
+        std::fill(dep, dep + kCopyStreams, -1);
+        std::vector<int> stream_of;
+        for (const PlanEntry& p : plan[w]) {
+          if (!p.paged) continue;
+          const int c = rr++ % kCopyStreams;
+          stream_of.push_back(c);
+          used[c] = true;
+          dep[c] = std::max(dep[c], p.after_wave);
+        }
+        for (int c = 0; c < kCopyStreams; ++c)
+          if (dep[c] >= 0) HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_wave_done[dep[c]], 0));
+        size_t i = 0;
         for (const PlanEntry& p : plan[w]) {
           if (!p.paged) continue;
           if (fault("h2d")) return fail(STRATA_E_HIP, "hipMemcpyAsync H2D failed (injected fault)");
-          const int c = rr++ % kCopyStreams;
-          if (!used[c]) {
-            if (w >= lag) HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_wave_done[w - lag], 0));
-            used[c] = true;
-          }
           HIP_CHECK(hipMemcpyAsync(h->h_slot_ptr[p.slot], h->host_store + h->slot_stride * p.expert, rec,
-                                   hipMemcpyHostToDevice, h->copy_streams[c]));
+                                   hipMemcpyHostToDevice, h->copy_streams[stream_of[i++]]));
         }
         for (int i = 0; i < kCopyStreams; ++i)
           if (used[i]) HIP_CHECK(hipEventRecord(h->ev_copied[w * kCopyStreams + i], h->copy_streams[i]));
