@@ -443,7 +443,7 @@ static void release(strata_moe* h) {
 }
 
 template <class T>
-static strata_status dev_alloc(strata_moe* h, T** p, size_t bytes) {
+static strata_status dev_alloc(T** p, size_t bytes) {
   if (fault("devalloc")) return fail(STRATA_E_NOMEM, "hipMalloc failed (injected fault)");
   bytes = std::max<size_t>(bytes, 256);
   hipError_t e = hipMalloc((void**)p, bytes);
@@ -512,23 +512,23 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   }
 
   // device: slot pool, shared expert, router, slot pointer table
-  if ((st = dev_alloc(h, &h->d_pool, h->slot_stride * h->budget))) return st;
+  if ((st = dev_alloc(&h->d_pool, h->slot_stride * h->budget))) return st;
   if (h->S) {
-    if ((st = dev_alloc(h, &h->d_shared, h->slot_stride))) return st;
+    if ((st = dev_alloc(&h->d_shared, h->slot_stride))) return st;
     std::vector<uint8_t> tmp(rec);
     pack_expert(tmp.data(), h->lay, d->sh_gate, d->sh_up, d->sh_down, 0, h->H, h->F, fi);
     HIP_CHECK(hipMemcpy(h->d_shared, tmp.data(), rec, hipMemcpyHostToDevice));
   }
-  if ((st = dev_alloc(h, &h->d_router_w, size_t(h->E) * h->H * 2))) return st;
+  if ((st = dev_alloc(&h->d_router_w, size_t(h->E) * h->H * 2))) return st;
   HIP_CHECK(hipMemcpy(h->d_router_w, d->router_w, size_t(h->E) * h->H * 2, hipMemcpyHostToDevice));
   if (d->router_bias) {
-    if ((st = dev_alloc(h, &h->d_router_bias, size_t(h->E) * 4))) return st;
+    if ((st = dev_alloc(&h->d_router_bias, size_t(h->E) * 4))) return st;
     HIP_CHECK(hipMemcpy(h->d_router_bias, d->router_bias, size_t(h->E) * 4, hipMemcpyHostToDevice));
   }
   h->h_slot_ptr.resize(h->budget + 1);
   for (int s = 0; s < h->budget; ++s) h->h_slot_ptr[s] = h->d_pool + h->slot_stride * s;
   h->h_slot_ptr[h->budget] = h->d_shared ? h->d_shared : h->d_pool;
-  if ((st = dev_alloc(h, &h->d_slot_ptr, sizeof(uint8_t*) * (h->budget + 1)))) return st;
+  if ((st = dev_alloc(&h->d_slot_ptr, sizeof(uint8_t*) * (h->budget + 1)))) return st;
   HIP_CHECK(hipMemcpy(h->d_slot_ptr, h->h_slot_ptr.data(), sizeof(uint8_t*) * (h->budget + 1),
                       hipMemcpyHostToDevice));
 
@@ -539,7 +539,7 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   uint64_t ws = 0;
   auto walloc = [&](auto** p, size_t bytes) -> strata_status {
     ws += std::max<size_t>(bytes, 256);
-    return dev_alloc(h, p, bytes);
+    return dev_alloc(p, bytes);
   };
   if ((st = walloc(&h->d_logits, T * h->E * 4)) || (st = walloc(&h->d_idx, TK * 4)) ||
       (st = walloc(&h->d_w, TK * 4)) || (st = walloc(&h->d_counts, size_t(h->E) * 4)) ||
