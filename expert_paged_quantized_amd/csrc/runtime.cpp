@@ -853,26 +853,26 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
       const bool any_paged = pe[w] > he[w];
       bool used[kCopyStreams] = {};
       if (any_paged) {
-        // streams for this wave's pages, and on each stream the latest wave
-        // of this forward that read one of the slots it overwrites
-        int dep[kCopyStreams];
-        std::fill(dep, dep + kCopyStreams, -1);
-        std::vector<int> stream_of;
-        for (const PlanEntry& p : plan[w]) {
-          if (!p.paged) continue;
-          const int c = rr++ % kCopyStreams;
-          stream_of.push_back(c);
-          used[c] = true;
-          dep[c] = std::max(dep[c], p.after_wave);
-        }
-        for (int c = 0; c < kCopyStreams; ++c)
-          if (dep[c] >= 0) HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_wave_done[dep[c]], 0));
-        size_t i = 0;
-        for (const PlanEntry& p : plan[w]) {
-          if (!p.paged) continue;
+        // pages with no dependency first, then by the wave they wait for;
+        // dealt round-robin, each stream waits for a wave's compute only
+        // just before its first page that needs it
+        std::vector<const PlanEntry*> pages;
+        for (const PlanEntry& p : plan[w])
+          if (p.paged) pages.push_back(&p);
+        std::stable_sort(pages.begin(), pages.end(),
+                         [](const PlanEntry* a, const PlanEntry* b) { return a->after_wave < b->after_wave; });
+        int waited[kCopyStreams];
+        std::fill(waited, waited + kCopyStreams, -1);
+        for (const PlanEntry* p : pages) {
           if (fault("h2d")) return fail(STRATA_E_HIP, "hipMemcpyAsync H2D failed (injected fault)");
-          HIP_CHECK(hipMemcpyAsync(h->h_slot_ptr[p.slot], h->host_store + h->slot_stride * p.expert, rec,
-                                   hipMemcpyHostToDevice, h->copy_streams[stream_of[i++]]));
+          const int c = rr++ % kCopyStreams;
+          used[c] = true;
+          if (p->after_wave > waited[c]) {
+            HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_wave_done[p->after_wave], 0));
+            waited[c] = p->after_wave;
+          }
+          HIP_CHECK(hipMemcpyAsync(h->h_slot_ptr[p->slot], h->host_store + h->slot_stride * p->expert, rec,
+                                   hipMemcpyHostToDevice, h->copy_streams[c]));
         }
         for (int i = 0; i < kCopyStreams; ++i)
           if (used[i]) HIP_CHECK(hipEventRecord(h->ev_copied[w * kCopyStreams + i], h->copy_streams[i]));
