@@ -52,7 +52,7 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     # the HIP runtime's first ~10 paged steps hold multi-millisecond host stalls
     # inside hipMemcpyAsync (measured; they stop once it has warmed up)
     ap.add_argument("--warmup", type=int, default=15)
