@@ -1,7 +1,7 @@
 // Routing kernels of the MoE layer for gfx950: router logits in one fixed fp32
 // summation order, top-k selection with routing weights, and the grouping of
 // tokens by expert (counts, offsets, permutation, inverse positions, tile list)
-// in two multi-block passes.
+// in two multi-block passes that synchronise only at kernel boundaries.
 //
 // The routing semantics (top-k, softmax or sigmoid renormalised over the
 // selected experts) come from the checkpoint and are never altered (ro99/strata
@@ -422,23 +422,11 @@ __device__ __forceinline__ void emit_counts_and_tiles(int c, int o, int total, i
 }
 
 // Per 64-token block: histogram over experts and each entry's rank inside the
-// block, from 64-bit LDS masks (bit = token of the block).  The last block to
-// finish (an atomic ticket taken after a device-scope fence) turns the
-// histograms into per-block prefixes (entries of e in earlier blocks), writes
-// counts, offsets and the tile list, and resets the ticket.
+// block, from 64-bit LDS masks (bit = token of the block).
 __global__ __launch_bounds__(1024) void rank_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
-                                                    int S, int tile_rows, int shared_slot,
                                                     int32_t* __restrict__ rank_in_block,
-                                                    int32_t* __restrict__ hist,
-                                                    unsigned int* __restrict__ ticket,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    Tile* __restrict__ tiles,
-                                                    int32_t* __restrict__ n_tiles,
-                                                    unsigned long long* __restrict__ distinct_total) {
+                                                    int32_t* __restrict__ hist) {
   __shared__ unsigned long long mask[kPermMaxE];
-  __shared__ int wave_tot[16];
-  __shared__ int last;
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 1024) mask[e] = 0ull;
   __syncthreads();
@@ -452,60 +440,73 @@ __global__ __launch_bounds__(1024) void rank_kernel(const int32_t* __restrict__ 
     const unsigned long long below = (tl == 0) ? 0ull : (~0ull >> (64 - tl));
     rank_in_block[(size_t)tb * k + i] = __popcll(mask[idx[(size_t)tb * k + i]] & below);
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last = (atomicAdd(ticket, 1u) == gridDim.x - 1) ? 1 : 0;
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  // last block: per expert, exclusive prefix over blocks (in place); the
-  // permute pass adds the expert's offset
-  const int nb = gridDim.x;
-  int run = 0;
-  if (tid < E) {
-    for (int b0 = 0; b0 < nb; b0 += 8) {
-      int h[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) h[u] = (b0 + u < nb) ? hist[(size_t)(b0 + u) * E + tid] : 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (b0 + u < nb) hist[(size_t)(b0 + u) * E + tid] = run;
-        run += h[u];
-      }
-    }
-  }
-  int total;
-  const int o = block_scan1024(tid < E ? run : 0, wave_tot, total);
-  emit_counts_and_tiles(run, o, total, T, k, E, S, tile_rows, shared_slot, wave_tot, counts, offsets,
-                        tiles, n_tiles, distinct_total);
-  if (tid == 0) *ticket = 0u;
 }
 
 // ---------------------------------------------------------------------------
-// Permute (one 256-thread workgroup per block of 64 tokens): token t's entry
-// for expert e lands at offsets[e] + prefix[block][e] + rank inside the
-// block, i.e. tokens
-// ascending inside each expert segment; pos is the inverse map.  Shared-expert
-// rows are the identity after the routed rows.
+// Permute (one 1024-thread workgroup per block of 64 tokens).  Every workgroup
+// reads all per-block histograms (G = 1024 / E threads per expert, each
+// summing every G-th block) to get, per expert, its total and its entries in
+// earlier blocks; a scan of the totals gives the expert offsets.  Token t's
+// entry for expert e lands at offset[e] + entries of e in earlier blocks +
+// its rank inside the block, i.e. tokens ascending inside each expert
+// segment; pos is the inverse map.  Shared-expert rows are the identity after
+// the routed rows.  Workgroup 0 also writes counts, offsets and the tile list.
+// No workgroup waits for another: the histograms are complete when the pass
+// starts.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict__ idx,
-                                                      const int32_t* __restrict__ rank_in_block,
-                                                      const int32_t* __restrict__ prefix,
-                                                      const int32_t* __restrict__ offsets, int T, int k,
-                                                      int E, int S, int32_t* __restrict__ perm,
-                                                      int32_t* __restrict__ pos) {
-  const int tid = threadIdx.x, b = blockIdx.x;
+__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ idx,
+                                                       const int32_t* __restrict__ rank_in_block,
+                                                       const int32_t* __restrict__ hist, int T, int E,
+                                                       int k, int S, int tile_rows, int shared_slot,
+                                                       int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ perm,
+                                                       int32_t* __restrict__ pos, Tile* __restrict__ tiles,
+                                                       int32_t* __restrict__ n_tiles,
+                                                       unsigned long long* __restrict__ distinct_total) {
+  __shared__ int tot_s[kPermMaxE];
+  __shared__ int pre_s[kPermMaxE];
+  __shared__ int wave_tot[16];
+  const int tid = threadIdx.x, b = blockIdx.x, nb = gridDim.x;
+  for (int e = tid; e < E; e += 1024) tot_s[e] = pre_s[e] = 0;
+  __syncthreads();
+  const int G = 1024 / E;  // E <= kPermMaxE = 1024
+  if (tid < G * E) {
+    const int e = tid % E, g = tid / E;
+    int tot = 0, pre = 0;
+    int bb = g;
+    for (; bb + 3 * G < nb; bb += 4 * G) {
+      const int h0 = hist[(size_t)bb * E + e], h1 = hist[(size_t)(bb + G) * E + e];
+      const int h2 = hist[(size_t)(bb + 2 * G) * E + e], h3 = hist[(size_t)(bb + 3 * G) * E + e];
+      tot += h0 + h1 + h2 + h3;
+      pre += (bb < b ? h0 : 0) + (bb + G < b ? h1 : 0) + (bb + 2 * G < b ? h2 : 0) + (bb + 3 * G < b ? h3 : 0);
+    }
+    for (; bb < nb; bb += G) {
+      const int h = hist[(size_t)bb * E + e];
+      tot += h;
+      pre += bb < b ? h : 0;
+    }
+    atomicAdd(&tot_s[e], tot);
+    atomicAdd(&pre_s[e], pre);
+  }
+  __syncthreads();
+  const int c = tid < E ? tot_s[tid] : 0;
+  int total;
+  const int o = block_scan1024(c, wave_tot, total);
+  if (tid < E) pre_s[tid] += o;
+  __syncthreads();
   const int tb = b * kRouteBlock;
   const int n = min(kRouteBlock, T - tb) * k;
-  for (int i = tid; i < n; i += 256) {
+  for (int i = tid; i < n; i += 1024) {
     const size_t q = (size_t)tb * k + i;
-    const int e = idx[q];
-    const int p = offsets[e] + prefix[(size_t)b * E + e] + rank_in_block[q];
+    const int p = pre_s[idx[q]] + rank_in_block[q];
     perm[p] = tb + i / k;
     pos[q] = p;
   }
-  if (S)
-    for (int t = tb + tid; t < min(T, tb + kRouteBlock); t += 256) perm[T * k + t] = t;
+  if (S && tid < min(kRouteBlock, T - tb)) perm[T * k + tb + tid] = tb + tid;
+  if (b == 0)
+    emit_counts_and_tiles(c, o, total, T, k, E, S, tile_rows, shared_slot, wave_tot, counts, offsets,
+                          tiles, n_tiles, distinct_total);
 }
 
 // ---------------------------------------------------------------------------
@@ -579,7 +580,7 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
 template <int JPL>
 static void launch_route_jpl(const float* logits, int T, int E, int k, int router, int S, int tile_rows,
                              int shared_slot, int32_t* idx, float* w, int32_t* rank_in_block,
-                             int32_t* hist, unsigned int* ticket, int32_t* counts, int32_t* offsets,
+                             int32_t* hist, int32_t* counts, int32_t* offsets,
                              int32_t* perm, int32_t* pos, Tile* tiles, int32_t* n_tiles,
                              unsigned long long* distinct_total, hipStream_t s) {
   if (T <= kSmallT) {
@@ -590,19 +591,19 @@ static void launch_route_jpl(const float* logits, int T, int E, int k, int route
   }
   const int nblk = (T + kRouteBlock - 1) / kRouteBlock;
   topk_kernel<JPL><<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, router, idx, w);
-  rank_kernel<<<nblk, 1024, 0, s>>>(idx, T, E, k, S, tile_rows, shared_slot, rank_in_block, hist, ticket,
-                                    counts, offsets, tiles, n_tiles, distinct_total);
-  permute_kernel<<<nblk, 256, 0, s>>>(idx, rank_in_block, hist, offsets, T, k, E, S, perm, pos);
+  rank_kernel<<<nblk, 1024, 0, s>>>(idx, T, E, k, rank_in_block, hist);
+  permute_kernel<<<nblk, 1024, 0, s>>>(idx, rank_in_block, hist, T, E, k, S, tile_rows, shared_slot, counts,
+                                       offsets, perm, pos, tiles, n_tiles, distinct_total);
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int router, int S, int tile_rows,
                         int shared_slot, int32_t* idx, float* w, int32_t* rank_in_block, int32_t* hist,
-                        unsigned int* ticket, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* counts, int32_t* offsets, int32_t* perm,
                         int32_t* pos, Tile* tiles, int32_t* n_tiles, unsigned long long* distinct_total,
                         hipStream_t s) {
 #define STRATA_ROUTE(J)                                                                             \
   launch_route_jpl<J>(logits, T, E, k, router, S, tile_rows, shared_slot, idx, w, rank_in_block, hist, \
-                      ticket, counts, offsets, perm, pos, tiles, n_tiles, distinct_total, s)
+                      counts, offsets, perm, pos, tiles, n_tiles, distinct_total, s)
   if (E <= 64)
     STRATA_ROUTE(1);
   else if (E <= 128)

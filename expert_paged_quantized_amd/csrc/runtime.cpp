@@ -37,7 +37,7 @@ namespace strata {
 hipError_t launch_router(const uint16_t*, const uint16_t*, const float*, float*, uint16_t*, int, int,
                          int, hipStream_t);
 hipError_t launch_route(const float*, int, int, int, int, int, int, int, int32_t*, float*, int32_t*,
-                        int32_t*, unsigned int*, int32_t*, int32_t*, int32_t*, int32_t*, Tile*, int32_t*,
+                        int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, Tile*, int32_t*,
                         unsigned long long*, hipStream_t);
 hipError_t launch_expert_gemm(const GemmArgs&, int, bool, bool, int, int, int, hipStream_t);
 int decode_log2_splits(int N, int K, int tiles_per_token, int T);
@@ -121,7 +121,6 @@ struct strata_moe {
   Tile* d_tiles_dev = nullptr;
   Tile* d_tiles_host = nullptr;
   int32_t* d_ntiles = nullptr;
-  unsigned int* d_ticket = nullptr;  // completion ticket of the rank pass (reset by its last block)
   unsigned long long* d_distinct = nullptr;
   void* d_h = nullptr;
   float* d_o = nullptr;
@@ -433,7 +432,7 @@ static void release(strata_moe* h) {
   void* dev[] = {h->d_pool, h->d_shared, h->d_router_w, h->d_router_bias, h->d_slot_ptr,
                  h->d_logits, h->d_idx, h->d_w, h->d_counts, h->d_offsets, h->d_perm, h->d_pos,
                  h->d_tiles_dev, h->d_tiles_host, h->d_ntiles, h->d_distinct, h->d_h, h->d_o,
-                 h->d_x16, h->d_rank, h->d_hist, h->d_ticket};
+                 h->d_x16, h->d_rank, h->d_hist};
   for (void* p : dev)
     if (p) (void)hipFree(p);
   if (h->host_store) (void)hipHostFree(h->host_store);
@@ -547,13 +546,12 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
       (st = walloc(&h->d_pos, TK * 4)) || (st = walloc(&h->d_rank, TK * 4)) ||
       (st = walloc(&h->d_hist, ((T + 63) / 64) * size_t(h->E) * 4)) || (st = walloc(&h->d_tiles_dev, h->max_tiles * sizeof(Tile))) ||
       (st = walloc(&h->d_tiles_host, h->max_tiles * sizeof(Tile))) || (st = walloc(&h->d_ntiles, 64)) ||
-      (st = walloc(&h->d_distinct, 64)) || (st = walloc(&h->d_ticket, 64)) || (st = walloc(&h->d_h, h->max_rows * h->F * 2)) ||
+      (st = walloc(&h->d_distinct, 64)) || (st = walloc(&h->d_h, h->max_rows * h->F * 2)) ||
       (st = walloc(&h->d_o, h->max_rows * h->H * 4 * h->ksplit)))
     return st;
   if (fi.f16 && (st = walloc(&h->d_x16, T * h->H * 2))) return st;
   h->ws_bytes = ws;
   HIP_CHECK(hipMemset(h->d_distinct, 0, 64));
-  HIP_CHECK(hipMemset(h->d_ticket, 0, 64));
   if ((st = host_alloc(&h->h_counts, size_t(h->E) * 4))) return st;
   if ((st = host_alloc(&h->h_tiles, h->max_tiles * sizeof(Tile)))) return st;
 
@@ -767,7 +765,7 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
   const int tile_rows = decode ? (1 << 30) : kPrefillTM;
   HIP_CHECK(timed(h, STRATA_K_GROUP, s, [&]() {
     return launch_route(h->d_logits, T, h->E, h->k, h->router, h->S, tile_rows, h->budget, h->d_idx,
-                        h->d_w, h->d_rank, h->d_hist, h->d_ticket, h->d_counts, h->d_offsets,
+                        h->d_w, h->d_rank, h->d_hist, h->d_counts, h->d_offsets,
                         h->d_perm, h->d_pos, h->d_tiles_dev, h->d_ntiles, h->d_distinct, s);
   }));
 
