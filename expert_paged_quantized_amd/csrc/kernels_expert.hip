@@ -642,64 +642,132 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------
 // Prefill kernel: persistent workgroups of 4 waves, two per CU.  A work item is
 // (tile of up to 128 token rows of one expert, block of 8 weight row-tiles =
-// 256 outputs, range of K when the down GEMM splits K).  Wave w owns row tiles 2w, 2w+1 of the block (64 outputs) and
-// all of the tile's tokens (NCT column tiles of 32, a template parameter so the
-// K loop has no branches).  Per K-block of 64 inputs the workgroup stages
-// the activation tile in LDS (two buffers, rows padded to 144 bytes) while
-// each wave decodes its weight chunks straight from global memory into MFMA
-// operands.  Software pipeline: weights and activations are loaded two
-// K-blocks ahead into register rings; activations are written to the other
-// LDS buffer one K-block ahead.  Loads never branch: padding rows read a valid
-// row of the tile and row tiles past N re-read the last row tile; those
-// results are computed and not stored.
+// 256 outputs, range of K when the down GEMM splits K).  Wave w owns row tiles
+// 2w, 2w+1 of the block (64 outputs) and all of the tile's tokens (NCT column
+// tiles of 32, a template parameter so the K loop has no branches).
+//
+// Every global load is a 16- or 4-byte LDS-DMA load (global memory straight
+// into LDS, no registers) into a ring of kPreStages stages, issued two
+// K-blocks ahead: per K-block the tile's activations (shared by the four
+// waves) and each wave's own weight codes and scales.  The only vector-memory
+// operations in the K loop are those DMA loads, so the wait before a K-block
+// is a fixed count of them.  One barrier per K-block: after it the K-block's
+// stage is complete for all waves and the stage read in the previous K-block
+// is free for the next DMA.  Inside a K-block the B operands and decoded
+// weights of the next MFMA step are read and decoded while the current step's
+// MFMAs run.  Loads never branch: padding rows read a valid row of the tile,
+// row tiles past N re-read the last row tile and K-blocks past the end
+// re-read the last one; those results are not stored.
 // ---------------------------------------------------------------------------
 constexpr int kPreThreads = 256;
 constexpr int kPreRowTilesPerWave = 2;
 constexpr int kPreRowTilesPerItem = 8;
-// LDS row: 64 16-bit inputs (32 u32) padded to 36 u32 (144 B), so 16
-// consecutive rows start in 16 different 16-byte bank groups and both the
-// staging writes (one row per lane) and the MFMA operand reads (one row per
-// lane) are free of bank conflicts.
-constexpr int kRowU32 = 36;
+constexpr int kPreStages = 3;
+// Activation rows in LDS: 64 16-bit inputs = 128 bytes = 8 chunks of 16
+// bytes, unpadded.  Chunk c of row r sits in slot c ^ f(r),
+// f(r) = (r ^ (r >> 3)) & 7, so the 8 (or 16) consecutive rows that one
+// ds_read_b128 pass serves fall in distinct 16-byte bank groups whether the
+// LDS has 32 or 64 banks.
+constexpr int kRowBytes = 128;
+constexpr int kActBytes = kPrefillTM * kRowBytes;           // 16 KB
+constexpr int kWaveWBytes = 2 * kTileCodeBytes + 256;       // codes of 2 row tiles + their scales
+constexpr int kStageBytes = kActBytes + 4 * kWaveWBytes;    // 25 KB
 
-template <int QF, bool GATE_UP, int NCT, int WD>
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maximum)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+
+// a row tile's scale word for this lane, from the tile's scale bytes in LDS
+template <int QF>
+__device__ __forceinline__ uint32_t lds_scale(const uint8_t* tile, int lane) {
+  if constexpr (QF == Q_INT4)
+    return *reinterpret_cast<const uint32_t*>(tile + (lane & 31) * 4);
+  else if constexpr (QF == Q_NVFP4)
+    return *reinterpret_cast<const uint16_t*>(tile + lane * 2);
+  else
+    return tile[lane];
+}
+
+// LDS-DMA loads of 16 and 4 bytes per lane: lane l's bytes land at
+// lds + l * size (lds wave-uniform, in M0).  They are written as inline asm
+// (with a memory clobber, so no memory access moves across them) because the
+// compiler cannot tell a DMA into one stage from a read of another and would
+// wait for every DMA before each LDS read; the waits for these loads are the
+// explicit vmcnt waits of the K loop.  The asm has no register outputs.
+__device__ __forceinline__ void dma16(const void* g, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds);
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds);
+  asm volatile("global_load_lds_dword %0, off" : : "v"(g), "{m0}"(m0) : "memory");
+}
+
+template <int QF, bool GATE_UP, int NCT>
 __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, int nb, int ks,
-                                             uint32_t (*lds)[kPrefillTM * kRowU32]) {
+                                             uint8_t* lds0, uint8_t* lds1, uint8_t* lds2) {
+  auto stage = [&](auto stc) -> uint8_t* {
+    constexpr int ST = decltype(stc)::value;
+    if constexpr (ST == 0) return lds0;
+    else if constexpr (ST == 1) return lds1;
+    else return lds2;
+  };
   using SL = ScaleLayout<QF>;
   constexpr int RTW = kPreRowTilesPerWave;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int S = kPreStages;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nrt = p.N >> 5;
   // this item's K range: k-blocks [kb0, kb0 + KB) (the whole K unless split)
   const int KB = (p.K >> 6) / p.ksplit;
   const int kb0 = ks * KB;
-  // staging: 8 consecutive lanes read one 128-byte activation row, so each
-  // load instruction covers 32 whole rows; chunk sc of rows q*32 + sr0, only
-  // for the NCT*32 rows the tile uses
-  const int sc = threadIdx.x & 7, sr0 = threadIdx.x >> 3;
   const int rt0 = nb * kPreRowTilesPerItem + wave * RTW;
 
-  // staging sources: rows past the tile's end re-read its first row
-  const uint16_t* s_src[NCT];
+  // Activation DMA: load q of wave w fills rows 8j .. 8j+7 (j = 4q + w) of
+  // the stage, 1 KB: lane l writes slot l & 7 of row 8j + (l >> 3), which
+  // holds chunk (l & 7) ^ f(row) of that row.  Rows past the tile's end
+  // re-read the tile's first row.
+  const uint16_t* a_src[NCT];
 #pragma unroll
   for (int q = 0; q < NCT; ++q) {
-    const int r = q * 32 + sr0;
+    const int j = 4 * q + wave;
+    const int r = 8 * j + (lane >> 3);
+    const int chunk = (lane & 7) ^ (lane >> 3) ^ (j & 7);
     const int srow = (r < t.nrows) ? r : 0;
     const int64_t gr = p.gather ? p.gather[t.row_begin + srow] : (t.row_begin + srow);
-    s_src[q] = reinterpret_cast<const uint16_t*>(p.act) + gr * p.K + kb0 * 64 + sc * 8;
+    a_src[q] = reinterpret_cast<const uint16_t*>(p.act) + gr * p.K + kb0 * 64 + chunk * 8;
   }
-
+  // Weight DMA: row tile r's 1 KB code chunk (lane l: bytes 16l..16l+15) and
+  // one dword per lane of the two row tiles' scale bytes: int4 and NVFP4
+  // (128 bytes per tile) lanes 0-31 tile 0, 32-63 tile 1; MXFP4 (64 bytes)
+  // lanes 0-15 tile 0, 16-31 tile 1, 32-63 repeat 0-31.
   const uint8_t* rec = p.slot_ptr[t.slot];
-  const uint8_t* codes[RTW];
-  const uint8_t* scs[RTW];
+  const int kbt = p.K >> 6;  // k-blocks per row tile in the record
+  const uint8_t* c_src[RTW];
 #pragma unroll
   for (int r = 0; r < RTW; ++r) {
     const int rtl = min(rt0 + r, nrt - 1);
-    const int kbt = p.K >> 6;  // k-blocks per row tile in the record
-    codes[r] = rec + p.off_codes + ((int64_t)rtl * kbt + kb0) * kTileCodeBytes + lane * 16;
-    // kb0 is a multiple of the scale block (1 << sshift k-blocks)
-    scs[r] = rec + p.off_scales + ((int64_t)rtl * (kbt >> p.sshift) + (kb0 >> p.sshift)) * SL::kTileBytes +
-             SL::lane_off(lane);
+    c_src[r] = rec + p.off_codes + ((int64_t)rtl * kbt + kb0) * kTileCodeBytes + lane * 16;
   }
+  const uint8_t* sc_src;
+  {
+    constexpr int TB = SL::kTileBytes;  // 128 or 64
+    const int r = (TB == 128) ? (lane >> 5) : ((lane >> 4) & 1);
+    const int off = (TB == 128) ? (lane & 31) * 4 : (lane & 15) * 4;
+    const int rtl = min(rt0 + r, nrt - 1);
+    // kb0 is a multiple of the scale block (1 << sshift k-blocks)
+    sc_src = rec + p.off_scales + ((int64_t)rtl * (kbt >> p.sshift) + (kb0 >> p.sshift)) * TB + off;
+  }
+  // B-operand reads: lane reads row ct*32 + (lane & 31), chunk 4*(lane >> 5) + st
+  const int key = (lane & 7) ^ ((lane >> 3) & 3);
+  const int rd_base = (lane & 31) * kRowBytes;
+  const int rd_hi = (lane >> 5) ^ (key >> 2);
 
   f32x16 acc[RTW][NCT];
 #pragma unroll
@@ -709,91 +777,92 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-  u32x4 sv[2][NCT];        // activation chunks of two K-blocks in flight
-  u32x4 wq[WD][RTW];       // weight ring: K-block kb lives in slot kb % WD
-  uint32_t ws[WD][RTW];
-
-  auto stage_load = [&](u32x4(&v)[NCT], int kb) {
+  auto dma = [&](auto stc, int kb) {
+    uint8_t* st = stage(stc);
     kb = min(kb, KB - 1);
 #pragma unroll
-    for (int q = 0; q < NCT; ++q) v[q] = ld16(s_src[q] + kb * 64);
-  };
-  auto stage_store = [&](const u32x4(&v)[NCT], int buf) {
+    for (int q = 0; q < NCT; ++q) dma16(a_src[q] + kb * 64, st + (4 * q + wave) * 8 * kRowBytes);
+    uint8_t* wst = st + kActBytes + wave * kWaveWBytes;
 #pragma unroll
-    for (int q = 0; q < NCT; ++q)
-      *reinterpret_cast<u32x4*>(&lds[buf][(q * 32 + sr0) * kRowU32 + sc * 4]) = v[q];
+    for (int r = 0; r < RTW; ++r) dma16(c_src[r] + (int64_t)kb * kTileCodeBytes, wst + r * kTileCodeBytes);
+    dma4(sc_src + (int64_t)(kb >> p.sshift) * SL::kTileBytes, wst + RTW * kTileCodeBytes);
   };
-  auto w_load = [&](u32x4(&q4)[RTW], uint32_t(&s4)[RTW], int kb) {
-    kb = min(kb, KB - 1);
-#pragma unroll
-    for (int r = 0; r < RTW; ++r) {
-      q4[r] = ld16(codes[r] + (int64_t)kb * kTileCodeBytes);
-      s4[r] = SL::load(scs[r] + (int64_t)(kb >> p.sshift) * SL::kTileBytes);
-    }
-  };
-  auto compute = [&](int buf, const u32x4(&q4)[RTW], const uint32_t(&s4)[RTW]) {
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int c = 4 * (lane >> 5) + st;
-      u32x4 b[NCT];
+  // One K-block from stage ST; `issue` (the DMA of a later K-block) runs
+  // once the first LDS reads are in flight.
+  auto compute = [&](auto stc, auto&& issue) {
+    const uint8_t* st = stage(stc);
+    const uint8_t* wst = st + kActBytes + wave * kWaveWBytes;
+    auto read_b = [&](int stp, u32x4(&b)[NCT]) {
+      const int slot_lo = (stp ^ key) & 3;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const int mrow = ct * 32 + (lane & 31);
-        b[ct] = *reinterpret_cast<const u32x4*>(&lds[buf][mrow * kRowU32 + c * 4]);
+        const int slot = slot_lo | ((rd_hi ^ (ct & 1)) << 2);
+        b[ct] = *reinterpret_cast<const u32x4*>(st + ct * 32 * kRowBytes + rd_base + slot * 16);
       }
-#pragma unroll
-      for (int r = 0; r < RTW; ++r) {
-        const u32x4 a = ChunkScale<QF>(s4[r]).step(q4[r][st], st);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) acc[r][ct] = mfma<QF>(a, b[ct], acc[r][ct]);
-      }
-    }
-  };
-  // One K-block: store activation kb+1 into the other LDS buffer, load
-  // activation kb+3 into the freed registers and weights kb+WD into the freed
-  // ring slot, compute K-block kb.  D = kb % WD and the buffer parity are
-  // compile-time, so every register index is static.
-  auto one_step = [&](int kb, auto dc) {
-    constexpr int D = decltype(dc)::value;
-    constexpr int BUF = D & 1;
-    stage_store(sv[BUF ^ 1], BUF ^ 1);
-    stage_load(sv[BUF ^ 1], kb + 3);
+    };
     u32x4 q4[RTW];
     uint32_t s4[RTW];
 #pragma unroll
     for (int r = 0; r < RTW; ++r) {
-      q4[r] = wq[D][r];
-      s4[r] = ws[D][r];
+      q4[r] = *reinterpret_cast<const u32x4*>(wst + r * kTileCodeBytes + lane * 16);
+      s4[r] = lds_scale<QF>(wst + RTW * kTileCodeBytes + r * SL::kTileBytes, lane);
     }
-    w_load(wq[D], ws[D], kb + WD);
-    compute(BUF, q4, s4);
-    __syncthreads();
+    u32x4 b0[NCT];
+    read_b(0, b0);
+    issue();
+    u32x4 a[RTW];
+#pragma unroll
+    for (int r = 0; r < RTW; ++r) a[r] = ChunkScale<QF>(s4[r]).step(q4[r][0], 0);
+#pragma unroll
+    for (int stp = 0; stp < 4; ++stp) {
+      u32x4 b[NCT];
+      if (stp == 0) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) b[ct] = b0[ct];
+      } else {
+        read_b(stp, b);
+      }
+      u32x4 an[RTW];
+      if (stp < 3) {
+#pragma unroll
+        for (int r = 0; r < RTW; ++r) an[r] = ChunkScale<QF>(s4[r]).step(q4[r][stp + 1], stp + 1);
+      }
+#pragma unroll
+      for (int r = 0; r < RTW; ++r)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[r][ct] = mfma<QF>(a[r], b[ct], acc[r][ct]);
+      if (stp < 3) {
+#pragma unroll
+        for (int r = 0; r < RTW; ++r) a[r] = an[r];
+      }
+    }
+  };
+  // Step kb: wait for this wave's DMA of K-block kb (the NCT + 3 loads of
+  // K-block kb + 1 may still be in flight), barrier (every wave's DMA of kb
+  // is in LDS; every wave is done with stage kb - 1), compute K-block kb,
+  // issuing the DMA of K-block kb + 2 into stage kb - 1 after its first reads.
+  constexpr int kPerStep = NCT + RTW + 1;
+  auto one_step = [&](int kb, auto uc) {
+    constexpr int U = decltype(uc)::value;  // kb % S
+    wait_vm<kPerStep>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    compute(std::integral_constant<int, U>{}, [&] { dma(std::integral_constant<int, (U + 2) % S>{}, kb + 2); });
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue: activation 0 in LDS, activations 1 and 2 and weights 0..WD-1 in flight
-  stage_load(sv[0], 0);
-  stage_load(sv[1], 1);
-#pragma unroll
-  for (int d = 0; d < WD; ++d) w_load(wq[d], ws[d], d);
-  stage_store(sv[0], 0);
-  stage_load(sv[0], 2);
-  __syncthreads();
-
+  dma(std::integral_constant<int, 0>{}, 0);
+  dma(std::integral_constant<int, 1>{}, 1);
   int kb = 0;
-  for (; kb + WD <= KB; kb += WD) {
+  for (; kb + S <= KB; kb += S) {
     one_step(kb + 0, std::integral_constant<int, 0>{});
     one_step(kb + 1, std::integral_constant<int, 1>{});
-    if constexpr (WD == 4) {
-      one_step(kb + 2, std::integral_constant<int, 2>{});
-      one_step(kb + 3, std::integral_constant<int, 3>{});
-    }
+    one_step(kb + 2, std::integral_constant<int, 2>{});
   }
-  // tail (KB not a multiple of WD): slots 0.. hold K-blocks kb..
   if (kb + 0 < KB) one_step(kb + 0, std::integral_constant<int, 0>{});
   if (kb + 1 < KB) one_step(kb + 1, std::integral_constant<int, 1>{});
-  if constexpr (WD == 4) {
-    if (kb + 2 < KB) one_step(kb + 2, std::integral_constant<int, 2>{});
-  }
+  // no DMA may still be writing LDS when the next item starts
+  wait_vm<0>();
 
   // epilogue (NVFP4: times the fp32 matrix scales)
   const float2 gs = matrix_scales<QF>(p, rec);
@@ -835,7 +904,9 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
 
 template <int QF, bool GATE_UP>
 __global__ __launch_bounds__(kPreThreads, 2) void moe_prefill_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint32_t lds[2][kPrefillTM * kRowU32];
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[kStageBytes];
   const int nrt = p.N >> 5;
   const int n_nb = (nrt + kPreRowTilesPerItem - 1) / kPreRowTilesPerItem;
   const int n_tiles = p.n_tiles_dev ? p.n_tiles_dev[0] : p.n_tiles;
@@ -846,11 +917,10 @@ __global__ __launch_bounds__(kPreThreads, 2) void moe_prefill_kernel(GemmArgs p)
     const int rem = item % per_tile;
     const int nb = rem / p.ksplit, ks = rem % p.ksplit;
     switch ((t.nrows + 31) >> 5) {
-      // (NVFP4 decodes need a few more registers: a shorter weight ring)
-      case 1: prefill_item<QF, GATE_UP, 1, (QF == Q_NVFP4 ? 2 : 4)>(p, t, nb, ks, lds); break;
-      case 2: prefill_item<QF, GATE_UP, 2, (QF == Q_NVFP4 ? 2 : 4)>(p, t, nb, ks, lds); break;
-      case 3: prefill_item<QF, GATE_UP, 3, 2>(p, t, nb, ks, lds); break;
-      default: prefill_item<QF, GATE_UP, 4, 2>(p, t, nb, ks, lds); break;
+      case 1: prefill_item<QF, GATE_UP, 1>(p, t, nb, ks, lds0, lds1, lds2); break;
+      case 2: prefill_item<QF, GATE_UP, 2>(p, t, nb, ks, lds0, lds1, lds2); break;
+      case 3: prefill_item<QF, GATE_UP, 3>(p, t, nb, ks, lds0, lds1, lds2); break;
+      default: prefill_item<QF, GATE_UP, 4>(p, t, nb, ks, lds0, lds1, lds2); break;
     }
     __syncthreads();
   }
