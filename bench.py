@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     # the HIP runtime's first ~10 paged steps hold multi-millisecond host stalls
     # inside hipMemcpyAsync (measured; they stop once it has warmed up)
-    ap.add_argument("--warmup", type=int, default=15)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="qwen3_30b_a3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=6)

@@ -417,7 +417,7 @@ __device__ __forceinline__ void emit_counts_and_tiles(int c, int o, int total, i
   if (e == 0) {
     offsets[E] = total;
     n_tiles[0] = ntot + nsh;
-    distinct_total[0] += (unsigned long long)nd_tot;
+    atomicAdd(distinct_total, (unsigned long long)nd_tot);  // no return value: nothing waits for it
   }
 }
 
