@@ -19,6 +19,7 @@ _QUANT = {"int4_g64": _capi.Q_INT4_G64, "mxfp4_g32": _capi.Q_MXFP4_G32,
           "int4_g128": _capi.Q_INT4_G128, "nvfp4_g16": _capi.Q_NVFP4_G16}
 _ROUTER = {"softmax": _capi.R_SOFTMAX, "sigmoid": _capi.R_SIGMOID}
 _POLICY = {"lru": _capi.P_LRU, "lfu": _capi.P_LFU, "warm": _capi.P_WARM}
+_PAGER = {"auto": _capi.PAGER_AUTO, "kernel": _capi.PAGER_KERNEL, "dma": _capi.PAGER_DMA}
 
 
 def _ptr(a):
@@ -45,7 +46,8 @@ class MoELayer:
 
     def __init__(self, *, hidden, ffn, num_experts, top_k, num_shared, quant, router, budget,
                  max_tokens, router_w, router_bias, gate, up, down, sh_gate=None, sh_up=None,
-                 sh_down=None, policy="lru", decay_shift=0, prefetch=0, profile=None, device=-1):
+                 sh_down=None, policy="lru", decay_shift=0, prefetch=0, profile=None, device=-1,
+                 pager="auto"):
         self.hidden, self.ffn, self.num_experts, self.top_k = hidden, ffn, num_experts, top_k
         self.num_shared, self.max_tokens = num_shared, max_tokens
         keep = []
@@ -59,6 +61,7 @@ class MoELayer:
         d.policy = _POLICY[policy] if isinstance(policy, str) else policy
         d.expert_budget, d.max_tokens, d.device = budget, max_tokens, device
         d.decay_shift, d.prefetch = decay_shift, prefetch
+        d.pager = _PAGER[pager] if isinstance(pager, str) else pager
         if profile is not None:
             prof = _profile_array(profile, num_experts)
             keep.append(prof)
@@ -72,7 +75,7 @@ class MoELayer:
 
     @classmethod
     def from_weights(cls, lw, budget=None, policy="lru", max_tokens=None, device=-1, decay_shift=0,
-                     prefetch=0, profile=None):
+                     prefetch=0, profile=None, pager="auto"):
         """Builds a layer from a weights object with .cfg and the packed arrays."""
         c = lw.cfg
         return cls(hidden=c.hidden, ffn=c.ffn, num_experts=c.num_experts, top_k=c.top_k,
@@ -82,7 +85,7 @@ class MoELayer:
                    router_w=lw.router_w, router_bias=lw.router_bias, gate=lw.gate, up=lw.up,
                    down=lw.down, sh_gate=lw.sh_gate, sh_up=lw.sh_up, sh_down=lw.sh_down,
                    policy=policy, decay_shift=decay_shift, prefetch=prefetch, profile=profile,
-                   device=device)
+                   device=device, pager=pager)
 
     # ------------------------------------------------------------------
     def forward(self, x, y=None, stream=None, dbg=False):

@@ -13,6 +13,7 @@ STATUS_NAMES = ["OK", "E_INVALID", "E_UNSUPPORTED", "E_BAD_SCALE", "E_NOMEM", "E
 Q_INT4_G64, Q_MXFP4_G32, Q_INT4_G128, Q_NVFP4_G16 = 1, 2, 3, 4
 R_SOFTMAX, R_SIGMOID = 1, 2
 P_LRU, P_LFU, P_WARM = 1, 2, 3
+PAGER_AUTO, PAGER_KERNEL, PAGER_DMA = 0, 1, 2
 KERNEL_CLASSES = ["router", "group", "decode_gate_up", "decode_down", "prefill_gate_up",
                   "prefill_down", "combine"]
 
@@ -25,7 +26,7 @@ class Desc(ctypes.Structure):
     _fields_ = [("hidden", c_i32), ("ffn", c_i32), ("num_experts", c_i32), ("top_k", c_i32),
                 ("num_shared", c_i32), ("quant", c_i32), ("router", c_i32), ("policy", c_i32),
                 ("expert_budget", c_i32), ("max_tokens", c_i32), ("device", c_i32),
-                ("decay_shift", c_i32), ("prefetch", c_i32), ("expert_profile", c_vp),
+                ("decay_shift", c_i32), ("prefetch", c_i32), ("pager", c_i32), ("expert_profile", c_vp),
                 ("router_w", c_vp), ("router_bias", c_vp),
                 ("gate", QMat), ("up", QMat), ("down", QMat),
                 ("sh_gate", QMat), ("sh_up", QMat), ("sh_down", QMat)]
@@ -41,10 +42,10 @@ class CacheStats(ctypes.Structure):
                 ("bytes_h2d", c_u64), ("waves", c_u64), ("budget", c_i32), ("resident", c_i32),
                 ("policy", c_i32), ("decay_shift", c_i32), ("resident_bytes", c_u64),
                 ("expert_bytes", c_u64), ("prefetched", c_u64), ("prefetch_hits", c_u64),
-                ("prefetch", c_i32), ("reserved", c_i32)]
+                ("prefetch", c_i32), ("pager", c_i32)]
 
     def as_dict(self):
-        return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
+        return {k: getattr(self, k) for k, _ in self._fields_}
 
 
 class MemoryInfo(ctypes.Structure):

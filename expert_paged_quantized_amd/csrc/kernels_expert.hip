@@ -927,6 +927,52 @@ __global__ __launch_bounds__(kPreThreads, 2) void moe_prefill_kernel(GemmArgs p)
 }
 
 // ---------------------------------------------------------------------------
+// Page-in: copies whole records (b.stride bytes each) from the pinned host
+// store, read through its device mapping, into device slots.  The work is cut
+// into 4 KB chunks (a workgroup's 256 lanes x 16 bytes); each of 64
+// workgroups keeps four chunks of loads in flight (1 MB in all), which runs
+// the host link at its full rate.  The kernel stays at 28 VGPRs so that one
+// of its waves fits on a SIMD beside two prefill waves (2 x 232 or 2 x 240 of
+// 512): with eight chunks in flight it needed 52, and the CUs it ran on then
+// held one prefill workgroup instead of two, which delayed part of the
+// persistent prefill grid (2-4% longer paged steps on the larger layers).
+// Host reads are non-temporal.
+// ---------------------------------------------------------------------------
+constexpr int kPageThreads = 256;
+constexpr int kPageUnroll = 4;
+constexpr int kPageGrid = 64;
+
+__global__ __launch_bounds__(kPageThreads) void page_in_kernel(PageBatch b) {
+  const int per_rec = (int)((b.stride + 4095) >> 12);  // chunks per record
+  const int total = per_rec * b.n;
+  for (int c0 = blockIdx.x * kPageUnroll; c0 < total; c0 += gridDim.x * kPageUnroll) {
+    u32x4 v[kPageUnroll];
+#pragma unroll
+    for (int u = 0; u < kPageUnroll; ++u) {
+      const int c = c0 + u;
+      const int r = c / per_rec;
+      const int64_t off = (int64_t)(c - r * per_rec) * 4096 + threadIdx.x * 16;
+      if (c < total && off < b.stride) v[u] = ld16_nt(b.src + (int64_t)b.expert[r] * b.stride + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kPageUnroll; ++u) {
+      const int c = c0 + u;
+      const int r = c / per_rec;
+      const int64_t off = (int64_t)(c - r * per_rec) * 4096 + threadIdx.x * 16;
+      if (c < total && off < b.stride) *reinterpret_cast<u32x4*>(b.slot_ptr[b.slot[r]] + off) = v[u];
+    }
+  }
+}
+
+hipError_t launch_page_in(const PageBatch& b, hipStream_t s) {
+  if (b.n <= 0) return hipSuccess;
+  const int per_rec = (int)((b.stride + 4095) >> 12);
+  const int grid = std::min(kPageGrid, (per_rec * b.n + kPageUnroll - 1) / kPageUnroll);
+  page_in_kernel<<<grid, kPageThreads, 0, s>>>(b);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Combine: y[t] = sum_j w[t,j] * o[pos[t,j]] (j ascending) + o[shared row of t],
 // fp32, rounded to bf16 (nearest-even).  One workgroup per token.  With a
 // K-split prefill down GEMM each o row is the sum of its partial planes, in

@@ -83,6 +83,19 @@ struct GemmArgs {
   int64_t split_stride;      // floats between partial-sum planes
 };
 
+// Expert records paged from the pinned host store into device slots by the
+// page-in kernel, which reads the store through its device mapping: one
+// launch per group of pages instead of one DMA-engine copy per page.
+constexpr int kPageJobs = 96;
+struct PageBatch {
+  const uint8_t* src;        // device address of the pinned host store
+  int64_t stride;            // bytes between records, in the store and in the slot pool (multiple of 256)
+  uint8_t* const* slot_ptr;  // device array: slot -> record base
+  int32_t n;                 // pages in this batch (1 .. kPageJobs)
+  int32_t expert[kPageJobs];
+  int32_t slot[kPageJobs];
+};
+
 // Kernel timing: when the runtime times a single-kernel step it sets this
 // per-thread pair, and that kernel is launched with the events attached to the
 // dispatch itself (hipExtLaunchKernel), which timestamps the kernel's own

@@ -40,6 +40,7 @@ hipError_t launch_route(const float*, int, int, int, int, int, int, int, int32_t
                         int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, Tile*, int32_t*,
                         unsigned long long*, hipStream_t);
 hipError_t launch_expert_gemm(const GemmArgs&, int, bool, bool, int, int, int, hipStream_t);
+hipError_t launch_page_in(const PageBatch&, hipStream_t);
 int decode_log2_splits(int N, int K, int tiles_per_token, int T);
 int decode_grid(int N, int log2S, int n_tiles);
 uint64_t read_probe_bytes(uint64_t bytes);
@@ -102,6 +103,7 @@ struct strata_moe {
   size_t max_rows = 0, max_tiles = 0;
 
   uint8_t* host_store = nullptr;  // pinned, E records at slot_stride
+  const uint8_t* host_dev = nullptr;  // the same store's device address (read by the page-in kernel)
   uint8_t* d_pool = nullptr;      // budget * slot_stride
   uint8_t* d_shared = nullptr;    // slot_stride
   uint16_t* d_router_w = nullptr;
@@ -143,6 +145,7 @@ struct strata_moe {
 
   ResidencyManager rm;
   int decay_shift = 0, prefetch = 0;
+  int pager = STRATA_PAGER_KERNEL;  // the paging engine in use
   uint64_t forwards = 0;
   bool poisoned = false;
 
@@ -218,6 +221,8 @@ static strata_status validate(const strata_moe_desc* d) {
   if (!format_of(d->quant, fi)) return fail(STRATA_E_INVALID, "unknown quant");
   if (d->router != STRATA_R_SOFTMAX_TOPK_RENORM && d->router != STRATA_R_SIGMOID_TOPK_RENORM)
     return fail(STRATA_E_INVALID, "unknown router");
+  if (d->pager != STRATA_PAGER_AUTO && d->pager != STRATA_PAGER_KERNEL && d->pager != STRATA_PAGER_DMA)
+    return fail(STRATA_E_INVALID, "unknown pager");
   if (strata_status st = check_residency(d->num_experts, d->expert_budget, d->policy, d->decay_shift,
                                          d->prefetch, d->expert_profile))
     return st;
@@ -487,6 +492,9 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   h->max_tokens = d->max_tokens;
   h->lay = RecordLayout::make(h->H, h->F, h->quant, h->sshift);
   h->slot_stride = (size_t(h->lay.bytes) + 255) & ~size_t(255);
+  // paging engine: the kernel for records up to 8 MiB, the DMA engines above
+  h->pager = d->pager != STRATA_PAGER_AUTO ? d->pager
+                                          : (h->slot_stride <= (size_t(8) << 20) ? STRATA_PAGER_KERNEL : STRATA_PAGER_DMA);
 
   int dev = d->device;
   if (dev < 0) HIP_CHECK(hipGetDevice(&dev));
@@ -499,6 +507,11 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   // records sit at the slot stride (256-byte aligned) in the pinned store too,
   // so every page is an aligned copy
   if ((st = host_alloc(&h->host_store, h->slot_stride * h->E))) return st;
+  {
+    void* dp = nullptr;
+    HIP_CHECK(hipHostGetDevicePointer(&dp, h->host_store, 0));
+    h->host_dev = static_cast<const uint8_t*>(dp);
+  }
   {
     unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
     std::vector<std::thread> th;
@@ -839,38 +852,65 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
       }
       h->ahead_pending = false;
     }
-    // A wave's misses are dealt round-robin over the copy streams, so the
-    // per-copy setup of one record overlaps the transfer of another; each
-    // stream first waits for the compute of the latest wave of this forward
-    // that read a slot it overwrites (never the current or the previous wave:
-    // pages overlap a wave's compute), and not at all when the evicted
-    // experts are not run by this forward.
-    const size_t rec = h->lay.bytes;
-    int rr = 0;  // the round-robin runs on across waves: small waves still spread
+    // A wave's misses go out first the pages that overwrite slots no compute
+    // of this forward still reads, then per wave whose compute must finish
+    // first (the latest wave of this forward that read a slot being
+    // overwritten; never the current or the previous wave: pages overlap a
+    // wave's compute).  Page-in kernel: one launch per group of pages that
+    // wait for the same wave, groups round-robin over the copy streams, so a
+    // group that waits does not hold back the next.  DMA engines: one copy
+    // per record, round-robin over the copy streams.
+    int rr = 0;  // the round-robin runs on across waves
     for (int w = 0; w < nw; ++w) {
       const bool any_paged = pe[w] > he[w];
       bool used[kCopyStreams] = {};
       if (any_paged) {
-        // pages with no dependency first, then by the wave they wait for;
-        // dealt round-robin, each stream waits for a wave's compute only
-        // just before its first page that needs it
         std::vector<const PlanEntry*> pages;
         for (const PlanEntry& p : plan[w])
           if (p.paged) pages.push_back(&p);
         std::stable_sort(pages.begin(), pages.end(),
                          [](const PlanEntry* a, const PlanEntry* b) { return a->after_wave < b->after_wave; });
-        int waited[kCopyStreams];
-        std::fill(waited, waited + kCopyStreams, -1);
-        for (const PlanEntry* p : pages) {
-          if (fault("h2d")) return fail(STRATA_E_HIP, "hipMemcpyAsync H2D failed (injected fault)");
-          const int c = rr++ % kCopyStreams;
-          used[c] = true;
-          if (p->after_wave > waited[c]) {
-            HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_wave_done[p->after_wave], 0));
-            waited[c] = p->after_wave;
+        if (h->pager == STRATA_PAGER_KERNEL) {
+          for (size_t g0 = 0; g0 < pages.size();) {
+            size_t g1 = g0;
+            while (g1 < pages.size() && pages[g1]->after_wave == pages[g0]->after_wave &&
+                   int(g1 - g0) < kPageJobs)
+              ++g1;
+            if (fault("h2d")) return fail(STRATA_E_HIP, "page-in launch failed (injected fault)");
+            const int c = rr++ % kCopyStreams;
+            used[c] = true;
+            if (pages[g0]->after_wave >= 0)
+              HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_wave_done[pages[g0]->after_wave], 0));
+            PageBatch b;
+            b.src = h->host_dev;
+            b.stride = int64_t(h->slot_stride);
+            b.slot_ptr = h->d_slot_ptr;
+            b.n = int(g1 - g0);
+            for (size_t i = g0; i < g1; ++i) {
+              b.expert[i - g0] = pages[i]->expert;
+              b.slot[i - g0] = pages[i]->slot;
+            }
+            HIP_CHECK(launch_page_in(b, h->copy_streams[c]));
+            g0 = g1;
           }
-          HIP_CHECK(hipMemcpyAsync(h->h_slot_ptr[p->slot], h->host_store + h->slot_stride * p->expert, rec,
-                                   hipMemcpyHostToDevice, h->copy_streams[c]));
+        } else {
+          // one copy per record, dealt round-robin over the copy streams (so
+          // one record's setup overlaps another's transfer); each stream waits
+          // for a wave's compute just before its first page that needs it
+          const size_t rec = h->lay.bytes;
+          int waited[kCopyStreams];
+          std::fill(waited, waited + kCopyStreams, -1);
+          for (const PlanEntry* p : pages) {
+            if (fault("h2d")) return fail(STRATA_E_HIP, "hipMemcpyAsync H2D failed (injected fault)");
+            const int c = rr++ % kCopyStreams;
+            used[c] = true;
+            if (p->after_wave > waited[c]) {
+              HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_wave_done[p->after_wave], 0));
+              waited[c] = p->after_wave;
+            }
+            HIP_CHECK(hipMemcpyAsync(h->h_slot_ptr[p->slot], h->host_store + h->slot_stride * p->expert, rec,
+                                     hipMemcpyHostToDevice, h->copy_streams[c]));
+          }
         }
         for (int i = 0; i < kCopyStreams; ++i)
           if (used[i]) HIP_CHECK(hipEventRecord(h->ev_copied[w * kCopyStreams + i], h->copy_streams[i]));
@@ -981,6 +1021,7 @@ strata_status strata_expert_cache_stats(const strata_moe* h, strata_cache_stats*
   out->prefetched = h->rm.prefetched;
   out->prefetch_hits = h->rm.prefetch_hits;
   out->prefetch = h->prefetch;
+  out->pager = h->pager;
   return STRATA_OK;
 }
 
@@ -1181,6 +1222,7 @@ strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32
   out->prefetched = rm.prefetched;
   out->prefetch_hits = rm.prefetch_hits;
   out->prefetch = prefetch;
+  out->pager = 0;
   if (scores_out) std::copy(rm.scores().begin(), rm.scores().end(), scores_out);
   return STRATA_OK;
 }

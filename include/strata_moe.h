@@ -98,6 +98,21 @@ typedef enum {
                      * per forward (the cache's adaptation rate) */
 } strata_policy;
 
+/* How missing experts travel from the pinned host store into HBM slots.
+ * KERNEL: the library's page-in kernel reads the store through its device
+ * mapping (64 small workgroups beside the expert kernels).  DMA: one
+ * hipMemcpyAsync per record on the copy streams (the DMA engines; no CU
+ * time, but the HIP runtime held the host 5-15 ms inside single copy calls
+ * now and then on layers with small records).  AUTO: KERNEL for records of
+ * at most 8 MiB, DMA above (measured: equal mean on small records without the
+ * stalls, 1-3% slower than DMA on records of 9 MB and more).  Only the paging
+ * engine differs; y is the same. */
+typedef enum {
+  STRATA_PAGER_AUTO = 0,
+  STRATA_PAGER_KERNEL = 1,
+  STRATA_PAGER_DMA = 2
+} strata_pager;
+
 /* One stacked packed matrix, host pointers, row-major [out, in] per expert and
  * quantised along `in`.  Element 2i of a row is the low nibble of byte i.
  *   codes  : u8   [n_exp, out, in/2]
@@ -130,6 +145,7 @@ typedef struct {
                           * (non-residents that outrank a resident under the
                           * policy's order, hottest first, into the coldest
                           * residents' slots); 0 = off                        */
+  int32_t pager;         /* strata_pager                                     */
   const uint64_t* expert_profile; /* host [E] scores (each <= 2^62) to warm the
                           * slots with at create, or NULL (see
                           * strata_expert_profile_load)                       */
@@ -179,7 +195,8 @@ typedef struct {
  * x and y must not overlap.  The call enqueues its work on `stream`.  When the
  * budget is smaller than E it waits once for the per-expert token counts to
  * reach the host, decides hits and misses, and pages missing experts from the
- * pinned store into slots with hipMemcpyAsync on internal copy streams; if
+ * pinned store into slots (by the engine desc->pager chose) on internal copy
+ * streams; if
  * more distinct experts are needed than there are slots, the policy's
  * hottest quarter of the slots stays put and the experts stream through the
  * rest in waves of half of it, so one wave's pages land while the previous
@@ -210,7 +227,8 @@ typedef struct {
                             * they overwrote an expert, in evictions           */
   uint64_t prefetch_hits;  /* hits on an expert paged ahead, first use only    */
   int32_t prefetch;        /* as created                                       */
-  int32_t reserved;
+  int32_t pager;           /* the paging engine in use (KERNEL or DMA; 0 in a
+                            * residency replay)                                */
 } strata_cache_stats;
 
 /* Reads the counters.  Does no device work except, when budget == E, one

@@ -84,18 +84,20 @@ def test_layer_matches_oracle_all_resident(torch_cuda, name):
 @pytest.mark.parametrize("name", ["qwen_s", "glm_s", "e512_s", "mixtral_s", "e896_s", "g128_s", "nvfp4_s",
                                   "longk_s", "longk_g128_s"])
 @pytest.mark.parametrize("policy", ["lru", "lfu"])
-def test_paged_output_is_bitwise_the_resident_output(torch_cuda, name, policy):
-    """Budgeted (paged, waves) vs all-resident: identical y bits; counters equal
-    the residency model fed with the oracle's needed sets."""
+@pytest.mark.parametrize("pager", ["kernel", "dma"])
+def test_paged_output_is_bitwise_the_resident_output(torch_cuda, name, policy, pager):
+    """Budgeted (paged, waves) vs all-resident, with either paging engine:
+    identical y bits; counters equal the residency model fed with the oracle's
+    needed sets."""
     lw = _get(name)
     cfg = lw.cfg
     res = _mk(lw, budget=cfg.num_experts)
     import expert_paged_quantized_amd as epq
-    paged = epq.MoELayer.from_weights(lw, budget=cfg.budget, policy=policy, max_tokens=512)
+    paged = epq.MoELayer.from_weights(lw, budget=cfg.budget, policy=policy, max_tokens=512, pager=pager)
     model = ResidencyModel(cfg.num_experts, cfg.budget, policy, cfg.expert_bytes())
     Ts = [1, 300, 1, 2, 8, 1, 257, 4, 1, 1, 5, 3]
     for i, T in enumerate(Ts):
-        print(f"[paged] {name} {policy} step={i} T={T}", flush=True)
+        print(f"[paged] {name} {policy} {pager} step={i} T={T}", flush=True)
         x = make_tokens(cfg, T, step=100 + i, seed=cfg.seed + 50)
         xd = to_dev(x)
         y_r = res.forward(xd)
@@ -107,11 +109,21 @@ def test_paged_output_is_bitwise_the_resident_output(torch_cuda, name, policy):
               "resident_bytes"):
         assert st[k] == want[k], (k, st[k], want[k])
     assert st["budget"] == cfg.budget
+    assert st["pager"] == {"kernel": 1, "dma": 2}[pager]
     assert st["misses"] > 0 and st["waves"] > len(Ts)  # paging and waves were exercised
     rs = res.stats()
     assert rs["forwards"] == len(Ts) and rs["misses"] == 0 and rs["hits"] == want["hits"] + want["misses"]
     res.close()
     paged.close()
+
+
+def test_auto_pager_picks_the_kernel_for_small_records(torch_cuda):
+    """pager="auto" pages records of at most 8 MiB with the page-in kernel."""
+    lw = _get("qwen_s")
+    import expert_paged_quantized_amd as epq
+    layer = epq.MoELayer.from_weights(lw, budget=lw.cfg.budget, max_tokens=64)
+    assert lw.cfg.expert_bytes() <= 8 << 20 and layer.stats()["pager"] == 1
+    layer.close()
 
 
 @pytest.mark.parametrize("name", ["qwen_s", "glm_s", "e512_s", "nvfp4_s"])

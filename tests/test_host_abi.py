@@ -99,6 +99,8 @@ def tiny_fp4():
     ("decay_shift", 2, _capi.E_INVALID),       # decay on LRU
     ("prefetch", 3, _capi.E_INVALID),          # prefetch > budget (2)
     ("prefetch", -1, _capi.E_INVALID),
+    ("pager", 3, _capi.E_INVALID),
+    ("pager", -1, _capi.E_INVALID),
     ("max_tokens", 0, _capi.E_INVALID),
     ("num_experts", 2000, _capi.E_UNSUPPORTED),
     ("router_w", None, _capi.E_INVALID),
