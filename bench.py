@@ -2,8 +2,8 @@
 
 One step = the layer's work for a prompt and its first generated token: one
 prefill forward over the configuration's prompt length followed by one decode
-forward of a single token, as configured (expert budget, LRU paging from the
-pinned host store).  Inputs are synthetic and already resident in HBM when the
+forward of a single token, as configured (expert budget, WARM residency with
+decay shift 5 paging from the pinned host store; --policy picks LRU or LFU).  Inputs are synthetic and already resident in HBM when the
 timed region starts.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=6)
     ap.add_argument("--no-policies", action="store_true", help="skip the paged decode policy runs")
+    ap.add_argument("--policy", default="warm", choices=["lru", "lfu", "warm"],
+                    help="residency policy of the paged layer (warm: decay_shift 5)")
     ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--trace-summary", metavar="TRACE_DIR")
@@ -227,7 +229,8 @@ def main():
     t0 = time.time()
     lw = make_layer(cfg)
     log(f"[bench] generated in {time.time() - t0:.1f}s; creating layers")
-    paged = epq.MoELayer.from_weights(lw, budget=cfg.budget, max_tokens=Tp)
+    paged = epq.MoELayer.from_weights(lw, budget=cfg.budget, max_tokens=Tp, policy=args.policy,
+                                      decay_shift=5 if args.policy == "warm" else 0)
     resident = epq.MoELayer.from_weights(lw, budget=cfg.num_experts, max_tokens=Tp)
 
     n = W + K
@@ -383,7 +386,7 @@ def main():
                                f"E={cfg.num_experts} top-{cfg.top_k} shared={cfg.num_shared} "
                                f"{cfg.quant} {cfg.router} router"
                                + (f" Zipf({cfg.zipf_s}) bias" if cfg.zipf_s else "")
-                               + f"; budget {cfg.budget}/{cfg.num_experts} slots, LRU; "
+                               + f"; budget {cfg.budget}/{cfg.num_experts} slots, {args.policy.upper()}; "
                                f"step = prefill {Tp} tokens + decode {Td} token",
                    "prefill_T": Tp, "decode_T": Td, "budget": cfg.budget,
                    "parallelism": "single GPU"},
