@@ -209,7 +209,10 @@ struct ScaleLayout {
   }
 };
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g) with the hardware reciprocal (1 ulp) in place of an
+// IEEE division (about ten instructions): the result is rounded to 16 bits
+// right after, and g = -inf.. +inf still give -0 .. g.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
