@@ -100,6 +100,8 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
     }
   for (int32_t e : needed)
     if (expert_slot_[e] < 0) order.push_back(e);
+  // misses coldest first (keys before this forward's updates)
+  std::sort(order.begin() + nh, order.end(), [&](int a, int b) { return before(a, b); });
   const uint64_t nm = needed.size() - nh;
 
   // keep_: 1 = pinned for the forward; in_wave_: 1 = current wave, 2 = previous

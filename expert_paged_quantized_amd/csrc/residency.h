@@ -13,7 +13,9 @@
 //     0..B-1 and, given a profile, sets the scores and rebalances (below);
 //   * a forward needs the experts with at least one token, N ascending;
 //     hits are those resident when it starts, misses the rest;
-//   * N is run as hits (ascending) then misses (ascending); if N fits in B
+//   * N is run as hits (ascending) then misses by increasing key (the
+//     coldest first, so the hottest misses stream last and are still
+//     resident for the next forward; keys as below); if N fits in B
 //     slots it is one wave; otherwise the floor(B/4) hits with the largest
 //     keys stay pinned for the whole forward (a long prompt does not flush the
 //     hot set) and the list runs in waves of W = floor(S/2) (1 if S < 2),

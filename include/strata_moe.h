@@ -321,7 +321,8 @@ strata_status strata_expert_profile_load(strata_moe* h, const uint64_t* scores, 
  * holds the needed expert ids of every forward back to back, needed_len[i] of
  * them for forward i (any order, duplicates ignored).  If plan_slots is not
  * NULL it receives, per forward and per needed expert in the order the
- * forward runs them (hits ascending, then misses ascending), the slot used;
+ * forward runs them (hits ascending, then misses by increasing key, the
+ * coldest first), the slot used;
  * its length must be sum(needed_len).  If scores_out is not NULL it receives
  * the E final scores.  Errors: E_INVALID. */
 strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32_t policy,

@@ -17,7 +17,9 @@ possible:
   given, the scores are set to it and the slots are then rebalanced (below);
 * forward n (n = 1, 2, ...): N = experts with at least one token, ascending;
   hits = N that are resident when the call starts, misses = the rest;
-* the needed list is hits (ascending) then misses (ascending).  If it holds
+* the needed list is hits (ascending) then misses by increasing key (keys
+  below, as they stand when the call starts): the coldest misses stream
+  first, so the hottest are still resident for the next forward.  If it holds
   at most B experts it is one wave.  Otherwise (a forward that streams more
   experts than there are slots) the P = floor(B/4) hits with the largest keys
   are pinned for the whole forward, so a long prompt does not flush the hot
@@ -142,7 +144,7 @@ class ResidencyModel:
         self.forwards += 1
         res = self.resident()
         hits = [e for e in N if e in res]
-        misses = [e for e in N if e not in res]
+        misses = sorted((e for e in N if e not in res), key=self._key)
         for e in hits:
             if self.from_prefetch[e]:
                 self.prefetch_hits += 1

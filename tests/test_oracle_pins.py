@@ -579,6 +579,27 @@ def test_p11_streaming_forward_keeps_the_pinned_hot_expert():
     assert m.forward([2, 8]) == [[(2, 2, False), (8, 1, True)]]
 
 
+def test_p11_misses_stream_coldest_first():
+    # E=6, B=2, LFU from the profile [0, 0, 5U, U, 3U, 0]: create keeps the two
+    # largest scores resident (2 in slot 0, 4 in slot 1).  f1 needs {0,1,3,5}:
+    # all misses, ordered by increasing key (score, last_use, id):
+    # 0 (0,0,0), 1 (0,0,1), 5 (0,0,5), 3 (U,0,3) -- not ascending by id.
+    # N > B: no pin (floor(2/4) = 0), S = 2, waves of 1; a page may not evict
+    # the current or the previous wave:
+    #   [0]: candidates 2 (5U), 4 (3U) -> 4 (slot 1)
+    #   [1]: candidates 2 (0 is the previous wave) -> 2 (slot 0)
+    #   [5]: candidates 0 (1 is the previous wave) -> slot 1
+    #   [3]: candidates 1 (5 is the previous wave) -> slot 0
+    U_ = 65536
+    m = ResidencyModel(6, 2, LFU, profile=[0, 0, 5 * U_, U_, 3 * U_, 0])
+    assert m.resident() == {2: 0, 4: 1}
+    plan = m.forward([0, 1, 3, 5])
+    assert plan == [[(0, 1, True)], [(1, 0, True)], [(5, 1, True)], [(3, 0, True)]]
+    assert m.resident() == {3: 0, 5: 1}
+    st = m.stats()
+    assert (st["hits"], st["misses"], st["evictions"], st["waves"]) == (0, 4, 4, 4)
+
+
 def test_p11_model_rejects_bad_budgets():
     with pytest.raises(ValueError):
         ResidencyModel(4, 0)
