@@ -435,85 +435,82 @@ __global__ __launch_bounds__(kDecWaves * 64) void moe_decode_kernel(GemmArgs p, 
 // 128 per lane, and every token adds accumulators and activation operands
 constexpr int dot_depth(int tt) { return tt == 1 ? 16 : (tt == 2 ? 12 : 8); }
 
-template <int QF, bool GATE_UP, int TT, int NPR>
-__global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t xs[];
-  using SL = ScaleLayout<QF>;
-  constexpr int DEPTH = dot_depth(TT);
-  const int S = blockDim.x >> 6;
-  const int nrt = p.N >> 5;
-  const int rt = blockIdx.x % nrt, tile_i = blockIdx.x / nrt;
-  const int n_tiles = p.n_tiles_dev ? p.n_tiles_dev[0] : p.n_tiles;
-  if (tile_i >= n_tiles) return;  // the whole workgroup leaves together
-  const Tile t = p.tiles[tile_i];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = p.K, KB = K >> 6;
-  const int kb0 = wave * KB / S, kb1 = (wave + 1) * KB / S, nkb = kb1 - kb0;
-  const int row_u32 = K / 2 + 4;                  // staged row: K 16-bit inputs + 16 B pad
-  float* xsum = reinterpret_cast<float*>(xs + TT * row_u32);  // [TT][K/32] (int4)
-
-  const uint8_t* rec = p.slot_ptr[t.slot];
-  const uint8_t* codes = rec + p.off_codes + ((int64_t)rt * KB + kb0) * kTileCodeBytes + lane * 16;
-  // scale block of (absolute) k-block kb0 + kb is (kb0 + kb) >> sshift
-  const uint8_t* scales =
-      rec + p.off_scales + (int64_t)rt * (KB >> p.sshift) * SL::kTileBytes + SL::lane_off(lane);
-
-  // activation loads first: waiting for them later leaves the weight loads
-  // issued after them in flight
-  const int pr = K >> 3;  // 16-byte pieces per row
-  u32x4 v[TT][NPR];
+// Token rows of a dot-decode unit into registers: thread tid loads the
+// 16-byte pieces tid + j * nthr (j < NPR) of each of the TT rows; rows past
+// nrows re-read the last row and pieces past the row re-read its last piece.
+template <int TT, int NPR>
+__device__ __forceinline__ void dot_load_rows(const GemmArgs& p, const Tile& t, int tid, int nthr,
+                                              u32x4 (&v)[TT][NPR]) {
+  const int pr = p.K >> 3;  // 16-byte pieces per row
 #pragma unroll
   for (int r = 0; r < TT; ++r) {
-    const int rr = min(r, t.nrows - 1);  // rows past nrows re-read the last row
+    const int rr = min(r, t.nrows - 1);
     const int64_t ar = p.gather ? p.gather[t.row_begin + rr] : (t.row_begin + rr);
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.act) + ar * K;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.act) + ar * p.K;
 #pragma unroll
-    for (int j = 0; j < NPR; ++j) v[r][j] = ld16(src + min(tid + j * (int)blockDim.x, pr - 1) * 8);
+    for (int j = 0; j < NPR; ++j) {
+      v[r][j] = ld16(src + min(tid + j * nthr, pr - 1) * 8);
+    }
   }
-  asm volatile("" ::: "memory");
-  // weight ring prologue (clamped inside the range)
-  u32x4 wq[DEPTH];
-  uint32_t ws[DEPTH];
-#pragma unroll
-  for (int j = 0; j < DEPTH; ++j) {
-    const int kb = min(j, nkb - 1);
-    wq[j] = ld16_nt(codes + (int64_t)kb * kTileCodeBytes);
-    ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kb) >> p.sshift) * SL::kTileBytes);
-  }
-  // stage the token rows; for int4 also the sums of each 32 inputs, four
-  // consecutive 8-input pieces per quad
+}
+
+// Stages the token rows in LDS (row r at xs + r * row_u32); for int4 also the
+// sums of each 32 inputs (xsum[r][K/32]), four consecutive 8-input pieces per
+// quad of threads, added in a fixed tree.
+template <int QF, int TT, int NPR>
+__device__ __forceinline__ void dot_store_rows(const u32x4 (&v)[TT][NPR], uint32_t* xs, int row_u32,
+                                               float* xsum, int tid, int nthr, int K) {
+  const int pr = K >> 3;
 #pragma unroll
   for (int r = 0; r < TT; ++r) {
 #pragma unroll
     for (int j = 0; j < NPR; ++j) {
-      const int c = tid + j * (int)blockDim.x;
+      const int c = tid + j * nthr;
       if (c < pr) *reinterpret_cast<u32x4*>(&xs[r * row_u32 + c * 4]) = v[r][j];
       if constexpr (QF == Q_INT4) {
         const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
         float sum = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) sum = __builtin_amdgcn_fdot2(bitcast<f16x2>(v[r][j][q]), one, sum, false);
-        // quad (xor 1, then xor 2) sum in a fixed tree; blockDim is a
-        // multiple of 64 and pr of 8, so a quad never straddles rows
+        // quad (xor 1, then xor 2) sum in a fixed tree; nthr is a multiple
+        // of 64 and pr of 8, so a quad never straddles rows
         sum += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, false));
         sum += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF, false));
         if (c < pr && (c & 3) == 0) xsum[r * (K >> 5) + (c >> 2)] = sum;
       }
     }
   }
-  __syncthreads();
+}
 
-  float acc[TT];
+// Weight ring prologue: slot j holds K-block kb0 + min(j, nkb - 1).
+template <int QF, int DEPTH>
+__device__ __forceinline__ void dot_prologue(u32x4 (&wq)[DEPTH], uint32_t (&ws)[DEPTH], const uint8_t* codes,
+                                             const uint8_t* scales, int kb0, int nkb, int sshift) {
+  using SL = ScaleLayout<QF>;
 #pragma unroll
-  for (int r = 0; r < TT; ++r) acc[r] = 0.0f;
+  for (int j = 0; j < DEPTH; ++j) {
+    const int kb = min(j, nkb - 1);
+    wq[j] = ld16_nt(codes + (int64_t)kb * kTileCodeBytes);
+    ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kb) >> sshift) * SL::kTileBytes);
+  }
+}
+
+// The K loop of one wave: K-blocks kb0 .. kb0 + nkb - 1 of its row tile against
+// the staged token rows; each ring slot is unpacked, refilled in place, then
+// contracted.  acc[r] = this lane's partial sum for token r (row lane % 32,
+// inputs of half lane / 32).
+template <int QF, int TT, int DEPTH>
+__device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[DEPTH], const uint8_t* codes,
+                                             const uint8_t* scales, int kb0, int nkb, int sshift,
+                                             const uint32_t* xs, int row_u32, const float* xsum, int K,
+                                             int lane, float (&acc)[TT]) {
+  using SL = ScaleLayout<QF>;
   const int h = lane >> 5;
   const uint32_t* xl = xs + (kb0 * 32 + h * 16);  // this lane's 32 inputs of block kb0, row 0
   const float* xsl = xsum + kb0 * 2 + h;
-
   for (int i = 0; i < nkb; i += DEPTH) {
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
-      // unpack slot j, refill it in place, then contract
       const int kbl = i + j;
       const int kn = min(kbl + DEPTH, nkb - 1);
       if constexpr (QF == Q_INT4) {
@@ -532,8 +529,11 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
                      "+v"(m[2][2]), "+v"(m[2][3]), "+v"(m[3][0]), "+v"(m[3][1]), "+v"(m[3][2]),
                      "+v"(m[3][3]), "+v"(s), "+v"(b)::"memory");
         wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
-        ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> p.sshift) * SL::kTileBytes);
+        ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes);
         if (kbl < nkb) {
+          float xsv[TT];  // sum(x) of the group: read first, used last
+#pragma unroll
+          for (int r = 0; r < TT; ++r) xsv[r] = xsl[r * (K >> 5) + kbl * 2];
 #pragma unroll
           for (int r = 0; r < TT; ++r) {
             const uint32_t* xr = xl + r * row_u32 + kbl * 32;
@@ -548,7 +548,7 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
             }
             const float xq = __builtin_fmaf(lo, 16.0f, hi) * 1048576.0f;  // sum(x q)
             acc[r] = __builtin_fmaf(s, xq, acc[r]);
-            acc[r] = __builtin_fmaf(b, xsl[r * (K >> 5) + kbl * 2], acc[r]);
+            acc[r] = __builtin_fmaf(b, xsv[r], acc[r]);
           }
         }
       } else if constexpr (QF == Q_NVFP4) {
@@ -561,7 +561,7 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
         float s0 = e4m3_to_f32(ws[j] & 0xffu), s1 = e4m3_to_f32(ws[j] >> 8);
         asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(s0), "+v"(s1)::"memory");
         wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
-        ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> p.sshift) * SL::kTileBytes);
+        ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes);
         if (kbl < nkb) {
 #pragma unroll
           for (int r = 0; r < TT; ++r) {
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
         float scale = __uint_as_float(ws[j] << 23);
         asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(scale)::"memory");
         wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
-        ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> p.sshift) * SL::kTileBytes);
+        ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes);
         if (kbl < nkb) {
 #pragma unroll
           for (int r = 0; r < TT; ++r) {
@@ -608,10 +608,48 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
       }
     }
   }
+}
+
+// One dot-decode unit: row tile rt of tile t, contracted by the S waves of
+// the workgroup (this wave is split sw, streaming the contiguous K-blocks
+// [sw*KB/S, (sw+1)*KB/S)).  Every thread of the workgroup stages the token
+// rows.  The halves of a row are added lane l + lane l+32, then the S
+// partial sums in split order, then the epilogue.
+template <int QF, bool GATE_UP, int TT, int NPR>
+__device__ __forceinline__ void dot_unit(const GemmArgs& p, const Tile& t, int rt, int S, int sw, uint32_t* xs) {
+  using SL = ScaleLayout<QF>;
+  constexpr int DEPTH = dot_depth(TT);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = blockDim.x;
+  const int K = p.K, KB = K >> 6;
+  const int kb0 = sw * KB / S, kb1 = (sw + 1) * KB / S, nkb = kb1 - kb0;
+  const int row_u32 = K / 2 + 4;                              // staged row: K 16-bit inputs + 16 B pad
+  float* xsum = reinterpret_cast<float*>(xs + TT * row_u32);  // [TT][K/32] (int4)
+
+  const uint8_t* rec = p.slot_ptr[t.slot];
+  const uint8_t* codes = rec + p.off_codes + ((int64_t)rt * KB + kb0) * kTileCodeBytes + lane * 16;
+  // scale block of (absolute) k-block kb0 + kb is (kb0 + kb) >> sshift
+  const uint8_t* scales =
+      rec + p.off_scales + (int64_t)rt * (KB >> p.sshift) * SL::kTileBytes + SL::lane_off(lane);
+
+  // activation loads first: waiting for them later leaves the weight loads
+  // issued after them in flight
+  u32x4 v[TT][NPR];
+  dot_load_rows<TT, NPR>(p, t, tid, nthr, v);
+  asm volatile("" ::: "memory");
+  u32x4 wq[DEPTH];
+  uint32_t ws[DEPTH];
+  dot_prologue<QF, DEPTH>(wq, ws, codes, scales, kb0, nkb, p.sshift);
+  dot_store_rows<QF, TT, NPR>(v, xs, row_u32, xsum, tid, nthr, K);
+  __syncthreads();
+
+  float acc[TT];
+#pragma unroll
+  for (int r = 0; r < TT; ++r) acc[r] = 0.0f;
+  dot_contract<QF, TT, DEPTH>(wq, ws, codes, scales, kb0, nkb, p.sshift, xs, row_u32, xsum, K, lane, acc);
 
   // halves: lane l (< 32) adds lane l+32; then the S waves in order
   __syncthreads();  // staging area reused below
-  float* red = reinterpret_cast<float*>(xs);  // [S][TT][32]
+  float* red = reinterpret_cast<float*>(xs);  // [waves][TT][32]
 #pragma unroll
   for (int r = 0; r < TT; ++r) {
     const float other = __shfl_down(acc[r], 32);
@@ -619,7 +657,7 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
   }
   __syncthreads();
   const float2 gs = matrix_scales<QF>(p, rec);  // NVFP4 matrix scales, else 1
-  for (int q = tid; q < TT * 32; q += blockDim.x) {
+  for (int q = tid; q < TT * 32; q += nthr) {
     const int n = q >> 5, row = q & 31;  // (token, row)
     if (n >= t.nrows) continue;
     if constexpr (GATE_UP) {
@@ -640,6 +678,18 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
       reinterpret_cast<float*>(p.out)[(int64_t)(t.row_begin + n) * p.out_ld + rt * 32 + row] = o;
     }
   }
+}
+
+template <int QF, bool GATE_UP, int TT, int NPR>
+__global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t xs[];
+  const int S = blockDim.x >> 6;
+  const int nrt = p.N >> 5;
+  const int rt = blockIdx.x % nrt, tile_i = blockIdx.x / nrt;
+  const int n_tiles = p.n_tiles_dev ? p.n_tiles_dev[0] : p.n_tiles;
+  if (tile_i >= n_tiles) return;  // the whole workgroup leaves together
+  const Tile t = p.tiles[tile_i];
+  dot_unit<QF, GATE_UP, TT, NPR>(p, t, rt, S, threadIdx.x >> 6, xs);
 }
 
 // ---------------------------------------------------------------------------
