@@ -30,6 +30,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import subprocess
 import sys
@@ -73,8 +74,16 @@ KERNEL_SRC = os.path.join(ROOT, "expert_paged_quantized_amd", "csrc", "kernels_e
 CALIB_BYTES = 256 << 20                        # plain device copy timed in the same run
 
 
+def code_hash(text):
+    """Hash of C++ source with comments and whitespace removed: it changes with
+    the code, not with its comments."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
+
+
 def kernel_source_hash():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    return code_hash(open(KERNEL_SRC).read())
 
 
 def traffic_path(workload):

@@ -1,14 +1,15 @@
 // Expert kernels of the MoE layer for gfx950: grouped SwiGLU FFN computed
-// straight from 4-bit packed weights on the MFMA units, and the weighted
-// combine.
+// straight from 4-bit packed weights (on the MFMA units for prefill and 5..8
+// decode tokens, on the VALU dot units for 1..4), and the weighted combine.
 //
-// Weights stay 4-bit in HBM and are decoded in registers into MFMA operands,
-// never into a wider resident copy (ro99/strata README: precision paragraph,
-// and the SM86 kernel paragraph, whose register-fed decode into matrix-core
-// operands is the prior art here; its prepack into operand order is a pure
-// byte permutation, as is the tile order used below).  One weight layout
-// serves both the decode kernel (T <= 8 tokens, one row tile per wave, split-K
-// across workgroups) and the prefill kernel (token tiles of 128 rows staged in LDS), as
+// Weights stay 4-bit in HBM and are decoded in registers into MFMA or dot
+// operands, never into a wider resident copy (ro99/strata README: precision
+// paragraph, and the SM86 kernel paragraph, whose register-fed decode into
+// matrix-core operands is the prior art here; its prepack into operand order
+// is a pure byte permutation, as is the tile order used below).  One weight
+// layout serves the decode kernels (T <= 8 tokens: a 32-row tile per group of
+// waves, K split across the waves of one workgroup and added in LDS in a fixed
+// order) and the prefill kernel (token tiles of 128 rows staged in LDS), as
 // the same README does with one layout for M=1 decode and M=128 pages.
 //
 // MFMA used: v_mfma_f32_32x32x16_{f16,bf16}.  The weight tile is the A
