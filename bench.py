@@ -360,6 +360,49 @@ def main():
     dec_gbps, dec_bytes, dec_ms = decode_pass(cold=True)
     warm_gbps, _, warm_ms = decode_pass(cold=False)
     del flush
+
+    # decode B=1 wall time, all resident: eager forwards against the same
+    # forward replayed from a HIP graph (no host launch work per kernel; each
+    # replay first copies the new token into the graph's input buffer)
+    def decode_b1():
+        x_st = xs_d[W].clone()
+        y_st = torch.empty_like(x_st)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            resident.forward(x_st, y=y_st)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            resident.forward(x_st, y=y_st)
+        out = {}
+        for mode in ("eager", "graph"):
+            def one(x):
+                if mode == "eager":
+                    resident.forward(x, y=y_d)
+                else:
+                    x_st.copy_(x)
+                    g.replay()
+            per = []
+            for i in range(W, n):
+                a = time.perf_counter()
+                one(xs_d[i])
+                torch.cuda.synchronize()
+                per.append(time.perf_counter() - a)
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            for i in range(W, n):
+                one(xs_d[i])
+            torch.cuda.synchronize()
+            bb = (time.perf_counter() - a) / K
+            out[mode] = {"us_per_token_synced_median": round(statistics.median(per) * 1e6, 1),
+                         "tokens_per_s_back_to_back": round(1.0 / bb, 1)}
+        del g
+        return out
+
+    log("[bench] decode B=1 latency: eager and graph replay")
+    dec_b1 = decode_b1()
     read_ceiling = epq.measure_hbm_read(0, 1 << 30, 5)
     decode_roof = {"bound": "hbm", "kernel": "decode gate+up and down (expert-weight bytes)",
                    "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -401,6 +444,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
         "decode_roofline": decode_roof,
+        "decode_b1_all_resident": dec_b1,
         "step_ms_median": round(statistics.median(per) * 1e3, 3),
         "step_ms_range": [round(min(per) * 1e3, 3), round(max(per) * 1e3, 3)],
         "all_resident": {"value": round(K * tokens_per_step / dt_r, 1),

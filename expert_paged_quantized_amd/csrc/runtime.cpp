@@ -769,7 +769,15 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
                                   const strata_route_dbg* dbg) {
   const bool decode = T <= kDecodeMaxT;
   const int TK = T * h->k;
-  if (h->fwd_recorded) HIP_CHECK(hipStreamWaitEvent(s, h->ev_fwd_done, 0));
+  // under stream capture only kernels may be enqueued: an all-resident
+  // forward is nothing else (the caller orders replays against other forwards)
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  HIP_CHECK(hipStreamIsCapturing(s, &cap));
+  const bool capturing = cap != hipStreamCaptureStatusNone;
+  if (capturing && h->budget != h->E)
+    return fail(STRATA_E_UNSUPPORTED, "a budgeted forward decides its pages on the host and cannot be captured");
+  if (capturing && h->timing) return fail(STRATA_E_UNSUPPORTED, "kernel timing cannot be captured");
+  if (h->fwd_recorded && !capturing) HIP_CHECK(hipStreamWaitEvent(s, h->ev_fwd_done, 0));
 
   HIP_CHECK(timed(h, STRATA_K_ROUTER, s, [&]() {
     return launch_router((const uint16_t*)x, h->d_router_w, h->d_router_bias, h->d_logits, h->d_x16, T,
@@ -943,8 +951,10 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
     HIP_CHECK(cp(dbg->offsets, h->d_offsets, size_t(h->E + 1) * 4));
     HIP_CHECK(cp(dbg->perm, h->d_perm, size_t(TK) * 4));
   }
-  HIP_CHECK(hipEventRecord(h->ev_fwd_done, s));
-  h->fwd_recorded = true;
+  if (!capturing) {
+    HIP_CHECK(hipEventRecord(h->ev_fwd_done, s));
+    h->fwd_recorded = true;
+  }
   if (getenv("STRATA_LOG")) {
     fprintf(stderr, "[strata] T=%d forwards=%llu hits=%llu misses=%llu waves=%llu bytes_h2d=%llu\n", T,
             (unsigned long long)h->rm.forwards, (unsigned long long)h->rm.hits,

@@ -202,8 +202,16 @@ typedef struct {
  * rest in waves of half of it, so one wave's pages land while the previous
  * wave computes.  Paging, waves and slot placement never change y (it is
  * bitwise the same as with budget = E).  T == 0 is a no-op.
- * Errors: E_INVALID (null handle or pointers, T < 0, T > max_tokens), E_HIP
- * (after which the handle is poisoned), E_POISONED. */
+ * Graph capture: a forward of a layer whose budget is E (all experts
+ * resident) enqueues only kernels, so it may be captured into a HIP graph on
+ * `stream` and replayed; a replay computes from whatever x holds then.  Replays
+ * share the layer's workspace with every other forward of the layer, so the
+ * caller orders them (one stream); the statistics count the captured forward
+ * once, not its replays.  A budgeted forward decides its pages on the host and
+ * cannot be captured (E_UNSUPPORTED), nor can a forward with kernel timing on.
+ * Errors: E_INVALID (null handle or pointers, T < 0, T > max_tokens),
+ * E_UNSUPPORTED (capture, above), E_HIP (after which the handle is poisoned),
+ * E_POISONED. */
 strata_status strata_moe_forward(strata_moe* h, const void* x, int32_t T, void* y, void* stream,
                                  const strata_route_dbg* dbg);
 

@@ -117,6 +117,51 @@ def test_paged_output_is_bitwise_the_resident_output(torch_cuda, name, policy, p
     paged.close()
 
 
+def test_all_resident_forward_replays_from_a_graph(torch_cuda):
+    """An all-resident forward captured into a HIP graph: every replay (with
+    eager forwards and synchronisations between replays) gives the eager
+    forward's bits for the input it finds in x; a budgeted layer refuses."""
+    torch = torch_cuda
+    import expert_paged_quantized_amd as epq
+    lw = _get("glm_s")
+    cfg = lw.cfg
+    layer = _mk(lw, budget=cfg.num_experts)
+    for T in (1, 4, 8, 300):
+        print(f"[graph] T={T}", flush=True)
+        xs = [to_dev(make_tokens(cfg, T, step=400 + 10 * T + i, seed=cfg.seed + 50)) for i in range(4)]
+        x_static = xs[0].clone()
+        y_static = torch.empty_like(x_static)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            layer.forward(x_static, y=y_static)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.forward(x_static, y=y_static)
+        for i, x in enumerate(xs):
+            x_static.copy_(x)
+            g.replay()
+            torch.cuda.synchronize()
+            y_eager = layer.forward(x)
+            torch.cuda.synchronize()
+            assert np.array_equal(y_bits(y_static), y_bits(y_eager)), f"T={T} replay {i} differs from eager"
+        del g
+    paged = _mk(lw, budget=cfg.budget)
+    x = to_dev(make_tokens(cfg, 1, step=499, seed=cfg.seed + 50))
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(epq.StrataError) as ei:
+        with torch.cuda.graph(g):
+            paged.forward(x)
+    assert ei.value.status == 2  # E_UNSUPPORTED
+    torch.cuda.synchronize()
+    y_p, y_r = paged.forward(x), layer.forward(x)
+    assert np.array_equal(y_bits(y_p), y_bits(y_r))  # both layers still usable
+    layer.close()
+    paged.close()
+
+
 def test_auto_pager_picks_the_kernel_for_small_records(torch_cuda):
     """pager="auto" pages records of at most 8 MiB with the page-in kernel."""
     lw = _get("qwen_s")
