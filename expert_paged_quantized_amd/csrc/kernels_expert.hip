@@ -1051,7 +1051,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int shared_row0, int ksplit, int64_t stride,
                                                       uint16_t* __restrict__ y) {
   const int t = blockIdx.x;
-  for (int c = threadIdx.x * 4; c < H; c += 1024) {
+  // workgroup (t, blockIdx.y) takes column blocks of 1024, gridDim.y apart
+  for (int c = blockIdx.y * 1024 + threadIdx.x * 4; c < H; c += gridDim.y * 1024) {
     float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int j = 0; j < k; ++j) {
       const float wj = w[(size_t)t * k + j];
@@ -1199,7 +1200,10 @@ hipError_t launch_expert_gemm(const GemmArgs& a, int quant, bool gate_up, bool d
 
 hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, int T, int k, int H,
                           int shared_row0, int ksplit, int64_t stride, uint16_t* y, hipStream_t s) {
-  launch_k(combine_kernel, dim3(T), dim3(256), 0, s, o, pos, w, k, H, shared_row0, ksplit, stride, y);
+  // one workgroup per (token, 1024 columns): a decode token's columns are
+  // read in parallel rather than in dependent rounds of one workgroup
+  launch_k(combine_kernel, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, o, pos, w, k, H, shared_row0, ksplit,
+           stride, y);
   return hipGetLastError();
 }
 
