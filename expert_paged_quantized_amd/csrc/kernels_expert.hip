@@ -20,12 +20,20 @@
 // inputs 32*(l/32)..+31 of its row, 8 per MFMA step, and the activations are
 // read with the same mapping, so the reduction covers each input exactly once.
 //
-// int4 group-64 affine weights are decoded to fp16 (w = s*q + b, one fp16
-// rounding; s and b are admitted only if exact in fp16) and the activations
-// arrive as fp16 (the router kernel writes that copy of x; exact in range).
-// MXFP4 weights are decoded to bf16 with the gfx950 scaled FP4 conversion
-// (exact: an E2M1 value times a power of two).  Accumulation is fp32 throughout; nothing uses float atomics,
-// so every expert's result depends only on its own rows and weights.
+// int4 affine weights are decoded to fp16 (w' = s'*q + b', one fp16 rounding,
+// where s', b' are the checkpoint's bf16 scale and bias times one power of
+// two 2^-c per matrix, chosen at load so that both are exact in fp16 and no
+// decoded weight exceeds 2^15) and the activations arrive as fp16 scaled per
+// token by 2^-xexp[t] (the router kernel writes that copy of x).  The GEMM
+// epilogues undo both powers of two in fp32, and the SwiGLU output h is
+// stored scaled by a further 2^-(xexp[t] + c_h), with c_h fixed per expert
+// from its weights so that |h| stays below 2^14 for any bf16 x: the fp16
+// operands never overflow.  NVFP4 takes the same route (its decoded weights
+// are exact in fp16).  MXFP4 weights are decoded to bf16 with the gfx950
+// scaled FP4 conversion (exact: an E2M1 value times a power of two) and run
+// on the bf16 input and a bf16 h, which have fp32's exponent range.
+// Accumulation is fp32 throughout; nothing uses float atomics, so every
+// expert's result depends only on its own rows and weights.
 #include <algorithm>
 #include <type_traits>
 
@@ -79,7 +87,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
 // (k2, k3); after a shift by 8 the same masks give (k4, k5) and (k6, k7).  A
 // low nibble OR 0x6400 is the fp16 1024 + q, a high nibble (bits 4..7) OR
 // 0x5400 is the fp16 64 + q; subtracting 1024 or 64 gives q exactly and one
-// fp16 fma gives s*q + b.
+// fp16 fma gives s'*q + b' (the matrix's rescaled scale and bias).
 __device__ __forceinline__ u32x4 dequant_int4_step(uint32_t w, f16x2 s2, f16x2 b2) {
   const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, mag_lo = 0x64006400u, mag_hi = 0x54005400u;
   const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
@@ -128,7 +136,8 @@ __device__ __forceinline__ u32x4 dequant_nvfp4_step(uint32_t w, f16x2 sc) {
   return a;
 }
 
-// Per-chunk decode parameters: fp16 (scale, bias) pairs for int4, the fp32
+// Per-chunk decode parameters: fp16 (scale, bias) pairs for int4 (the scale
+// word holds fp16 s' in its low half and b' in its high half), the fp32
 // power of two for MXFP4, the fp16 scales of the chunk's two 16-input blocks
 // for NVFP4 (words 0-1 and 2-3 of the chunk).
 template <int QF>
@@ -137,10 +146,9 @@ struct ChunkScale {
   float scale;
   __device__ __forceinline__ explicit ChunkScale(uint32_t sc) {
     if constexpr (QF == Q_INT4) {
-      const _Float16 s = (_Float16)__uint_as_float(sc << 16);
-      const _Float16 b = (_Float16)__uint_as_float(sc & 0xffff0000u);
-      s2 = f16x2{s, s};
-      b2 = f16x2{b, b};
+      const f16x2 sb = bitcast<f16x2>(sc);
+      s2 = __builtin_shufflevector(sb, sb, 0, 0);
+      b2 = __builtin_shufflevector(sb, sb, 1, 1);
       scale = 0.0f;
     } else if constexpr (QF == Q_NVFP4) {
       // both block scales in one register: (first 16 inputs, second 16)
@@ -228,6 +236,48 @@ __device__ __forceinline__ uint16_t to_h_elem(float f) {
     return f32_to_bf16_rne(f);
 }
 
+// Epilogue exponents of one output column (a row of the permuted space) of
+// expert `expert`, for the fp16 formats; all zero for MXFP4.  Gate+up: the
+// gate accumulator times 2^g is g itself, the up accumulator times 2^u is u
+// times the h row's 2^-(2 xexp[t] + c_h).  Down: the accumulator times 2^o.
+struct ColExp {
+  int g, u, o;
+};
+template <int QF, bool GATE_UP>
+__device__ __forceinline__ ColExp col_exp(const GemmArgs& p, int expert, int64_t row) {
+  ColExp r{0, 0, 0};
+  if constexpr (QF != Q_MXFP4) {
+    const int et = p.xexp[p.tok_of_row[row]];
+    const int32_t* we = p.wexp + expert * kWexpCount;
+    if constexpr (GATE_UP) {
+      r.g = et + we[kWexpGate];
+      r.u = we[kWexpUp] - et - we[kWexpH];
+    } else {
+      r.o = 2 * et + we[kWexpH] + we[kWexpDown];
+    }
+  }
+  return r;
+}
+__device__ __forceinline__ float pow2_scale(float v, int e) { return __builtin_amdgcn_ldexpf(v, e); }
+
+// The stored h element from the gate and up accumulators (gs: NVFP4 matrix
+// scales, else 1).
+template <int QF>
+__device__ __forceinline__ uint16_t h_elem(float ag, float au, float2 gs, const ColExp& ce) {
+  if constexpr (QF == Q_MXFP4)
+    return to_h_elem<QF>(silu(ag) * au);
+  else
+    return to_h_elem<QF>(silu(pow2_scale(ag * gs.x, ce.g)) * pow2_scale(au * gs.y, ce.u));
+}
+// One element of o from the down accumulator.
+template <int QF>
+__device__ __forceinline__ float o_elem(float acc, float gsx, const ColExp& ce) {
+  if constexpr (QF == Q_MXFP4)
+    return acc;
+  else
+    return pow2_scale(acc * gsx, ce.o);
+}
+
 // ---------------------------------------------------------------------------
 // Decode kernel (T <= 8 tokens).  Workgroup = 8 waves = R row tiles (32
 // weight rows each) of one expert x S K-splits, R*S = 8.  K is walked in
@@ -253,6 +303,7 @@ __device__ __forceinline__ void decode_store(const GemmArgs& p, const Tile& t, i
   const int n = lane & 31;
   if (n >= t.nrows) return;
   const int64_t row = t.row_begin + n;
+  const ColExp ce = col_exp<QF, GATE_UP>(p, t.expert, row);
   if constexpr (GATE_UP) {
     uint16_t* h = reinterpret_cast<uint16_t*>(p.out) + row * p.out_ld + rt * 16;
 #pragma unroll
@@ -261,7 +312,7 @@ __device__ __forceinline__ void decode_store(const GemmArgs& p, const Tile& t, i
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = g4 * 4 + q;
-        v[q] = to_h_elem<QF>(silu(acc[i] * gs.x) * (acc[i + 8] * gs.y));
+        v[q] = h_elem<QF>(acc[i], acc[i + 8], gs, ce);
       }
       const uint2 pk = {(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16)};
       *reinterpret_cast<uint2*>(h + g4 * 8 + (lane >> 5) * 4) = pk;
@@ -270,8 +321,8 @@ __device__ __forceinline__ void decode_store(const GemmArgs& p, const Tile& t, i
     float* o = reinterpret_cast<float*>(p.out) + row * p.out_ld + rt * 32;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const float4 v = {acc[g4 * 4 + 0] * gs.x, acc[g4 * 4 + 1] * gs.x, acc[g4 * 4 + 2] * gs.x,
-                        acc[g4 * 4 + 3] * gs.x};
+      const float4 v = {o_elem<QF>(acc[g4 * 4 + 0], gs.x, ce), o_elem<QF>(acc[g4 * 4 + 1], gs.x, ce),
+                        o_elem<QF>(acc[g4 * 4 + 2], gs.x, ce), o_elem<QF>(acc[g4 * 4 + 3], gs.x, ce)};
       *reinterpret_cast<float4*>(o + g4 * 8 + (lane >> 5) * 4) = v;
     }
   }
@@ -413,10 +464,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void moe_decode_kernel(GemmArgs p, 
 // decode time, so the contraction runs on the VALU dot units instead:
 //   int4:  an AND leaves a code pair as fp16 denormals (q * 2^-24 for the low
 //          nibbles, q * 2^-20 for the high ones, exact), v_dot2_f32_f16
-//          multiplies them with the fp16 activations, and the group's affine
-//          parameters are applied once per 32 inputs: s * sum(x q) + b * sum(x),
-//          with sum(x) staged alongside the activations.  No weight is rounded
-//          to 16 bits on this path.
+//          multiplies them with the scaled fp16 activations, and the group's
+//          affine parameters are applied once per 32 inputs in fp32:
+//          s' * sum(x q) + b' * sum(x), with sum(x) staged alongside the
+//          activations.  No weight is rounded to 16 bits on this path.
 //   MXFP4: the gfx950 FP4 conversion (unit scale) gives exact bf16 pairs,
 //          v_dot2_f32_bf16 contracts them, and the E8M0 power of two scales
 //          the 32-input group sum.
@@ -524,7 +575,8 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
           m[st][2] = w8 & 0x000F000Fu;  // (k4, k5) * 2^-24
           m[st][3] = w8 & 0x00F000F0u;  // (k6, k7) * 2^-20
         }
-        float s = __uint_as_float(ws[j] << 16), b = __uint_as_float(ws[j] & 0xffff0000u);
+        const f16x2 sbh = bitcast<f16x2>(ws[j]);  // (s', b') in fp16
+        float s = (float)sbh[0], b = (float)sbh[1];
         asm volatile("" : "+v"(m[0][0]), "+v"(m[0][1]), "+v"(m[0][2]), "+v"(m[0][3]), "+v"(m[1][0]),
                      "+v"(m[1][1]), "+v"(m[1][2]), "+v"(m[1][3]), "+v"(m[2][0]), "+v"(m[2][1]),
                      "+v"(m[2][2]), "+v"(m[2][3]), "+v"(m[3][0]), "+v"(m[3][1]), "+v"(m[3][2]),
@@ -661,6 +713,7 @@ __device__ __forceinline__ void dot_unit(const GemmArgs& p, const Tile& t, int r
   for (int q = tid; q < TT * 32; q += nthr) {
     const int n = q >> 5, row = q & 31;  // (token, row)
     if (n >= t.nrows) continue;
+    const ColExp ce = col_exp<QF, GATE_UP>(p, t.expert, t.row_begin + n);
     if constexpr (GATE_UP) {
       if (row >= 16) continue;
       float g = red[n * 32 + row], u = red[n * 32 + row + 16];
@@ -668,15 +721,13 @@ __device__ __forceinline__ void dot_unit(const GemmArgs& p, const Tile& t, int r
         g += red[(w * TT + n) * 32 + row];
         u += red[(w * TT + n) * 32 + row + 16];
       }
-      g *= gs.x;
-      u *= gs.y;
       uint16_t* hp = reinterpret_cast<uint16_t*>(p.out);
-      hp[(int64_t)(t.row_begin + n) * p.out_ld + rt * 16 + row] = to_h_elem<QF>(silu(g) * u);
+      hp[(int64_t)(t.row_begin + n) * p.out_ld + rt * 16 + row] = h_elem<QF>(g, u, gs, ce);
     } else {
       float o = red[n * 32 + row];
       for (int w = 1; w < S; ++w) o += red[(w * TT + n) * 32 + row];
-      o *= gs.x;
-      reinterpret_cast<float*>(p.out)[(int64_t)(t.row_begin + n) * p.out_ld + rt * 32 + row] = o;
+      reinterpret_cast<float*>(p.out)[(int64_t)(t.row_begin + n) * p.out_ld + rt * 32 + row] =
+          o_elem<QF>(o, gs.x, ce);
     }
   }
 }
@@ -929,6 +980,7 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
       const int mm = ct * 32 + (lane & 31);
       if (mm >= t.nrows) continue;
       const int64_t row = t.row_begin + mm;
+      const ColExp ce = col_exp<QF, GATE_UP>(p, t.expert, row);
       if constexpr (GATE_UP) {
         uint16_t* h = reinterpret_cast<uint16_t*>(p.out) + row * p.out_ld + rt * 16;
 #pragma unroll
@@ -937,7 +989,7 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int i = g4 * 4 + q;
-            v[q] = to_h_elem<QF>(silu(acc[r][ct][i] * gs.x) * (acc[r][ct][i + 8] * gs.y));
+            v[q] = h_elem<QF>(acc[r][ct][i], acc[r][ct][i + 8], gs, ce);
           }
           const uint2 pk = {(uint32_t)v[0] | ((uint32_t)v[1] << 16),
                             (uint32_t)v[2] | ((uint32_t)v[3] << 16)};
@@ -947,8 +999,8 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
         float* o = reinterpret_cast<float*>(p.out) + ks * p.split_stride + row * p.out_ld + rt * 32;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 v = {acc[r][ct][g4 * 4 + 0] * gs.x, acc[r][ct][g4 * 4 + 1] * gs.x,
-                            acc[r][ct][g4 * 4 + 2] * gs.x, acc[r][ct][g4 * 4 + 3] * gs.x};
+          const float4 v = {o_elem<QF>(acc[r][ct][g4 * 4 + 0], gs.x, ce), o_elem<QF>(acc[r][ct][g4 * 4 + 1], gs.x, ce),
+                            o_elem<QF>(acc[r][ct][g4 * 4 + 2], gs.x, ce), o_elem<QF>(acc[r][ct][g4 * 4 + 3], gs.x, ce)};
           *reinterpret_cast<float4*>(o + g4 * 8 + (lane >> 5) * 4) = v;
         }
       }

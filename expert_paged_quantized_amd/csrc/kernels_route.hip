@@ -20,12 +20,72 @@ namespace strata {
 // from +0; the 64 lane partials are then folded with offsets 32, 16, 8, 4, 2,
 // 1 (p[L] += p[L + o]) and lane 0 holds the logit; the bias is added last.
 // That order is part of the layer's definition so that the top-k decision is
-// reproducible bit for bit.  When x16 is given (int4 layers, whose expert
-// GEMMs run in fp16) the waves of the first expert block also write the fp16
-// copy of their token rows (bf16 -> fp16 is exact in the fp16 range).
+// reproducible bit for bit.
+//
+// When x16 is given (int4 and NVFP4 layers, whose expert GEMMs take fp16
+// operands) the waves of the first expert block also write each token's row
+// scaled into the fp16 range: x * 2^-e with e = floor(log2 max|x|) - 14, so
+// the row's largest magnitude lands in [2^14, 2^15) whatever the bf16 input
+// (bf16 reaches 2^128, fp16 only 65504), and e goes to xexp[t] for the GEMM
+// epilogues to undo in fp32.  The scaling is exact except for elements below
+// 2^-32 of the row's largest, which round to fp16's 2^-24 grid.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Running max of the magnitudes of a word of two bf16 values, compared as
+// their 15-bit magnitude patterns (for non-negative floats the bit order is
+// the numeric order).
+__device__ __forceinline__ uint32_t amax_bits(uint32_t am, uint32_t w) {
+  return max(am, max(w & 0x7fffu, (w >> 16) & 0x7fffu));
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+// floor(log2 of the magnitude with bf16 bits `am`) - 14; 0 for a zero row.
+// Exponent field 0 is a subnormal m * 2^-133.
+__device__ __forceinline__ int token_exponent(uint32_t am) {
+  if (am == 0) return 0;
+  const int ef = (int)(am >> 7);
+  const int fl = ef ? ef - 127 : (31 - __clz(am)) - 133;
+  return fl - 14;
+}
+// Two bf16 values times 2^ne (exact in fp32), rounded to fp16 (nearest-even).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2_scaled(uint32_t w, int ne) {
+  const _Float16 lo = (_Float16)__builtin_amdgcn_ldexpf(bf16_lo(w), ne);
+  const _Float16 hi = (_Float16)__builtin_amdgcn_ldexpf(bf16_hi(w), ne);
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+// Second pass of the waves that write the fp16 copy: the scaled rows of
+// tokens t0 .. t0 + NT - 1 (< T) from their running magnitude maxima.
+template <int NT>
+__device__ __forceinline__ void write_scaled_rows(const uint16_t* __restrict__ x, uint16_t* __restrict__ x16,
+                                                  int32_t* __restrict__ xexp, const uint32_t (&am)[NT], int t0,
+                                                  int T, int H, int lane) {
+  int ex[NT];
+#pragma unroll
+  for (int a = 0; a < NT; ++a) ex[a] = token_exponent(wave_max(am[a]));
+  const int C = H >> 9;
+  for (int c = 0; c < C; ++c) {
+    const int off = (c * 64 + lane) * 8;
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+      if (t0 + a >= T) continue;
+      const uint4 xv = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + a) * H + off);
+      uint4 hv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) (&hv.x)[q] = bf16x2_to_f16x2_scaled((&xv.x)[q], -ex[a]);
+      *reinterpret_cast<uint4*>(x16 + (size_t)(t0 + a) * H + off) = hv;
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int a = 0; a < NT; ++a)
+      if (t0 + a < T) xexp[t0 + a] = ex[a];
+  }
+}
 
 // p[L] += p[L + o] for o = 32, 16 (cross-row lane permutes) then 8, 4, 2, 1
 // (DPP row shifts inside 16-lane rows); lane 0 ends with the canonical sum.
@@ -49,18 +109,23 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ wr,
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ logits,
-                                                            uint16_t* __restrict__ x16, int T, int E,
+                                                            uint16_t* __restrict__ x16,
+                                                            int32_t* __restrict__ xexp, int T, int E,
                                                             int H) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int neb = (E + TE - 1) / TE;
   const int t0 = (wave / neb) * TT, e0 = (wave % neb) * TE;
   if (t0 >= T) return;
+  const bool copy = x16 && e0 == 0;  // this wave writes the scaled fp16 rows
+  uint32_t am[TT];
   float acc[TT][TE];
 #pragma unroll
-  for (int a = 0; a < TT; ++a)
+  for (int a = 0; a < TT; ++a) {
+    am[a] = 0;
 #pragma unroll
     for (int b = 0; b < TE; ++b) acc[a][b] = 0.0f;
+  }
   const int C = H >> 9;
   for (int c = 0; c < C; ++c) {
     const int off = (c * 64 + lane) * 8;
@@ -75,21 +140,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
       const int e = min(e0 + b, E - 1);
       wv[b] = *reinterpret_cast<const uint4*>(wr + (size_t)e * H + off);
     }
-    if (x16 && e0 == 0) {
+    if (copy) {
 #pragma unroll
-      for (int a = 0; a < TT; ++a) {
-        if (t0 + a < T) {
-          uint4 hv;
+      for (int a = 0; a < TT; ++a)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t w = (&xv[a].x)[q];
-            const _Float16 lo = (_Float16)bf16_lo(w), hi = (_Float16)bf16_hi(w);
-            (&hv.x)[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-          }
-          *reinterpret_cast<uint4*>(x16 + (size_t)(t0 + a) * H + off) = hv;
-        }
-      }
+        for (int q = 0; q < 4; ++q) am[a] = amax_bits(am[a], (&xv[a].x)[q]);
     }
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
@@ -119,6 +174,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
         if (t < T && e < E) logits[(size_t)t * E + e] = bias ? acc[a][b] + bias[e] : acc[a][b];
       }
   }
+  if (copy) write_scaled_rows<TT>(x, x16, xexp, am, t0, T, H, lane);
 }
 
 
@@ -136,7 +192,8 @@ __global__ __launch_bounds__(256) void router_block_kernel(const uint16_t* __res
                                                           const uint16_t* __restrict__ wr,
                                                           const float* __restrict__ bias,
                                                           float* __restrict__ logits,
-                                                          uint16_t* __restrict__ x16, int T, int E,
+                                                          uint16_t* __restrict__ x16,
+                                                          int32_t* __restrict__ xexp, int T, int E,
                                                           int H) {
   __shared__ __attribute__((aligned(16))) float red[4][64 * kRbPitch];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -144,11 +201,15 @@ __global__ __launch_bounds__(256) void router_block_kernel(const uint16_t* __res
   const int neb = (E + kRbTE - 1) / kRbTE;
   const int t0 = (wave / neb) * kRbTT, e0 = (wave % neb) * kRbTE;
   const bool active = t0 < T;
+  const bool copy = active && x16 && e0 == 0;  // this wave writes the scaled fp16 rows
+  uint32_t am[kRbTT];
   float acc[kRbTT][kRbTE];
 #pragma unroll
-  for (int a = 0; a < kRbTT; ++a)
+  for (int a = 0; a < kRbTT; ++a) {
+    am[a] = 0;
 #pragma unroll
     for (int b = 0; b < kRbTE; ++b) acc[a][b] = 0.0f;
+  }
   const int C = H >> 9;
   for (int c = 0; c < C && active; ++c) {
     const int off = (c * 64 + lane) * 8;
@@ -159,21 +220,11 @@ __global__ __launch_bounds__(256) void router_block_kernel(const uint16_t* __res
 #pragma unroll
     for (int b = 0; b < kRbTE; ++b)
       wv[b] = *reinterpret_cast<const uint4*>(wr + (size_t)min(e0 + b, E - 1) * H + off);
-    if (x16 && e0 == 0) {
+    if (copy) {
 #pragma unroll
-      for (int a = 0; a < kRbTT; ++a) {
-        if (t0 + a < T) {
-          uint4 hv;
+      for (int a = 0; a < kRbTT; ++a)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t wd = (&xv[a].x)[q];
-            const _Float16 lo = (_Float16)bf16_lo(wd), hi = (_Float16)bf16_hi(wd);
-            (&hv.x)[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-          }
-          *reinterpret_cast<uint4*>(x16 + (size_t)(t0 + a) * H + off) = hv;
-        }
-      }
+        for (int q = 0; q < 4; ++q) am[a] = amax_bits(am[a], (&xv[a].x)[q]);
     }
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
@@ -214,6 +265,7 @@ __global__ __launch_bounds__(256) void router_block_kernel(const uint16_t* __res
     for (int i = 0; i < o; ++i) q[i] = q[i] + q[i + o];
   const int t = t0 + lane / kRbTE, e = e0 + lane % kRbTE;
   if (active && t < T && e < E) logits[(size_t)t * E + e] = bias ? q[0] + bias[e] : q[0];
+  if (copy) write_scaled_rows<kRbTT>(x, x16, xexp, am, t0, T, H, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -564,15 +616,17 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
-                         uint16_t* x16, int T, int E, int H, hipStream_t s) {
+                         uint16_t* x16, int32_t* xexp, int T, int E, int H, hipStream_t s) {
   // 8 x 8 blocks when they still give the GPU thousands of waves, else one
   // logit per wave (small T or few experts)
   const int blocked_waves = ((T + kRbTT - 1) / kRbTT) * ((E + kRbTE - 1) / kRbTE);
   if (blocked_waves >= 2048) {
-    launch_k(router_block_kernel, dim3((blocked_waves + 3) / 4), dim3(256), 0, s, x, wr, bias, logits, x16, T, E, H);
+    launch_k(router_block_kernel, dim3((blocked_waves + 3) / 4), dim3(256), 0, s, x, wr, bias, logits, x16,
+             xexp, T, E, H);
   } else {
     const int waves = T * E;
-    launch_k(router_logits_kernel<1, 1>, dim3((waves + 3) / 4), dim3(256), 0, s, x, wr, bias, logits, x16, T, E, H);
+    launch_k(router_logits_kernel<1, 1>, dim3((waves + 3) / 4), dim3(256), 0, s, x, wr, bias, logits, x16,
+             xexp, T, E, H);
   }
   return hipGetLastError();
 }

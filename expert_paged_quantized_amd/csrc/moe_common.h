@@ -40,7 +40,8 @@ struct Tile {
 //   codes: 1024 B per tile, lane l holds tile row l%32, inputs 32*(l/32)..+31;
 //   scales, per row tile and scale block (a k-block, or a pair of k-blocks for
 //   int4 group-128: block index kb >> sshift):
-//     int4  128 B (u32 per row: bf16 scale | bf16 bias << 16),
+//     int4  128 B (u32 per row: fp16 scale | fp16 bias << 16: the bf16 values
+//           times 2^-c of their matrix, exactly; same bytes, re-encoded once),
 //     MXFP4  64 B (E8M0 byte per (half, row)),
 //     NVFP4 128 B (two E4M3 bytes per (half, row): its two 16-input blocks);
 //   gscale (NVFP4 only): fp32 matrix scales of gate, up, down (12 B).
@@ -64,7 +65,9 @@ struct RecordLayout {
 
 // Arguments of one grouped-GEMM launch (gate+up or down).
 struct GemmArgs {
-  const void* act;           // gate+up: x bf16 [T, H]; down: h [R, F] (f16 int4, bf16 MXFP4)
+  const void* act;           // gate+up: x [T, H] (MXFP4: bf16 as given; int4, NVFP4:
+                             // fp16 x * 2^-xexp[t]); down: h [R, F] (bf16 MXFP4;
+                             // int4, NVFP4: fp16 scaled as wexp says)
   const int32_t* gather;     // gate+up: perm (row -> token); down: nullptr (row -> row)
   const Tile* tiles;
   const int32_t* n_tiles_dev;  // device-side tile count, or nullptr to use n_tiles
@@ -81,7 +84,16 @@ struct GemmArgs {
   int32_t ksplit;            // prefill down: K is cut into ksplit equal ranges,
                              // range ks writes its partial sums to out + ks * split_stride
   int64_t split_stride;      // floats between partial-sum planes
+  // Power-of-two rescaling of the fp16 formats (int4, NVFP4; unused for
+  // MXFP4, whose bf16 operands already have the fp32 exponent range):
+  const int32_t* tok_of_row;  // row of the permuted space -> token (perm)
+  const int32_t* xexp;        // per token: x reached the GEMM as x * 2^-xexp[t]
+  const int32_t* wexp;        // per expert (E + 1 for the shared one) 4 exponents:
+                              // kWexpGate, kWexpUp, kWexpDown (fp16 weights hold
+                              // w * 2^-c), kWexpH (h row of token t holds
+                              // h * 2^-(2 xexp[t] + c))
 };
+enum WexpIndex : int { kWexpGate = 0, kWexpUp = 1, kWexpDown = 2, kWexpH = 3, kWexpCount = 4 };
 
 // Expert records paged from the pinned host store into device slots by the
 // page-in kernel, which reads the store through its device mapping: one

@@ -23,6 +23,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <chrono>
 #include <cstdio>
 #include <string>
@@ -34,8 +35,8 @@
 #include "residency.h"
 
 namespace strata {
-hipError_t launch_router(const uint16_t*, const uint16_t*, const float*, float*, uint16_t*, int, int,
-                         int, hipStream_t);
+hipError_t launch_router(const uint16_t*, const uint16_t*, const float*, float*, uint16_t*, int32_t*, int,
+                         int, int, hipStream_t);
 hipError_t launch_route(const float*, int, int, int, int, int, int, int, int32_t*, float*, int32_t*,
                         int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, Tile*, int32_t*,
                         unsigned long long*, hipStream_t);
@@ -126,7 +127,10 @@ struct strata_moe {
   unsigned long long* d_distinct = nullptr;
   void* d_h = nullptr;
   float* d_o = nullptr;
-  uint16_t* d_x16 = nullptr;  // fp16 copy of x (int4 and NVFP4 layers)
+  uint16_t* d_x16 = nullptr;   // fp16 copy of x scaled per token (int4 and NVFP4 layers)
+  int32_t* d_xexp = nullptr;   // per token: the copy holds x * 2^-xexp
+  int32_t* d_wexp = nullptr;   // per expert (+ shared): kWexpCount rescaling exponents
+  std::vector<int32_t> wexp;   // host copy of the same
   uint64_t ws_bytes = 0;
 
   int32_t* h_counts = nullptr;  // pinned
@@ -159,13 +163,63 @@ struct strata_moe {
 // ---------------------------------------------------------------------------
 // validation / admission (pure host; runs before any HIP call)
 // ---------------------------------------------------------------------------
-static bool fp16_exact(uint16_t bf) {
+static float bf16_float(uint16_t bf) {
   const uint32_t u = uint32_t(bf) << 16;
   float f;
   memcpy(&f, &u, 4);
-  if (!(f == f) || f == __builtin_inff() || f == -__builtin_inff()) return false;
-  const _Float16 h = (_Float16)f;
-  return (float)h == f;
+  return f;
+}
+
+// OCP FP8 E4M3 byte (NaN bytes refused at admission): sign bit 7, exponent
+// bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 is m * 2^-9.
+static double e4m3_float(uint8_t byte) {
+  const int ex = (byte >> 3) & 15, man = byte & 7;
+  const double mag = ex ? std::ldexp(1.0 + man / 8.0, ex - 7) : std::ldexp((double)man, -9);
+  return (byte & 0x80) ? -mag : mag;
+}
+
+// int4 scale and bias re-encoding.  The kernels compute int4 layers in fp16,
+// whose exponent range (2^-24 .. 65504) is far narrower than bf16's, so every
+// matrix (gate, up or down of one expert) gets one power of two 2^-c: its
+// scales and biases are stored as the fp16 numbers s * 2^-c, b * 2^-c, which
+// must be exact (lowest set bit at or above 2^-24), and no decoded weight
+// s' q + b' may exceed 2^15 in magnitude (15 |s'| + |b'| <= 2^15).  Of the
+// exponents that satisfy both, the smallest is taken: it puts the largest
+// decoded weight in (2^14, 2^15], as far above fp16's subnormal range as the
+// matrix allows.  A matrix whose values span more than fp16 holds exactly
+// under one c is refused (E_UNSUPPORTED), a NaN or infinite scale or bias
+// fails admission (E_BAD_SCALE).  The epilogues multiply the results by
+// 2^c again, so the weights the layer computes with are the checkpoint's.
+static strata_status int4_matrix_exponent(const uint16_t* s, const uint16_t* b, size_t n, const char* name,
+                                          int* c_out) {
+  int c_max = 1 << 20;  // every value's lowest set bit, + 24
+  double m = 0.0;       // max 15 |s| + |b|
+  for (size_t i = 0; i < n; ++i) {
+    for (uint16_t v : {s[i], b[i]}) {
+      const int ef = (v >> 7) & 0xff, man = v & 0x7f;
+      if (ef == 255) return fail(STRATA_E_BAD_SCALE, std::string(name) + ": int4 scale or bias is not a finite number");
+      if (ef == 0 && man == 0) continue;
+      // value = sig * 2^(q0): normal sig = 1.man (8 bits) at q0 = ef - 134,
+      // subnormal sig = man at q0 = -133
+      const int sig = ef ? (man | 0x80) : man;
+      const int q0 = ef ? ef - 134 : -133;
+      c_max = std::min(c_max, q0 + __builtin_ctz(sig) + 24);
+    }
+    m = std::max(m, 15.0 * std::fabs((double)bf16_float(s[i])) + std::fabs((double)bf16_float(b[i])));
+  }
+  if (m == 0.0) {
+    *c_out = 0;
+    return STRATA_OK;
+  }
+  int e;
+  const double f = std::frexp(m, &e);  // m = f 2^e, f in [0.5, 1)
+  const int c_min = (f == 0.5 ? e - 1 : e) - 15;  // smallest c with m <= 2^(15 + c)
+  if (c_min > c_max)
+    return fail(STRATA_E_UNSUPPORTED, std::string(name) +
+                                          ": int4 scales and biases span more than fp16 holds exactly under one "
+                                          "power-of-two rescaling (2^-24 .. 2^15)");
+  *c_out = c_min;
+  return STRATA_OK;
 }
 
 // What the host needs to know about a weight format.
@@ -253,13 +307,13 @@ static strata_status validate(const strata_moe_desc* d) {
   const size_t H = d->hidden, F = d->ffn;
   auto admit = [&](const strata_qmat& m, size_t n_exp, size_t rows, size_t cols, const char* name) -> strata_status {
     if (int4) {
-      const size_t n = n_exp * rows * (cols / fi.group);
-      const uint16_t* s = (const uint16_t*)m.scales;
-      const uint16_t* b = (const uint16_t*)m.biases;
-      for (size_t i = 0; i < n; ++i)
-        if (!fp16_exact(s[i]) || !fp16_exact(b[i]))
-          return fail(STRATA_E_UNSUPPORTED, std::string(name) +
-                                                ": int4 scale/bias not exactly representable in fp16");
+      const size_t n = rows * (cols / fi.group);  // per expert
+      for (size_t e = 0; e < n_exp; ++e) {
+        int c;
+        if (strata_status st2 = int4_matrix_exponent((const uint16_t*)m.scales + e * n,
+                                                     (const uint16_t*)m.biases + e * n, n, name, &c))
+          return st2;
+      }
     } else if (nvfp4) {
       const size_t n = n_exp * rows * (cols / 16);
       const uint8_t* s = (const uint8_t*)m.scales;
@@ -312,6 +366,7 @@ struct MatView {
   const uint8_t* scales;  // int4: bf16 [rows, cols/G]; MXFP4: u8 [rows, cols/32]; NVFP4: u8 [rows, cols/16]
   const uint8_t* biases;  // int4: bf16 [rows, cols/G]
   float gscale;           // NVFP4 matrix scale
+  int c = 0;              // int4: scales and biases are stored times 2^-c (fp16)
 };
 
 static MatView view(const strata_qmat& m, size_t e, size_t rows, size_t cols, const FormatInfo& fi) {
@@ -363,7 +418,13 @@ static void pack_matrix(uint8_t* codes_dst, uint8_t* scales_dst, int n_rt, int K
           uint16_t sc, b;
           memcpy(&sc, mv->scales + gi * 2, 2);
           memcpy(&b, mv->biases + gi * 2, 2);
-          const uint32_t u = uint32_t(sc) | (uint32_t(b) << 16);
+          // exact by admission (int4_matrix_exponent)
+          const _Float16 s16 = (_Float16)std::ldexp(bf16_float(sc), -mv->c);
+          const _Float16 b16 = (_Float16)std::ldexp(bf16_float(b), -mv->c);
+          uint16_t sbits, bbits;
+          memcpy(&sbits, &s16, 2);
+          memcpy(&bbits, &b16, 2);
+          const uint32_t u = uint32_t(sbits) | (uint32_t(bbits) << 16);
           memcpy(sd + r * 4, &u, 4);
         }
       } else if (fi.kq == Q_NVFP4) {
@@ -391,10 +452,71 @@ static void pack_matrix(uint8_t* codes_dst, uint8_t* scales_dst, int n_rt, int K
   }
 }
 
+// Sum of |w| along each row of one matrix, the largest over its rows (fp64;
+// int4 and NVFP4, the formats the kernels compute in fp16).  Bounds the
+// matrix's output: |W x| <= this * max|x|.
+static double max_row_l1(const MatView& v, int rows, int cols, const FormatInfo& fi) {
+  static const double e2m1_mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  double best = 0.0;
+  const int G = fi.group, ng = cols / G;
+  for (int r = 0; r < rows; ++r) {
+    const uint8_t* c = v.codes + (size_t)r * (cols / 2);
+    double sum = 0.0;
+    for (int g = 0; g < ng; ++g) {
+      double tab[16];
+      if (fi.affine) {
+        uint16_t sb, bb;
+        memcpy(&sb, v.scales + ((size_t)r * ng + g) * 2, 2);
+        memcpy(&bb, v.biases + ((size_t)r * ng + g) * 2, 2);
+        const double sv = bf16_float(sb), bv = bf16_float(bb);
+        for (int q = 0; q < 16; ++q) tab[q] = std::fabs(sv * q + bv);
+      } else {  // NVFP4: |e2m1| * |E4M3 block scale| * matrix scale
+        const double sc = std::fabs(e4m3_float(v.scales[(size_t)r * ng + g])) * v.gscale;
+        for (int q = 0; q < 16; ++q) tab[q] = e2m1_mag[q & 7] * sc;
+      }
+      for (int k = g * G; k < (g + 1) * G; k += 2) {
+        const uint8_t byte = c[k / 2];
+        sum += tab[byte & 15] + tab[byte >> 4];
+      }
+    }
+    best = std::max(best, sum);
+  }
+  return best;
+}
+
+// Rescaling exponents of one expert (kWexp* order).  The h exponent c_h makes
+// the stored h row of token t, h * 2^-(2 xexp[t] + c_h), stay below 2^14:
+// the fp16 x row is below 2^15, so |g| <= 2^(xexp[t] + 15) A_g and likewise
+// |u|, and |h| = |silu(g) u| <= |g| |u| (A = largest row sum of |w|).
+static void expert_exponents(const strata_qmat& g, const strata_qmat& u, const strata_qmat& d, size_t e, int H,
+                             int F, const FormatInfo& fi, int32_t* out) {
+  for (int i = 0; i < kWexpCount; ++i) out[i] = 0;
+  if (!fi.f16) return;  // MXFP4: bf16 operands, nothing to rescale
+  if (fi.affine) {
+    const size_t ng = H / fi.group, nd = F / fi.group;
+    int c;
+    (void)int4_matrix_exponent((const uint16_t*)g.scales + e * F * ng, (const uint16_t*)g.biases + e * F * ng,
+                               F * ng, "gate", &c);  // admitted: cannot fail
+    out[kWexpGate] = c;
+    (void)int4_matrix_exponent((const uint16_t*)u.scales + e * F * ng, (const uint16_t*)u.biases + e * F * ng,
+                               F * ng, "up", &c);
+    out[kWexpUp] = c;
+    (void)int4_matrix_exponent((const uint16_t*)d.scales + e * H * nd, (const uint16_t*)d.biases + e * H * nd,
+                               H * nd, "down", &c);
+    out[kWexpDown] = c;
+  }
+  const double ag = max_row_l1(view(g, e, F, H, fi), F, H, fi);
+  const double au = max_row_l1(view(u, e, F, H, fi), F, H, fi);
+  if (ag > 0.0 && au > 0.0) out[kWexpH] = (int)std::ceil(std::log2(ag) + std::log2(au)) + 16;
+}
+
 static void pack_expert(uint8_t* rec, const RecordLayout& lay, const strata_qmat& g,
                         const strata_qmat& u, const strata_qmat& d, size_t e, int H, int F,
-                        const FormatInfo& fi) {
-  const MatView vg = view(g, e, F, H, fi), vu = view(u, e, F, H, fi), vd = view(d, e, H, F, fi);
+                        const FormatInfo& fi, const int32_t* wexp) {
+  MatView vg = view(g, e, F, H, fi), vu = view(u, e, F, H, fi), vd = view(d, e, H, F, fi);
+  vg.c = wexp[kWexpGate];
+  vu.c = wexp[kWexpUp];
+  vd.c = wexp[kWexpDown];
   // w1: tile rt = gate rows 16rt..+15 then up rows 16rt..+15
   pack_matrix(rec + lay.w1_codes, rec + lay.w1_scales, F / 16, H, fi,
               [&](int rt, int r, const MatView*& mv, int& row) {
@@ -437,7 +559,7 @@ static void release(strata_moe* h) {
   void* dev[] = {h->d_pool, h->d_shared, h->d_router_w, h->d_router_bias, h->d_slot_ptr,
                  h->d_logits, h->d_idx, h->d_w, h->d_counts, h->d_offsets, h->d_perm, h->d_pos,
                  h->d_tiles_dev, h->d_tiles_host, h->d_ntiles, h->d_distinct, h->d_h, h->d_o,
-                 h->d_x16, h->d_rank, h->d_hist};
+                 h->d_x16, h->d_xexp, h->d_wexp, h->d_rank, h->d_hist};
   for (void* p : dev)
     if (p) (void)hipFree(p);
   if (h->host_store) (void)hipHostFree(h->host_store);
@@ -512,27 +634,36 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
     HIP_CHECK(hipHostGetDevicePointer(&dp, h->host_store, 0));
     h->host_dev = static_cast<const uint8_t*>(dp);
   }
+  // rescaling exponents of every expert (fp16 formats), then the prepack
+  h->wexp.assign(size_t(h->E + 1) * kWexpCount, 0);
   {
     unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
     std::vector<std::thread> th;
     for (unsigned t = 0; t < nth; ++t)
       th.emplace_back([&, t]() {
-        for (int e = t; e < h->E; e += nth)
-          pack_expert(h->host_store + h->slot_stride * e, h->lay, d->gate, d->up, d->down, e, h->H, h->F, fi);
+        for (int e = t; e < h->E; e += nth) {
+          int32_t* we = h->wexp.data() + size_t(e) * kWexpCount;
+          expert_exponents(d->gate, d->up, d->down, e, h->H, h->F, fi, we);
+          pack_expert(h->host_store + h->slot_stride * e, h->lay, d->gate, d->up, d->down, e, h->H, h->F, fi, we);
+        }
       });
     for (auto& t : th) t.join();
   }
+  if (h->S) expert_exponents(d->sh_gate, d->sh_up, d->sh_down, 0, h->H, h->F, fi, h->wexp.data() + size_t(h->E) * kWexpCount);
 
   // device: slot pool, shared expert, router, slot pointer table
   if ((st = dev_alloc(&h->d_pool, h->slot_stride * h->budget))) return st;
   if (h->S) {
     if ((st = dev_alloc(&h->d_shared, h->slot_stride))) return st;
     std::vector<uint8_t> tmp(rec);
-    pack_expert(tmp.data(), h->lay, d->sh_gate, d->sh_up, d->sh_down, 0, h->H, h->F, fi);
+    pack_expert(tmp.data(), h->lay, d->sh_gate, d->sh_up, d->sh_down, 0, h->H, h->F, fi,
+                h->wexp.data() + size_t(h->E) * kWexpCount);
     HIP_CHECK(hipMemcpy(h->d_shared, tmp.data(), rec, hipMemcpyHostToDevice));
   }
   if ((st = dev_alloc(&h->d_router_w, size_t(h->E) * h->H * 2))) return st;
   HIP_CHECK(hipMemcpy(h->d_router_w, d->router_w, size_t(h->E) * h->H * 2, hipMemcpyHostToDevice));
+  if ((st = dev_alloc(&h->d_wexp, h->wexp.size() * 4))) return st;
+  HIP_CHECK(hipMemcpy(h->d_wexp, h->wexp.data(), h->wexp.size() * 4, hipMemcpyHostToDevice));
   if (d->router_bias) {
     if ((st = dev_alloc(&h->d_router_bias, size_t(h->E) * 4))) return st;
     HIP_CHECK(hipMemcpy(h->d_router_bias, d->router_bias, size_t(h->E) * 4, hipMemcpyHostToDevice));
@@ -562,7 +693,7 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
       (st = walloc(&h->d_distinct, 64)) || (st = walloc(&h->d_h, h->max_rows * h->F * 2)) ||
       (st = walloc(&h->d_o, h->max_rows * h->H * 4 * h->ksplit)))
     return st;
-  if (fi.f16 && (st = walloc(&h->d_x16, T * h->H * 2))) return st;
+  if (fi.f16 && ((st = walloc(&h->d_x16, T * h->H * 2)) || (st = walloc(&h->d_xexp, T * 4)))) return st;
   h->ws_bytes = ws;
   HIP_CHECK(hipMemset(h->d_distinct, 0, 64));
   if ((st = host_alloc(&h->h_counts, size_t(h->E) * 4))) return st;
@@ -650,6 +781,9 @@ static GemmArgs gemm_args(strata_moe* h, bool gate_up, const void* x, const Tile
   a.off_gscale = h->quant == Q_NVFP4 ? h->lay.gscale + (gate_up ? 0 : 8) : -1;
   a.ksplit = 1;
   a.split_stride = 0;
+  a.tok_of_row = h->d_perm;
+  a.xexp = h->d_xexp;
+  a.wexp = h->d_wexp;
   return a;
 }
 
@@ -780,8 +914,8 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
   if (h->fwd_recorded && !capturing) HIP_CHECK(hipStreamWaitEvent(s, h->ev_fwd_done, 0));
 
   HIP_CHECK(timed(h, STRATA_K_ROUTER, s, [&]() {
-    return launch_router((const uint16_t*)x, h->d_router_w, h->d_router_bias, h->d_logits, h->d_x16, T,
-                         h->E, h->H, s);
+    return launch_router((const uint16_t*)x, h->d_router_w, h->d_router_bias, h->d_logits, h->d_x16, h->d_xexp,
+                         T, h->E, h->H, s);
   }));
   const int tile_rows = decode ? (1 << 30) : kPrefillTM;
   HIP_CHECK(timed(h, STRATA_K_GROUP, s, [&]() {
@@ -1067,7 +1201,7 @@ strata_status strata_moe_memory(const strata_moe* h, strata_memory_info* out) {
   out->slot_pool = uint64_t(h->slot_stride) * h->budget;
   out->shared = h->S ? h->slot_stride : 0;
   out->router = uint64_t(h->E) * h->H * 2 + (h->d_router_bias ? uint64_t(h->E) * 4 : 0) +
-                uint64_t(sizeof(uint8_t*)) * (h->budget + 1);
+                uint64_t(sizeof(uint8_t*)) * (h->budget + 1) + uint64_t(h->wexp.size()) * 4;
   out->workspace = h->ws_bytes;
   out->device_total = out->slot_pool + out->shared + out->router + out->workspace;
   out->host_store = uint64_t(h->slot_stride) * h->E;

@@ -50,7 +50,8 @@ typedef enum {
   STRATA_OK = 0,
   STRATA_E_INVALID = 1,     /* null pointer, size out of range, bad enum       */
   STRATA_E_UNSUPPORTED = 2, /* shape or value the kernels cannot take exactly  */
-  STRATA_E_BAD_SCALE = 3,   /* admission: MXFP4 E8M0 byte 0 or 255, NVFP4 E4M3 NaN byte or matrix scale not finite and > 0 */
+  STRATA_E_BAD_SCALE = 3,   /* admission: MXFP4 E8M0 byte 0 or 255, NVFP4 E4M3 NaN byte or matrix scale
+                             * not finite and > 0, int4 scale or bias NaN or infinite */
   STRATA_E_NOMEM = 4,       /* host-pinned or device allocation failed         */
   STRATA_E_HIP = 5,         /* a HIP runtime call failed                       */
   STRATA_E_POISONED = 6     /* an earlier HIP failure left the handle unusable */
@@ -157,8 +158,12 @@ typedef struct {
 
 /* Creates a layer.  Validates the descriptor, admits the weights (every MXFP4
  * scale byte must be in 1..254, every NVFP4 E4M3 byte a number and every
- * NVFP4 matrix scale finite and > 0, every int4 scale and bias exactly
- * representable in fp16, which the kernels compute in), copies every routed
+ * NVFP4 matrix scale finite and > 0, every int4 scale and bias a finite
+ * bf16 number; int4 layers run in fp16, so each matrix's scales and biases
+ * are stored times one power of two that makes them exact fp16 numbers, and
+ * a matrix whose values span more than fp16 holds exactly under one such
+ * power of two, about 2^-24 .. 2^15 relative to each other, is refused with
+ * E_UNSUPPORTED), copies every routed
  * expert once into a library-owned pinned host store (a byte permutation into
  * kernel tile order: same byte count, no wider copy), allocates the HBM slot
  * pool (expert_budget slots), the resident shared expert, the router and a
@@ -188,7 +193,11 @@ typedef struct {
 } strata_route_dbg;
 
 /* One forward of the layer on T tokens.
- *   x      device, bf16 bits [T, H] row-major, caller-owned, read only
+ *   x      device, bf16 bits [T, H] row-major, caller-owned, read only; any
+ *          finite bf16 values (int4 and NVFP4 layers compute in fp16 and
+ *          rescale every token row, and the SwiGLU output, by powers of two,
+ *          so neither overflows nor flushes; elements below 2^-32 of their
+ *          row's largest magnitude round to that row's fp16 grid)
  *   y      device, bf16 bits [T, H] row-major, caller-owned, written (RNE)
  *   stream hipStream_t to enqueue on (NULL = the null stream)
  *   dbg    optional routing outputs (NULL = none)

@@ -1,0 +1,153 @@
+"""Range safety of the layer through the C ABI: activations, weights and
+SwiGLU outputs far outside fp16's range (the int4 and NVFP4 paths compute in
+fp16 with power-of-two rescaling) must give the oracle's y, never an
+overflow or a flush to zero under STRATA_OK.  The ro99/strata README's list
+of enforced rules asks that an exact mode either completes or fails; here it
+completes.
+
+Every variant runs the decode kernels (T = 1, 3 on the dot-product kernel,
+T = 6 on the MFMA decode kernel) and the prefill kernel (T = 40), all
+resident and with a budget (paged output must stay bitwise the resident
+output).  y is compared with the oracle relatively: rel-L2 <= 5e-3 as
+everywhere, and max |dy| <= 1% of max |y| (the absolute 2e-2 bound of the
+other tests taken at their |y| <= 2 scale).
+"""
+import copy
+
+import numpy as np
+import pytest
+
+from oracle import moe as om
+from synth import CONFIGS, make_layer, make_tokens
+
+from gpu_util import Y_REL_L2, assert_routing_equal, to_dev, y_bits, y_to_f64
+
+pytestmark = pytest.mark.gpu
+
+LAYERS = {
+    "int4_g64": CONFIGS["qwen3_30b_a3b"].scaled(hidden=1024, ffn=256, num_experts=16, top_k=4,
+                                                 budget_frac=0.25),
+    "int4_g128_shared": CONFIGS["e256_int4g128"].scaled(hidden=1024, ffn=256, num_experts=16, top_k=4,
+                                                         num_shared=1, budget_frac=0.25),
+    "nvfp4_shared": CONFIGS["e256_nvfp4"].scaled(hidden=1024, ffn=256, num_experts=16, top_k=4,
+                                                 budget_frac=0.25),
+    "mxfp4_shared": CONFIGS["e512_mxfp4"].scaled(hidden=1024, ffn=256, num_experts=16, top_k=4,
+                                                 budget_frac=0.25),
+}
+TS = (1, 3, 6, 40)
+
+
+def bf16_times_pow2(bits, k):
+    """bf16 bit patterns times 2^k: an exponent shift, exact while the values
+    stay normal (asserted)."""
+    b = np.asarray(bits).astype(np.int32)
+    e = (b >> 7) & 0xFF
+    nz = e > 0
+    assert np.all(e[nz] + k > 0) and np.all(e[nz] + k < 255), "shift leaves the normal range"
+    b[nz] += k << 7
+    return b.astype(np.uint16)
+
+
+def scale_matrix(quant, m, k):
+    """The packed matrix m (stacked) times 2^k, in its own format."""
+    if quant.startswith("int4"):
+        m.scales = bf16_times_pow2(m.scales, k)
+        m.biases = bf16_times_pow2(m.biases, k)
+    elif quant == "nvfp4_g16":
+        m.global_scale = (np.asarray(m.global_scale, dtype=np.float32) * np.float32(2.0 ** k)).astype(np.float32)
+    else:
+        e = m.scales.astype(np.int32) + k
+        assert e.min() >= 1 and e.max() <= 254
+        m.scales = e.astype(np.uint8)
+
+
+def variant(lw, kind):
+    """(weights, x exponent shift) of one range variant."""
+    out = copy.deepcopy(lw)
+    q = out.cfg.quant
+    if kind == "x_large":
+        return out, 15          # |x| up to about 1.3e5, above fp16's 65504
+    if kind == "x_tiny":
+        return out, -20         # |x| around 1e-6, below fp16's normal range
+    if kind == "h_large":       # gate and up times 2^8: |h| far above 65504
+        for name in ("gate", "up", "sh_gate", "sh_up"):
+            if getattr(out, name) is not None:
+                scale_matrix(q, getattr(out, name), 8)
+        return out, 0
+    if kind == "w_tiny":        # every weight times 2^-30 (int4: scales ~1e-12)
+        for name in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+            if getattr(out, name) is not None:
+                scale_matrix(q, getattr(out, name), -30)
+        return out, 0
+    if kind == "w_large":       # every weight times 2^20 (int4: scales ~1e4)
+        for name in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+            if getattr(out, name) is not None:
+                scale_matrix(q, getattr(out, name), 20)
+        return out, 0
+    raise ValueError(kind)
+
+
+def max_abs_h(lw, x_bits, ref):
+    """Largest |silu(g) u| over the routed (token, expert) pairs and the shared
+    expert, from the oracle's dequantised weights (fp64)."""
+    x = om.bf16_to_f64(x_bits)
+    cfg = lw.cfg
+    best = 0.0
+    mats = [(x[ref["perm"][ref["offsets"][e]:ref["offsets"][e + 1]]], lw.expert(int(e)))
+            for e in np.nonzero(ref["counts"])[0]]
+    if cfg.num_shared:
+        mats.append((x, lw.shared()))
+    for xr, (g, u, _) in mats:
+        h = om.silu(xr @ om.dequant_qmat(cfg.quant, g).T) * (xr @ om.dequant_qmat(cfg.quant, u).T)
+        best = max(best, float(np.abs(h).max()))
+    return best
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+_base = {}
+
+
+def _layer(name):
+    if name not in _base:
+        cfg = LAYERS[name]
+        _base[name] = make_layer(cfg, seed=cfg.seed + 70)
+    return _base[name]
+
+
+@pytest.mark.parametrize("kind", ["x_large", "x_tiny", "h_large", "w_tiny", "w_large"])
+@pytest.mark.parametrize("name", list(LAYERS))
+def test_out_of_fp16_range_matches_oracle(torch_cuda, name, kind):
+    import expert_paged_quantized_amd as epq
+    lw, xshift = variant(_layer(name), kind)
+    cfg = lw.cfg
+    res = epq.MoELayer.from_weights(lw, budget=cfg.num_experts, max_tokens=64)
+    paged = epq.MoELayer.from_weights(lw, budget=cfg.budget, max_tokens=64)
+    for i, T in enumerate(TS):
+        print(f"[range] {name} {kind} T={T}", flush=True)
+        x = bf16_times_pow2(make_tokens(cfg, T, step=i, seed=cfg.seed + 70), xshift)
+        xd = to_dev(x)
+        y, dbg = res.forward(xd, dbg=True)
+        ref = om.moe_forward(lw, x)
+        assert_routing_equal(dbg, ref, T, cfg.num_experts, cfg.top_k, f"{name} {kind} T={T}")
+        yg = y_to_f64(y)
+        assert np.all(np.isfinite(yg)), f"{name} {kind} T={T}: non-finite y"
+        yr = ref["y"]
+        rel = np.linalg.norm(yg - yr) / np.linalg.norm(yr)
+        dmax = np.abs(yg - yr).max()
+        assert rel <= Y_REL_L2 and dmax <= 1e-2 * np.abs(yr).max(), \
+            f"{name} {kind} T={T}: relL2={rel:.3g} max|dy|={dmax:.3g} max|y|={np.abs(yr).max():.3g}"
+        if kind == "h_large" and i == len(TS) - 1:
+            assert max_abs_h(lw, x, ref) > 65504.0, "the variant did not push h past fp16"
+        if kind == "x_large":
+            assert np.abs(om.bf16_to_f64(x)).max() > 65504.0
+        y_p = paged.forward(xd)
+        assert np.array_equal(y_bits(y_p), y_bits(y)), f"{name} {kind} T={T}: paged != resident"
+    res.close()
+    paged.close()

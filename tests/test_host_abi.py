@@ -152,16 +152,61 @@ def test_e8m0_admission_refuses_0_and_255(tiny_fp4, bad, which):
         m.scales[...] = saved
 
 
-def test_int4_scales_must_be_exact_in_fp16(tiny_int4):
+def _bf16_times_pow2(bits, k):
+    """bf16 bit patterns times 2^k (exact for normal values that stay normal)."""
+    b = bits.astype(np.int32)
+    e = (b >> 7) & 0xFF
+    nz = e > 0
+    assert np.all(e[nz] + k > 0) and np.all(e[nz] + k < 255)
+    b[nz] += k << 7
+    return b.astype(np.uint16)
+
+
+@pytest.mark.parametrize("k", [-30, 20])
+def test_int4_scales_outside_the_fp16_range_are_admitted(tiny_int4, k):
+    """bf16 scales and biases far below or above fp16's range are stored with
+    one power-of-two rescaling per matrix, not refused."""
+    lw = tiny_int4
+    saved = [(m, m.scales.copy(), m.biases.copy()) for m in (lw.gate, lw.up, lw.down)]
+    try:
+        for m, s, b in saved:
+            m.scales[...] = _bf16_times_pow2(s, k)
+            m.biases[...] = _bf16_times_pow2(b, k)
+        d, keep = _desc_from(lw)
+        st, msg = _create_status(d)
+        # admission passes; without a GPU the first HIP call then fails
+        assert st in (_capi.OK, _capi.E_HIP), msg
+    finally:
+        for m, s, b in saved:
+            m.scales[...] = s
+            m.biases[...] = b
+
+
+def test_int4_scales_spanning_more_than_fp16_are_refused(tiny_int4):
     lw = tiny_int4
     saved = lw.up.scales.copy()
     try:
-        lw.up.scales.reshape(-1)[3] = 0x0081  # bf16 ~1.2e-38: no exact fp16 value
+        # bf16 ~1.2e-38 beside scales near 1e-2 in the same matrix: no single
+        # power of two brings both into fp16 exactly
+        lw.up.scales.reshape(-1)[3] = 0x0081
         d, keep = _desc_from(lw)
         st, msg = _create_status(d)
-        assert st == _capi.E_UNSUPPORTED and "fp16" in msg
+        assert st == _capi.E_UNSUPPORTED and "span" in msg and "up" in msg, msg
     finally:
         lw.up.scales[...] = saved
+
+
+@pytest.mark.parametrize("bad", [0x7FC0, 0x7F80, 0xFF80])
+def test_int4_nan_or_infinite_scale_fails_admission(tiny_int4, bad):
+    lw = tiny_int4
+    saved = lw.down.biases.copy()
+    try:
+        lw.down.biases.reshape(-1)[5] = bad
+        d, keep = _desc_from(lw)
+        st, msg = _create_status(d)
+        assert st == _capi.E_BAD_SCALE and "finite" in msg, msg
+    finally:
+        lw.down.biases[...] = saved
 
 
 # ----------------------------------------------------------------------------
