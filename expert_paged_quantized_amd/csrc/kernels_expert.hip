@@ -1080,9 +1080,10 @@ hipError_t launch_page_in(const PageBatch& b, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Combine: y[t] = sum_j w[t,j] * o[pos[t,j]] (j ascending) + o[shared row of t],
-// fp32, rounded to bf16 (nearest-even).  One workgroup per token.  With a
-// K-split prefill down GEMM each o row is the sum of its partial planes, in
-// plane order, before it is weighted.
+// fp32, rounded to bf16 (nearest-even).  One workgroup per (token, block of
+// 1024 columns); each thread owns 4 consecutive columns.  With a K-split
+// prefill down GEMM each o row is the sum of its partial planes, in plane
+// order, before it is weighted.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float4 o_row(const float* __restrict__ o, size_t at, int ksplit,
                                         int64_t stride) {

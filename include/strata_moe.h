@@ -17,10 +17,11 @@
  *     router, the shared experts and a cache of the most-used experts that
  *     adapts to the workload, host RAM holds every expert pinned; a 512-expert
  *     layer activates 10 routed experts plus 1 shared expert per token.
- *   - ro99/strata README (C++20/CUDA engine): list of enforced rules (never
- *     below four bits; routing semantics, expert count and top-k come from the
- *     checkpoint and never change silently; a predictor may only reorder work;
- *     exact mode completes or fails); precision paragraph (MXFP4 = two E2M1
+ *   - ro99/strata README (C++20/CUDA engine): its list of enforced rules
+ *     (weights stay at four bits or more; the router's arithmetic, the expert
+ *     count and k are the checkpoint's, unchanged; prediction may change the
+ *     order of work, not its numbers; a configuration that cannot be served
+ *     exactly is an error, not a cheaper substitute); precision paragraph (MXFP4 = two E2M1
  *     codes per byte and one E8M0 exponent per 32, read as stored with no
  *     wider copy; E8M0 bytes 0 and 255 fail admission at load); SM86 kernel
  *     paragraph (a prepack of the 4-bit weights into kernel operand order is a

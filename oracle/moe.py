@@ -9,9 +9,9 @@ Sources, cited by page title and section:
   E2M1 codes per byte with one E8M0 exponent per group of 32 and is read as
   such; an E8M0 byte is placed in a bf16 exponent field, so bytes 0 and 255
   (+0 and +inf there) are refused when the checkpoint is admitted.
-* Same README, list of enforced rules: routing semantics, expert count and
-  top-k come from the checkpoint; a predictor may reorder work but not change
-  it.
+* Same README, its list of enforced rules: the router's arithmetic, the expert
+  count and k are the checkpoint's; prediction changes the order of work only,
+  never its numbers.
 * "Strata, Explained" (Medium tutorial), section 2: a 512-expert layer runs
   10 routed experts plus 1 shared expert per token.
 

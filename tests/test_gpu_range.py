@@ -1,9 +1,9 @@
 """Range safety of the layer through the C ABI: activations, weights and
 SwiGLU outputs far outside fp16's range (the int4 and NVFP4 paths compute in
 fp16 with power-of-two rescaling) must give the oracle's y, never an
-overflow or a flush to zero under STRATA_OK.  The ro99/strata README's list
-of enforced rules asks that an exact mode either completes or fails; here it
-completes.
+overflow or a flush to zero under STRATA_OK (the ro99/strata README's list
+of enforced rules: a configuration that cannot be served exactly must be an
+error, never a silently different result; these are served).
 
 Every variant runs the decode kernels (T = 1, 3 on the dot-product kernel,
 T = 6 on the MFMA decode kernel) and the prefill kernel (T = 40), all
