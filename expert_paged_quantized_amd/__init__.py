@@ -91,6 +91,16 @@ class MoELayer:
     def forward(self, x, y=None, stream=None, dbg=False):
         """x: torch bf16 [T, H] on the layer's GPU.  Returns y (bf16 [T, H]) or,
         with dbg=True, (y, dict of routing tensors)."""
+        return self._forward(lib().strata_moe_forward, x, y, stream, dbg)
+
+    def forward_noalloc(self, x, y=None, stream=None, dbg=False):
+        """The same forward on the library's static device scratch
+        (strata_moe_forward_noalloc): no device allocation by the library.
+        Pass y (and the dbg tensors are allocated here by torch) if the
+        caller itself must not allocate."""
+        return self._forward(lib().strata_moe_forward_noalloc, x, y, stream, dbg)
+
+    def _forward(self, fn, x, y, stream, dbg):
         import torch
         if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != self.hidden:
             raise ValueError("x must be bf16 [T, hidden]")
@@ -114,10 +124,8 @@ class MoELayer:
             d = _capi.RouteDbg(out["logits"].data_ptr(), out["idx"].data_ptr(), out["w"].data_ptr(),
                                out["counts"].data_ptr(), out["offsets"].data_ptr(),
                                out["perm"].data_ptr())
-        check(lib().strata_moe_forward(self._h, ctypes.c_void_p(x.data_ptr()), T,
-                                       ctypes.c_void_p(y.data_ptr()),
-                                       ctypes.c_void_p(stream.cuda_stream),
-                                       ctypes.byref(d) if d is not None else None))
+        check(fn(self._h, ctypes.c_void_p(x.data_ptr()), T, ctypes.c_void_p(y.data_ptr()),
+                 ctypes.c_void_p(stream.cuda_stream), ctypes.byref(d) if d is not None else None))
         return (y, out) if dbg else y
 
     __call__ = forward

@@ -63,6 +63,7 @@ class Timing(ctypes.Structure):
 EXPORTS = {
     "strata_moe_create": (c_i32, [ctypes.POINTER(Desc), ctypes.POINTER(c_vp)]),
     "strata_moe_forward": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, ctypes.POINTER(RouteDbg)]),
+    "strata_moe_forward_noalloc": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, ctypes.POINTER(RouteDbg)]),
     "strata_expert_cache_stats": (c_i32, [c_vp, ctypes.POINTER(CacheStats)]),
     "strata_moe_memory": (c_i32, [c_vp, ctypes.POINTER(MemoryInfo)]),
     "strata_moe_set_timing": (c_i32, [c_vp, c_i32]),

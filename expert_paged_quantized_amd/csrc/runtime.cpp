@@ -23,6 +23,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <cmath>
 #include <chrono>
 #include <cstdio>
@@ -50,6 +51,9 @@ int decode_dot_waves(int N, int K, int quant, int tiles_per_token, int T);
 hipError_t launch_decode_dot(const GemmArgs& a, int quant, bool gate_up, int T, int S, int n_tiles, hipStream_t s);
 hipError_t launch_combine(const float*, const int32_t*, const float*, int, int, int, int, int, int64_t,
                           uint16_t*, hipStream_t);
+uint64_t scratch_bytes();
+hipError_t scratch_init(int device);
+void* scratch_ptr(int device);
 }  // namespace strata
 
 using namespace strata;
@@ -94,6 +98,31 @@ thread_local KernelTimer g_ktimer;
 // Side streams the expert pages are copied on (all at the default priority).
 constexpr int kCopyStreams = STRATA_COPY_STREAMS;
 
+// Device buffers of one forward, carved from one block of device memory: the
+// handle's own (sized for max_tokens at create) or, for the no-allocation
+// entry point, the library's static scratch (sized for the call's T).  Every
+// forward writes each element before it reads it, so nothing here needs
+// clearing between forwards.
+struct Workspace {
+  float* logits = nullptr;      // [T, E]
+  int32_t* idx = nullptr;       // [T, k]
+  float* w = nullptr;           // [T, k]
+  int32_t* counts = nullptr;    // [E]
+  int32_t* offsets = nullptr;   // [E + 1]
+  int32_t* perm = nullptr;      // [max_rows]: routed rows, then the shared rows
+  int32_t* pos = nullptr;       // [T, k]
+  int32_t* rank = nullptr;      // [T, k]: rank inside its 64-token block
+  int32_t* hist = nullptr;      // [ceil(T / 64), E]
+  Tile* tiles_dev = nullptr;    // tile list built by the routing kernels
+  Tile* tiles_host = nullptr;   // tile lists built by the residency manager
+  int32_t* ntiles = nullptr;
+  void* hbuf = nullptr;         // h [max_rows, F], 16-bit
+  float* o = nullptr;           // [ksplit][max_rows, H]
+  uint16_t* x16 = nullptr;      // fp16 formats: the scaled fp16 copy of x [T, H]
+  int32_t* xexp = nullptr;      // fp16 formats: its per-token exponents [T]
+  size_t max_rows = 0, max_tiles = 0;
+};
+
 struct strata_moe {
   int H = 0, F = 0, E = 0, k = 0, S = 0, quant = 0, router = 0, policy = 0, budget = 0;
   int sshift = 0;  // scale block of k-block kb is kb >> sshift (int4 group-128: 1)
@@ -101,7 +130,7 @@ struct strata_moe {
   int max_tokens = 0, device = 0;
   RecordLayout lay{};
   size_t slot_stride = 0;
-  size_t max_rows = 0, max_tiles = 0;
+  bool f16 = false;  // int4 / NVFP4: fp16 GEMMs on the scaled fp16 copy of x
 
   uint8_t* host_store = nullptr;  // pinned, E records at slot_stride
   const uint8_t* host_dev = nullptr;  // the same store's device address (read by the page-in kernel)
@@ -112,26 +141,11 @@ struct strata_moe {
   uint8_t** d_slot_ptr = nullptr;  // budget + 1 entries
   std::vector<uint8_t*> h_slot_ptr;
 
-  float* d_logits = nullptr;
-  int32_t* d_idx = nullptr;
-  float* d_w = nullptr;
-  int32_t* d_counts = nullptr;
-  int32_t* d_offsets = nullptr;
-  int32_t* d_perm = nullptr;
-  int32_t* d_pos = nullptr;
-  int32_t* d_rank = nullptr;  // rank of each (token, choice) inside its 64-token block
-  int32_t* d_hist = nullptr;  // per 64-token block, per expert token counts
-  Tile* d_tiles_dev = nullptr;
-  Tile* d_tiles_host = nullptr;
-  int32_t* d_ntiles = nullptr;
-  unsigned long long* d_distinct = nullptr;
-  void* d_h = nullptr;
-  float* d_o = nullptr;
-  uint16_t* d_x16 = nullptr;   // fp16 copy of x scaled per token (int4 and NVFP4 layers)
-  int32_t* d_xexp = nullptr;   // per token: the copy holds x * 2^-xexp
+  Workspace ws;                // per-forward buffers for max_tokens (one allocation)
+  uint8_t* d_ws = nullptr;
+  unsigned long long* d_distinct = nullptr;  // distinct experts used, summed over forwards
   int32_t* d_wexp = nullptr;   // per expert (+ shared): kWexpCount rescaling exponents
   std::vector<int32_t> wexp;   // host copy of the same
-  uint64_t ws_bytes = 0;
 
   int32_t* h_counts = nullptr;  // pinned
   Tile* h_tiles = nullptr;      // pinned
@@ -557,9 +571,7 @@ static void release(strata_moe* h) {
   for (auto cs : h->copy_streams)
     if (cs) (void)hipStreamDestroy(cs);
   void* dev[] = {h->d_pool, h->d_shared, h->d_router_w, h->d_router_bias, h->d_slot_ptr,
-                 h->d_logits, h->d_idx, h->d_w, h->d_counts, h->d_offsets, h->d_perm, h->d_pos,
-                 h->d_tiles_dev, h->d_tiles_host, h->d_ntiles, h->d_distinct, h->d_h, h->d_o,
-                 h->d_x16, h->d_xexp, h->d_wexp, h->d_rank, h->d_hist};
+                 h->d_ws, h->d_distinct, h->d_wexp};
   for (void* p : dev)
     if (p) (void)hipFree(p);
   if (h->host_store) (void)hipHostFree(h->host_store);
@@ -595,6 +607,42 @@ static strata_status host_alloc(T** p, size_t bytes) {
 
 static int prefill_ksplit(int K, int sshift);
 
+// Lays out the workspace of layer h for T tokens at `base` (nullptr: only
+// sizes it); every buffer starts on a 256-byte boundary.  Returns the bytes.
+static uint64_t carve(const strata_moe* h, size_t T, uint8_t* base, Workspace* ws) {
+  const size_t TK = T * h->k;
+  ws->max_rows = TK + (h->S ? T : 0);
+  ws->max_tiles = TK / kPrefillTM + std::min<size_t>(h->E, TK) + (T + kPrefillTM - 1) / kPrefillTM + 4;
+  uint64_t at = 0;
+  auto take = [&](auto*& p, size_t bytes) {
+    using P = std::remove_reference_t<decltype(p)>;
+    p = base ? reinterpret_cast<P>(base + at) : nullptr;
+    at += (std::max<size_t>(bytes, 1) + 255) & ~size_t(255);
+  };
+  take(ws->logits, T * h->E * 4);
+  take(ws->idx, TK * 4);
+  take(ws->w, TK * 4);
+  take(ws->counts, size_t(h->E) * 4);
+  take(ws->offsets, size_t(h->E + 1) * 4);
+  take(ws->perm, ws->max_rows * 4);
+  take(ws->pos, TK * 4);
+  take(ws->rank, TK * 4);
+  take(ws->hist, ((T + 63) / 64) * size_t(h->E) * 4);
+  take(ws->tiles_dev, ws->max_tiles * sizeof(Tile));
+  take(ws->tiles_host, ws->max_tiles * sizeof(Tile));
+  take(ws->ntiles, 4);
+  take(ws->hbuf, ws->max_rows * h->F * 2);
+  take(ws->o, ws->max_rows * h->H * 4 * h->ksplit);
+  if (h->f16) {
+    take(ws->x16, T * h->H * 2);
+    take(ws->xexp, T * 4);
+  } else {
+    ws->x16 = nullptr;
+    ws->xexp = nullptr;
+  }
+  return at;
+}
+
 static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   h->H = d->hidden;
   h->F = d->ffn;
@@ -622,6 +670,8 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   if (dev < 0) HIP_CHECK(hipGetDevice(&dev));
   h->device = dev;
   HIP_CHECK(hipSetDevice(dev));
+  // this device's copy of the static scratch (no-allocation forwards)
+  HIP_CHECK(scratch_init(dev));
 
   // pinned host store, prepacked in parallel over experts
   strata_status st;
@@ -676,28 +726,13 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
                       hipMemcpyHostToDevice));
 
   // workspace for max_tokens
-  const size_t T = h->max_tokens, TK = T * h->k;
-  h->max_rows = TK + (h->S ? T : 0);
-  h->max_tiles = TK / kPrefillTM + std::min<size_t>(h->E, TK) + (T + kPrefillTM - 1) / kPrefillTM + 4;
-  uint64_t ws = 0;
-  auto walloc = [&](auto** p, size_t bytes) -> strata_status {
-    ws += std::max<size_t>(bytes, 256);
-    return dev_alloc(p, bytes);
-  };
-  if ((st = walloc(&h->d_logits, T * h->E * 4)) || (st = walloc(&h->d_idx, TK * 4)) ||
-      (st = walloc(&h->d_w, TK * 4)) || (st = walloc(&h->d_counts, size_t(h->E) * 4)) ||
-      (st = walloc(&h->d_offsets, size_t(h->E + 1) * 4)) || (st = walloc(&h->d_perm, h->max_rows * 4)) ||
-      (st = walloc(&h->d_pos, TK * 4)) || (st = walloc(&h->d_rank, TK * 4)) ||
-      (st = walloc(&h->d_hist, ((T + 63) / 64) * size_t(h->E) * 4)) || (st = walloc(&h->d_tiles_dev, h->max_tiles * sizeof(Tile))) ||
-      (st = walloc(&h->d_tiles_host, h->max_tiles * sizeof(Tile))) || (st = walloc(&h->d_ntiles, 64)) ||
-      (st = walloc(&h->d_distinct, 64)) || (st = walloc(&h->d_h, h->max_rows * h->F * 2)) ||
-      (st = walloc(&h->d_o, h->max_rows * h->H * 4 * h->ksplit)))
-    return st;
-  if (fi.f16 && ((st = walloc(&h->d_x16, T * h->H * 2)) || (st = walloc(&h->d_xexp, T * 4)))) return st;
-  h->ws_bytes = ws;
+  h->f16 = fi.f16;
+  if ((st = dev_alloc(&h->d_ws, carve(h, h->max_tokens, nullptr, &h->ws)))) return st;
+  (void)carve(h, h->max_tokens, h->d_ws, &h->ws);
+  if ((st = dev_alloc(&h->d_distinct, 64))) return st;
   HIP_CHECK(hipMemset(h->d_distinct, 0, 64));
   if ((st = host_alloc(&h->h_counts, size_t(h->E) * 4))) return st;
-  if ((st = host_alloc(&h->h_tiles, h->max_tiles * sizeof(Tile)))) return st;
+  if ((st = host_alloc(&h->h_tiles, h->ws.max_tiles * sizeof(Tile)))) return st;
 
   for (auto& cs : h->copy_streams) HIP_CHECK(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
   HIP_CHECK(hipEventCreateWithFlags(&h->ev_fwd_done, hipEventDisableTiming));
@@ -762,11 +797,11 @@ static hipError_t timed(strata_moe* h, int cls, hipStream_t s, Fn&& fn) {
   return e;
 }
 
-static GemmArgs gemm_args(strata_moe* h, bool gate_up, const void* x, const Tile* tiles,
+static GemmArgs gemm_args(strata_moe* h, const Workspace& ws, bool gate_up, const void* x, const Tile* tiles,
                           const int32_t* n_dev, int n_tiles) {
   GemmArgs a;
-  a.act = gate_up ? (h->d_x16 ? (const void*)h->d_x16 : x) : h->d_h;
-  a.gather = gate_up ? h->d_perm : nullptr;
+  a.act = gate_up ? (ws.x16 ? (const void*)ws.x16 : x) : ws.hbuf;
+  a.gather = gate_up ? ws.perm : nullptr;
   a.tiles = tiles;
   a.n_tiles_dev = n_dev;
   a.n_tiles = n_tiles;
@@ -775,14 +810,14 @@ static GemmArgs gemm_args(strata_moe* h, bool gate_up, const void* x, const Tile
   a.off_scales = gate_up ? h->lay.w1_scales : h->lay.w2_scales;
   a.N = gate_up ? 2 * h->F : h->H;
   a.K = gate_up ? h->H : h->F;
-  a.out = gate_up ? h->d_h : (void*)h->d_o;
+  a.out = gate_up ? ws.hbuf : (void*)ws.o;
   a.out_ld = gate_up ? h->F : h->H;
   a.sshift = h->sshift;
   a.off_gscale = h->quant == Q_NVFP4 ? h->lay.gscale + (gate_up ? 0 : 8) : -1;
   a.ksplit = 1;
   a.split_stride = 0;
-  a.tok_of_row = h->d_perm;
-  a.xexp = h->d_xexp;
+  a.tok_of_row = ws.perm;
+  a.xexp = ws.xexp;
   a.wexp = h->d_wexp;
   return a;
 }
@@ -805,12 +840,12 @@ static int prefill_grid(int items) { return std::max(1, std::min(items, 512)); }
 
 // Runs gate+up then down over a tile range.  n_dev != nullptr: the count lives
 // on the device and `n_tiles` is only an upper bound.
-static hipError_t run_experts(strata_moe* h, const void* x, const Tile* tiles, const int32_t* n_dev,
-                              int n_tiles, bool decode, int T, hipStream_t s) {
+static hipError_t run_experts(strata_moe* h, const Workspace& ws, const void* x, const Tile* tiles,
+                              const int32_t* n_dev, int n_tiles, bool decode, int T, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
   for (int pass = 0; pass < 2; ++pass) {
     const bool gate_up = pass == 0;
-    GemmArgs a = gemm_args(h, gate_up, x, tiles, n_dev, n_tiles);
+    GemmArgs a = gemm_args(h, ws, gate_up, x, tiles, n_dev, n_tiles);
     const int nrt = a.N / 32;
     int grid;
     int log2S = 0;
@@ -827,7 +862,7 @@ static hipError_t run_experts(strata_moe* h, const void* x, const Tile* tiles, c
     } else {
       if (!gate_up) {
         a.ksplit = h->ksplit;
-        a.split_stride = int64_t(h->max_rows) * h->H;
+        a.split_stride = int64_t(ws.max_rows) * h->H;
       }
       grid = prefill_grid(n_tiles * ((nrt + 7) / 8) * a.ksplit);
     }
@@ -899,8 +934,8 @@ static hipError_t page_ahead(strata_moe* h, const std::vector<PlanEntry>& pages,
   return hipSuccess;
 }
 
-static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, hipStream_t s,
-                                  const strata_route_dbg* dbg) {
+static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void* x, int T, void* y,
+                                  hipStream_t s, const strata_route_dbg* dbg) {
   const bool decode = T <= kDecodeMaxT;
   const int TK = T * h->k;
   // under stream capture only kernels may be enqueued: an all-resident
@@ -914,24 +949,24 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
   if (h->fwd_recorded && !capturing) HIP_CHECK(hipStreamWaitEvent(s, h->ev_fwd_done, 0));
 
   HIP_CHECK(timed(h, STRATA_K_ROUTER, s, [&]() {
-    return launch_router((const uint16_t*)x, h->d_router_w, h->d_router_bias, h->d_logits, h->d_x16, h->d_xexp,
+    return launch_router((const uint16_t*)x, h->d_router_w, h->d_router_bias, ws.logits, ws.x16, ws.xexp,
                          T, h->E, h->H, s);
   }));
   const int tile_rows = decode ? (1 << 30) : kPrefillTM;
   HIP_CHECK(timed(h, STRATA_K_GROUP, s, [&]() {
-    return launch_route(h->d_logits, T, h->E, h->k, h->router, h->S, tile_rows, h->budget, h->d_idx,
-                        h->d_w, h->d_rank, h->d_hist, h->d_counts, h->d_offsets,
-                        h->d_perm, h->d_pos, h->d_tiles_dev, h->d_ntiles, h->d_distinct, s);
+    return launch_route(ws.logits, T, h->E, h->k, h->router, h->S, tile_rows, h->budget, ws.idx,
+                        ws.w, ws.rank, ws.hist, ws.counts, ws.offsets,
+                        ws.perm, ws.pos, ws.tiles_dev, ws.ntiles, h->d_distinct, s);
   }));
 
   if (h->budget == h->E) {
     const int ub = decode ? std::min(h->E, TK) + h->S
                           : TK / kPrefillTM + std::min(h->E, TK) + (h->S ? (T + kPrefillTM - 1) / kPrefillTM : 0);
-    HIP_CHECK(run_experts(h, x, h->d_tiles_dev, h->d_ntiles, ub, decode, T, s));
+    HIP_CHECK(run_experts(h, ws, x, ws.tiles_dev, ws.ntiles, ub, decode, T, s));
     h->rm.forwards++;
     h->rm.waves++;
   } else {
-    HIP_CHECK(hipMemcpyAsync(h->h_counts, h->d_counts, size_t(h->E) * 4, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipMemcpyAsync(h->h_counts, ws.counts, size_t(h->E) * 4, hipMemcpyDeviceToHost, s));
     HIP_CHECK(hipEventRecord(h->ev_counts, s));
     HIP_CHECK(wait_spin(h->ev_counts));
     std::vector<int32_t> needed;
@@ -958,7 +993,7 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
         if (p.paged) add_tiles(h, p.expert, p.slot, off[p.expert], h->h_counts[p.expert], decode, n);
       pe[w] = n;
     }
-    if ((size_t)n > h->max_tiles) return fail(STRATA_E_HIP, "tile list overflow");
+    if ((size_t)n > ws.max_tiles) return fail(STRATA_E_HIP, "tile list overflow");
     // group indices are relative to the first tile of each launch's range;
     // prefill ranges then run heaviest tiles first (more 32-row column tiles
     // first, list order otherwise), as the device-built list does
@@ -971,7 +1006,7 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
         std::stable_sort(h->h_tiles + he[w], h->h_tiles + pe[w], heavier);
       }
     }
-    HIP_CHECK(hipMemcpyAsync(h->d_tiles_host, h->h_tiles, size_t(n) * sizeof(Tile), hipMemcpyHostToDevice, s));
+    HIP_CHECK(hipMemcpyAsync(ws.tiles_host, h->h_tiles, size_t(n) * sizeof(Tile), hipMemcpyHostToDevice, s));
     while ((int)h->ev_wave_done.size() < nw) {
       hipEvent_t b;
       HIP_CHECK(hipEventCreateWithFlags(&b, hipEventDisableTiming));
@@ -1057,11 +1092,11 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
         for (int i = 0; i < kCopyStreams; ++i)
           if (used[i]) HIP_CHECK(hipEventRecord(h->ev_copied[w * kCopyStreams + i], h->copy_streams[i]));
       }
-      HIP_CHECK(run_experts(h, x, h->d_tiles_host + hb[w], nullptr, he[w] - hb[w], decode, T, s));
+      HIP_CHECK(run_experts(h, ws, x, ws.tiles_host + hb[w], nullptr, he[w] - hb[w], decode, T, s));
       if (any_paged) {
         for (int i = 0; i < kCopyStreams; ++i)
           if (used[i]) HIP_CHECK(hipStreamWaitEvent(s, h->ev_copied[w * kCopyStreams + i], 0));
-        HIP_CHECK(run_experts(h, x, h->d_tiles_host + he[w], nullptr, pe[w] - he[w], decode, T, s));
+        HIP_CHECK(run_experts(h, ws, x, ws.tiles_host + he[w], nullptr, pe[w] - he[w], decode, T, s));
       }
       HIP_CHECK(hipEventRecord(h->ev_wave_done[w], s));
     }
@@ -1070,20 +1105,20 @@ static strata_status forward_impl(strata_moe* h, const void* x, int T, void* y, 
   }
 
   HIP_CHECK(timed(h, STRATA_K_COMBINE, s, [&]() {
-    return launch_combine(h->d_o, h->d_pos, h->d_w, T, h->k, h->H, h->S ? TK : -1, decode ? 1 : h->ksplit,
-                          int64_t(h->max_rows) * h->H, (uint16_t*)y, s);
+    return launch_combine(ws.o, ws.pos, ws.w, T, h->k, h->H, h->S ? TK : -1, decode ? 1 : h->ksplit,
+                          int64_t(ws.max_rows) * h->H, (uint16_t*)y, s);
   }));
 
   if (dbg) {
     auto cp = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
       return dst ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s) : hipSuccess;
     };
-    HIP_CHECK(cp(dbg->logits, h->d_logits, size_t(T) * h->E * 4));
-    HIP_CHECK(cp(dbg->topk_idx, h->d_idx, size_t(TK) * 4));
-    HIP_CHECK(cp(dbg->topk_w, h->d_w, size_t(TK) * 4));
-    HIP_CHECK(cp(dbg->counts, h->d_counts, size_t(h->E) * 4));
-    HIP_CHECK(cp(dbg->offsets, h->d_offsets, size_t(h->E + 1) * 4));
-    HIP_CHECK(cp(dbg->perm, h->d_perm, size_t(TK) * 4));
+    HIP_CHECK(cp(dbg->logits, ws.logits, size_t(T) * h->E * 4));
+    HIP_CHECK(cp(dbg->topk_idx, ws.idx, size_t(TK) * 4));
+    HIP_CHECK(cp(dbg->topk_w, ws.w, size_t(TK) * 4));
+    HIP_CHECK(cp(dbg->counts, ws.counts, size_t(h->E) * 4));
+    HIP_CHECK(cp(dbg->offsets, ws.offsets, size_t(h->E + 1) * 4));
+    HIP_CHECK(cp(dbg->perm, ws.perm, size_t(TK) * 4));
   }
   if (!capturing) {
     HIP_CHECK(hipEventRecord(h->ev_fwd_done, s));
@@ -1134,7 +1169,46 @@ strata_status strata_moe_forward(strata_moe* h, const void* x, int32_t T, void* 
   if ((xa | ya) & 15) return fail(STRATA_E_INVALID, "x and y must be 16-byte aligned");
   int cur = -1;
   if (hipGetDevice(&cur) == hipSuccess && cur != h->device) (void)hipSetDevice(h->device);
-  strata_status st = forward_impl(h, x, T, y, (hipStream_t)stream, dbg);
+  strata_status st = forward_impl(h, h->ws, x, T, y, (hipStream_t)stream, dbg);
+  if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
+  if (st == STRATA_E_HIP) h->poisoned = true;
+  return st;
+}
+
+strata_status strata_moe_forward_noalloc(strata_moe* h, const void* x, int32_t T, void* y, void* stream,
+                                         const strata_route_dbg* dbg) {
+  if (!h) return fail(STRATA_E_INVALID, "handle is NULL");
+  if (h->poisoned) return fail(STRATA_E_POISONED, "handle poisoned by an earlier HIP failure");
+  if (T < 0 || T > h->max_tokens) return fail(STRATA_E_INVALID, "T out of range [0, max_tokens]");
+  if (h->budget != h->E)
+    return fail(STRATA_E_UNSUPPORTED, "no-allocation forwards need every expert resident (budget == E): "
+                                      "a budgeted forward plans its pages in host memory it allocates");
+  if (h->timing) return fail(STRATA_E_UNSUPPORTED, "kernel timing creates events; turn it off");
+  if (T == 0) return STRATA_OK;
+  if (!x || !y) return fail(STRATA_E_INVALID, "x or y is NULL");
+  const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y, nb = (uintptr_t)T * h->H * 2;
+  if (xa < ya + nb && ya < xa + nb) return fail(STRATA_E_INVALID, "x and y overlap");
+  if ((xa | ya) & 15) return fail(STRATA_E_INVALID, "x and y must be 16-byte aligned");
+  Workspace ws;
+  const uint64_t need = carve(h, T, nullptr, &ws);
+  if (need > scratch_bytes()) {
+    int lo = 0, hi = T;  // largest T whose workspace fits
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      Workspace tmp;
+      if (carve(h, mid, nullptr, &tmp) <= scratch_bytes()) lo = mid; else hi = mid - 1;
+    }
+    return fail(STRATA_E_INVALID, "T = " + std::to_string(T) + " needs " + std::to_string(need) +
+                                      " bytes of workspace; the static scratch holds " +
+                                      std::to_string(scratch_bytes()) + " (at most " + std::to_string(lo) +
+                                      " tokens of this layer)");
+  }
+  void* base = scratch_ptr(h->device);  // looked up at create, never the array's host stand-in
+  if (!base) return fail(STRATA_E_HIP, "static scratch was not set up on this device");
+  (void)carve(h, T, static_cast<uint8_t*>(base), &ws);
+  int cur = -1;
+  if (hipGetDevice(&cur) == hipSuccess && cur != h->device) (void)hipSetDevice(h->device);
+  strata_status st = forward_impl(h, ws, x, T, y, (hipStream_t)stream, dbg);
   if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
   if (st == STRATA_E_HIP) h->poisoned = true;
   return st;
@@ -1202,7 +1276,8 @@ strata_status strata_moe_memory(const strata_moe* h, strata_memory_info* out) {
   out->shared = h->S ? h->slot_stride : 0;
   out->router = uint64_t(h->E) * h->H * 2 + (h->d_router_bias ? uint64_t(h->E) * 4 : 0) +
                 uint64_t(sizeof(uint8_t*)) * (h->budget + 1) + uint64_t(h->wexp.size()) * 4;
-  out->workspace = h->ws_bytes;
+  Workspace lay;
+  out->workspace = carve(h, h->max_tokens, nullptr, &lay);
   out->device_total = out->slot_pool + out->shared + out->router + out->workspace;
   out->host_store = uint64_t(h->slot_stride) * h->E;
   return STRATA_OK;

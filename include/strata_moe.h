@@ -225,6 +225,28 @@ typedef struct {
 strata_status strata_moe_forward(strata_moe* h, const void* x, int32_t T, void* y, void* stream,
                                  const strata_route_dbg* dbg);
 
+/* No-allocation forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, semantics and result as strata_moe_forward
+ * (bitwise the same y and routing outputs), except that the forward's device
+ * buffers (logits, routing lists, h, o, the scaled fp16 copy of x) come from
+ * a static scratch array inside the library instead of the handle's
+ * workspace, and the call allocates nothing.  The array is 64 MiB, one copy
+ * per GPU, held until the process ends; its address on a device is looked up
+ * when the first layer is created there.  T may exceed neither max_tokens
+ * nor the largest T whose buffers fit 64 MiB (about T * (4 E + R (2 F +
+ * 4 H P) + 2 H) bytes with R = k + num_shared rows per token and P the
+ * prefill down GEMM's partial-sum planes; E_INVALID names that T).  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or different layers without ordering between them)
+ * race; calls on one stream are ordered.  The array keeps what the last call
+ * left in it; no part needs clearing, since a forward writes every element
+ * before reading it.  Requires budget == E (a budgeted forward plans its
+ * pages in host memory that it allocates: E_UNSUPPORTED) and kernel timing
+ * off (E_UNSUPPORTED).  Errors: as strata_moe_forward. */
+strata_status strata_moe_forward_noalloc(strata_moe* h, const void* x, int32_t T, void* y, void* stream,
+                                         const strata_route_dbg* dbg);
+
 /* Cumulative counters since create ("/health" style live state: policy,
  * budget, resident bytes). */
 typedef struct {
