@@ -8,19 +8,22 @@ timed region starts.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline]
-  python bench.py --trace-summary TRACE_DIR
+  python bench.py --trace-summary TRACE_DIR [--workload NAME]
       per-kernel duration table (markdown) of a rocprofv3 --kernel-trace run of
       this script: the events-timed paged region, the events-timed all-resident
       region (both delimited by the one-element cumsum markers recorded around
-      them) and the whole run.
+      them) and the whole run; also writes profiles/kernels_<workload>.json
+      (average duration per expert-kernel kind and region), which later runs
+      quote beside their own event timings while the kernel code is unchanged.
   python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload NAME]
       turns two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
-      WRITE_SIZE) into profiles/traffic_<workload>.json, which later runs use
-      for the roofline's `traffic` while the kernel source is unchanged.
-  python bench.py --counter-summary DIR [DIR ...]
+      WRITE_SIZE) into profiles/traffic_<workload>.json (HBM bytes per launch of
+      each expert-kernel kind), which later runs use for the rooflines'
+      `traffic` while the kernel code is unchanged.
+  python bench.py --counter-summary DIR [DIR ...] [--kind KIND]
       median per dispatch of every counter in rocprofv3 --pmc runs of this
-      script, for the prefill gate+up kernel in the all-resident region
-      (markdown table).
+      script, for one expert-kernel kind (prefill_gate_up, prefill_down,
+      decode_gate_up, decode_down) in the all-resident region (markdown).
 """
 from __future__ import annotations
 
@@ -67,11 +70,23 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--trace-summary", metavar="TRACE_DIR")
     ap.add_argument("--counter-summary", nargs="+", metavar="DIR")
+    ap.add_argument("--kind", default="prefill_gate_up", choices=["prefill_gate_up", "prefill_down",
+                                                                   "decode_gate_up", "decode_down"],
+                    help="expert-kernel kind of --counter-summary")
     return ap.parse_args()
 
 
-KERNEL_SRC = os.path.join(ROOT, "expert_paged_quantized_amd", "csrc", "kernels_expert.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "expert_paged_quantized_amd", "csrc", f)
+               for f in ("kernels_expert.hip", "kernels_route.hip", "moe_common.h")]
 CALIB_BYTES = 256 << 20                        # plain device copy timed in the same run
+
+# Expert-kernel kinds the profile summaries report, by their mangled-name test.
+KINDS = {
+    "prefill_gate_up": lambda n: "moe_prefill_kernel" in n and ", true>" in n,
+    "prefill_down": lambda n: "moe_prefill_kernel" in n and ", false>" in n,
+    "decode_gate_up": lambda n: "moe_decode" in n and ", true" in n,
+    "decode_down": lambda n: "moe_decode" in n and ", false" in n,
+}
 
 
 def code_hash(text):
@@ -83,41 +98,76 @@ def code_hash(text):
 
 
 def kernel_source_hash():
-    return code_hash(open(KERNEL_SRC).read())
+    """One hash over the code of every kernel source file."""
+    return code_hash("\n".join(open(f).read() for f in KERNEL_SRCS))
 
 
 def traffic_path(workload):
     return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
 
-def trace_summary(trace_dir):
+def durations_path(workload):
+    return os.path.join(ROOT, "profiles", f"kernels_{workload}.json")
+
+
+def load_profile_json(path):
+    """A stored profile summary, only while the kernel code it was taken on is unchanged."""
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    return d if d.get("kernel_source_sha256_16") == kernel_source_hash() else None
+
+
+def _short(n):
+    return n[n.find("strata::") + 8:].split("(")[0] if "strata::" in n else n[:60]
+
+
+def trace_summary(trace_dir, workload):
     """Markdown tables of kernel durations from a rocprofv3 kernel trace of this
-    script, per marked region (see the module docstring)."""
+    script, per marked region (see the module docstring), and
+    profiles/kernels_<workload>.json: the average duration per expert-kernel
+    kind in each events-timed region, for bench.py to quote beside its own
+    event timings."""
     f = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     assert f, f"no kernel_trace.csv under {trace_dir}"
     rows = sorted(csv.DictReader(open(f[0])), key=lambda r: int(r["Start_Timestamp"]))
-
-    def short(n):
-        return n[n.find("strata::") + 8:].split("(")[0] if "strata::" in n else n[:60]
     marks = [i for i, r in enumerate(rows) if "scan" in r["Kernel_Name"].lower()]
+
+    def dur(r):
+        return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
 
     def table(sel, title):
         agg = {}
         for r in sel:
-            agg.setdefault(short(r["Kernel_Name"]), []).append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            agg.setdefault(_short(r["Kernel_Name"]), []).append(dur(r))
         out = [f"### {title}", "", "| kernel | calls | total us | avg us | min us | max us |",
                "|---|---|---|---|---|---|"]
         for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
             out.append(f"| `{k}` | {len(v)} | {sum(v):.1f} | {statistics.mean(v):.2f} | {min(v):.2f} | "
                        f"{max(v):.2f} |")
         return "\n".join(out) + "\n"
-    parts = []
+
+    def kinds(sel):
+        out = {}
+        for kind, test in KINDS.items():
+            v = [dur(r) for r in sel if test(r["Kernel_Name"])]
+            if v:
+                out[kind] = {"launches": len(v), "avg_us": round(statistics.mean(v), 3),
+                             "total_us": round(sum(v), 2)}
+        return out
+
+    parts, regions = [], {}
     if len(marks) >= 4:
-        parts.append(table(rows[marks[0] + 1:marks[1]], "Events-timed paged region (as configured)"))
-        parts.append(table(rows[marks[2] + 1:marks[3]], "Events-timed all-resident region"))
+        paged, res = rows[marks[0] + 1:marks[1]], rows[marks[2] + 1:marks[3]]
+        parts.append(table(paged, "Events-timed paged region (as configured)"))
+        parts.append(table(res, "Events-timed all-resident region"))
+        regions = {"paged": kinds(paged), "all_resident": kinds(res)}
     parts.append(table(rows, "Whole run"))
     print("\n".join(parts))
+    with open(durations_path(workload), "w") as fo:
+        json.dump({"workload": workload, "kernel_source_sha256_16": kernel_source_hash(),
+                   "source": "rocprofv3 --kernel-trace of bench.py (events-timed regions)",
+                   "regions": regions}, fo, indent=1)
 
 
 def region_rows(d, counter):
@@ -133,47 +183,49 @@ def region_rows(d, counter):
     return rows, rows[marks[2] + 1:marks[3]]
 
 
-def is_gate_up_prefill(name):
-    return "moe_prefill_kernel" in name and ", true>" in name
-
-
-def counter_summary(dirs):
-    out = ["| counter | median per dispatch | dispatches |", "|---|---|---|"]
+def counter_summary(dirs, kind="prefill_gate_up"):
+    """Median per dispatch of every counter of rocprofv3 --pmc runs, for one
+    expert-kernel kind in the all-resident events-timed region."""
+    out = [f"| counter | median per dispatch ({kind}) | dispatches |", "|---|---|---|"]
     for d in dirs:
         f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
         assert f, f"no counter_collection.csv under {d}"
         names = sorted({r["Counter_Name"] for r in csv.DictReader(open(f[0]))})
         for c in names:
             _, region = region_rows(d, c)
-            v = [float(r["Counter_Value"]) for r in region if is_gate_up_prefill(r["Kernel_Name"])]
-            out.append(f"| {c} | {statistics.median(v):,.0f} | {len(v)} |")
+            v = [float(r["Counter_Value"]) for r in region if KINDS[kind](r["Kernel_Name"])]
+            if v:
+                out.append(f"| {c} | {statistics.median(v):,.0f} | {len(v)} |")
     print("\n".join(out))
 
 
 def pmc_summary(fetch_dir, write_dir, workload):
-    """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the prefill gate+up
-    kernel, each scaled by what the counter reads for the calibration copy
-    (CALIB_BYTES read and written by one copy kernel in the same process)."""
-    def read(d, counter):
+    """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each expert-kernel
+    kind in the all-resident region, each scaled by what the counter reads for
+    the calibration copy (CALIB_BYTES read and written by one copy kernel in
+    the same process); written to profiles/traffic_<workload>.json."""
+    kinds = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows, region = region_rows(d, counter)
         per = {}
         for r in rows:
             per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        up = [float(r["Counter_Value"]) for r in region if is_gate_up_prefill(r["Kernel_Name"])]
-        return per, up
-    out = {}
-    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        per, up = read(d, counter)
         # the calibration copy (a same-dtype device copy, run by the HIP
         # runtime's copy kernel) is by far the largest copyBuffer dispatch
         cal = max(max(vs) for k, vs in per.items() if "copyBuffer" in k)
         factor = CALIB_BYTES / (cal * 1024.0)
-        out[counter] = {"kib_per_dispatch": sum(up) / len(up), "dispatches": len(up),
-                        "calibration_kib": cal, "factor": round(factor, 4)}
-    tb = sum(v["kib_per_dispatch"] * 1024.0 * v["factor"] for v in out.values())
-    res = {"workload": workload, "kernel": "moe_prefill_kernel (gate+up), all-resident region",
-           "kernel_source_sha256_16": kernel_source_hash(), "counters": out,
-           "traffic_bytes_per_launch": round(tb)}
+        for kind, test in KINDS.items():
+            v = [float(r["Counter_Value"]) for r in region if test(r["Kernel_Name"])]
+            if not v:
+                continue
+            kinds.setdefault(kind, {})[counter] = {
+                "kib_per_dispatch": sum(v) / len(v), "dispatches": len(v),
+                "calibration_kib": cal, "factor": round(factor, 4)}
+    for kind, c in kinds.items():
+        c["traffic_bytes_per_launch"] = round(sum(x["kib_per_dispatch"] * 1024.0 * x["factor"]
+                                                  for x in c.values() if isinstance(x, dict)))
+    res = {"workload": workload, "region": "all-resident events-timed steps",
+           "kernel_source_sha256_16": kernel_source_hash(), "kinds": kinds}
     with open(traffic_path(workload), "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res))
@@ -208,10 +260,10 @@ def main():
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
         return
     if args.trace_summary:
-        trace_summary(args.trace_summary)
+        trace_summary(args.trace_summary, args.workload)
         return
     if args.counter_summary:
-        counter_summary(args.counter_summary)
+        counter_summary(args.counter_summary, args.kind)
         return
     if args.cpu_baseline_only:
         from synth import CONFIGS, make_layer
@@ -256,6 +308,7 @@ def main():
         layer.forward(xs_d[i], y=y_d)
 
     mark = torch.ones(4, device=dev)
+    region_stats = {}
 
     def timed_region(layer, events=False, per_step_sync=True):
         for i in range(W):
@@ -267,6 +320,7 @@ def main():
         if events:  # a one-element cumsum marks the timed steps in a kernel trace
             mark.cumsum(0)
         torch.cuda.synchronize()
+        s0 = layer.stats()
         t_all = time.perf_counter()
         for i in range(W, n):
             a = time.perf_counter()
@@ -276,6 +330,8 @@ def main():
                 per.append(time.perf_counter() - a)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t_all
+        s1 = layer.stats()
+        region_stats["delta"] = {k: s1[k] - s0[k] for k in ("hits", "misses", "bytes_h2d", "waves", "forwards")}
         if events:
             mark.cumsum(0)
         tm = layer.timing()
@@ -285,6 +341,7 @@ def main():
     # (1) headline: as configured, no instrumentation
     log("[bench] timed region: as configured")
     dt, per, _ = timed_region(paged)
+    st_timed = region_stats["delta"]  # cache counters of the K timed steps
     # (2) the same inputs with HIP events on every kernel (kernel durations)
     log("[bench] timed region: kernel events")
     dt_ev, _, tm = timed_region(paged, events=True)
@@ -324,13 +381,20 @@ def main():
             "paged_region": {"launches": int(pg_n), "avg_launch_us": round(pg_ms / max(pg_n, 1) * 1e3, 2),
                              "achieved": round(ach_pg, 2), "frac": round(ach_pg / peak, 4),
                              "note": "the same kernel once per wave of the paged steps (same FLOPs in all)"}}
-    tp = traffic_path(cfg.name)
-    if os.path.exists(tp):
-        tr = json.load(open(tp))
-        if tr.get("kernel_source_sha256_16") == kernel_source_hash():
-            roof["traffic"] = tr["traffic_bytes_per_launch"]
-            roof["traffic_over_algorithmic"] = round(tr["traffic_bytes_per_launch"] / gu_bytes, 3)
-            roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    # stored profiler figures of the same kernel code (profiles/, hash-checked)
+    tr = load_profile_json(traffic_path(cfg.name))
+    if tr and "prefill_gate_up" in tr["kinds"]:
+        t_b = tr["kinds"]["prefill_gate_up"]["traffic_bytes_per_launch"]
+        roof["traffic"] = t_b
+        roof["traffic_over_algorithmic"] = round(t_b / gu_bytes, 3)
+        roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    kd = load_profile_json(durations_path(cfg.name))
+    if kd and "prefill_gate_up" in kd["regions"].get("all_resident", {}):
+        rp_us = kd["regions"]["all_resident"]["prefill_gate_up"]["avg_us"]
+        roof["rocprof_avg_launch_us"] = rp_us
+        roof["rocprof_frac"] = round(flops_gate_up(cfg, rows) / (rp_us * 1e-6) / 1e12 / peak, 4)
+        roof["duration_sources"] = ("avg_launch_us: HIP events on each dispatch in this run; "
+                                    "rocprof_avg_launch_us: profiles/kernels_<workload>.json, same kernel code")
 
     # decode kernels: all-resident layer; cold = 1 GiB streamed (read) between
     # forwards, so the last-level cache holds other, clean data; warm = the
@@ -413,6 +477,17 @@ def main():
                    "kernel_us_per_forward": round(dec_ms * 1e3, 2),
                    "mall": "cold (1 GiB streamed between forwards)",
                    "warm": {"achieved": round(warm_gbps, 1), "kernel_us_per_forward": round(warm_ms * 1e3, 2)}}
+    if tr and "decode_gate_up" in tr["kinds"] and "decode_down" in tr["kinds"]:
+        t_b = tr["kinds"]["decode_gate_up"]["traffic_bytes_per_launch"] + \
+            tr["kinds"]["decode_down"]["traffic_bytes_per_launch"]
+        decode_roof["traffic"] = t_b
+        decode_roof["traffic_over_algorithmic"] = round(t_b / dec_bytes, 3)
+        decode_roof["traffic_unit"] = ("HBM bytes per decode forward, gate+up + down launches (rocprofv3 "
+                                       "FETCH_SIZE + WRITE_SIZE, copy-calibrated; warm-region dispatches)")
+    if kd and "decode_gate_up" in kd["regions"].get("all_resident", {}):
+        ra = kd["regions"]["all_resident"]
+        decode_roof["rocprof_kernel_us_per_forward"] = round(ra["decode_gate_up"]["avg_us"] +
+                                                             ra.get("decode_down", {}).get("avg_us", 0.0), 2)
 
     # calibration copy for the HBM byte counters (FETCH_SIZE / WRITE_SIZE):
     # CALIB_BYTES read and written by one device-to-device copy
@@ -427,6 +502,39 @@ def main():
 
     # paged decode streams (B=1, fresh x per token) under each residency policy
     policies = None if args.no_policies else decode_policies(epq, torch, lw, cfg, dev, make_tokens)
+
+    # the step's resources (ro99/strata README, contribution rules: the step
+    # time is bounded by max over resources of work / rate, plus the serial
+    # part): host link (expert bytes paged), HBM (algorithmic bytes),
+    # matrix cores (prefill FLOPs), and the serial kernels (router, routing,
+    # combine) measured with events in the paged region
+    ms_step = dt / K * 1e3
+    link_bytes = st_timed["bytes_h2d"] / K
+    link = {"bytes_per_step": round(link_bytes), "achieved_GBps": round(link_bytes / (ms_step * 1e-3) / 1e9, 2),
+            "peak_GBps": round(h2d_gbps, 2), "peak_source": "pinned hipMemcpyAsync of 256 MB, this run",
+            "frac": round(link_bytes / (ms_step * 1e-3) / 1e9 / h2d_gbps, 4),
+            "pages_per_step": round(st_timed["misses"] / K, 2)}
+    _, dbg_d = resident.forward(xs_d[W], y=y_d, dbg=True)
+    distinct_d = int((dbg_d["counts"] > 0).sum().item())
+    eb = cfg.expert_bytes()
+    rows_d = Td * (cfg.top_k + cfg.num_shared)
+    ksplit_planes = 1  # activations and o rows; o planes of a split-K down GEMM add reads
+    hbm_bytes = ((distinct + cfg.num_shared + distinct_d + cfg.num_shared) * eb   # expert records
+                 + 2 * cfg.num_experts * cfg.hidden * 2                        # router weights, 2 forwards
+                 + (Tp + Td) * cfg.hidden * 2 * (2 if cfg.quant == "mxfp4_g32" else 3)  # x, fp16 copy, y
+                 + (rows + rows_d) * (cfg.hidden * 2 + cfg.ffn * 4 + cfg.hidden * 8 * ksplit_planes)
+                 + link_bytes)                                                  # pages written to HBM
+    fl_step = flops_gate_up(cfg, rows) + flops_down(cfg, rows)
+    serial_ms = sum(tm[k][0] for k in ("router", "group", "combine")) / K
+    terms = {"host_link_ms": link_bytes / (h2d_gbps * 1e9) * 1e3,
+             "hbm_ms": hbm_bytes / (HBM_PEAK_GBPS * 1e9) * 1e3,
+             "mfma_ms": fl_step / (peak * 1e12) * 1e3}
+    arg = max(terms, key=terms.get)
+    tau = {"terms_ms": {k: round(v, 4) for k, v in terms.items()}, "serial_ms": round(serial_ms, 4),
+           "serial_kernels": "router + routing (top-k, permute) + combine, HIP events, paged region",
+           "tau_ms": round(max(terms.values()) + serial_ms, 4), "measured_ms_per_step": round(ms_step, 4),
+           "argmax_r": arg.replace("_ms", ""),
+           "hbm_bytes_per_step": round(hbm_bytes), "flops_per_step": fl_step}
 
     tokens_per_step = Tp + Td
     value = K * tokens_per_step / dt
@@ -452,6 +560,7 @@ def main():
                          "kernel_ms_per_step": {k: round(v[0] / K, 4) for k, v in tm_r.items()}},
         "kernel_ms_per_step": {k: round(v[0] / K, 4) for k, v in tm.items()},
         "events_pass_ms_per_step": round(dt_ev / K * 1e3, 4),
+        "link": link, "tau": tau,
         "cache": st, "h2d_GBps": round(h2d_gbps, 2),
         "paged_decode": policies,
         "gpu": {"name": props.name, "cus": props.multi_processor_count},

@@ -23,12 +23,15 @@ namespace strata {
 // reproducible bit for bit.
 //
 // When x16 is given (int4 and NVFP4 layers, whose expert GEMMs take fp16
-// operands) the waves of the first expert block also write each token's row
-// scaled into the fp16 range: x * 2^-e with e = floor(log2 max|x|) - 14, so
-// the row's largest magnitude lands in [2^14, 2^15) whatever the bf16 input
-// (bf16 reaches 2^128, fp16 only 65504), and e goes to xexp[t] for the GEMM
-// epilogues to undo in fp32.  The scaling is exact except for elements below
-// 2^-32 of the row's largest, which round to fp16's 2^-24 grid.
+// operands) the waves also write each token's row scaled into the fp16 range:
+// x * 2^-e with e = floor(log2 max|x|) - 14, so the row's largest magnitude
+// lands in [2^14, 2^15) whatever the bf16 input (bf16 reaches 2^128, fp16
+// only 65504), and e goes to xexp[t] for the GEMM epilogues to undo in fp32.
+// Every wave of a token block tracks the rows' largest magnitudes while it
+// streams them for its logits, then converts its own share of the rows'
+// 16-byte pieces (the wave of expert block b takes pieces b, b + nb, ...), so
+// no wave pays a whole extra pass.  The scaling is exact except for elements
+// below 2^-32 of the row's largest, which round to fp16's 2^-24 grid.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -58,29 +61,31 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2_scaled(uint32_t w, int ne) {
   const _Float16 hi = (_Float16)__builtin_amdgcn_ldexpf(bf16_hi(w), ne);
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
-// Second pass of the waves that write the fp16 copy: the scaled rows of
-// tokens t0 .. t0 + NT - 1 (< T) from their running magnitude maxima.
+// The scaled fp16 copy of tokens t0 .. t0 + NT - 1 (< T): from the rows'
+// running magnitude maxima (per lane), this wave (share `part` of `nparts`)
+// converts the 16-byte pieces part, part + nparts, ... of the NT rows; share
+// 0 also writes the exponents.
 template <int NT>
 __device__ __forceinline__ void write_scaled_rows(const uint16_t* __restrict__ x, uint16_t* __restrict__ x16,
                                                   int32_t* __restrict__ xexp, const uint32_t (&am)[NT], int t0,
-                                                  int T, int H, int lane) {
+                                                  int T, int H, int lane, int part, int nparts) {
   int ex[NT];
 #pragma unroll
   for (int a = 0; a < NT; ++a) ex[a] = token_exponent(wave_max(am[a]));
-  const int C = H >> 9;
-  for (int c = 0; c < C; ++c) {
-    const int off = (c * 64 + lane) * 8;
+  const int pieces = NT * (H >> 3);  // 8 values per piece
+  for (int q = part + nparts * lane; q < pieces; q += nparts * 64) {
+    const int a = q / (H >> 3), off = (q - a * (H >> 3)) * 8;
+    if (t0 + a >= T) continue;
+    int e = ex[0];
 #pragma unroll
-    for (int a = 0; a < NT; ++a) {
-      if (t0 + a >= T) continue;
-      const uint4 xv = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + a) * H + off);
-      uint4 hv;
+    for (int i = 1; i < NT; ++i) e = (a == i) ? ex[i] : e;
+    const uint4 xv = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + a) * H + off);
+    uint4 hv;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) (&hv.x)[q] = bf16x2_to_f16x2_scaled((&xv.x)[q], -ex[a]);
-      *reinterpret_cast<uint4*>(x16 + (size_t)(t0 + a) * H + off) = hv;
-    }
+    for (int w = 0; w < 4; ++w) (&hv.x)[w] = bf16x2_to_f16x2_scaled((&xv.x)[w], -e);
+    *reinterpret_cast<uint4*>(x16 + (size_t)(t0 + a) * H + off) = hv;
   }
-  if (lane == 0) {
+  if (part == 0 && lane == 0) {
 #pragma unroll
     for (int a = 0; a < NT; ++a)
       if (t0 + a < T) xexp[t0 + a] = ex[a];
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   const int neb = (E + TE - 1) / TE;
   const int t0 = (wave / neb) * TT, e0 = (wave % neb) * TE;
   if (t0 >= T) return;
-  const bool copy = x16 && e0 == 0;  // this wave writes the scaled fp16 rows
+  const bool copy = x16 != nullptr;  // the waves write the scaled fp16 rows
   uint32_t am[TT];
   float acc[TT][TE];
 #pragma unroll
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
         if (t < T && e < E) logits[(size_t)t * E + e] = bias ? acc[a][b] + bias[e] : acc[a][b];
       }
   }
-  if (copy) write_scaled_rows<TT>(x, x16, xexp, am, t0, T, H, lane);
+  if (copy) write_scaled_rows<TT>(x, x16, xexp, am, t0, T, H, lane, wave % neb, neb);
 }
 
 
@@ -201,7 +206,7 @@ __global__ __launch_bounds__(256) void router_block_kernel(const uint16_t* __res
   const int neb = (E + kRbTE - 1) / kRbTE;
   const int t0 = (wave / neb) * kRbTT, e0 = (wave % neb) * kRbTE;
   const bool active = t0 < T;
-  const bool copy = active && x16 && e0 == 0;  // this wave writes the scaled fp16 rows
+  const bool copy = active && x16;  // the waves write the scaled fp16 rows
   uint32_t am[kRbTT];
   float acc[kRbTT][kRbTE];
 #pragma unroll
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(256) void router_block_kernel(const uint16_t* __res
     for (int i = 0; i < o; ++i) q[i] = q[i] + q[i + o];
   const int t = t0 + lane / kRbTE, e = e0 + lane % kRbTE;
   if (active && t < T && e < E) logits[(size_t)t * E + e] = bias ? q[0] + bias[e] : q[0];
-  if (copy) write_scaled_rows<kRbTT>(x, x16, xexp, am, t0, T, H, lane);
+  if (copy) write_scaled_rows<kRbTT>(x, x16, xexp, am, t0, T, H, lane, wave % neb, neb);
 }
 
 // ---------------------------------------------------------------------------
