@@ -47,7 +47,7 @@ class MoELayer:
     def __init__(self, *, hidden, ffn, num_experts, top_k, num_shared, quant, router, budget,
                  max_tokens, router_w, router_bias, gate, up, down, sh_gate=None, sh_up=None,
                  sh_down=None, policy="lru", decay_shift=0, prefetch=0, profile=None, device=-1,
-                 pager="auto"):
+                 pager="auto", shared_gate_w=None):
         self.hidden, self.ffn, self.num_experts, self.top_k = hidden, ffn, num_experts, top_k
         self.num_shared, self.max_tokens = num_shared, max_tokens
         keep = []
@@ -69,6 +69,10 @@ class MoELayer:
         d.router_w, d.router_bias = rw.ctypes.data, (None if rb is None else rb.ctypes.data)
         d.gate, d.up, d.down = _qmat(gate, keep), _qmat(up, keep), _qmat(down, keep)
         d.sh_gate, d.sh_up, d.sh_down = _qmat(sh_gate, keep), _qmat(sh_up, keep), _qmat(sh_down, keep)
+        if shared_gate_w is not None:
+            gw = np.ascontiguousarray(shared_gate_w, dtype=np.uint16)
+            keep.append(gw)
+            d.shared_gate_w = gw.ctypes.data
         h = ctypes.c_void_p()
         check(lib().strata_moe_create(ctypes.byref(d), ctypes.byref(h)))
         self._h = h
@@ -85,7 +89,7 @@ class MoELayer:
                    router_w=lw.router_w, router_bias=lw.router_bias, gate=lw.gate, up=lw.up,
                    down=lw.down, sh_gate=lw.sh_gate, sh_up=lw.sh_up, sh_down=lw.sh_down,
                    policy=policy, decay_shift=decay_shift, prefetch=prefetch, profile=profile,
-                   device=device, pager=pager)
+                   device=device, pager=pager, shared_gate_w=getattr(lw, "shared_gate_w", None))
 
     # ------------------------------------------------------------------
     def forward(self, x, y=None, stream=None, dbg=False):

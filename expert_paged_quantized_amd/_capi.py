@@ -29,7 +29,7 @@ class Desc(ctypes.Structure):
                 ("decay_shift", c_i32), ("prefetch", c_i32), ("pager", c_i32), ("expert_profile", c_vp),
                 ("router_w", c_vp), ("router_bias", c_vp),
                 ("gate", QMat), ("up", QMat), ("down", QMat),
-                ("sh_gate", QMat), ("sh_up", QMat), ("sh_down", QMat)]
+                ("sh_gate", QMat), ("sh_up", QMat), ("sh_down", QMat), ("shared_gate_w", c_vp)]
 
 
 class RouteDbg(ctypes.Structure):

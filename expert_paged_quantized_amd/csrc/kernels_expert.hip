@@ -1079,8 +1079,9 @@ hipError_t launch_page_in(const PageBatch& b, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine: y[t] = sum_j w[t,j] * o[pos[t,j]] (j ascending) + o[shared row of t],
-// fp32, rounded to bf16 (nearest-even).  One workgroup per (token, block of
+// Combine: y[t] = sum_j w[t,j] * o[pos[t,j]] (j ascending) + g_t o[shared row of t],
+// fp32, rounded to bf16 (nearest-even); g_t = sigmoid(gate logit of t) for a
+// layer with a shared-expert gate, else 1 (added without a multiply).  One workgroup per (token, block of
 // 1024 columns); each thread owns 4 consecutive columns.  With a K-split
 // prefill down GEMM each o row is the sum of its partial planes, in plane
 // order, before it is weighted.
@@ -1102,8 +1103,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ pos,
                                                       const float* __restrict__ w, int k, int H,
                                                       int shared_row0, int ksplit, int64_t stride,
+                                                      const float* __restrict__ gate,
                                                       uint16_t* __restrict__ y) {
   const int t = blockIdx.x;
+  // the shared expert's weight: sigmoid of its gate logit, or 1 without a gate
+  const float gw = gate ? __builtin_amdgcn_rcpf(1.0f + __expf(-gate[t])) : 1.0f;
   // workgroup (t, blockIdx.y) takes column blocks of 1024, gridDim.y apart
   for (int c = blockIdx.y * 1024 + threadIdx.x * 4; c < H; c += gridDim.y * 1024) {
     float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1117,10 +1121,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
     if (shared_row0 >= 0) {
       const float4 v = o_row(o, (size_t)(shared_row0 + t) * H + c, ksplit, stride);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+      if (gate) {
+        acc.x = __builtin_fmaf(gw, v.x, acc.x);
+        acc.y = __builtin_fmaf(gw, v.y, acc.y);
+        acc.z = __builtin_fmaf(gw, v.z, acc.z);
+        acc.w = __builtin_fmaf(gw, v.w, acc.w);
+      } else {
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
     }
     const uint2 pk = {(uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16),
                       (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16)};
@@ -1252,11 +1263,12 @@ hipError_t launch_expert_gemm(const GemmArgs& a, int quant, bool gate_up, bool d
 }
 
 hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, int T, int k, int H,
-                          int shared_row0, int ksplit, int64_t stride, uint16_t* y, hipStream_t s) {
+                          int shared_row0, int ksplit, int64_t stride, const float* gate, uint16_t* y,
+                          hipStream_t s) {
   // one workgroup per (token, 1024 columns): a decode token's columns are
   // read in parallel rather than in dependent rounds of one workgroup
   launch_k(combine_kernel, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, o, pos, w, k, H, shared_row0, ksplit,
-           stride, y);
+           stride, gate, y);
   return hipGetLastError();
 }
 

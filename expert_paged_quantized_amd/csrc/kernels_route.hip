@@ -20,7 +20,9 @@ namespace strata {
 // from +0; the 64 lane partials are then folded with offsets 32, 16, 8, 4, 2,
 // 1 (p[L] += p[L + o]) and lane 0 holds the logit; the bias is added last.
 // That order is part of the layer's definition so that the top-k decision is
-// reproducible bit for bit.
+// reproducible bit for bit.  wr has E rows: the Eo routed experts' rows, then,
+// for a layer with a shared-expert gate, the gate row, whose fp32 logit goes
+// to gate_out[t] (no bias).
 //
 // When x16 is given (int4 and NVFP4 layers, whose expert GEMMs take fp16
 // operands) the waves also write each token's row scaled into the fp16 range:
@@ -115,8 +117,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ logits,
                                                             uint16_t* __restrict__ x16,
-                                                            int32_t* __restrict__ xexp, int T, int E,
-                                                            int H) {
+                                                            int32_t* __restrict__ xexp,
+                                                            float* __restrict__ gate_out, int T, int E,
+                                                            int Eo, int H) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int neb = (E + TE - 1) / TE;
@@ -176,7 +179,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 #pragma unroll
       for (int b = 0; b < TE; ++b) {
         const int t = t0 + a, e = e0 + b;
-        if (t < T && e < E) logits[(size_t)t * E + e] = bias ? acc[a][b] + bias[e] : acc[a][b];
+        if (t < T && e < Eo) logits[(size_t)t * Eo + e] = bias ? acc[a][b] + bias[e] : acc[a][b];
+        else if (t < T && e < E) gate_out[t] = acc[a][b];  // the shared-expert gate row
       }
   }
   if (copy) write_scaled_rows<TT>(x, x16, xexp, am, t0, T, H, lane, wave % neb, neb);
@@ -198,8 +202,9 @@ __global__ __launch_bounds__(256) void router_block_kernel(const uint16_t* __res
                                                           const float* __restrict__ bias,
                                                           float* __restrict__ logits,
                                                           uint16_t* __restrict__ x16,
-                                                          int32_t* __restrict__ xexp, int T, int E,
-                                                          int H) {
+                                                          int32_t* __restrict__ xexp,
+                                                          float* __restrict__ gate_out, int T, int E,
+                                                          int Eo, int H) {
   __shared__ __attribute__((aligned(16))) float red[4][64 * kRbPitch];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wave = blockIdx.x * 4 + w;
@@ -269,7 +274,8 @@ __global__ __launch_bounds__(256) void router_block_kernel(const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < o; ++i) q[i] = q[i] + q[i + o];
   const int t = t0 + lane / kRbTE, e = e0 + lane % kRbTE;
-  if (active && t < T && e < E) logits[(size_t)t * E + e] = bias ? q[0] + bias[e] : q[0];
+  if (active && t < T && e < Eo) logits[(size_t)t * Eo + e] = bias ? q[0] + bias[e] : q[0];
+  else if (active && t < T && e < E) gate_out[t] = q[0];  // the shared-expert gate row
   if (copy) write_scaled_rows<kRbTT>(x, x16, xexp, am, t0, T, H, lane, wave % neb, neb);
 }
 
@@ -621,17 +627,18 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
-                         uint16_t* x16, int32_t* xexp, int T, int E, int H, hipStream_t s) {
+                         uint16_t* x16, int32_t* xexp, float* gate_out, int T, int E, int Eo, int H,
+                         hipStream_t s) {
   // 8 x 8 blocks when they still give the GPU thousands of waves, else one
   // logit per wave (small T or few experts)
   const int blocked_waves = ((T + kRbTT - 1) / kRbTT) * ((E + kRbTE - 1) / kRbTE);
   if (blocked_waves >= 2048) {
     launch_k(router_block_kernel, dim3((blocked_waves + 3) / 4), dim3(256), 0, s, x, wr, bias, logits, x16,
-             xexp, T, E, H);
+             xexp, gate_out, T, E, Eo, H);
   } else {
     const int waves = T * E;
     launch_k(router_logits_kernel<1, 1>, dim3((waves + 3) / 4), dim3(256), 0, s, x, wr, bias, logits, x16,
-             xexp, T, E, H);
+             xexp, gate_out, T, E, Eo, H);
   }
   return hipGetLastError();
 }

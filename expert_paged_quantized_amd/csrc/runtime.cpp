@@ -36,8 +36,8 @@
 #include "residency.h"
 
 namespace strata {
-hipError_t launch_router(const uint16_t*, const uint16_t*, const float*, float*, uint16_t*, int32_t*, int,
-                         int, int, hipStream_t);
+hipError_t launch_router(const uint16_t*, const uint16_t*, const float*, float*, uint16_t*, int32_t*, float*,
+                         int, int, int, int, hipStream_t);
 hipError_t launch_route(const float*, int, int, int, int, int, int, int, int32_t*, float*, int32_t*,
                         int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, Tile*, int32_t*,
                         unsigned long long*, hipStream_t);
@@ -50,7 +50,7 @@ hipError_t launch_read_probe(const void* p, uint64_t bytes, uint32_t* out, hipSt
 int decode_dot_waves(int N, int K, int quant, int tiles_per_token, int T);
 hipError_t launch_decode_dot(const GemmArgs& a, int quant, bool gate_up, int T, int S, int n_tiles, hipStream_t s);
 hipError_t launch_combine(const float*, const int32_t*, const float*, int, int, int, int, int, int64_t,
-                          uint16_t*, hipStream_t);
+                          const float*, uint16_t*, hipStream_t);
 uint64_t scratch_bytes();
 hipError_t scratch_init(int device);
 void* scratch_ptr(int device);
@@ -120,6 +120,7 @@ struct Workspace {
   float* o = nullptr;           // [ksplit][max_rows, H]
   uint16_t* x16 = nullptr;      // fp16 formats: the scaled fp16 copy of x [T, H]
   int32_t* xexp = nullptr;      // fp16 formats: its per-token exponents [T]
+  float* gate = nullptr;        // shared-expert gate logits [T] (gated layers)
   size_t max_rows = 0, max_tiles = 0;
 };
 
@@ -130,7 +131,8 @@ struct strata_moe {
   int max_tokens = 0, device = 0;
   RecordLayout lay{};
   size_t slot_stride = 0;
-  bool f16 = false;  // int4 / NVFP4: fp16 GEMMs on the scaled fp16 copy of x
+  bool f16 = false;    // int4 / NVFP4: fp16 GEMMs on the scaled fp16 copy of x
+  bool gated = false;  // the shared expert is weighted by sigmoid(x . w_s)
 
   uint8_t* host_store = nullptr;  // pinned, E records at slot_stride
   const uint8_t* host_dev = nullptr;  // the same store's device address (read by the page-in kernel)
@@ -316,6 +318,8 @@ static strata_status validate(const strata_moe_desc* d) {
       return st;
   } else if (d->sh_gate.codes || d->sh_up.codes || d->sh_down.codes) {
     return fail(STRATA_E_INVALID, "shared expert weights given with num_shared = 0");
+  } else if (d->shared_gate_w) {
+    return fail(STRATA_E_INVALID, "shared_gate_w given with num_shared = 0");
   }
   // admission of scales
   const size_t H = d->hidden, F = d->ffn;
@@ -640,6 +644,10 @@ static uint64_t carve(const strata_moe* h, size_t T, uint8_t* base, Workspace* w
     ws->x16 = nullptr;
     ws->xexp = nullptr;
   }
+  if (h->gated)
+    take(ws->gate, T * 4);
+  else
+    ws->gate = nullptr;
   return at;
 }
 
@@ -710,8 +718,13 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
                 h->wexp.data() + size_t(h->E) * kWexpCount);
     HIP_CHECK(hipMemcpy(h->d_shared, tmp.data(), rec, hipMemcpyHostToDevice));
   }
-  if ((st = dev_alloc(&h->d_router_w, size_t(h->E) * h->H * 2))) return st;
+  // router rows, then the shared-expert gate row of a gated layer
+  h->gated = d->shared_gate_w != nullptr;
+  if ((st = dev_alloc(&h->d_router_w, size_t(h->E + h->gated) * h->H * 2))) return st;
   HIP_CHECK(hipMemcpy(h->d_router_w, d->router_w, size_t(h->E) * h->H * 2, hipMemcpyHostToDevice));
+  if (h->gated)
+    HIP_CHECK(hipMemcpy(h->d_router_w + size_t(h->E) * h->H, d->shared_gate_w, size_t(h->H) * 2,
+                        hipMemcpyHostToDevice));
   if ((st = dev_alloc(&h->d_wexp, h->wexp.size() * 4))) return st;
   HIP_CHECK(hipMemcpy(h->d_wexp, h->wexp.data(), h->wexp.size() * 4, hipMemcpyHostToDevice));
   if (d->router_bias) {
@@ -950,7 +963,7 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
 
   HIP_CHECK(timed(h, STRATA_K_ROUTER, s, [&]() {
     return launch_router((const uint16_t*)x, h->d_router_w, h->d_router_bias, ws.logits, ws.x16, ws.xexp,
-                         T, h->E, h->H, s);
+                         ws.gate, T, h->E + h->gated, h->E, h->H, s);
   }));
   const int tile_rows = decode ? (1 << 30) : kPrefillTM;
   HIP_CHECK(timed(h, STRATA_K_GROUP, s, [&]() {
@@ -1106,7 +1119,7 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
 
   HIP_CHECK(timed(h, STRATA_K_COMBINE, s, [&]() {
     return launch_combine(ws.o, ws.pos, ws.w, T, h->k, h->H, h->S ? TK : -1, decode ? 1 : h->ksplit,
-                          int64_t(ws.max_rows) * h->H, (uint16_t*)y, s);
+                          int64_t(ws.max_rows) * h->H, ws.gate, (uint16_t*)y, s);
   }));
 
   if (dbg) {
@@ -1274,7 +1287,7 @@ strata_status strata_moe_memory(const strata_moe* h, strata_memory_info* out) {
   memset(out, 0, sizeof(*out));
   out->slot_pool = uint64_t(h->slot_stride) * h->budget;
   out->shared = h->S ? h->slot_stride : 0;
-  out->router = uint64_t(h->E) * h->H * 2 + (h->d_router_bias ? uint64_t(h->E) * 4 : 0) +
+  out->router = uint64_t(h->E + h->gated) * h->H * 2 + (h->d_router_bias ? uint64_t(h->E) * 4 : 0) +
                 uint64_t(sizeof(uint8_t*)) * (h->budget + 1) + uint64_t(h->wexp.size()) * 4;
   Workspace lay;
   out->workspace = carve(h, h->max_tokens, nullptr, &lay);

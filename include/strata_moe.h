@@ -155,6 +155,13 @@ typedef struct {
   const float* router_bias;   /* host, fp32 [E], or NULL                       */
   strata_qmat gate, up, down; /* routed experts, n_exp = E                     */
   strata_qmat sh_gate, sh_up, sh_down; /* shared expert, n_exp = 1, or all NULL */
+  /* Shared-expert gate: host, bf16 bits [H], or NULL.  With it (num_shared
+   * must be 1) the shared expert's output is weighted by sigmoid(l_s) per
+   * token, l_s = x . w_s formed in fp32 in the router's summation order;
+   * without it the weight is 1.  The ro99/strata README's model table lists
+   * shared experts beside routed ones without saying how they are weighted;
+   * both forms are offered. */
+  const uint16_t* shared_gate_w;
 } strata_moe_desc;
 
 /* Creates a layer.  Validates the descriptor, admits the weights (every MXFP4

@@ -36,8 +36,13 @@ R6  nibble 2i of a row is the low nibble of byte i.  int4: w = s*q + b with
     bias 7) scale per 16 inputs times one fp32 scale per matrix; E4M3 NaN
     bytes (0x7F, 0xFF) are refused like E8M0 0/255.
 R7  expert: g = Wg x, u = Wu x, a = silu(g)*u, o = Wd a; the shared expert is
-    the same FFN with weight 1 and no gate.
-R8  y[t] = sum_j w[t,j] o_j + shared(x[t]), j ascending, shared last.
+    the same FFN with weight 1, or, for a layer that carries a shared-expert
+    gate row w_s (the ro99/strata README's model table lists shared experts
+    beside routed ones without saying how they are weighted, so the gated
+    form is a reading), with weight sigmoid(l_s), l_s = x . w_s formed in fp32
+    in the R2 order like a router logit.
+R8  y[t] = sum_j w[t,j] o_j + g_t shared(x[t]), j ascending, shared last
+    (g_t = 1 without a gate).
 """
 from __future__ import annotations
 
@@ -280,13 +285,28 @@ def moe_forward(layer, x_bits, tokens=None, want_rows=False) -> dict:
     for j in range(cfg.top_k):
         y += w[:, j:j + 1] * o[pos[:, j]]
     shared = None
+    shared_w = None
     if cfg.num_shared:
         g, u, d = layer.shared()
         shared = expert_ffn(x, dequant_qmat(cfg.quant, g), dequant_qmat(cfg.quant, u),
                             dequant_qmat(cfg.quant, d))
-        y += shared
+        gate_w = getattr(layer, "shared_gate_w", None)
+        if gate_w is None:
+            y += shared
+        else:
+            shared_w = shared_gate_weight(x_bits, gate_w)
+            y += shared_w[:, None] * shared
     out = dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, pos=pos, y=y)
     if want_rows:
         out["o"] = o
         out["shared"] = shared
+        out["shared_w"] = shared_w
     return out
+
+
+def shared_gate_weight(x_bits, gate_w_bits) -> np.ndarray:
+    """Weight of the shared expert per token, fp64 [T]: sigmoid of the fp32
+    gate logit x . w_s, formed in the R2 order (R7)."""
+    l = router_logits_fp32(x_bits, np.asarray(gate_w_bits, dtype=np.uint16)[None, :])[:, 0]
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-l.astype(np.float64)))

@@ -64,6 +64,7 @@ class LayerConfig:
     budget_frac: float
     decode_T: tuple
     prefill_T: int
+    shared_gate: bool = False  # the shared expert's output is scaled by sigmoid(x . w_s)
 
     @property
     def group(self) -> int:
@@ -262,6 +263,7 @@ class LayerWeights:
     sh_gate: Optional[QMat] = None
     sh_up: Optional[QMat] = None
     sh_down: Optional[QMat] = None
+    shared_gate_w: Optional[np.ndarray] = None  # uint16 bf16 bits [H]: the shared expert's gate row
 
     def expert(self, e: int):
         """(gate, up, down) QMats of routed expert e (views)."""
@@ -345,7 +347,8 @@ def make_layer(cfg: LayerConfig, seed: Optional[int] = None, threads: Optional[i
     """Seeded synthetic layer weights for `cfg` (deterministic in seed, whatever the thread count).
 
     Routed expert e draws from the stream (seed, 104729, e); the shared expert
-    from (seed, 104729, E)."""
+    from (seed, 104729, E); a shared-expert gate row w_s ~ N(0, 1/H) in bf16
+    from (seed, 4241)."""
     seed = cfg.seed if seed is None else seed
     if threads is None:
         threads = min(16, len(os.sched_getaffinity(0)))
@@ -361,6 +364,10 @@ def make_layer(cfg: LayerConfig, seed: Optional[int] = None, threads: Optional[i
     lw = LayerWeights(cfg, router_w, bias, gate, up, down)
     if cfg.num_shared:
         lw.sh_gate, lw.sh_up, lw.sh_down = _gen_experts(cfg, seed, E, 1, 1)
+        if cfg.shared_gate:
+            g = np.random.default_rng([seed, 4241])
+            lw.shared_gate_w = f32_to_bf16_bits(g.standard_normal(H, dtype=np.float32)
+                                                * np.float32(1.0 / math.sqrt(H)))
     return lw
 
 

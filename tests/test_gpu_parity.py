@@ -40,6 +40,13 @@ SMALL = {
     "longk_s": (CONFIGS["mixtral"].scaled(hidden=512, ffn=8192), (1, 3, 257)),
     "longk_g128_s": (CONFIGS["e256_int4g128"].scaled(hidden=512, ffn=8192, num_experts=8, top_k=2,
                                                        budget_frac=0.5), (1, 200)),
+    # a gated shared expert (its output weighted by sigmoid(x . w_s)) in three formats
+    "glm_gate_s": (CONFIGS["glm45_air"].scaled(hidden=1024, ffn=320, num_experts=16, top_k=4, budget_frac=0.2,
+                                               shared_gate=True), (1, 3, 8, 300)),
+    "e512_gate_s": (CONFIGS["e512_mxfp4"].scaled(hidden=1024, ffn=256, num_experts=64, budget_frac=0.18,
+                                                 shared_gate=True), (1, 5, 333)),
+    "nvfp4_gate_s": (CONFIGS["e256_nvfp4"].scaled(hidden=1024, ffn=256, num_experts=64, shared_gate=True),
+                     (2, 8, 129)),
 }
 
 
@@ -82,7 +89,7 @@ def test_layer_matches_oracle_all_resident(torch_cuda, name):
 
 
 @pytest.mark.parametrize("name", ["qwen_s", "glm_s", "e512_s", "mixtral_s", "e896_s", "g128_s", "nvfp4_s",
-                                  "longk_s", "longk_g128_s"])
+                                  "longk_s", "longk_g128_s", "glm_gate_s", "e512_gate_s"])
 @pytest.mark.parametrize("policy", ["lru", "lfu"])
 @pytest.mark.parametrize("pager", ["kernel", "dma"])
 def test_paged_output_is_bitwise_the_resident_output(torch_cuda, name, policy, pager):

@@ -30,7 +30,7 @@ LAYERS = {
     "int4_g128_shared": CONFIGS["e256_int4g128"].scaled(hidden=1024, ffn=256, num_experts=16, top_k=4,
                                                          num_shared=1, budget_frac=0.25),
     "nvfp4_shared": CONFIGS["e256_nvfp4"].scaled(hidden=1024, ffn=256, num_experts=16, top_k=4,
-                                                 budget_frac=0.25),
+                                                 budget_frac=0.25, shared_gate=True),
     "mxfp4_shared": CONFIGS["e512_mxfp4"].scaled(hidden=1024, ffn=256, num_experts=16, top_k=4,
                                                  budget_frac=0.25),
 }

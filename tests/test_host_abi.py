@@ -131,6 +131,13 @@ def test_int4_requires_biases_and_mxfp4_refuses_them(tiny_int4, tiny_fp4):
     assert _create_status(d)[0] == _capi.E_INVALID
 
 
+def test_shared_gate_needs_a_shared_expert(tiny_int4):
+    gw = np.zeros(tiny_int4.cfg.hidden, np.uint16)
+    d, keep = _desc_from(tiny_int4, shared_gate_w=gw.ctypes.data)
+    st, msg = _create_status(d)
+    assert st == _capi.E_INVALID and "shared_gate_w" in msg
+
+
 def test_shared_weights_must_match_num_shared(tiny_fp4):
     d, keep = _desc_from(tiny_fp4, num_shared=0)
     assert _create_status(d)[0] == _capi.E_INVALID

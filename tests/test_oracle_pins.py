@@ -452,6 +452,74 @@ def test_p8_mixed_routing_combine(router, shared):
     assert 0.0 < out["w"][:, 1:].min()
 
 
+# ----------------------------------------------------------------------------
+# P-14 gated shared expert: y = routed + sigmoid(x . w_s) * shared
+# ----------------------------------------------------------------------------
+def _gated(quant="int4_g64", seed=21):
+    cfg = _tiny(router="sigmoid", num_shared=1, quant=quant).scaled(shared_gate=True)
+    return cfg, make_layer(cfg, seed=seed)
+
+
+@pytest.mark.parametrize("quant", ["int4_g64", "mxfp4_g32", "nvfp4_g16"])
+def test_p14_gate_of_zero_halves_the_shared_expert(quant):
+    """w_s = 0: the gate logit is exactly 0 and sigmoid(0) = 1/2, so the gated
+    output is the ungated one minus half the shared expert's output, whose
+    value comes from per-element loops."""
+    cfg, layer = _gated(quant)
+    x = make_tokens(cfg, 3, seed=21)
+    layer.shared_gate_w = np.zeros(cfg.hidden, np.uint16)
+    gated = om.moe_forward(layer, x)
+    gw = layer.shared_gate_w
+    layer.shared_gate_w = None
+    plain = om.moe_forward(layer, x)
+    layer.shared_gate_w = gw
+    x64 = om.bf16_to_f64(x)
+    dq = lambda m: om.dequant_qmat(quant, m)
+    g, u, d = layer.shared()
+    for t in range(3):
+        sh = _loop_ffn(x64[t], dq(g), dq(u), dq(d))
+        assert np.allclose(gated["y"][t], plain["y"][t] - 0.5 * sh, rtol=1e-12, atol=1e-12)
+
+
+def test_p14_gate_weight_closed_form():
+    """x = 1 everywhere and w_s with one entry 2.0 (all exact): logit 2, weight
+    1 / (1 + e^-2); with the entry -2.0 the weight is 1 / (1 + e^2)."""
+    cfg, layer = _gated()
+    x = bf(np.ones((2, cfg.hidden)))
+    for v, want in ((2.0, 1.0 / (1.0 + math.exp(-2.0))), (-2.0, 1.0 / (1.0 + math.exp(2.0)))):
+        ws = np.zeros(cfg.hidden, np.float32)
+        ws[37] = v
+        layer.shared_gate_w = bf(ws)
+        assert np.all(om.shared_gate_weight(x, layer.shared_gate_w) == want)
+        out = om.moe_forward(layer, x, want_rows=True)
+        assert np.all(out["shared_w"] == want)
+
+
+def test_p14_saturated_gate_keeps_or_drops_the_shared_expert():
+    """w_s = +-c x (a large multiple of the token's own direction): the weight
+    saturates to 1 (the ungated layer) or to 0 (routed experts only, from
+    per-element loops): the gate scales the shared expert, not the routed sum."""
+    cfg, layer = _gated(seed=22)
+    x = make_tokens(cfg, 1, seed=22)
+    x64 = om.bf16_to_f64(x)
+    gw = layer.shared_gate_w
+    layer.shared_gate_w = None
+    plain = om.moe_forward(layer, x)
+    for sign in (1.0, -1.0):
+        layer.shared_gate_w = bf(sign * 64.0 * x64[0])
+        out = om.moe_forward(layer, x)
+        if sign > 0:
+            assert np.array_equal(out["y"], plain["y"])
+        else:
+            dq = lambda m: om.dequant_qmat(cfg.quant, m)
+            want = np.zeros(cfg.hidden)
+            for j in range(cfg.top_k):
+                g, u, d = layer.expert(int(out["idx"][0, j]))
+                want += out["w"][0, j] * _loop_ffn(x64[0], dq(g), dq(u), dq(d))
+            assert np.allclose(out["y"][0], want, rtol=1e-12, atol=1e-12)
+    layer.shared_gate_w = gw
+
+
 def test_p10_identical_experts_make_routing_irrelevant():
     cfg = _tiny(num_experts=6, top_k=3)
     layer = make_layer(cfg, seed=12)

@@ -2,7 +2,7 @@
 against the ordinary forward of the same layer: bitwise the same y and
 routing outputs, on two calls in a row (the second with fewer tokens, so it
 reuses a scratch that still holds the first call's buffers), on int4 (with
-the scaled fp16 copy of x), NVFP4 with a shared expert, and MXFP4 layers.
+the scaled fp16 copy of x), NVFP4 with a gated shared expert, and MXFP4 layers.
 Then the refusals: a T whose buffers exceed the static scratch, a budgeted
 layer, and kernel timing on."""
 import numpy as np
@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 LAYERS = {
     "int4": CONFIGS["qwen3_30b_a3b"].scaled(hidden=1024, ffn=256, num_experts=32),
-    "nvfp4_shared": CONFIGS["e256_nvfp4"].scaled(hidden=1024, ffn=256, num_experts=64),
+    "nvfp4_shared": CONFIGS["e256_nvfp4"].scaled(hidden=1024, ffn=256, num_experts=64, shared_gate=True),
     "mxfp4_shared": CONFIGS["e512_mxfp4"].scaled(hidden=1024, ffn=256, num_experts=64),
 }
 
