@@ -583,7 +583,10 @@ DECODE_WARM, DECODE_TIMED = 64, 256
 POLICY_RUNS = [("lru", dict(policy="lru")),
                ("lfu", dict(policy="lfu")),
                ("warm_d5", dict(policy="warm", decay_shift=5)),
-               ("warm_d5_prefetch2", dict(policy="warm", decay_shift=5, prefetch=2))]
+               ("warm_d5_prefetch2", dict(policy="warm", decay_shift=5, prefetch=2)),
+               # host threads compute the non-resident experts of each token
+               ("hybrid_lfu", dict(policy="lfu", hybrid=True)),
+               ("hybrid_warm_d5_prefetch2", dict(policy="warm", decay_shift=5, prefetch=2, hybrid=True))]
 
 
 def decode_policies(epq, torch, lw, cfg, dev, make_tokens):
@@ -610,12 +613,19 @@ def decode_policies(epq, torch, lw, cfg, dev, make_tokens):
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         s1 = layer.stats()
-        d = {k: s1[k] - s0[k] for k in ("hits", "misses", "bytes_h2d", "prefetched", "prefetch_hits")}
-        return {"tokens_per_s": round(len(xs_run) / dt, 1), "us_per_token": round(dt / len(xs_run) * 1e6, 2),
-                "hit_rate": round(d["hits"] / max(1, d["hits"] + d["misses"]), 4),
-                "misses_per_token": round(d["misses"] / len(xs_run), 3),
-                "h2d_MB_per_token": round(d["bytes_h2d"] / len(xs_run) / 1e6, 3),
-                "prefetched": d["prefetched"], "prefetch_hits": d["prefetch_hits"]}
+        d = {k: s1[k] - s0[k] for k in ("hits", "misses", "bytes_h2d", "prefetched", "prefetch_hits",
+                                        "host_experts", "host_ns")}
+        out = {"tokens_per_s": round(len(xs_run) / dt, 1), "us_per_token": round(dt / len(xs_run) * 1e6, 2),
+               "hit_rate": round(d["hits"] / max(1, d["hits"] + d["misses"] + d["host_experts"]), 4),
+               "misses_per_token": round(d["misses"] / len(xs_run), 3),
+               "h2d_MB_per_token": round(d["bytes_h2d"] / len(xs_run) / 1e6, 3),
+               "prefetched": d["prefetched"], "prefetch_hits": d["prefetch_hits"]}
+        if d["host_experts"]:
+            hb = d["host_experts"] * cfg.expert_bytes()
+            out.update({"host_experts_per_token": round(d["host_experts"] / len(xs_run), 3),
+                        "host_us_per_token": round(d["host_ns"] / len(xs_run) / 1e3, 2),
+                        "host_GBps": round(hb / max(d["host_ns"], 1), 2)})
+        return out
 
     out = {"budget": cfg.budget, "experts": cfg.num_experts, "warmup_tokens": DECODE_WARM,
            "timed_tokens": DECODE_TIMED, "runs": {}}

@@ -29,7 +29,8 @@ class Desc(ctypes.Structure):
                 ("decay_shift", c_i32), ("prefetch", c_i32), ("pager", c_i32), ("expert_profile", c_vp),
                 ("router_w", c_vp), ("router_bias", c_vp),
                 ("gate", QMat), ("up", QMat), ("down", QMat),
-                ("sh_gate", QMat), ("sh_up", QMat), ("sh_down", QMat), ("shared_gate_w", c_vp)]
+                ("sh_gate", QMat), ("sh_up", QMat), ("sh_down", QMat), ("shared_gate_w", c_vp),
+                ("hybrid", c_i32), ("host_threads", c_i32)]
 
 
 class RouteDbg(ctypes.Structure):
@@ -42,7 +43,7 @@ class CacheStats(ctypes.Structure):
                 ("bytes_h2d", c_u64), ("waves", c_u64), ("budget", c_i32), ("resident", c_i32),
                 ("policy", c_i32), ("decay_shift", c_i32), ("resident_bytes", c_u64),
                 ("expert_bytes", c_u64), ("prefetched", c_u64), ("prefetch_hits", c_u64),
-                ("prefetch", c_i32), ("pager", c_i32)]
+                ("prefetch", c_i32), ("pager", c_i32), ("host_experts", c_u64), ("host_ns", c_u64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -75,7 +76,7 @@ EXPORTS = {
     "strata_expert_profile_save": (c_i32, [c_vp, c_vp, c_i32]),
     "strata_expert_profile_load": (c_i32, [c_vp, c_vp, c_i32]),
     "strata_residency_replay": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_u64, c_i32,
-                                        c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(CacheStats)]),
+                                        c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(CacheStats)]),
 }
 
 _lib = None

@@ -14,7 +14,7 @@ void ResidencyManager::init(int num_experts, int budget, int policy, int decay_s
   expert_bytes_ = expert_bytes;
   n_ = 0;
   forwards = hits = misses = evictions = bytes_h2d = waves = 0;
-  prefetched = prefetch_hits = 0;
+  prefetched = prefetch_hits = host_experts = 0;
   slot_expert_.assign(budget, -1);
   expert_slot_.assign(num_experts, -1);
   last_use_.assign(num_experts, 0);
@@ -165,17 +165,46 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
   }
   for (int32_t e : pinned) keep_[e] = 0;
   for (int32_t e : needed) wave_of_[e] = -1;
+  hits += nh;
+  misses += nm;
+  bytes_h2d += nm * expert_bytes_;
+  waves += plan.size();
+  finish(needed, ahead);
+}
+
+void ResidencyManager::forward_hybrid(const std::vector<int32_t>& needed, std::vector<PlanEntry>& hit_list,
+                                      std::vector<int32_t>& host, std::vector<PlanEntry>& ahead) {
+  hit_list.clear();
+  host.clear();
+  ahead.clear();
+  if (needed.empty()) return;
+  ++n_;
+  ++forwards;
+  for (int32_t e : needed) {
+    if (expert_slot_[e] >= 0) {
+      hit_list.push_back({e, expert_slot_[e], false});
+      if (from_prefetch_[e]) {
+        ++prefetch_hits;
+        from_prefetch_[e] = 0;
+      }
+    } else {
+      host.push_back(e);
+    }
+  }
+  hits += hit_list.size();
+  host_experts += host.size();
+  ++waves;
+  finish(needed, ahead);
+}
+
+// Score updates of a forward, then the policy's pages ahead of need.
+void ResidencyManager::finish(const std::vector<int32_t>& needed, std::vector<PlanEntry>& ahead) {
   if (decay_shift_ > 0)
     for (int e = 0; e < num_experts_; ++e) score_[e] -= score_[e] >> decay_shift_;
   for (int32_t e : needed) {
     last_use_[e] = n_;
     score_[e] += kUnit;
   }
-  hits += nh;
-  misses += nm;
-  bytes_h2d += nm * expert_bytes_;
-  waves += plan.size();
-
   if (prefetch_ > 0) {
     std::vector<int32_t> out, in;
     for (int e = 0; e < num_experts_; ++e) (expert_slot_[e] < 0 ? out : in).push_back(e);

@@ -33,7 +33,12 @@
 //     the resident strictly, the candidate is paged into that slot;
 //   * a profile load sets the scores, then the B experts with the largest
 //     score (ties to the lower id) take the slots of the residents outside
-//     that set, newcomers ascending by id into freed slots ascending.
+//     that set, newcomers ascending by id into freed slots ascending;
+//   * a hybrid forward (host cores compute what the GPU does not hold:
+//     "Strata, Explained", section 2; the `hybrid` policy value of the
+//     "Documentation" page) runs its hits from their slots and hands every
+//     other needed expert to the host; it pages nothing for them, then updates
+//     scores and prefetches like any forward, as one wave.
 // None of this changes what a forward computes, only what it copies.
 #pragma once
 #include <stdint.h>
@@ -67,6 +72,10 @@ class ResidencyManager {
   // rebalances; `count` books the pages as prefetches (run time) or not
   // (create).  Fills `pages` with the copies to make.
   void load_profile(const uint64_t* scores, bool count, std::vector<PlanEntry>& pages);
+  // Hybrid forward: `hits` gets the resident experts of `needed` (ascending,
+  // unique) with their slots, `host` the others; `ahead` as in forward().
+  void forward_hybrid(const std::vector<int32_t>& needed, std::vector<PlanEntry>& hits,
+                      std::vector<int32_t>& host, std::vector<PlanEntry>& ahead);
   const std::vector<uint64_t>& scores() const { return score_; }
 
   int budget() const { return budget_; }
@@ -75,9 +84,10 @@ class ResidencyManager {
   int expert_in(int slot) const { return slot_expert_[slot]; }
 
   uint64_t forwards = 0, hits = 0, misses = 0, evictions = 0, bytes_h2d = 0, waves = 0;
-  uint64_t prefetched = 0, prefetch_hits = 0;
+  uint64_t prefetched = 0, prefetch_hits = 0, host_experts = 0;
 
  private:
+  void finish(const std::vector<int32_t>& needed, std::vector<PlanEntry>& ahead);
   bool rank_less(int a, int b) const;  // rank of a < rank of b (ids ignored)
   bool before(int a, int b) const;     // a is a better victim than b
   void page(int e, int slot, bool count, std::vector<PlanEntry>& pages);

@@ -19,6 +19,7 @@
 // forward waits for those pages.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <sched.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -33,6 +34,7 @@
 
 #include "../../include/strata_moe.h"
 #include "moe_common.h"
+#include "host_experts.h"
 #include "residency.h"
 
 namespace strata {
@@ -151,6 +153,15 @@ struct strata_moe {
 
   int32_t* h_counts = nullptr;  // pinned
   Tile* h_tiles = nullptr;      // pinned
+  // hybrid decode forwards: the host pool and pinned staging of the tokens,
+  // their grouping and the host-computed output rows
+  bool hybrid = false;
+  HostPool* pool = nullptr;
+  int32_t* h_perm = nullptr;    // pinned [kDecodeMaxT * k]
+  uint16_t* h_x = nullptr;      // pinned bf16 [kDecodeMaxT, H]
+  float* h_o = nullptr;         // pinned fp32 [kDecodeMaxT * k, H]
+  std::vector<float> h_xf, h_hbuf;
+  uint64_t host_ns = 0;         // wall time of the host expert computations
   hipStream_t copy_streams[kCopyStreams] = {};
   hipEvent_t ev_fwd_done = nullptr;
   hipEvent_t ev_counts = nullptr;  // the token counts have reached h_counts
@@ -296,6 +307,8 @@ static strata_status validate(const strata_moe_desc* d) {
   if (strata_status st = check_residency(d->num_experts, d->expert_budget, d->policy, d->decay_shift,
                                          d->prefetch, d->expert_profile))
     return st;
+  if (d->hybrid != 0 && d->hybrid != 1) return fail(STRATA_E_INVALID, "hybrid must be 0 or 1");
+  if (d->host_threads < 0) return fail(STRATA_E_INVALID, "host_threads must be >= 0");
   if (d->max_tokens > (1 << 20)) return fail(STRATA_E_UNSUPPORTED, "max_tokens > 2^20");
   if (d->hidden % 512) return fail(STRATA_E_UNSUPPORTED, "hidden must be a multiple of 512");
   if (d->ffn % 64) return fail(STRATA_E_UNSUPPORTED, "ffn must be a multiple of 64");
@@ -581,6 +594,9 @@ static void release(strata_moe* h) {
   if (h->host_store) (void)hipHostFree(h->host_store);
   if (h->h_counts) (void)hipHostFree(h->h_counts);
   if (h->h_tiles) (void)hipHostFree(h->h_tiles);
+  delete h->pool;
+  for (void* p : {(void*)h->h_perm, (void*)h->h_x, (void*)h->h_o})
+    if (p) (void)hipHostFree(p);
   delete h;
 }
 
@@ -745,6 +761,21 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   if ((st = dev_alloc(&h->d_distinct, 64))) return st;
   HIP_CHECK(hipMemset(h->d_distinct, 0, 64));
   if ((st = host_alloc(&h->h_counts, size_t(h->E) * 4))) return st;
+  h->hybrid = d->hybrid != 0;
+  if (h->hybrid) {
+    const size_t rows = size_t(kDecodeMaxT) * h->k;
+    if ((st = host_alloc(&h->h_perm, rows * 4)) || (st = host_alloc(&h->h_x, size_t(kDecodeMaxT) * h->H * 2)) ||
+        (st = host_alloc(&h->h_o, rows * h->H * 4)))
+      return st;
+    h->h_xf.resize(rows * h->H);
+    h->h_hbuf.resize(rows * h->F);
+    int nth = d->host_threads;
+    if (nth <= 0) {
+      cpu_set_t set;
+      nth = sched_getaffinity(0, sizeof set, &set) == 0 ? CPU_COUNT(&set) : 1;
+    }
+    h->pool = new HostPool(std::max(1, std::min(nth, 256)));
+  }
   if ((st = host_alloc(&h->h_tiles, h->ws.max_tiles * sizeof(Tile)))) return st;
 
   for (auto& cs : h->copy_streams) HIP_CHECK(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
@@ -947,6 +978,98 @@ static hipError_t page_ahead(strata_moe* h, const std::vector<PlanEntry>& pages,
   return hipSuccess;
 }
 
+// Waits, on the compute stream and on every copy stream, for the pages made
+// ahead of this forward (prefetch, profile loads).
+static hipError_t wait_ahead(strata_moe* h, hipStream_t s) {
+  if (!h->ahead_pending) return hipSuccess;
+  for (int i = 0; i < kCopyStreams; ++i) {
+    if (!h->ahead_used[i]) continue;
+    hipError_t e = hipStreamWaitEvent(s, h->ev_ahead[i], 0);
+    for (int c = 0; c < kCopyStreams && e == hipSuccess; ++c)
+      if (c != i) e = hipStreamWaitEvent(h->copy_streams[c], h->ev_ahead[i], 0);
+    if (e != hipSuccess) return e;
+    h->ahead_used[i] = false;
+  }
+  h->ahead_pending = false;
+  return hipSuccess;
+}
+
+// Decode forward of a hybrid layer, after routing: the resident experts run
+// on the GPU while the host threads compute the others from the pinned store;
+// their output rows are then copied into o for the combine.  The tokens,
+// their grouping and the counts reach the host with one wait.
+static strata_status forward_hybrid(strata_moe* h, const Workspace& ws, const void* x, int T, hipStream_t s) {
+  const int TK = T * h->k;
+  HIP_CHECK(hipMemcpyAsync(h->h_counts, ws.counts, size_t(h->E) * 4, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipMemcpyAsync(h->h_perm, ws.perm, size_t(TK) * 4, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipMemcpyAsync(h->h_x, x, size_t(T) * h->H * 2, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipEventRecord(h->ev_counts, s));
+  HIP_CHECK(wait_spin(h->ev_counts));
+  std::vector<int32_t> needed, off(h->E + 1, 0);
+  for (int e = 0; e < h->E; ++e) {
+    off[e + 1] = off[e] + h->h_counts[e];
+    if (h->h_counts[e] > 0) needed.push_back(e);
+  }
+  if (off[h->E] != TK) return fail(STRATA_E_HIP, "token counts do not add up to T*k");
+  std::vector<PlanEntry> hits, ahead;
+  std::vector<int32_t> host;
+  h->rm.forward_hybrid(needed, hits, host, ahead);
+  // GPU: the hits and the shared expert, one launch set
+  int n = 0;
+  for (const PlanEntry& p : hits) add_tiles(h, p.expert, p.slot, off[p.expert], h->h_counts[p.expert], true, n);
+  if (h->S) add_tiles(h, h->E, h->budget, TK, T, true, n);
+  if ((size_t)n > ws.max_tiles) return fail(STRATA_E_HIP, "tile list overflow");
+  if (n > 0)
+    HIP_CHECK(hipMemcpyAsync(ws.tiles_host, h->h_tiles, size_t(n) * sizeof(Tile), hipMemcpyHostToDevice, s));
+  if (h->ev_wave_done.empty()) {
+    hipEvent_t b;
+    HIP_CHECK(hipEventCreateWithFlags(&b, hipEventDisableTiming));
+    h->ev_wave_done.push_back(b);
+    for (int c = 0; c < kCopyStreams; ++c) {
+      hipEvent_t a;
+      HIP_CHECK(hipEventCreateWithFlags(&a, hipEventDisableTiming));
+      h->ev_copied.push_back(a);
+    }
+  }
+  HIP_CHECK(wait_ahead(h, s));
+  HIP_CHECK(run_experts(h, ws, x, ws.tiles_host, nullptr, n, true, T, s));
+  HIP_CHECK(hipEventRecord(h->ev_wave_done[0], s));
+  // host: the other experts, for their tokens (rows off[e] .. of the grouping)
+  if (!host.empty()) {
+    std::vector<HostJob> jobs;
+    int row = 0;
+    for (int32_t e : host) {
+      const int c = h->h_counts[e];
+      for (int i = 0; i < c; ++i) {
+        const int t = h->h_perm[off[e] + i];
+        const uint16_t* src = h->h_x + size_t(t) * h->H;
+        float* dst = h->h_xf.data() + size_t(row + i) * h->H;
+        for (int k = 0; k < h->H; ++k) {
+          const uint32_t u = uint32_t(src[k]) << 16;
+          memcpy(&dst[k], &u, 4);
+        }
+      }
+      jobs.push_back({h->host_store + h->slot_stride * e, h->wexp.data() + size_t(e) * kWexpCount, c,
+                      h->h_xf.data() + size_t(row) * h->H, h->h_o + size_t(row) * h->H});
+      row += c;
+    }
+    const auto t0 = std::chrono::steady_clock::now();
+    host_experts_run(*h->pool, jobs, h->H, h->F, h->quant, h->sshift, h->lay, h->h_hbuf.data());
+    h->host_ns += (uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(
+                      std::chrono::steady_clock::now() - t0)
+                      .count();
+    row = 0;
+    for (int32_t e : host) {
+      const int c = h->h_counts[e];
+      HIP_CHECK(hipMemcpyAsync(ws.o + size_t(off[e]) * h->H, h->h_o + size_t(row) * h->H, size_t(c) * h->H * 4,
+                               hipMemcpyHostToDevice, s));
+      row += c;
+    }
+  }
+  if (!ahead.empty()) HIP_CHECK(page_ahead(h, ahead, h->ev_wave_done[0]));
+  return STRATA_OK;
+}
+
 static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void* x, int T, void* y,
                                   hipStream_t s, const strata_route_dbg* dbg) {
   const bool decode = T <= kDecodeMaxT;
@@ -978,6 +1101,9 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
     HIP_CHECK(run_experts(h, ws, x, ws.tiles_dev, ws.ntiles, ub, decode, T, s));
     h->rm.forwards++;
     h->rm.waves++;
+  } else if (h->hybrid && decode) {
+    strata_status hs = forward_hybrid(h, ws, x, T, s);
+    if (hs) return hs;
   } else {
     HIP_CHECK(hipMemcpyAsync(h->h_counts, ws.counts, size_t(h->E) * 4, hipMemcpyDeviceToHost, s));
     HIP_CHECK(hipEventRecord(h->ev_counts, s));
@@ -1032,16 +1158,7 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
     }
     // Pages made ahead of this forward (prefetch, profile load) land before
     // its compute reads the slots and before any copy of it overwrites one.
-    if (h->ahead_pending) {
-      for (int i = 0; i < kCopyStreams; ++i) {
-        if (!h->ahead_used[i]) continue;
-        HIP_CHECK(hipStreamWaitEvent(s, h->ev_ahead[i], 0));
-        for (int c = 0; c < kCopyStreams; ++c)
-          if (c != i) HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_ahead[i], 0));
-        h->ahead_used[i] = false;
-      }
-      h->ahead_pending = false;
-    }
+    HIP_CHECK(wait_ahead(h, s));
     // A wave's misses go out first the pages that overwrite slots no compute
     // of this forward still reads, then per wave whose compute must finish
     // first (the latest wave of this forward that read a slot being
@@ -1253,6 +1370,8 @@ strata_status strata_expert_cache_stats(const strata_moe* h, strata_cache_stats*
   out->prefetch_hits = h->rm.prefetch_hits;
   out->prefetch = h->prefetch;
   out->pager = h->pager;
+  out->host_experts = h->rm.host_experts;
+  out->host_ns = h->host_ns;
   return STRATA_OK;
 }
 
@@ -1409,8 +1528,8 @@ strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32
                                       int32_t decay_shift, int32_t prefetch, const uint64_t* profile,
                                       uint64_t expert_bytes, int32_t n_forwards,
                                       const int32_t* needed_len, const int32_t* needed_flat,
-                                      int32_t* plan_slots, uint64_t* scores_out,
-                                      strata_cache_stats* out) {
+                                      const int32_t* hybrid_flags, int32_t* plan_slots,
+                                      uint64_t* scores_out, strata_cache_stats* out) {
   if (!out || n_forwards < 0 || (n_forwards > 0 && (!needed_len || !needed_flat)))
     return fail(STRATA_E_INVALID, "NULL argument or negative count");
   if (num_experts < 1 || num_experts > (1 << 20)) return fail(STRATA_E_INVALID, "num_experts out of range");
@@ -1429,12 +1548,25 @@ strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32
       if (e < 0 || e >= num_experts) return fail(STRATA_E_INVALID, "expert id out of range");
     std::sort(nd.begin(), nd.end());
     nd.erase(std::unique(nd.begin(), nd.end()), nd.end());
-    rm.forward(nd, plan, ahead);
-    for (auto& w : plan)
-      for (auto& p : w) {
-        if (plan_slots) plan_slots[out_pos] = p.slot;
+    if (hybrid_flags && hybrid_flags[f]) {
+      std::vector<PlanEntry> hit_list;
+      std::vector<int32_t> host;
+      rm.forward_hybrid(nd, hit_list, host, ahead);
+      size_t hi = 0;
+      for (int32_t e : nd) {  // ascending: the hit's slot, or -1 for a host expert
+        const bool hit = hi < hit_list.size() && hit_list[hi].expert == e;
+        if (plan_slots) plan_slots[out_pos] = hit ? hit_list[hi].slot : -1;
+        hi += hit;
         ++out_pos;
       }
+    } else {
+      rm.forward(nd, plan, ahead);
+      for (auto& w : plan)
+        for (auto& p : w) {
+          if (plan_slots) plan_slots[out_pos] = p.slot;
+          ++out_pos;
+        }
+    }
     // duplicates collapse: keep the output aligned with needed_len
     out_pos += (size_t)needed_len[f] - nd.size();
   }
@@ -1455,6 +1587,7 @@ strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32
   out->prefetch_hits = rm.prefetch_hits;
   out->prefetch = prefetch;
   out->pager = 0;
+  out->host_experts = rm.host_experts;
   if (scores_out) std::copy(rm.scores().begin(), rm.scores().end(), scores_out);
   return STRATA_OK;
 }

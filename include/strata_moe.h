@@ -162,6 +162,20 @@ typedef struct {
    * shared experts beside routed ones without saying how they are weighted;
    * both forms are offered. */
   const uint16_t* shared_gate_w;
+  /* Hybrid decode (the "Documentation" page's policy value hybrid; "Strata,
+   * Explained", section 2: the host computes the experts the GPU does not
+   * hold, at the same time): 0 = off; 1 = in a decode forward (T <= 8) of a
+   * budgeted layer, the experts resident at call start run on the GPU and
+   * every other needed expert is computed by host threads from the pinned
+   * store (fp32, each output row summed by one thread in a fixed order), with
+   * no page made for it; scores and prefetch (desc.prefetch) are updated as
+   * in any forward, so the cache still adapts.  y is then within the layer's
+   * tolerance of the all-resident y, not bitwise equal to it.  Prefill
+   * forwards page as usual. */
+  int32_t hybrid;
+  int32_t host_threads; /* hybrid: host threads computing experts (the
+                         * calling thread is one of them); 0 = the CPUs this
+                         * process may run on */
 } strata_moe_desc;
 
 /* Creates a layer.  Validates the descriptor, admits the weights (every MXFP4
@@ -276,6 +290,8 @@ typedef struct {
   int32_t prefetch;        /* as created                                       */
   int32_t pager;           /* the paging engine in use (KERNEL or DMA; 0 in a
                             * residency replay)                                */
+  uint64_t host_experts;   /* hybrid: needed experts computed on the host      */
+  uint64_t host_ns;        /* hybrid: wall time of those host computations     */
 } strata_cache_stats;
 
 /* Reads the counters.  Does no device work except, when budget == E, one
@@ -366,18 +382,20 @@ strata_status strata_expert_profile_load(strata_moe* h, const uint64_t* scores, 
  * decision.  policy, decay_shift, prefetch and profile (NULL or E scores
  * applied at create) mean what they mean in strata_moe_desc.  needed_flat
  * holds the needed expert ids of every forward back to back, needed_len[i] of
- * them for forward i (any order, duplicates ignored).  If plan_slots is not
- * NULL it receives, per forward and per needed expert in the order the
- * forward runs them (hits ascending, then misses by increasing key, the
- * coldest first), the slot used;
+ * them for forward i (any order, duplicates ignored).  hybrid_flags (NULL =
+ * none) marks the forwards that are hybrid decode forwards (see
+ * strata_moe_desc.hybrid).  If plan_slots is not NULL it receives, per
+ * forward and per needed expert in the order the forward runs them (hits
+ * ascending, then misses by increasing key, the coldest first; a hybrid
+ * forward: ascending id), the slot used (-1: computed on the host);
  * its length must be sum(needed_len).  If scores_out is not NULL it receives
  * the E final scores.  Errors: E_INVALID. */
 strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32_t policy,
                                       int32_t decay_shift, int32_t prefetch, const uint64_t* profile,
                                       uint64_t expert_bytes, int32_t n_forwards,
                                       const int32_t* needed_len, const int32_t* needed_flat,
-                                      int32_t* plan_slots, uint64_t* scores_out,
-                                      strata_cache_stats* out);
+                                      const int32_t* hybrid_flags, int32_t* plan_slots,
+                                      uint64_t* scores_out, strata_cache_stats* out);
 
 #ifdef __cplusplus
 }

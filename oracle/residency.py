@@ -46,7 +46,14 @@ possible:
   them in ascending id order.  At run time each such page counts as an
   eviction and a prefetch; at create it counts nothing;
 * prefetch_hits counts hits on an expert whose residency came from a prefetch
-  or a run-time profile load, once, at its first use.
+  or a run-time profile load, once, at its first use;
+* hybrid forward (the Documentation page's policy value `hybrid`, undefined
+  there; "Strata, Explained" section 2: the CPU computes the experts the GPU
+  does not hold, at the same time): hits are run from their slots, every
+  other needed expert is computed on the host and counted in host_experts;
+  nothing is paged for them, so slots, misses, evictions and bytes do not
+  move; the score updates and the prefetch step are those of any forward, and
+  the forward is one wave.
 
 Outputs of the layer do not depend on any of this; only the counters do.
 """
@@ -81,7 +88,7 @@ class ResidencyModel:
         self.from_prefetch = [False] * num_experts
         self.n = 0
         self.forwards = self.hits = self.misses = self.evictions = self.bytes_h2d = self.waves = 0
-        self.prefetched = self.prefetch_hits = 0
+        self.prefetched = self.prefetch_hits = self.host_experts = 0
         if profile is not None:
             self._set_profile(profile)
             self._rebalance(count=False)
@@ -195,6 +202,33 @@ class ResidencyModel:
             self._prefetch()
         return plan
 
+    def forward_hybrid(self, needed):
+        """A hybrid forward: returns (hits as (expert, slot) pairs, host-computed experts)."""
+        N = sorted(set(int(e) for e in needed))
+        if not N:
+            return [], []
+        self.n += 1
+        self.forwards += 1
+        res = self.resident()
+        hits = [(e, res[e]) for e in N if e in res]
+        host = [e for e in N if e not in res]
+        for e, _ in hits:
+            if self.from_prefetch[e]:
+                self.prefetch_hits += 1
+                self.from_prefetch[e] = False
+        if self.policy == WARM:
+            for e in range(self.E):
+                self.score[e] -= self.score[e] >> self.d
+        for e in N:
+            self.last_use[e] = self.n
+            self.score[e] += UNIT
+        self.hits += len(hits)
+        self.host_experts += len(host)
+        self.waves += 1
+        if self.P:
+            self._prefetch()
+        return hits, host
+
     def _prefetch(self):
         res = self.resident()
         outside = sorted((e for e in range(self.E) if e not in res),
@@ -210,4 +244,5 @@ class ResidencyModel:
         return dict(forwards=self.forwards, hits=self.hits, misses=self.misses,
                     evictions=self.evictions, bytes_h2d=self.bytes_h2d, waves=self.waves,
                     budget=self.B, resident=resident, resident_bytes=resident * self.expert_bytes,
-                    prefetched=self.prefetched, prefetch_hits=self.prefetch_hits)
+                    prefetched=self.prefetched, prefetch_hits=self.prefetch_hits,
+                    host_experts=self.host_experts)

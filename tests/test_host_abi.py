@@ -104,6 +104,8 @@ def tiny_fp4():
     ("max_tokens", 0, _capi.E_INVALID),
     ("num_experts", 2000, _capi.E_UNSUPPORTED),
     ("router_w", None, _capi.E_INVALID),
+    ("hybrid", 2, _capi.E_INVALID),
+    ("host_threads", -1, _capi.E_INVALID),
 ])
 def test_invalid_descriptors(tiny_int4, field, value, status):
     d, keep = _desc_from(tiny_int4, **{field: value})
@@ -297,6 +299,41 @@ def test_residency_replay_with_decay_prefetch_and_profile_matches_model(policy, 
                   "resident_bytes", "prefetched", "prefetch_hits"):
             assert got[k] == st[k], (trial, k, got[k], st[k])
         assert got["slots"].tolist() == want_slots, trial
+        assert got["scores"].tolist() == m.profile(), trial
+
+
+@pytest.mark.parametrize("policy,d,P", [(LRU, 0, 0), (LFU, 0, 2), (WARM, 3, 1)])
+def test_residency_replay_with_hybrid_forwards_matches_model(policy, d, P):
+    """Traces mixing hybrid decode forwards (hits from slots, the rest on the
+    host, nothing paged) with plain forwards: the C++ manager and the model
+    agree on every counter, slot (-1 for a host expert) and score."""
+    rng = np.random.default_rng(5 + d + P)
+    for trial in range(30):
+        E = int(rng.integers(2, 40))
+        B = int(rng.integers(1, E + 1))
+        P_ = min(P, B)
+        trace, flags = [], []
+        for f in range(int(rng.integers(1, 40))):
+            n = int(rng.integers(1, E + 1))
+            trace.append(rng.choice(E, size=n, replace=False).tolist())
+            flags.append(int(rng.random() < 0.6))
+        m = ResidencyModel(E, B, policy, expert_bytes=100, decay_shift=d, prefetch=P_)
+        want = []
+        for n, h in zip(trace, flags):
+            if h:
+                hits, host = m.forward_hybrid(n)
+                slot = dict(hits)
+                want += [slot.get(e, -1) for e in sorted(set(n))]
+            else:
+                for wave in m.forward(n):
+                    want += [s for (_, s, _) in wave]
+        got = epq.replay_residency(E, B, trace, policy=policy, expert_bytes=100, want_slots=True,
+                                   decay_shift=d, prefetch=P_, hybrid=flags)
+        st = m.stats()
+        for k in ("forwards", "hits", "misses", "evictions", "bytes_h2d", "waves", "resident",
+                  "prefetched", "prefetch_hits", "host_experts"):
+            assert got[k] == st[k], (trial, k, got[k], st[k])
+        assert got["slots"].tolist() == want, trial
         assert got["scores"].tolist() == m.profile(), trial
 
 

@@ -682,6 +682,40 @@ def test_p11_model_rejects_bad_budgets():
 U = 65536
 
 
+def test_p11c_hybrid_forwards_hand_worked():
+    """E = 5, B = 2, LFU, prefetch 1.  Create: slots [0, 1].
+    hybrid {2}: no hit; 2 on the host; scores e2 = 1U; prefetch pairs the best
+      non-resident (e2) with the coldest resident (e0: key (0, 0, 0)) and
+      pages it into slot 0 (an eviction and a prefetch).
+    hybrid {2, 3}: hit e2 (slot 0; a prefetch hit), 3 on the host; scores e2 =
+      2U, e3 = 1U; prefetch pages e3 over e1 (slot 1).
+    plain {4}: a miss; victims outside the wave: e3 (1U) before e2 (2U):
+      e4 takes slot 1."""
+    m = ResidencyModel(5, 2, LFU, expert_bytes=10, prefetch=1)
+    assert m.forward_hybrid([2]) == ([], [2])
+    assert m.resident() == {2: 0, 1: 1}
+    assert m.forward_hybrid([3, 2]) == ([(2, 0)], [3])
+    assert m.resident() == {2: 0, 3: 1}
+    assert m.forward([4]) == [[(4, 1, True)]]
+    st = m.stats()
+    assert (st["forwards"], st["hits"], st["host_experts"], st["misses"], st["evictions"], st["prefetched"],
+            st["prefetch_hits"], st["bytes_h2d"], st["waves"]) == (3, 1, 2, 1, 3, 2, 1, 30, 3)
+
+
+def test_p11c_hybrid_without_prefetch_moves_no_slot():
+    m = ResidencyModel(8, 3, LRU, expert_bytes=7)
+    for need in ([5, 6], [0, 7], [1, 2, 3, 4]):
+        m.forward_hybrid(need)
+    assert m.resident() == {0: 0, 1: 1, 2: 2}
+    st = m.stats()
+    assert st["misses"] == st["evictions"] == st["bytes_h2d"] == 0
+    # hits: e0 (second forward), e1 and e2 (third); on the host: 5, 6, 7, 3, 4
+    assert st["hits"] == 3 and st["host_experts"] == 5 and st["waves"] == 3
+    # the uses still count: a plain forward now evicts the least recent (e0,
+    # used in the second forward, before e1 and e2 of the third)
+    assert m.forward([6]) == [[(6, 0, True)]]
+
+
 def test_p11b_decay_changes_the_victim():
     # E=3, B=2 (slots hold 0 and 1).  Expert 0 is used three times, expert 2
     # twice later, then expert 1 is needed.  Scores under WARM d=1, by hand:
