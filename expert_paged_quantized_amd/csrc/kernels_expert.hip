@@ -560,7 +560,12 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
   const int h = lane >> 5;
   const uint32_t* xl = xs + (kb0 * 32 + h * 16);  // this lane's 32 inputs of block kb0, row 0
   const float* xsl = xsum + kb0 * 2 + h;
-  for (int i = 0; i < nkb; i += DEPTH) {
+  // One round of DEPTH slots from K-block i; RF: refill each slot with the
+  // K-block DEPTH later (clamped to the last one).  The last round refills
+  // nothing, so a wave whose K range is a multiple of DEPTH loads each of its
+  // blocks exactly once.
+  auto round = [&](int i, auto rf) {
+    constexpr bool RF = decltype(rf)::value;
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
       const int kbl = i + j;
@@ -581,8 +586,10 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
                      "+v"(m[1][1]), "+v"(m[1][2]), "+v"(m[1][3]), "+v"(m[2][0]), "+v"(m[2][1]),
                      "+v"(m[2][2]), "+v"(m[2][3]), "+v"(m[3][0]), "+v"(m[3][1]), "+v"(m[3][2]),
                      "+v"(m[3][3]), "+v"(s), "+v"(b)::"memory");
-        wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
-        ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes);
+        if constexpr (RF) {
+          wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
+          ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes);
+        }
         if (kbl < nkb) {
           float xsv[TT];  // sum(x) of the group: read first, used last
 #pragma unroll
@@ -613,8 +620,10 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
         for (int st = 0; st < 4; ++st) m[st] = dequant_nvfp4_step(wq[j][st], one);
         float s0 = e4m3_to_f32(ws[j] & 0xffu), s1 = e4m3_to_f32(ws[j] >> 8);
         asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(s0), "+v"(s1)::"memory");
-        wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
-        ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes);
+        if constexpr (RF) {
+          wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
+          ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes);
+        }
         if (kbl < nkb) {
 #pragma unroll
           for (int r = 0; r < TT; ++r) {
@@ -641,8 +650,10 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
         for (int st = 0; st < 4; ++st) m[st] = dequant_fp4_step(wq[j][st], 1.0f);
         float scale = __uint_as_float(ws[j] << 23);
         asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(scale)::"memory");
-        wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
-        ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes);
+        if constexpr (RF) {
+          wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
+          ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes);
+        }
         if (kbl < nkb) {
 #pragma unroll
           for (int r = 0; r < TT; ++r) {
@@ -660,7 +671,10 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
         }
       }
     }
-  }
+  };
+  int i = 0;
+  for (; i + DEPTH < nkb; i += DEPTH) round(i, std::true_type{});
+  round(i, std::false_type{});
 }
 
 // One dot-decode unit: row tile rt of tile t, contracted by the S waves of
@@ -1174,16 +1188,24 @@ int decode_grid(int N, int log2S, int n_tiles) {
 }
 
 // Dot decode eligibility and split for an N x K weight at T tokens: waves per
-// row tile (1..16, enough for about 16 waves per CU at one token, at least a
-// full ring of 16 K-blocks each), 16-byte staging pieces per thread per row (<= 4), and the
+// row tile (1..16), 16-byte staging pieces per thread per row (<= 4), and the
 // LDS the staged rows need (<= 64 KB).  Returns 0 if the MFMA kernel is to be
-// used instead.  Depends only on the layer shape and T.
+// used instead.  Depends only on the layer shape and T.  The split doubles
+// while each wave keeps a full ring of 16 K-blocks and the launch stays within
+// 8,192 waves, or, up to 4 splits, while each wave keeps 8 K-blocks and the
+// launch stays within 4,096 waves (small layers: shorter serial K loops).
 int decode_dot_waves(int N, int K, int quant, int tiles_per_token, int T) {
   if (T > 4) return 0;
   const int TT = T <= 1 ? 1 : (T <= 2 ? 2 : 4);
   const int KB = K / 64, units = tiles_per_token * (N / 32);
   int S = 1;
-  while (S < 16 && units * 2 * S <= 4096 && KB / (2 * S) >= 16) S *= 2;
+  while (S < 16) {
+    const int per_wave = KB / (2 * S), waves = units * 2 * S;
+    const bool full_ring = per_wave >= 16 && waves <= 8192;
+    const bool short_loop = per_wave >= 8 && waves <= 4096 && 2 * S <= 4;
+    if (!full_ring && !short_loop) break;
+    S *= 2;
+  }
   while (S < 16 && (K / 8 + 64 * S - 1) / (64 * S) > 4) S *= 2;
   if ((K / 8 + 64 * S - 1) / (64 * S) > 4) return 0;
   const size_t lds = (size_t)TT * (K * 2 + 16) + (quant == Q_INT4 ? (size_t)TT * (K / 32) * 4 : 0);
