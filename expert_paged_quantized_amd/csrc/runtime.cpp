@@ -95,10 +95,17 @@ thread_local KernelTimer g_ktimer;
 }  // namespace strata
 
 #ifndef STRATA_COPY_STREAMS
-#define STRATA_COPY_STREAMS 4
+#define STRATA_COPY_STREAMS 2
 #endif
 // Side streams the expert pages are copied on (all at the default priority).
+// A budgeted forward uses the caller's stream, the paged compute stream and
+// these: four streams, the hardware queues HIP gives a process by default.
 constexpr int kCopyStreams = STRATA_COPY_STREAMS;
+// CUs set aside for the page-in kernel of a budgeted layer (the copy streams'
+// CU mask); its expert GEMMs run on an internal stream masked to the others.
+// The runtime deals CU-mask bits round-robin over the XCDs, so the first 16
+// bits are two CUs of each of the 8 XCDs.
+constexpr int kPageCUs = 16;
 
 // Device buffers of one forward, carved from one block of device memory: the
 // handle's own (sized for max_tokens at create) or, for the no-allocation
@@ -163,6 +170,14 @@ struct strata_moe {
   std::vector<float> h_xf, h_hbuf;
   uint64_t host_ns = 0;         // wall time of the host expert computations
   hipStream_t copy_streams[kCopyStreams] = {};
+  // Budgeted layers: the expert GEMMs of a paged forward run on pstream, whose
+  // CU mask excludes the copy streams' CUs (a page-in workgroup's host reads
+  // stall the memory path of the CU it shares: expert GEMM launches beside it
+  // took 3-6x longer).  ev_pfork orders pstream after the forward's routing
+  // on the caller's stream, ev_pjoin the combine after pstream.  Null when
+  // the split is not in use (all experts resident, or the masks were refused).
+  hipStream_t pstream = nullptr;
+  hipEvent_t ev_pfork = nullptr, ev_pjoin = nullptr;
   hipEvent_t ev_fwd_done = nullptr;
   hipEvent_t ev_counts = nullptr;  // the token counts have reached h_counts
   bool fwd_recorded = false;
@@ -587,6 +602,9 @@ static void release(strata_moe* h) {
   if (h->ev_counts) (void)hipEventDestroy(h->ev_counts);
   for (auto cs : h->copy_streams)
     if (cs) (void)hipStreamDestroy(cs);
+  if (h->pstream) (void)hipStreamDestroy(h->pstream);
+  if (h->ev_pfork) (void)hipEventDestroy(h->ev_pfork);
+  if (h->ev_pjoin) (void)hipEventDestroy(h->ev_pjoin);
   void* dev[] = {h->d_pool, h->d_shared, h->d_router_w, h->d_router_bias, h->d_slot_ptr,
                  h->d_ws, h->d_distinct, h->d_wexp};
   for (void* p : dev)
@@ -778,7 +796,38 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   }
   if ((st = host_alloc(&h->h_tiles, h->ws.max_tiles * sizeof(Tile)))) return st;
 
-  for (auto& cs : h->copy_streams) HIP_CHECK(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  // copy streams: on a budgeted layer with enough CUs, masked to kPageCUs
+  // CUs with the paged compute stream on the rest; plain streams otherwise
+  // (also if the runtime refuses the masks)
+  {
+    int ncu = 0;
+    HIP_CHECK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, h->device));
+    bool split = h->budget < h->E && ncu >= 8 * kPageCUs;
+    if (split) {
+      std::vector<uint32_t> mc((ncu + 31) / 32, 0u), mp((ncu + 31) / 32, 0u);
+      for (int i = 0; i < ncu; ++i) (i < kPageCUs ? mc : mp)[i / 32] |= 1u << (i % 32);
+      for (auto& cs : h->copy_streams)
+        if (split && hipExtStreamCreateWithCUMask(&cs, (uint32_t)mc.size(), mc.data()) != hipSuccess) split = false;
+      if (split && hipExtStreamCreateWithCUMask(&h->pstream, (uint32_t)mp.size(), mp.data()) != hipSuccess)
+        split = false;
+      if (!split) {
+        (void)hipGetLastError();
+        for (auto& cs : h->copy_streams)
+          if (cs) {
+            (void)hipStreamDestroy(cs);
+            cs = nullptr;
+          }
+        if (h->pstream) (void)hipStreamDestroy(h->pstream);
+        h->pstream = nullptr;
+      }
+    }
+    if (split) {
+      HIP_CHECK(hipEventCreateWithFlags(&h->ev_pfork, hipEventDisableTiming));
+      HIP_CHECK(hipEventCreateWithFlags(&h->ev_pjoin, hipEventDisableTiming));
+    } else {
+      for (auto& cs : h->copy_streams) HIP_CHECK(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+    }
+  }
   HIP_CHECK(hipEventCreateWithFlags(&h->ev_fwd_done, hipEventDisableTiming));
   HIP_CHECK(hipEventCreateWithFlags(&h->ev_counts, hipEventDisableTiming));
   for (auto& e : h->ev_ahead) HIP_CHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
@@ -1156,9 +1205,16 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
         h->ev_copied.push_back(a);
       }
     }
+    // The expert GEMMs of this forward run on the paged compute stream ps
+    // (after the routing on s; the combine on s waits for them below).
+    hipStream_t ps = h->pstream ? h->pstream : s;
+    if (ps != s) {
+      HIP_CHECK(hipEventRecord(h->ev_pfork, s));
+      HIP_CHECK(hipStreamWaitEvent(ps, h->ev_pfork, 0));
+    }
     // Pages made ahead of this forward (prefetch, profile load) land before
     // its compute reads the slots and before any copy of it overwrites one.
-    HIP_CHECK(wait_ahead(h, s));
+    HIP_CHECK(wait_ahead(h, ps));
     // A wave's misses go out first the pages that overwrite slots no compute
     // of this forward still reads, then per wave whose compute must finish
     // first (the latest wave of this forward that read a slot being
@@ -1222,16 +1278,20 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
         for (int i = 0; i < kCopyStreams; ++i)
           if (used[i]) HIP_CHECK(hipEventRecord(h->ev_copied[w * kCopyStreams + i], h->copy_streams[i]));
       }
-      HIP_CHECK(run_experts(h, ws, x, ws.tiles_host + hb[w], nullptr, he[w] - hb[w], decode, T, s));
+      HIP_CHECK(run_experts(h, ws, x, ws.tiles_host + hb[w], nullptr, he[w] - hb[w], decode, T, ps));
       if (any_paged) {
         for (int i = 0; i < kCopyStreams; ++i)
-          if (used[i]) HIP_CHECK(hipStreamWaitEvent(s, h->ev_copied[w * kCopyStreams + i], 0));
-        HIP_CHECK(run_experts(h, ws, x, ws.tiles_host + he[w], nullptr, pe[w] - he[w], decode, T, s));
+          if (used[i]) HIP_CHECK(hipStreamWaitEvent(ps, h->ev_copied[w * kCopyStreams + i], 0));
+        HIP_CHECK(run_experts(h, ws, x, ws.tiles_host + he[w], nullptr, pe[w] - he[w], decode, T, ps));
       }
-      HIP_CHECK(hipEventRecord(h->ev_wave_done[w], s));
+      HIP_CHECK(hipEventRecord(h->ev_wave_done[w], ps));
     }
     // the policy's pages ahead of need, once this forward's experts are done
     if (!ahead.empty()) HIP_CHECK(page_ahead(h, ahead, h->ev_wave_done[nw - 1]));
+    if (ps != s) {
+      HIP_CHECK(hipEventRecord(h->ev_pjoin, ps));
+      HIP_CHECK(hipStreamWaitEvent(s, h->ev_pjoin, 0));
+    }
   }
 
   HIP_CHECK(timed(h, STRATA_K_COMBINE, s, [&]() {

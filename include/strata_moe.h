@@ -102,7 +102,9 @@ typedef enum {
 
 /* How missing experts travel from the pinned host store into HBM slots.
  * KERNEL: the library's page-in kernel reads the store through its device
- * mapping (64 small workgroups beside the expert kernels).  DMA: one
+ * mapping (64 small workgroups on 16 CUs set aside for paging: two per XCD,
+ * the copy streams' CU mask; the layer's expert kernels of paged forwards run
+ * on an internal stream masked to the other CUs).  DMA: one
  * hipMemcpyAsync per record on the copy streams (the DMA engines; no CU
  * time, but the HIP runtime held the host 5-15 ms inside single copy calls
  * now and then on layers with small records).  AUTO: KERNEL for records of
@@ -227,7 +229,8 @@ typedef struct {
  * budget is smaller than E it waits once for the per-expert token counts to
  * reach the host, decides hits and misses, and pages missing experts from the
  * pinned store into slots (by the engine desc->pager chose) on internal copy
- * streams; if
+ * streams, and runs the expert kernels on an internal compute stream (ordered
+ * after the routing on `stream`, and the combine on `stream` after it); if
  * more distinct experts are needed than there are slots, the policy's
  * hottest quarter of the slots stays put and the experts stream through the
  * rest in waves of half of it, so one wave's pages land while the previous
