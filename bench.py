@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="qwen3_30b_a3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hybrid-rows", type=int, default=0,
+                    help="hybrid layer whose prefill computes the missed experts with at most this many "
+                         "tokens on the host (0: every miss is paged)")
     ap.add_argument("--cpu-steps", type=int, default=6)
     ap.add_argument("--no-policies", action="store_true", help="skip the paged decode policy runs")
     ap.add_argument("--policy", default="warm", choices=["lru", "lfu", "warm"],
@@ -291,7 +294,8 @@ def main():
     lw = make_layer(cfg)
     log(f"[bench] generated in {time.time() - t0:.1f}s; creating layers")
     paged = epq.MoELayer.from_weights(lw, budget=cfg.budget, max_tokens=Tp, policy=args.policy,
-                                      decay_shift=5 if args.policy == "warm" else 0)
+                                      decay_shift=5 if args.policy == "warm" else 0,
+                                      hybrid=args.hybrid_rows > 0, hybrid_rows=args.hybrid_rows)
     resident = epq.MoELayer.from_weights(lw, budget=cfg.num_experts, max_tokens=Tp)
 
     n = W + K
@@ -547,8 +551,11 @@ def main():
                                f"{cfg.quant} {cfg.router} router"
                                + (f" Zipf({cfg.zipf_s}) bias" if cfg.zipf_s else "")
                                + f"; budget {cfg.budget}/{cfg.num_experts} slots, {args.policy.upper()}; "
-                               f"step = prefill {Tp} tokens + decode {Td} token",
-                   "prefill_T": Tp, "decode_T": Td, "budget": cfg.budget,
+                               f"step = prefill {Tp} tokens + decode {Td} token"
+                               + (f"; hybrid: the host computes the missed experts of at most "
+                                  f"{args.hybrid_rows} tokens in prefill and every miss in decode"
+                                  if args.hybrid_rows else ""),
+                   "prefill_T": Tp, "decode_T": Td, "budget": cfg.budget, "hybrid_rows": args.hybrid_rows,
                    "parallelism": "single GPU"},
         "roofline": roof,
         "decode_roofline": decode_roof,

@@ -47,7 +47,7 @@ class MoELayer:
     def __init__(self, *, hidden, ffn, num_experts, top_k, num_shared, quant, router, budget,
                  max_tokens, router_w, router_bias, gate, up, down, sh_gate=None, sh_up=None,
                  sh_down=None, policy="lru", decay_shift=0, prefetch=0, profile=None, device=-1,
-                 pager="auto", shared_gate_w=None, hybrid=False, host_threads=0):
+                 pager="auto", shared_gate_w=None, hybrid=False, host_threads=0, hybrid_rows=0):
         self.hidden, self.ffn, self.num_experts, self.top_k = hidden, ffn, num_experts, top_k
         self.num_shared, self.max_tokens = num_shared, max_tokens
         keep = []
@@ -62,7 +62,7 @@ class MoELayer:
         d.expert_budget, d.max_tokens, d.device = budget, max_tokens, device
         d.decay_shift, d.prefetch = decay_shift, prefetch
         d.pager = _PAGER[pager] if isinstance(pager, str) else pager
-        d.hybrid, d.host_threads = int(bool(hybrid)), host_threads
+        d.hybrid, d.host_threads, d.hybrid_rows = int(bool(hybrid)), host_threads, hybrid_rows
         if profile is not None:
             prof = _profile_array(profile, num_experts)
             keep.append(prof)
@@ -80,7 +80,7 @@ class MoELayer:
 
     @classmethod
     def from_weights(cls, lw, budget=None, policy="lru", max_tokens=None, device=-1, decay_shift=0,
-                     prefetch=0, profile=None, pager="auto", hybrid=False, host_threads=0):
+                     prefetch=0, profile=None, pager="auto", hybrid=False, host_threads=0, hybrid_rows=0):
         """Builds a layer from a weights object with .cfg and the packed arrays."""
         c = lw.cfg
         return cls(hidden=c.hidden, ffn=c.ffn, num_experts=c.num_experts, top_k=c.top_k,
@@ -91,7 +91,7 @@ class MoELayer:
                    down=lw.down, sh_gate=lw.sh_gate, sh_up=lw.sh_up, sh_down=lw.sh_down,
                    policy=policy, decay_shift=decay_shift, prefetch=prefetch, profile=profile,
                    device=device, pager=pager, shared_gate_w=getattr(lw, "shared_gate_w", None),
-                   hybrid=hybrid, host_threads=host_threads)
+                   hybrid=hybrid, host_threads=host_threads, hybrid_rows=hybrid_rows)
 
     # ------------------------------------------------------------------
     def forward(self, x, y=None, stream=None, dbg=False):
@@ -199,11 +199,15 @@ def _profile_array(profile, num_experts):
 
 
 def replay_residency(num_experts, budget, trace, policy="lru", expert_bytes=0, want_slots=False,
-                     decay_shift=0, prefetch=0, profile=None, hybrid=None):
+                     decay_shift=0, prefetch=0, profile=None, hybrid=None, rows=None, host_rows=0):
     """Dry-run of the residency policy on a trace of needed-expert lists (host
-    only); `hybrid` optionally flags the hybrid decode forwards of the trace.
-    Returns the counters, plus "slots" (want_slots) and the final "scores"."""
+    only); `hybrid` optionally flags the hybrid decode forwards of the trace;
+    host_rows > 0 replays the other forwards as hybrid prefills with that row
+    limit, `rows` then giving each needed expert's token count (a list per
+    forward, parallel to the trace).  Returns the counters, plus "slots"
+    (want_slots) and the final "scores"."""
     lens = np.array([len(n) for n in trace], dtype=np.int32)
+    nrows = None if rows is None else np.array([r for rr in rows for r in rr], dtype=np.int32)
     hyb = None if hybrid is None else np.ascontiguousarray(hybrid, dtype=np.int32)
     flat = np.array([e for n in trace for e in n], dtype=np.int32)
     slots = np.full(max(1, flat.size), -1, dtype=np.int32) if want_slots else None
@@ -214,7 +218,8 @@ def replay_residency(num_experts, budget, trace, policy="lru", expert_bytes=0, w
                                         prefetch, None if prof is None else prof.ctypes.data,
                                         expert_bytes, len(trace), _ptr(lens),
                                         _ptr(flat if flat.size else np.zeros(1, np.int32)),
-                                        _ptr(hyb), _ptr(slots), scores.ctypes.data, ctypes.byref(s)))
+                                        _ptr(hyb), _ptr(nrows), host_rows, _ptr(slots), scores.ctypes.data,
+                                        ctypes.byref(s)))
     res = s.as_dict()
     if want_slots:
         res["slots"] = slots[:flat.size]

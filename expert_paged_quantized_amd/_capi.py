@@ -30,7 +30,7 @@ class Desc(ctypes.Structure):
                 ("router_w", c_vp), ("router_bias", c_vp),
                 ("gate", QMat), ("up", QMat), ("down", QMat),
                 ("sh_gate", QMat), ("sh_up", QMat), ("sh_down", QMat), ("shared_gate_w", c_vp),
-                ("hybrid", c_i32), ("host_threads", c_i32)]
+                ("hybrid", c_i32), ("host_threads", c_i32), ("hybrid_rows", c_i32)]
 
 
 class RouteDbg(ctypes.Structure):
@@ -76,7 +76,8 @@ EXPORTS = {
     "strata_expert_profile_save": (c_i32, [c_vp, c_vp, c_i32]),
     "strata_expert_profile_load": (c_i32, [c_vp, c_vp, c_i32]),
     "strata_residency_replay": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_u64, c_i32,
-                                        c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(CacheStats)]),
+                                        c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp,
+                                        ctypes.POINTER(CacheStats)]),
 }
 
 _lib = None

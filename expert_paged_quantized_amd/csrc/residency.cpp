@@ -80,15 +80,17 @@ void ResidencyManager::load_profile(const uint64_t* scores, bool count, std::vec
 }
 
 void ResidencyManager::forward(const std::vector<int32_t>& needed,
-                               std::vector<std::vector<PlanEntry>>& plan, std::vector<PlanEntry>& ahead) {
+                               std::vector<std::vector<PlanEntry>>& plan, std::vector<PlanEntry>& ahead,
+                               const int32_t* rows, int host_rows, std::vector<int32_t>* host) {
   plan.clear();
   ahead.clear();
+  if (host) host->clear();
   if (needed.empty()) return;
   ++n_;
   ++forwards;
   std::vector<int32_t> order;
   order.reserve(needed.size());
-  uint64_t nh = 0;
+  uint64_t nh = 0, nm = 0;
   for (int32_t e : needed)
     if (expert_slot_[e] >= 0) {
       order.push_back(e);
@@ -99,10 +101,16 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
       }
     }
   for (int32_t e : needed)
-    if (expert_slot_[e] < 0) order.push_back(e);
+    if (expert_slot_[e] < 0) {
+      if (host && host_rows > 0 && rows[e] <= host_rows) {
+        host->push_back(e);  // hybrid prefill: computed by the host threads
+      } else {
+        order.push_back(e);
+        ++nm;
+      }
+    }
   // misses coldest first (keys before this forward's updates)
   std::sort(order.begin() + nh, order.end(), [&](int a, int b) { return before(a, b); });
-  const uint64_t nm = needed.size() - nh;
 
   // keep_: 1 = pinned for the forward; in_wave_: 1 = current wave, 2 = previous
   size_t W = budget_;
@@ -168,7 +176,8 @@ void ResidencyManager::forward(const std::vector<int32_t>& needed,
   hits += nh;
   misses += nm;
   bytes_h2d += nm * expert_bytes_;
-  waves += plan.size();
+  waves += plan.empty() ? 1 : plan.size();
+  if (host) host_experts += host->size();
   finish(needed, ahead);
 }
 

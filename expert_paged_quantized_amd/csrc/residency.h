@@ -38,7 +38,11 @@
 //     "Strata, Explained", section 2; the `hybrid` policy value of the
 //     "Documentation" page) runs its hits from their slots and hands every
 //     other needed expert to the host; it pages nothing for them, then updates
-//     scores and prefetches like any forward, as one wave.
+//     scores and prefetches like any forward, as one wave;
+//   * a hybrid prefill with row limit R hands the needed experts that are not
+//     resident and have at most R tokens to the host and runs the others as
+//     above (hits, misses in waves); scores and prefetch cover every needed
+//     expert; at least one wave is counted.
 // None of this changes what a forward computes, only what it copies.
 #pragma once
 #include <stdint.h>
@@ -65,9 +69,13 @@ class ResidencyManager {
 
   void init(int num_experts, int budget, int policy, int decay_shift, int prefetch, uint64_t expert_bytes);
   // `needed` must be ascending and unique.  Fills `waves` with the plan and
-  // `ahead` with the pages to make once the forward's compute is done.
+  // `ahead` with the pages to make once the forward's compute is done.  With
+  // `host` (hybrid prefill), the needed experts that are not resident and have
+  // at most host_rows tokens (rows[e]) go to `host` (ascending) instead of
+  // being paged; the scores and the prefetch still cover every needed expert.
   void forward(const std::vector<int32_t>& needed, std::vector<std::vector<PlanEntry>>& waves,
-               std::vector<PlanEntry>& ahead);
+               std::vector<PlanEntry>& ahead, const int32_t* rows = nullptr, int host_rows = 0,
+               std::vector<int32_t>* host = nullptr);
   // Sets the scores (E values, each <= kMaxScore; checked by the caller) and
   // rebalances; `count` books the pages as prefetches (run time) or not
   // (create).  Fills `pages` with the copies to make.

@@ -106,6 +106,8 @@ constexpr int kCopyStreams = STRATA_COPY_STREAMS;
 // The runtime deals CU-mask bits round-robin over the XCDs, so the first 16
 // bits are two CUs of each of the 8 XCDs.
 constexpr int kPageCUs = 16;
+// Tokens per host expert the host kernels take (hybrid_rows at most this).
+constexpr int kHostMaxRows = 8;
 
 // Device buffers of one forward, carved from one block of device memory: the
 // handle's own (sized for max_tokens at create) or, for the no-allocation
@@ -160,13 +162,17 @@ struct strata_moe {
 
   int32_t* h_counts = nullptr;  // pinned
   Tile* h_tiles = nullptr;      // pinned
-  // hybrid decode forwards: the host pool and pinned staging of the tokens,
-  // their grouping and the host-computed output rows
+  // hybrid forwards: the host pool and pinned staging of the tokens, their
+  // grouping and the host-computed output rows (decode: kDecodeMaxT tokens;
+  // with hybrid_rows, prefill: max_tokens tokens, at most E * hybrid_rows
+  // host rows)
   bool hybrid = false;
+  int hybrid_rows = 0;          // hybrid prefill: row limit of a host expert (0: none)
   HostPool* pool = nullptr;
-  int32_t* h_perm = nullptr;    // pinned [kDecodeMaxT * k]
-  uint16_t* h_x = nullptr;      // pinned bf16 [kDecodeMaxT, H]
-  float* h_o = nullptr;         // pinned fp32 [kDecodeMaxT * k, H]
+  int32_t* h_perm = nullptr;    // pinned [tokens * k]
+  uint16_t* h_x = nullptr;      // pinned bf16 [tokens, H]
+  float* h_o = nullptr;         // pinned fp32 [host rows, H]
+  hipEvent_t ev_hx = nullptr;   // perm and x of a hybrid prefill have reached the host
   std::vector<float> h_xf, h_hbuf;
   uint64_t host_ns = 0;         // wall time of the host expert computations
   hipStream_t copy_streams[kCopyStreams] = {};
@@ -324,6 +330,9 @@ static strata_status validate(const strata_moe_desc* d) {
     return st;
   if (d->hybrid != 0 && d->hybrid != 1) return fail(STRATA_E_INVALID, "hybrid must be 0 or 1");
   if (d->host_threads < 0) return fail(STRATA_E_INVALID, "host_threads must be >= 0");
+  if (d->hybrid_rows < 0 || d->hybrid_rows > kHostMaxRows)
+    return fail(STRATA_E_INVALID, "hybrid_rows must be in [0, 8]");
+  if (d->hybrid_rows > 0 && d->hybrid != 1) return fail(STRATA_E_INVALID, "hybrid_rows needs hybrid = 1");
   if (d->max_tokens > (1 << 20)) return fail(STRATA_E_UNSUPPORTED, "max_tokens > 2^20");
   if (d->hidden % 512) return fail(STRATA_E_UNSUPPORTED, "hidden must be a multiple of 512");
   if (d->ffn % 64) return fail(STRATA_E_UNSUPPORTED, "ffn must be a multiple of 64");
@@ -600,6 +609,7 @@ static void release(strata_moe* h) {
     if (e) (void)hipEventDestroy(e);
   if (h->ev_fwd_done) (void)hipEventDestroy(h->ev_fwd_done);
   if (h->ev_counts) (void)hipEventDestroy(h->ev_counts);
+  if (h->ev_hx) (void)hipEventDestroy(h->ev_hx);
   for (auto cs : h->copy_streams)
     if (cs) (void)hipStreamDestroy(cs);
   if (h->pstream) (void)hipStreamDestroy(h->pstream);
@@ -780,11 +790,15 @@ static strata_status create_impl(const strata_moe_desc* d, strata_moe* h) {
   HIP_CHECK(hipMemset(h->d_distinct, 0, 64));
   if ((st = host_alloc(&h->h_counts, size_t(h->E) * 4))) return st;
   h->hybrid = d->hybrid != 0;
+  h->hybrid_rows = h->hybrid ? d->hybrid_rows : 0;
   if (h->hybrid) {
-    const size_t rows = size_t(kDecodeMaxT) * h->k;
-    if ((st = host_alloc(&h->h_perm, rows * 4)) || (st = host_alloc(&h->h_x, size_t(kDecodeMaxT) * h->H * 2)) ||
+    const size_t toks = h->hybrid_rows > 0 ? std::max<size_t>(kDecodeMaxT, h->max_tokens) : size_t(kDecodeMaxT);
+    const size_t rows = std::max(size_t(kDecodeMaxT) * h->k,
+                                 std::min(toks * h->k, size_t(h->E) * size_t(h->hybrid_rows)));
+    if ((st = host_alloc(&h->h_perm, toks * h->k * 4)) || (st = host_alloc(&h->h_x, toks * h->H * 2)) ||
         (st = host_alloc(&h->h_o, rows * h->H * 4)))
       return st;
+    HIP_CHECK(hipEventCreateWithFlags(&h->ev_hx, hipEventDisableTiming));
     h->h_xf.resize(rows * h->H);
     h->h_hbuf.resize(rows * h->F);
     int nth = d->host_threads;
@@ -1043,6 +1057,47 @@ static hipError_t wait_ahead(strata_moe* h, hipStream_t s) {
   return hipSuccess;
 }
 
+// Computes the experts `host` on the host threads for their tokens (rows
+// off[e] .. off[e] + count of the grouping; token ids in h_perm, bf16 rows in
+// h_x, both on the host already) and copies their output rows into o on
+// stream s: plane 0 gets the rows, planes 1 .. planes-1 (a K-split down GEMM's
+// partial sums) get zeros, so the combine's plane sum is the host result.
+static strata_status host_experts_to_o(strata_moe* h, const Workspace& ws, const std::vector<int32_t>& host,
+                                       const std::vector<int32_t>& off, int planes, hipStream_t s) {
+  std::vector<HostJob> jobs;
+  int row = 0;
+  for (int32_t e : host) {
+    const int c = h->h_counts[e];
+    for (int i = 0; i < c; ++i) {
+      const int t = h->h_perm[off[e] + i];
+      const uint16_t* src = h->h_x + size_t(t) * h->H;
+      float* dst = h->h_xf.data() + size_t(row + i) * h->H;
+      for (int k = 0; k < h->H; ++k) {
+        const uint32_t u = uint32_t(src[k]) << 16;
+        memcpy(&dst[k], &u, 4);
+      }
+    }
+    jobs.push_back({h->host_store + h->slot_stride * e, h->wexp.data() + size_t(e) * kWexpCount, c,
+                    h->h_xf.data() + size_t(row) * h->H, h->h_o + size_t(row) * h->H});
+    row += c;
+  }
+  const auto t0 = std::chrono::steady_clock::now();
+  host_experts_run(*h->pool, jobs, h->H, h->F, h->quant, h->sshift, h->lay, h->h_hbuf.data());
+  h->host_ns +=
+      (uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0).count();
+  row = 0;
+  const int64_t plane = int64_t(ws.max_rows) * h->H;
+  for (int32_t e : host) {
+    const int c = h->h_counts[e];
+    HIP_CHECK(hipMemcpyAsync(ws.o + size_t(off[e]) * h->H, h->h_o + size_t(row) * h->H, size_t(c) * h->H * 4,
+                             hipMemcpyHostToDevice, s));
+    for (int p = 1; p < planes; ++p)
+      HIP_CHECK(hipMemsetAsync(ws.o + p * plane + size_t(off[e]) * h->H, 0, size_t(c) * h->H * 4, s));
+    row += c;
+  }
+  return STRATA_OK;
+}
+
 // Decode forward of a hybrid layer, after routing: the resident experts run
 // on the GPU while the host threads compute the others from the pinned store;
 // their output rows are then copied into o for the combine.  The tokens,
@@ -1085,35 +1140,8 @@ static strata_status forward_hybrid(strata_moe* h, const Workspace& ws, const vo
   HIP_CHECK(hipEventRecord(h->ev_wave_done[0], s));
   // host: the other experts, for their tokens (rows off[e] .. of the grouping)
   if (!host.empty()) {
-    std::vector<HostJob> jobs;
-    int row = 0;
-    for (int32_t e : host) {
-      const int c = h->h_counts[e];
-      for (int i = 0; i < c; ++i) {
-        const int t = h->h_perm[off[e] + i];
-        const uint16_t* src = h->h_x + size_t(t) * h->H;
-        float* dst = h->h_xf.data() + size_t(row + i) * h->H;
-        for (int k = 0; k < h->H; ++k) {
-          const uint32_t u = uint32_t(src[k]) << 16;
-          memcpy(&dst[k], &u, 4);
-        }
-      }
-      jobs.push_back({h->host_store + h->slot_stride * e, h->wexp.data() + size_t(e) * kWexpCount, c,
-                      h->h_xf.data() + size_t(row) * h->H, h->h_o + size_t(row) * h->H});
-      row += c;
-    }
-    const auto t0 = std::chrono::steady_clock::now();
-    host_experts_run(*h->pool, jobs, h->H, h->F, h->quant, h->sshift, h->lay, h->h_hbuf.data());
-    h->host_ns += (uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(
-                      std::chrono::steady_clock::now() - t0)
-                      .count();
-    row = 0;
-    for (int32_t e : host) {
-      const int c = h->h_counts[e];
-      HIP_CHECK(hipMemcpyAsync(ws.o + size_t(off[e]) * h->H, h->h_o + size_t(row) * h->H, size_t(c) * h->H * 4,
-                               hipMemcpyHostToDevice, s));
-      row += c;
-    }
+    strata_status hs = host_experts_to_o(h, ws, host, off, 1, s);
+    if (hs) return hs;
   }
   if (!ahead.empty()) HIP_CHECK(page_ahead(h, ahead, h->ev_wave_done[0]));
   return STRATA_OK;
@@ -1154,8 +1182,16 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
     strata_status hs = forward_hybrid(h, ws, x, T, s);
     if (hs) return hs;
   } else {
+    // hybrid prefill: the tokens and their grouping follow the counts to the
+    // host, for the experts the host will compute
+    const bool hprefill = h->hybrid && h->hybrid_rows > 0 && !decode;
     HIP_CHECK(hipMemcpyAsync(h->h_counts, ws.counts, size_t(h->E) * 4, hipMemcpyDeviceToHost, s));
     HIP_CHECK(hipEventRecord(h->ev_counts, s));
+    if (hprefill) {
+      HIP_CHECK(hipMemcpyAsync(h->h_perm, ws.perm, size_t(TK) * 4, hipMemcpyDeviceToHost, s));
+      HIP_CHECK(hipMemcpyAsync(h->h_x, x, size_t(T) * h->H * 2, hipMemcpyDeviceToHost, s));
+      HIP_CHECK(hipEventRecord(h->ev_hx, s));
+    }
     HIP_CHECK(wait_spin(h->ev_counts));
     std::vector<int32_t> needed;
     std::vector<int32_t> off(h->E + 1, 0);
@@ -1166,8 +1202,10 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
     if (off[h->E] != TK) return fail(STRATA_E_HIP, "token counts do not add up to T*k");
     std::vector<std::vector<PlanEntry>> plan;
     std::vector<PlanEntry> ahead;
-    h->rm.forward(needed, plan, ahead);
+    std::vector<int32_t> host;  // hybrid prefill: experts the host computes
+    h->rm.forward(needed, plan, ahead, h->h_counts, hprefill ? h->hybrid_rows : 0, hprefill ? &host : nullptr);
     // tile lists: per wave [hits (+ shared in wave 0)] [paged]
+    if (plan.empty()) plan.emplace_back();  // every needed expert on the host: the shared expert's wave
     const int nw = (int)plan.size();
     std::vector<int> hb(nw), he(nw), pe(nw);
     int n = 0;
@@ -1291,6 +1329,13 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
     if (ps != s) {
       HIP_CHECK(hipEventRecord(h->ev_pjoin, ps));
       HIP_CHECK(hipStreamWaitEvent(s, h->ev_pjoin, 0));
+    }
+    // hybrid prefill: the host computes its experts while the GPU runs the
+    // waves enqueued above; their rows reach o before the combine
+    if (!host.empty()) {
+      HIP_CHECK(wait_spin(h->ev_hx));
+      strata_status hs = host_experts_to_o(h, ws, host, off, h->ksplit, s);
+      if (hs) return hs;
     }
   }
 
@@ -1588,10 +1633,13 @@ strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32
                                       int32_t decay_shift, int32_t prefetch, const uint64_t* profile,
                                       uint64_t expert_bytes, int32_t n_forwards,
                                       const int32_t* needed_len, const int32_t* needed_flat,
-                                      const int32_t* hybrid_flags, int32_t* plan_slots,
-                                      uint64_t* scores_out, strata_cache_stats* out) {
+                                      const int32_t* hybrid_flags, const int32_t* needed_rows,
+                                      int32_t host_rows, int32_t* plan_slots, uint64_t* scores_out,
+                                      strata_cache_stats* out) {
   if (!out || n_forwards < 0 || (n_forwards > 0 && (!needed_len || !needed_flat)))
     return fail(STRATA_E_INVALID, "NULL argument or negative count");
+  if (host_rows < 0 || host_rows > kHostMaxRows || (host_rows > 0 && !needed_rows))
+    return fail(STRATA_E_INVALID, "host_rows must be in [0, 8], with needed_rows");
   if (num_experts < 1 || num_experts > (1 << 20)) return fail(STRATA_E_INVALID, "num_experts out of range");
   if (strata_status st = check_residency(num_experts, budget, policy, decay_shift, prefetch, profile)) return st;
   ResidencyManager rm;
@@ -1600,12 +1648,21 @@ strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32
   if (profile) rm.load_profile(profile, false, ahead);
   size_t pos = 0, out_pos = 0;
   std::vector<std::vector<PlanEntry>> plan;
+  std::vector<int32_t> rows(host_rows > 0 ? num_experts : 0), host;
   for (int32_t f = 0; f < n_forwards; ++f) {
     if (needed_len[f] < 0) return fail(STRATA_E_INVALID, "negative needed_len");
     std::vector<int32_t> nd(needed_flat + pos, needed_flat + pos + needed_len[f]);
-    pos += needed_len[f];
     for (int32_t e : nd)
       if (e < 0 || e >= num_experts) return fail(STRATA_E_INVALID, "expert id out of range");
+    if (host_rows > 0) {  // rows of each needed expert, at its first occurrence
+      std::fill(rows.begin(), rows.end(), -1);
+      for (int32_t j = 0; j < needed_len[f]; ++j) {
+        const int32_t e = needed_flat[pos + j], r = needed_rows[pos + j];
+        if (r < 1) return fail(STRATA_E_INVALID, "needed_rows entries must be >= 1");
+        if (rows[e] < 0) rows[e] = r;
+      }
+    }
+    pos += needed_len[f];
     std::sort(nd.begin(), nd.end());
     nd.erase(std::unique(nd.begin(), nd.end()), nd.end());
     if (hybrid_flags && hybrid_flags[f]) {
@@ -1620,10 +1677,17 @@ strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32
         ++out_pos;
       }
     } else {
-      rm.forward(nd, plan, ahead);
+      // a hybrid prefill (host_rows > 0): its run order, then its host
+      // experts ascending with slot -1
+      rm.forward(nd, plan, ahead, rows.data(), host_rows, host_rows > 0 ? &host : nullptr);
       for (auto& w : plan)
         for (auto& p : w) {
           if (plan_slots) plan_slots[out_pos] = p.slot;
+          ++out_pos;
+        }
+      if (host_rows > 0)
+        for (size_t i = 0; i < host.size(); ++i) {
+          if (plan_slots) plan_slots[out_pos] = -1;
           ++out_pos;
         }
     }

@@ -173,11 +173,19 @@ typedef struct {
    * no page made for it; scores and prefetch (desc.prefetch) are updated as
    * in any forward, so the cache still adapts.  y is then within the layer's
    * tolerance of the all-resident y, not bitwise equal to it.  Prefill
-   * forwards page as usual. */
+   * forwards page as usual unless hybrid_rows is set. */
   int32_t hybrid;
   int32_t host_threads; /* hybrid: host threads computing experts (the
                          * calling thread is one of them); 0 = the CPUs this
                          * process may run on */
+  /* Hybrid prefill (hybrid = 1 only): 0 = off; R in 1..8 = in a forward of
+   * more than 8 tokens of a budgeted layer, a needed expert that is not
+   * resident at call start and has at most R tokens is computed by the host
+   * threads (as above) instead of being paged, while the GPU runs and pages
+   * the others; scores and prefetch cover every needed expert.  Few-token
+   * experts cost the host little arithmetic but a whole record over the
+   * link, so the host takes part of the link's load. */
+  int32_t hybrid_rows;
 } strata_moe_desc;
 
 /* Creates a layer.  Validates the descriptor, admits the weights (every MXFP4
@@ -387,18 +395,24 @@ strata_status strata_expert_profile_load(strata_moe* h, const uint64_t* scores, 
  * holds the needed expert ids of every forward back to back, needed_len[i] of
  * them for forward i (any order, duplicates ignored).  hybrid_flags (NULL =
  * none) marks the forwards that are hybrid decode forwards (see
- * strata_moe_desc.hybrid).  If plan_slots is not NULL it receives, per
- * forward and per needed expert in the order the forward runs them (hits
- * ascending, then misses by increasing key, the coldest first; a hybrid
- * forward: ascending id), the slot used (-1: computed on the host);
+ * strata_moe_desc.hybrid).  host_rows (0..8) replays the other forwards as
+ * hybrid prefills with that row limit (strata_moe_desc.hybrid_rows); then
+ * needed_rows (parallel to needed_flat, each >= 1; a duplicate id keeps its
+ * first count) gives each needed expert's token count.  If plan_slots is not
+ * NULL it receives, per forward and per needed expert in the order the
+ * forward runs them (hits ascending, then misses by increasing key, the
+ * coldest first; a hybrid decode forward: ascending id; a hybrid prefill:
+ * that order, then its host experts ascending), the slot used (-1: computed
+ * on the host);
  * its length must be sum(needed_len).  If scores_out is not NULL it receives
  * the E final scores.  Errors: E_INVALID. */
 strata_status strata_residency_replay(int32_t num_experts, int32_t budget, int32_t policy,
                                       int32_t decay_shift, int32_t prefetch, const uint64_t* profile,
                                       uint64_t expert_bytes, int32_t n_forwards,
                                       const int32_t* needed_len, const int32_t* needed_flat,
-                                      const int32_t* hybrid_flags, int32_t* plan_slots,
-                                      uint64_t* scores_out, strata_cache_stats* out);
+                                      const int32_t* hybrid_flags, const int32_t* needed_rows,
+                                      int32_t host_rows, int32_t* plan_slots, uint64_t* scores_out,
+                                      strata_cache_stats* out);
 
 #ifdef __cplusplus
 }

@@ -53,7 +53,14 @@ possible:
   other needed expert is computed on the host and counted in host_experts;
   nothing is paged for them, so slots, misses, evictions and bytes do not
   move; the score updates and the prefetch step are those of any forward, and
-  the forward is one wave.
+  the forward is one wave;
+* hybrid prefill (the same policy for forwards of more than eight tokens,
+  with a row limit R): the needed experts that are not resident when the
+  forward starts and have at most R tokens are computed on the host (counted
+  in host_experts); the other needed experts run as an ordinary forward (hits,
+  then misses paged in waves, as above, the pinned quarter chosen among the
+  hits); the score updates and the prefetch step cover every needed expert,
+  and the forward counts at least one wave.
 
 Outputs of the layer do not depend on any of this; only the counters do.
 """
@@ -144,14 +151,22 @@ class ResidencyModel:
     def forward(self, needed):
         """Apply one forward with needed expert set `needed`; return the plan:
         a list of waves, each a list of (expert, slot, paged) tuples."""
+        return self.forward_split(needed)[0]
+
+    def forward_split(self, needed, rows=None, host_rows=0):
+        """A forward whose non-resident experts with at most `host_rows` tokens
+        (rows[e]) run on the host (hybrid prefill; host_rows 0: none).  Returns
+        (plan of the others, host experts ascending)."""
         N = sorted(set(int(e) for e in needed))
         if not N:
-            return []
+            return [], []
         self.n += 1
         self.forwards += 1
         res = self.resident()
-        hits = [e for e in N if e in res]
-        misses = sorted((e for e in N if e not in res), key=self._key)
+        host = [e for e in N if e not in res and host_rows > 0 and rows[e] <= host_rows]
+        run = [e for e in N if e not in host]
+        hits = [e for e in run if e in res]
+        misses = sorted((e for e in run if e not in res), key=self._key)
         for e in hits:
             if self.from_prefetch[e]:
                 self.prefetch_hits += 1
@@ -197,10 +212,11 @@ class ResidencyModel:
         self.hits += len(hits)
         self.misses += len(misses)
         self.bytes_h2d += len(misses) * self.expert_bytes
-        self.waves += len(plan)
+        self.waves += max(1, len(plan))
+        self.host_experts += len(host)
         if self.P:
             self._prefetch()
-        return plan
+        return plan, host
 
     def forward_hybrid(self, needed):
         """A hybrid forward: returns (hits as (expert, slot) pairs, host-computed experts)."""

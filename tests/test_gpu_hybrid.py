@@ -94,3 +94,61 @@ def test_hybrid_prefill_is_bitwise_the_paged_prefill(torch_cuda):
     assert a.stats()["host_experts"] == 0
     a.close()
     b.close()
+
+
+# hybrid prefill: a needed expert that is not resident and has at most R
+# tokens is computed on the host in a forward of more than 8 tokens
+PREFILL_LAYERS = {
+    "int4_zipf": (LAYERS["int4_zipf"], 4, [300, 129, 1, 257, 64, 3, 96]),
+    "int4_sigmoid_gated": (LAYERS["int4_sigmoid_gated"], 2, [40, 17, 2, 33]),
+    "mxfp4_shared": (LAYERS["mxfp4_shared"], 3, [300, 1, 120, 200]),
+    "nvfp4_shared": (LAYERS["nvfp4_shared"], 8, [250, 64, 4]),
+    # down GEMM split in two K planes (ffn 6144): host rows fill plane 0, zero plane 1
+    "int4_ksplit": (CONFIGS["mixtral"].scaled(hidden=512, ffn=6144, num_experts=8, top_k=2, budget_frac=0.375),
+                    4, [12, 20, 9, 1, 16]),
+}
+
+
+def _run_prefill(lw, xs, R, threads=0):
+    import expert_paged_quantized_amd as epq
+    cfg = lw.cfg
+    layer = epq.MoELayer.from_weights(lw, budget=cfg.budget, max_tokens=512, policy="lfu", prefetch=1,
+                                      hybrid=True, host_threads=threads, hybrid_rows=R)
+    ys, counts = [], []
+    for x in xs:
+        y, dbg = layer.forward(to_dev(x), dbg=True)
+        ys.append(y_bits(y))
+        counts.append(dbg["counts"].cpu().numpy())
+    st = layer.stats()
+    layer.close()
+    return ys, counts, st
+
+
+@pytest.mark.parametrize("name", list(PREFILL_LAYERS))
+def test_hybrid_prefill_matches_oracle_and_model(torch_cuda, name):
+    cfg, R, Ts = PREFILL_LAYERS[name]
+    lw = make_layer(cfg, seed=cfg.seed + 90)
+    xs = [make_tokens(cfg, T, step=i, seed=cfg.seed + 90) for i, T in enumerate(Ts)]
+    print(f"[hybrid prefill] {name} R={R}", flush=True)
+    ys, counts, st = _run_prefill(lw, xs, R)
+    model = ResidencyModel(cfg.num_experts, cfg.budget, "lfu", cfg.expert_bytes(), prefetch=1)
+    for i, (x, T) in enumerate(zip(xs, Ts)):
+        ref = om.moe_forward(lw, x)
+        assert_y_close(om.bf16_to_f64(ys[i]), ref["y"], f"{name} step {i} T={T}")
+        assert counts[i].tolist() == np.asarray(ref["counts"]).tolist()
+        need = np.nonzero(counts[i])[0].tolist()
+        if T <= 8:
+            model.forward_hybrid(need)
+        else:
+            model.forward_split(need, {e: int(counts[i][e]) for e in need}, host_rows=R)
+    want = model.stats()
+    for k in ("forwards", "hits", "misses", "evictions", "bytes_h2d", "waves", "resident", "prefetched",
+              "prefetch_hits", "host_experts"):
+        assert st[k] == want[k], (k, st[k], want[k])
+    assert st["host_experts"] > 0, "no expert went to the host"
+    # the same sequence again, and with one host thread: the same bits
+    ys2, _, _ = _run_prefill(lw, xs, R)
+    ys1, _, _ = _run_prefill(lw, xs, R, threads=1)
+    for i in range(len(Ts)):
+        assert np.array_equal(ys2[i], ys[i]), f"{name} step {i}: repeat differs"
+        assert np.array_equal(ys1[i], ys[i]), f"{name} step {i}: one host thread differs"

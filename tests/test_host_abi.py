@@ -106,6 +106,8 @@ def tiny_fp4():
     ("router_w", None, _capi.E_INVALID),
     ("hybrid", 2, _capi.E_INVALID),
     ("host_threads", -1, _capi.E_INVALID),
+    ("hybrid_rows", 2, _capi.E_INVALID),       # a row limit without hybrid
+    ("hybrid_rows", -1, _capi.E_INVALID),
 ])
 def test_invalid_descriptors(tiny_int4, field, value, status):
     d, keep = _desc_from(tiny_int4, **{field: value})
@@ -335,6 +337,61 @@ def test_residency_replay_with_hybrid_forwards_matches_model(policy, d, P):
             assert got[k] == st[k], (trial, k, got[k], st[k])
         assert got["slots"].tolist() == want, trial
         assert got["scores"].tolist() == m.profile(), trial
+
+
+def test_hybrid_rows_above_eight_is_refused(tiny_int4):
+    d, keep = _desc_from(tiny_int4, hybrid=1, hybrid_rows=9)
+    st, msg = _create_status(d)
+    assert st == _capi.E_INVALID and "hybrid_rows" in msg
+
+
+@pytest.mark.parametrize("policy,d,P,R", [(LRU, 0, 0, 2), (LFU, 0, 2, 4), (WARM, 3, 1, 8)])
+def test_residency_replay_with_hybrid_prefills_matches_model(policy, d, P, R):
+    """Traces of hybrid prefills (a needed expert that is not resident and has
+    at most R rows goes to the host) mixed with hybrid decode forwards: the C++
+    manager and the model agree on every counter, slot (-1 for a host expert,
+    listed after the forward's run order) and score."""
+    rng = np.random.default_rng(11 + d + P + R)
+    for trial in range(30):
+        E = int(rng.integers(2, 40))
+        B = int(rng.integers(1, E + 1))
+        P_ = min(P, B)
+        trace, rows, flags = [], [], []
+        for f in range(int(rng.integers(1, 40))):
+            n = int(rng.integers(1, E + 1))
+            need = rng.choice(E, size=n, replace=False).tolist()
+            trace.append(need)
+            rows.append([int(rng.integers(1, 2 * R + 2)) for _ in need])
+            flags.append(int(rng.random() < 0.25))
+        m = ResidencyModel(E, B, policy, expert_bytes=100, decay_shift=d, prefetch=P_)
+        want = []
+        for n, r, h in zip(trace, rows, flags):
+            if h:
+                hits, host = m.forward_hybrid(n)
+                slot = dict(hits)
+                want += [slot.get(e, -1) for e in sorted(set(n))]
+            else:
+                plan, host = m.forward_split(n, dict(zip(n, r)), host_rows=R)
+                for wave in plan:
+                    want += [s for (_, s, _) in wave]
+                want += [-1] * len(host)
+        got = epq.replay_residency(E, B, trace, policy=policy, expert_bytes=100, want_slots=True,
+                                   decay_shift=d, prefetch=P_, hybrid=flags, rows=rows, host_rows=R)
+        st = m.stats()
+        for k in ("forwards", "hits", "misses", "evictions", "bytes_h2d", "waves", "resident",
+                  "prefetched", "prefetch_hits", "host_experts"):
+            assert got[k] == st[k], (trial, k, got[k], st[k])
+        assert got["slots"].tolist() == want, trial
+        assert got["scores"].tolist() == m.profile(), trial
+
+
+def test_residency_replay_rejects_bad_row_limits():
+    with pytest.raises(epq.StrataError):
+        epq.replay_residency(4, 2, [[0]], host_rows=2)                  # no rows
+    with pytest.raises(epq.StrataError):
+        epq.replay_residency(4, 2, [[0]], rows=[[1]], host_rows=9)
+    with pytest.raises(epq.StrataError):
+        epq.replay_residency(4, 2, [[0]], rows=[[0]], host_rows=2)      # a count below 1
 
 
 def test_ctypes_mirrors_match_the_c_struct_sizes(tmp_path):

@@ -716,6 +716,42 @@ def test_p11c_hybrid_without_prefetch_moves_no_slot():
     assert m.forward([6]) == [[(6, 0, True)]]
 
 
+def test_p11d_hybrid_prefill_split_hand_worked():
+    """E = 8, B = 2, LRU, row limit 2.  Create: slots [0, 1].
+    {0: 5 rows, 1: 4, 3: 1, 5: 3}: hits 0, 1; e3 (1 row, not resident) to the
+      host; e5 (3 rows) is a miss.  Order [0, 1, 5] is longer than B, so
+      floor(B/4) = 0 hits are pinned, S = 2, W = 1, previous wave kept: waves
+      [0], [1], [5]; e5 may evict neither e5 (current) nor e1 (previous):
+      e0's slot 0.
+    {3: 2 rows, 5: 9}: e5 hits slot 0; e3 (2 rows, not resident) to the host.
+    {6: 1 row}: all on the host; no wave runs an expert, one is counted.
+    {1: 1 row}: e1 is resident (slot 1): a hit, whatever its rows."""
+    m = ResidencyModel(8, 2, LRU, expert_bytes=10)
+    rows = {0: 5, 1: 4, 3: 1, 5: 3}
+    plan, host = m.forward_split([0, 1, 3, 5], rows, host_rows=2)
+    assert plan == [[(0, 0, False)], [(1, 1, False)], [(5, 0, True)]] and host == [3]
+    assert m.resident() == {5: 0, 1: 1}
+    assert m.forward_split([3, 5], {3: 2, 5: 9}, host_rows=2) == ([[(5, 0, False)]], [3])
+    assert m.forward_split([6], {6: 1}, host_rows=2) == ([], [6])
+    assert m.forward_split([1], {1: 1}, host_rows=2) == ([[(1, 1, False)]], [])
+    st = m.stats()
+    assert (st["forwards"], st["hits"], st["misses"], st["evictions"], st["host_experts"], st["waves"],
+            st["bytes_h2d"]) == (4, 4, 1, 1, 3, 6, 10)
+    # every needed expert counts as used: LRU last uses are 1 (e0), 4 (e1),
+    # 2 (e3), 2 (e5), 3 (e6), so a plain forward needing e7 evicts e5
+    assert m.forward([7]) == [[(7, 0, True)]]
+
+
+def test_p11d_row_limit_zero_is_the_plain_forward():
+    a, b = ResidencyModel(16, 4, LFU, expert_bytes=3), ResidencyModel(16, 4, LFU, expert_bytes=3)
+    rng = np.random.default_rng(7)
+    for _ in range(30):
+        need = sorted(set(rng.integers(0, 16, size=6).tolist()))
+        rows = {e: int(rng.integers(1, 5)) for e in need}
+        assert a.forward(need) == b.forward_split(need, rows, host_rows=0)[0]
+    assert a.stats() == b.stats()
+
+
 def test_p11b_decay_changes_the_victim():
     # E=3, B=2 (slots hold 0 and 1).  Expert 0 is used three times, expert 2
     # twice later, then expert 1 is needed.  Scores under WARM d=1, by hand:
