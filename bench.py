@@ -44,6 +44,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# row limit of the hybrid comparison run (the best of 2, 3 and 4 on the
+# Qwen3-shaped layer: 351k, 403k, 369k tokens/s)
+HYBRID_ROWS = 3
 METRIC = "MoE-layer tokens/s (decode B=1, prefill 1180) + expert-weight HBM GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
@@ -354,6 +357,25 @@ def main():
     dt_r, _, _ = timed_region(resident, per_step_sync=False)
     _, per_r, tm_r = timed_region(resident, events=True)
     st = paged.stats()
+    # (4) the same budget and policy as a hybrid layer (the host computes the
+    # few-token missed experts of each prefill and every decode miss), beside
+    # the paged headline
+    hybrid = None
+    if args.hybrid_rows == 0 and cfg.budget < cfg.num_experts:
+        log(f"[bench] timed region: hybrid, row limit {HYBRID_ROWS}")
+        hl = epq.MoELayer.from_weights(lw, budget=cfg.budget, max_tokens=Tp, policy=args.policy,
+                                       decay_shift=5 if args.policy == "warm" else 0, hybrid=True,
+                                       hybrid_rows=HYBRID_ROWS)
+        dt_h, per_h, _ = timed_region(hl)
+        dh = dict(region_stats["delta"])
+        s1 = hl.stats()
+        hybrid = {"value": round(K * (Tp + Td) / dt_h, 1), "unit": "tokens/s", "hybrid_rows": HYBRID_ROWS,
+                  "ms_per_step": round(dt_h / K * 1e3, 4),
+                  "step_ms_median": round(float(np.median(per_h)) * 1e3, 3),
+                  "pages_per_step": round(dh["bytes_h2d"] / max(cfg.expert_bytes(), 1) / K, 2),
+                  "host_experts_total": s1["host_experts"], "host_ms_total": round(s1["host_ns"] / 1e6, 2),
+                  "note": "host experts and host time since the layer's creation (warm-up included)"}
+        hl.close()
 
     rows = Tp * cfg.top_k + cfg.num_shared * Tp
     up_fl = flops_gate_up(cfg, rows) * K
@@ -570,6 +592,7 @@ def main():
         "link": link, "tau": tau,
         "cache": st, "h2d_GBps": round(h2d_gbps, 2),
         "paged_decode": policies,
+        "hybrid": hybrid,
         "gpu": {"name": props.name, "cus": props.multi_processor_count},
     }
 
