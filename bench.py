@@ -493,6 +493,65 @@ def main():
 
     log("[bench] decode B=1 latency: eager and graph replay")
     dec_b1 = decode_b1()
+
+    # decode at each batch size the configuration lists (B tokens per
+    # forward, fresh tokens each time): all resident (wall time with a
+    # synchronisation after each forward, decode-kernel time by HIP events,
+    # expert bytes per forward) and paged as configured (B tokens per forward
+    # through the residency policy)
+    def decode_batches():
+        out = {}
+        nf = 48
+        for B in cfg.decode_T:
+            xb = [torch.from_numpy(make_tokens(cfg, B, step=900000 + 1000 * B + i).view(np.int16))
+                  .view(torch.bfloat16).to(dev) for i in range(2 * nf)]
+            yb = torch.empty((B, cfg.hidden), dtype=torch.bfloat16, device=dev)
+            for i in range(8):
+                resident.forward(xb[i], y=yb)
+            torch.cuda.synchronize()
+            resident.set_timing(True)
+            resident.timing()
+            per, nbytes = [], 0
+            for i in range(nf, 2 * nf):
+                a = time.perf_counter()
+                resident.forward(xb[i], y=yb)
+                torch.cuda.synchronize()
+                per.append(time.perf_counter() - a)
+            t = resident.timing()
+            resident.set_timing(False)
+            for i in range(nf, 2 * nf):  # the same forwards again, for their distinct experts
+                _, dbg = resident.forward(xb[i], y=yb, dbg=True)
+                nbytes += (int((dbg["counts"] > 0).sum().item()) + cfg.num_shared) * cfg.expert_bytes()
+            kms = t["decode_gate_up"][0] + t["decode_down"][0]
+            med = statistics.median(per)
+            pl = epq.MoELayer.from_weights(lw, budget=cfg.budget, max_tokens=max(cfg.decode_T),
+                                           policy=args.policy, decay_shift=5 if args.policy == "warm" else 0)
+            for i in range(nf):
+                pl.forward(xb[i], y=yb)
+            torch.cuda.synchronize()
+            s0 = pl.stats()
+            a = time.perf_counter()
+            for i in range(nf, 2 * nf):
+                pl.forward(xb[i], y=yb)
+            torch.cuda.synchronize()
+            dtp = time.perf_counter() - a
+            s1 = pl.stats()
+            pl.close()
+            hits, miss = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
+            out[str(B)] = {"all_resident_tokens_per_s": round(B / med, 1),
+                           "all_resident_us_per_forward_synced_median": round(med * 1e6, 1),
+                           "decode_kernel_us_per_forward": round(kms * 1e3 / nf, 2),
+                           "expert_bytes_per_forward": nbytes // nf,
+                           "decode_kernel_GBps": round(nbytes / (kms * 1e-3) / 1e9, 1),
+                           "paged_tokens_per_s": round(nf * B / dtp, 1),
+                           "paged_hit_rate": round(hits / max(hits + miss, 1), 3),
+                           "paged_misses_per_forward": round(miss / nf, 2)}
+        return out
+
+    dec_batches = None
+    if len(cfg.decode_T) > 1 and not args.no_policies:
+        log(f"[bench] decode at B = {cfg.decode_T}")
+        dec_batches = decode_batches()
     read_ceiling = epq.measure_hbm_read(0, 1 << 30, 5)
     decode_roof = {"bound": "hbm", "kernel": "decode gate+up and down (expert-weight bytes)",
                    "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -582,6 +641,7 @@ def main():
         "roofline": roof,
         "decode_roofline": decode_roof,
         "decode_b1_all_resident": dec_b1,
+        "decode_batches": dec_batches,
         "step_ms_median": round(statistics.median(per) * 1e3, 3),
         "step_ms_range": [round(min(per) * 1e3, 3), round(max(per) * 1e3, 3)],
         "all_resident": {"value": round(K * tokens_per_step / dt_r, 1),
