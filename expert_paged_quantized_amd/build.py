@@ -30,7 +30,7 @@ def _hipcc() -> str:
 
 def _flags():
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
         # packed fp32 instructions stay off (plain float code only)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,

@@ -766,9 +766,13 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
 // tiles of 32, a template parameter so the K loop has no branches).
 //
 // Every global load is a 16- or 4-byte LDS-DMA load (global memory straight
-// into LDS, no registers) into a ring of kPreStages stages, issued two
-// K-blocks ahead: per K-block the tile's activations (shared by the four
-// waves) and each wave's own weight codes and scales.  The only vector-memory
+// into LDS, no registers) into a ring of stages, issued S - 1 K-blocks ahead:
+// per K-block the tile's activations (shared by the four waves) and each
+// wave's own weight codes and scales.  A stage holds NCT * 4 KB of
+// activations and 9 KB of weights, so the 75 KB of a workgroup hold 3 stages
+// of a full token tile but 4 (2 column tiles) or 5 (1) of a small one: the
+// items of small experts, which stream a whole weight block for a few rows,
+// keep more of it in flight.  The only vector-memory
 // operations in the K loop are those DMA loads, so the wait before a K-block
 // is a fixed count of them.  One barrier per K-block: after it the K-block's
 // stage is complete for all waves and the stage read in the previous K-block
@@ -781,16 +785,24 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
 constexpr int kPreThreads = 256;
 constexpr int kPreRowTilesPerWave = 2;
 constexpr int kPreRowTilesPerItem = 8;
-constexpr int kPreStages = 3;
+constexpr int kPreLdsBytes = 3 * 25 * 1024;  // per workgroup; two workgroups per CU
 // Activation rows in LDS: 64 16-bit inputs = 128 bytes = 8 chunks of 16
 // bytes, unpadded.  Chunk c of row r sits in slot c ^ f(r),
 // f(r) = (r ^ (r >> 3)) & 7, so the 8 (or 16) consecutive rows that one
 // ds_read_b128 pass serves fall in distinct 16-byte bank groups whether the
 // LDS has 32 or 64 banks.
 constexpr int kRowBytes = 128;
-constexpr int kActBytes = kPrefillTM * kRowBytes;           // 16 KB
 constexpr int kWaveWBytes = 2 * kTileCodeBytes + 256;       // codes of 2 row tiles + their scales
-constexpr int kStageBytes = kActBytes + 4 * kWaveWBytes;    // 25 KB
+// activation bytes, stage bytes and stages of an item with NCT column tiles
+// (every stage starts at a multiple of 1 KB, so the row swizzle below keeps
+// its bank pattern in every stage)
+constexpr int pre_act_bytes(int nct) { return nct * 32 * kRowBytes; }
+constexpr int pre_stage_bytes(int nct) { return pre_act_bytes(nct) + 4 * kWaveWBytes; }
+constexpr int pre_stages(int nct) { return kPreLdsBytes / pre_stage_bytes(nct) < 5 ? kPreLdsBytes / pre_stage_bytes(nct) : 5; }
+static_assert(pre_stages(4) == 3 && pre_stages(3) == 3 && pre_stages(2) == 4 && pre_stages(1) == 5, "stages");
+static_assert(pre_stage_bytes(1) % 1024 == 0 && pre_stage_bytes(2) % 1024 == 0 && pre_stage_bytes(3) % 1024 == 0 &&
+                  pre_stage_bytes(4) % 1024 == 0,
+              "stage alignment");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -799,6 +811,16 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+// wait until at most n * PER loads are in flight, n in [0, NMAX] wave-uniform
+template <int PER, int NMAX>
+__device__ __forceinline__ void wait_vm_groups(int n) {
+  if constexpr (NMAX <= 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= NMAX) wait_vm<NMAX * PER>();
+    else wait_vm_groups<PER, NMAX - 1>(n);
+  }
 }
 
 
@@ -829,17 +851,13 @@ __device__ __forceinline__ void dma4(const void* g, const void* lds) {
 }
 
 template <int QF, bool GATE_UP, int NCT>
-__device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, int nb, int ks,
-                                             uint8_t* lds0, uint8_t* lds1, uint8_t* lds2) {
-  auto stage = [&](auto stc) -> uint8_t* {
-    constexpr int ST = decltype(stc)::value;
-    if constexpr (ST == 0) return lds0;
-    else if constexpr (ST == 1) return lds1;
-    else return lds2;
-  };
+__device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, int nb, int ks, uint8_t* lds) {
+  constexpr int S = pre_stages(NCT);
+  constexpr int SB = pre_stage_bytes(NCT);
+  constexpr int kActBytes = pre_act_bytes(NCT);
+  auto stage = [&](auto stc) -> uint8_t* { return lds + decltype(stc)::value * SB; };
   using SL = ScaleLayout<QF>;
   constexpr int RTW = kPreRowTilesPerWave;
-  constexpr int S = kPreStages;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nrt = p.N >> 5;
@@ -956,30 +974,37 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
       }
     }
   };
-  // Step kb: wait for this wave's DMA of K-block kb (the NCT + 3 loads of
-  // K-block kb + 1 may still be in flight), barrier (every wave's DMA of kb
-  // is in LDS; every wave is done with stage kb - 1), compute K-block kb,
-  // issuing the DMA of K-block kb + 2 into stage kb - 1 after its first reads.
+  // Step kb: wait for this wave's DMA of K-block kb (the loads of the
+  // K-blocks after it, up to S - 2 of them, may still be in flight), barrier
+  // (every wave's DMA of kb is in LDS; every wave is done with stage kb - 1),
+  // compute K-block kb, issuing the DMA of K-block kb + S - 1 into stage
+  // kb - 1 after its first reads.  No DMA is issued past the last K-block;
+  // the waits of the last steps count only the loads that were issued.
   constexpr int kPerStep = NCT + RTW + 1;
+  static_assert((S - 2) * kPerStep < 64, "vmcnt range");
   auto one_step = [&](int kb, auto uc) {
     constexpr int U = decltype(uc)::value;  // kb % S
-    wait_vm<kPerStep>();
+    wait_vm_groups<kPerStep, S - 2>(KB - 1 - kb);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    compute(std::integral_constant<int, U>{}, [&] { dma(std::integral_constant<int, (U + 2) % S>{}, kb + 2); });
+    compute(std::integral_constant<int, U>{}, [&] {
+      if (kb + S - 1 < KB) dma(std::integral_constant<int, (U + S - 1) % S>{}, kb + S - 1);
+    });
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  dma(std::integral_constant<int, 0>{}, 0);
-  dma(std::integral_constant<int, 1>{}, 1);
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((I < KB ? dma(std::integral_constant<int, I>{}, I) : void()), ...);
+  }(std::make_integer_sequence<int, S - 1>{});
   int kb = 0;
   for (; kb + S <= KB; kb += S) {
-    one_step(kb + 0, std::integral_constant<int, 0>{});
-    one_step(kb + 1, std::integral_constant<int, 1>{});
-    one_step(kb + 2, std::integral_constant<int, 2>{});
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (one_step(kb + I, std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, S>{});
   }
-  if (kb + 0 < KB) one_step(kb + 0, std::integral_constant<int, 0>{});
-  if (kb + 1 < KB) one_step(kb + 1, std::integral_constant<int, 1>{});
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((kb + I < KB ? one_step(kb + I, std::integral_constant<int, I>{}) : void()), ...);
+  }(std::make_integer_sequence<int, S - 1>{});
   // no DMA may still be writing LDS when the next item starts
   wait_vm<0>();
 
@@ -1024,23 +1049,42 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
 
 template <int QF, bool GATE_UP>
 __global__ __launch_bounds__(kPreThreads, 2) void moe_prefill_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kPreLdsBytes];
   const int nrt = p.N >> 5;
   const int n_nb = (nrt + kPreRowTilesPerItem - 1) / kPreRowTilesPerItem;
   const int n_tiles = p.n_tiles_dev ? p.n_tiles_dev[0] : p.n_tiles;
   const int per_tile = n_nb * p.ksplit;
   const int n_items = n_tiles * per_tile;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  // Consecutive workgroups are dispatched to the 8 XCDs in turn, so those
+  // with equal blockIdx % 8 share an XCD and its L2.  With few items per
+  // tile (at most 16 row blocks and K ranges) the tiles of the list are dealt
+  // to the XCDs in a snake order (0..7, 7..0, ...), which keeps the work of
+  // the XCDs even under the heaviest-first list, and all the items of a tile
+  // (which read the same activations) run on the same XCD, about at the same
+  // time: each XCD's workgroups take its items in turn.  With more (a wide
+  // expert: its row blocks are the bulk of the bytes) the items go out in
+  // list order, which puts the same row block of an expert's consecutive
+  // tiles on one XCD when per_tile is a multiple of 8.
+  const int G = gridDim.x;
+  const bool by_xcd = G % 8 == 0 && G > 8 && per_tile <= 16;
+  const int x = blockIdx.x & 7, gx = by_xcd ? G >> 3 : G;
+  const int n_local = by_xcd ? ((n_tiles + 7) >> 3) * per_tile : n_items;  // XCD: rounds of 8 tiles
+  for (int i = by_xcd ? (blockIdx.x >> 3) : blockIdx.x; i < n_local; i += gx) {
+    int item = i;
+    if (by_xcd) {
+      const int r = (i / per_tile);  // this XCD's r-th tile: list tile 8r + x or 8r + 7 - x
+      const int tl = 8 * r + ((r & 1) ? 7 - x : x);
+      if (tl >= n_tiles) continue;
+      item = tl * per_tile + i % per_tile;
+    }
     const Tile t = p.tiles[item / per_tile];
     const int rem = item % per_tile;
     const int nb = rem / p.ksplit, ks = rem % p.ksplit;
     switch ((t.nrows + 31) >> 5) {
-      case 1: prefill_item<QF, GATE_UP, 1>(p, t, nb, ks, lds0, lds1, lds2); break;
-      case 2: prefill_item<QF, GATE_UP, 2>(p, t, nb, ks, lds0, lds1, lds2); break;
-      case 3: prefill_item<QF, GATE_UP, 3>(p, t, nb, ks, lds0, lds1, lds2); break;
-      default: prefill_item<QF, GATE_UP, 4>(p, t, nb, ks, lds0, lds1, lds2); break;
+      case 1: prefill_item<QF, GATE_UP, 1>(p, t, nb, ks, lds); break;
+      case 2: prefill_item<QF, GATE_UP, 2>(p, t, nb, ks, lds); break;
+      case 3: prefill_item<QF, GATE_UP, 3>(p, t, nb, ks, lds); break;
+      default: prefill_item<QF, GATE_UP, 4>(p, t, nb, ks, lds); break;
     }
     __syncthreads();
   }

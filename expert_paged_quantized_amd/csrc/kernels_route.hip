@@ -393,14 +393,27 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 
 // exclusive scan over up to 1024 values held one per thread of a 1024-thread
 // workgroup; returns the thread's prefix and the total
+// inclusive prefix sum over the wave: row shifts 1, 2, 4, 8 inside each
+// 16-lane row (lanes shifted in from outside the row add 0), then the row
+// totals broadcast forward (lane 15 into row 1, 47 into row 3; lane 31 into
+// rows 2 and 3)
+template <int CTRL, int ROWS, int BANKS>
+__device__ __forceinline__ int dpp_add(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, BANKS, true);
+}
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v = dpp_add<0x111, 0xf, 0xf>(v);  // row_shr:1
+  v = dpp_add<0x112, 0xf, 0xf>(v);  // row_shr:2
+  v = dpp_add<0x114, 0xf, 0xf>(v);  // row_shr:4
+  v = dpp_add<0x118, 0xf, 0xf>(v);  // row_shr:8
+  v = dpp_add<0x142, 0xa, 0xf>(v);  // row_bcast:15
+  v = dpp_add<0x143, 0xc, 0xf>(v);  // row_bcast:31
+  return v;
+}
+
 __device__ __forceinline__ int block_scan1024(int v, int* wave_tot, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += n;
-  }
+  const int inc = wave_inclusive_scan(v);
   if (lane == 63) wave_tot[wave] = inc;
   __syncthreads();
   int wbase = 0, tot = 0;
@@ -424,21 +437,29 @@ __device__ __forceinline__ int block_scan1024(int v, int* wave_tot, int& total) 
 // tiles (4, 3, 2, 1), experts ascending inside a group.  Tiles cover disjoint
 // rows, so their order changes no result.  With one tile per expert (decode)
 // the order is simply by expert.
+// pre_used (>= 0 only with one tile per expert): this thread's exclusive
+// prefix of used experts and, in pre_total, their number, when the caller
+// has scanned them already (then nt = used and both scans below are that one).
 __device__ __forceinline__ void emit_counts_and_tiles(int c, int o, int total, int T, int k, int E,
                                                       int S, int tile_rows, int shared_slot,
                                                       int* wave_tot, int32_t* counts,
                                                       int32_t* offsets, Tile* tiles,
                                                       int32_t* n_tiles,
-                                                      unsigned long long* distinct_total) {
+                                                      unsigned long long* distinct_total,
+                                                      int pre_used = -1, int pre_total = 0) {
   const int e = threadIdx.x;
   const bool used = e < E && c > 0;
   const int nt = used ? (c + tile_rows - 1) / tile_rows : 0;
   const int TK = T * k;
   const int nsh = S ? (T + tile_rows - 1) / tile_rows : 0;
-  int ntot;
-  const int to = block_scan1024(nt, wave_tot, ntot);
-  int nd_tot;
-  (void)block_scan1024(used ? 1 : 0, wave_tot, nd_tot);
+  int ntot, nd_tot, to;
+  if (pre_used >= 0) {
+    to = pre_used;
+    ntot = nd_tot = pre_total;
+  } else {
+    to = block_scan1024(nt, wave_tot, ntot);
+    (void)block_scan1024(used ? 1 : 0, wave_tot, nd_tot);
+  }
   auto put = [&](int at, int ex, int slot, int row_begin, int nrows, int first, int count) {
     Tile tl;
     tl.expert = ex;
@@ -578,6 +599,20 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 // list as the multi-block passes.
 // ---------------------------------------------------------------------------
 constexpr int kSmallT = 16;
+// Small batches with few experts select by counting: T * E^2 comparisons
+// spread over the workgroup's 1024 threads, against k dependent rounds of a
+// one-wave selection.
+constexpr int kRankCountWork = 65536;  // largest T * E * E
+constexpr int kRankCountSlots = 1024;  // largest T * E
+
+// Selection key of a logit of expert e: larger is better.  The fp32 order
+// (with -0 == +0: adding +0 maps -0 to +0) in the high word, the complement
+// of the id in the low word, so equal logits rank the lower id first.
+__device__ __forceinline__ uint64_t select_key(float l, int e) {
+  const uint32_t u = __float_as_uint(l + 0.0f);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+}
 
 template <int JPL>
 __global__ __launch_bounds__(1024) void route_small_kernel(
@@ -589,14 +624,63 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
   __shared__ unsigned int mask[kPermMaxE];  // bit = token (T <= 16)
   __shared__ int off[kPermMaxE];
   __shared__ int sel[kSmallT * 32];
+  __shared__ float selv[kSmallT * 32];
+  __shared__ uint64_t keys[kRankCountSlots];
   __shared__ int wave_tot[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += 1024) mask[e] = 0u;
+  // Selection by counting (uniform branch): the expert of slot q = t * E + e
+  // takes rank r = the number of its token's keys above its own, and the
+  // ranks below k are the picks in order.
+  // The slot's comparisons are split over P = 1024 / (T * E) threads
+  // (a power of two): thread (part, q) counts over keys part * E / P ..
+  // (part + 1) * E / P - 1 and the parts meet in an LDS sum.
+  const bool by_count = T * E <= kRankCountSlots && T * E * E <= kRankCountWork;
+  if (by_count) {
+    const int n = T * E;
+    int P = 1;
+    while (P * 2 * n <= 1024 && P * 2 <= E) P *= 2;
+    const int q = tid % n, part = tid / n, t = q / E, e = q - t * E;
+    const bool live = part < P;
+    uint64_t kq = 0;
+    float lq = 0.0f;
+    if (live) {
+      lq = logits[(size_t)t * E + e];
+      kq = select_key(lq, e);
+      if (part == 0) {
+        keys[q] = kq;
+        off[q] = 0;  // rank accumulator (off is rewritten after the scan)
+      }
+    }
+    __syncthreads();
+    if (live) {
+      const uint64_t* kt = keys + t * E;
+      const int j0 = part * E / P, j1 = (part + 1) * E / P;
+      int r = 0;
+      for (int j = j0; j < j1; ++j) r += kt[j] > kq ? 1 : 0;
+      if (r) atomicAdd(&off[q], r);
+    }
+    __syncthreads();
+    if (live && part == 0) {
+      const int r = off[q];
+      if (r < k) {
+        sel[t * k + r] = e;
+        selv[t * k + r] = lq;
+      }
+    }
+  }
   __syncthreads();
   if (wave < T) {
-    float my_v;
-    int my_e;
-    topk_token<JPL>(logits, wave, E, k, lane, my_v, my_e);
+    float my_v = 0.0f;
+    int my_e = 0;
+    if (by_count) {
+      if (lane < k) {
+        my_v = selv[wave * k + lane];
+        my_e = sel[wave * k + lane];
+      }
+    } else {
+      topk_token<JPL>(logits, wave, E, k, lane, my_v, my_e);
+    }
     const float wt = topk_weight(my_v, k, router, lane);
     if (lane < k) {
       idx[wave * k + lane] = my_e;
@@ -607,8 +691,19 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
   }
   __syncthreads();
   const int c = (tid < E) ? __popc(mask[tid]) : 0;
-  int total;
-  const int o = block_scan1024(c, wave_tot, total);
+  int total, o, pre_used = -1, n_used = 0;
+  if (tile_rows > kPrefillTM) {
+    // one tile per expert: the offsets and the used-expert prefix in one
+    // scan (counts in the low 16 bits: T * k <= 16 * 32; used in the high)
+    int tot2;
+    const int o2 = block_scan1024(c | ((c > 0 ? 1 : 0) << 16), wave_tot, tot2);
+    o = o2 & 0xffff;
+    pre_used = o2 >> 16;
+    total = tot2 & 0xffff;
+    n_used = tot2 >> 16;
+  } else {
+    o = block_scan1024(c, wave_tot, total);
+  }
   if (tid < E) off[tid] = o;
   __syncthreads();
   const int TK = T * k;
@@ -620,7 +715,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
   }
   if (S && tid < T) perm[TK + tid] = tid;
   emit_counts_and_tiles(c, o, total, T, k, E, S, tile_rows, shared_slot, wave_tot, counts, offsets,
-                        tiles, n_tiles, distinct_total);
+                        tiles, n_tiles, distinct_total, pre_used, n_used);
 }
 
 // ---------------------------------------------------------------------------

@@ -942,8 +942,13 @@ static int prefill_ksplit(int K, int sshift) {
   return 1;
 }
 
-// Persistent prefill grid: at most two workgroups per CU.
-static int prefill_grid(int items) { return std::max(1, std::min(items, 512)); }
+// Persistent prefill grid: at most two workgroups per CU; a multiple of 8
+// (the XCD count) above 8, so the kernel can give each XCD its own runs of
+// items.
+static int prefill_grid(int items) {
+  int g = std::max(1, std::min(items, 512));
+  return g > 8 ? (g & ~7) : g;
+}
 
 // Runs gate+up then down over a tile range.  n_dev != nullptr: the count lives
 // on the device and `n_tiles` is only an upper bound.
