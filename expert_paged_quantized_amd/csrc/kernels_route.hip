@@ -111,17 +111,17 @@ __device__ __forceinline__ float fold_to_lane0(float p) {
   return p;
 }
 
-template <int TT, int TE>
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ wr,
-                                                            const float* __restrict__ bias,
-                                                            float* __restrict__ logits,
-                                                            uint16_t* __restrict__ x16,
-                                                            int32_t* __restrict__ xexp,
-                                                            float* __restrict__ gate_out, int T, int E,
-                                                            int Eo, int H) {
+// One wave's TT x TE logits (wave index `wave` of the launch).  COHERENT:
+// the logits are stored at device scope (through to memory), for a
+// workgroup of the same launch on another XCD to read them.
+template <int TT, int TE, bool COHERENT>
+__device__ __forceinline__ void router_logits_wave(int wave, const uint16_t* __restrict__ x,
+                                                   const uint16_t* __restrict__ wr,
+                                                   const float* __restrict__ bias,
+                                                   float* __restrict__ logits, uint16_t* __restrict__ x16,
+                                                   int32_t* __restrict__ xexp, float* __restrict__ gate_out,
+                                                   int T, int E, int Eo, int H) {
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int neb = (E + TE - 1) / TE;
   const int t0 = (wave / neb) * TT, e0 = (wave % neb) * TE;
   if (t0 >= T) return;
@@ -179,11 +179,31 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 #pragma unroll
       for (int b = 0; b < TE; ++b) {
         const int t = t0 + a, e = e0 + b;
-        if (t < T && e < Eo) logits[(size_t)t * Eo + e] = bias ? acc[a][b] + bias[e] : acc[a][b];
-        else if (t < T && e < E) gate_out[t] = acc[a][b];  // the shared-expert gate row
+        if (t < T && e < Eo) {
+          const float l = bias ? acc[a][b] + bias[e] : acc[a][b];
+          if constexpr (COHERENT)
+            __hip_atomic_store(&logits[(size_t)t * Eo + e], l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            logits[(size_t)t * Eo + e] = l;
+        } else if (t < T && e < E) {
+          gate_out[t] = acc[a][b];  // the shared-expert gate row
+        }
       }
   }
   if (copy) write_scaled_rows<TT>(x, x16, xexp, am, t0, T, H, lane, wave % neb, neb);
+}
+
+template <int TT, int TE>
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wr,
+                                                            const float* __restrict__ bias,
+                                                            float* __restrict__ logits,
+                                                            uint16_t* __restrict__ x16,
+                                                            int32_t* __restrict__ xexp,
+                                                            float* __restrict__ gate_out, int T, int E,
+                                                            int Eo, int H) {
+  router_logits_wave<TT, TE, false>(blockIdx.x * 4 + (threadIdx.x >> 6), x, wr, bias, logits, x16, xexp, gate_out,
+                                    T, E, Eo, H);
 }
 
 
@@ -310,14 +330,25 @@ __device__ __forceinline__ void best_of_impl(float& v, int& e, float ov, int oe)
 
 // Lanes r < k end with the r-th selected (logit, expert) of token t.  JPL =
 // logits per lane (E <= 64 * JPL); the per-round scan is branch-free.
-template <int JPL>
+// COHERENT: the logits were stored at device scope by other workgroups of
+// the same launch and are loaded at device scope (from memory, not from a
+// possibly stale line of this XCD's L2).
+template <bool COHERENT>
+__device__ __forceinline__ float load_logit(const float* p) {
+  if constexpr (COHERENT)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+
+template <int JPL, bool COHERENT = false>
 __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
                                            int lane, float& my_v, int& my_e) {
   float vals[JPL];
 #pragma unroll
   for (int j = 0; j < JPL; ++j) {
     const int e = lane + 64 * j;
-    const float v = logits[(size_t)t * E + min(e, E - 1)];
+    const float v = load_logit<COHERENT>(&logits[(size_t)t * E + min(e, E - 1)]);
     vals[j] = (e < E) ? v : -INFINITY;
   }
   uint32_t taken = 0;
@@ -614,8 +645,8 @@ __device__ __forceinline__ uint64_t select_key(float l, int e) {
   return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
 }
 
-template <int JPL>
-__global__ __launch_bounds__(1024) void route_small_kernel(
+template <int JPL, bool COHERENT>
+__device__ __forceinline__ void route_small_body(
     const float* __restrict__ logits, int T, int E, int k, int router, int S, int tile_rows,
     int shared_slot, int32_t* __restrict__ idx, float* __restrict__ w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ pos,
@@ -645,7 +676,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     uint64_t kq = 0;
     float lq = 0.0f;
     if (live) {
-      lq = logits[(size_t)t * E + e];
+      lq = load_logit<COHERENT>(&logits[(size_t)t * E + e]);
       kq = select_key(lq, e);
       if (part == 0) {
         keys[q] = kq;
@@ -679,7 +710,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
         my_e = sel[wave * k + lane];
       }
     } else {
-      topk_token<JPL>(logits, wave, E, k, lane, my_v, my_e);
+      topk_token<JPL, COHERENT>(logits, wave, E, k, lane, my_v, my_e);
     }
     const float wt = topk_weight(my_v, k, router, lane);
     if (lane < k) {
@@ -719,6 +750,55 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Router and small-batch routing in one launch (T <= 16): 1024-thread
+// workgroups whose first four waves each compute the logits of the router's
+// one-logit-per-wave layout (so the launch spreads the router bytes over as
+// many CUs as the four-wave router kernel does), stored at device scope.
+// Each workgroup then counts itself in `arrive` (device scope, after its
+// stores are acknowledged); the workgroup that arrives last resets the
+// counter for the next launch and runs the whole routing on the logits,
+// loaded at device scope.  No workgroup waits for another.
+// ---------------------------------------------------------------------------
+template <int JPL>
+__global__ __launch_bounds__(1024) void route_decode_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
+    float* __restrict__ logits, uint16_t* __restrict__ x16, int32_t* __restrict__ xexp,
+    float* __restrict__ gate_out, int Eall, int H, uint32_t* __restrict__ arrive, int T, int E, int k,
+    int router, int S, int tile_rows, int shared_slot, int32_t* __restrict__ idx, float* __restrict__ w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ pos, Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+    unsigned long long* __restrict__ distinct_total) {
+  __shared__ int is_last;
+  const int wave = threadIdx.x >> 6;
+  if (wave < 4)
+    router_logits_wave<1, 1, true>(blockIdx.x * 4 + wave, x, wr, bias, logits, x16, xexp, gate_out, T, Eall, E,
+                                   H);
+  // the stores of this wave are acknowledged at device scope
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t n = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = n + 1 == gridDim.x;
+    if (is_last) __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  route_small_body<JPL, true>(logits, T, E, k, router, S, tile_rows, shared_slot, idx, w, counts, offsets,
+                              perm, pos, tiles, n_tiles, distinct_total);
+}
+
+template <int JPL>
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int router, int S, int tile_rows,
+    int shared_slot, int32_t* __restrict__ idx, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ pos,
+    Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+    unsigned long long* __restrict__ distinct_total) {
+  route_small_body<JPL, false>(logits, T, E, k, router, S, tile_rows, shared_slot, idx, w, counts, offsets, perm,
+                               pos, tiles, n_tiles, distinct_total);
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
@@ -755,6 +835,47 @@ static void launch_route_jpl(const float* logits, int T, int E, int k, int route
   rank_kernel<<<nblk, 1024, 0, s>>>(idx, T, E, k, rank_in_block, hist);
   permute_kernel<<<nblk, 1024, 0, s>>>(idx, rank_in_block, hist, T, E, k, S, tile_rows, shared_slot, counts,
                                        offsets, perm, pos, tiles, n_tiles, distinct_total);
+}
+
+template <int JPL>
+static void launch_route_decode_jpl(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
+                                    uint16_t* x16, int32_t* xexp, float* gate_out, int Eall, int H,
+                                    uint32_t* arrive, int T, int E, int k, int router, int S, int tile_rows,
+                                    int shared_slot, int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
+                                    int32_t* perm, int32_t* pos, Tile* tiles, int32_t* n_tiles,
+                                    unsigned long long* distinct_total, hipStream_t s) {
+  const int waves = T * Eall;  // one logit per router wave, four router waves per workgroup
+  launch_k(route_decode_kernel<JPL>, dim3((waves + 3) / 4), dim3(1024), 0, s, x, wr, bias, logits, x16, xexp,
+           gate_out, Eall, H, arrive, T, E, k, router, S, tile_rows, shared_slot, idx, w, counts, offsets, perm,
+           pos, tiles, n_tiles, distinct_total);
+}
+
+// The fused launch holds one 1024-thread workgroup per four logits; beyond
+// 256 workgroups (T * E > 1024) the two launches take less time.
+bool route_decode_fits(int T, int Eall) { return T >= 1 && T <= kSmallT && T * Eall <= 1024; }
+
+hipError_t launch_route_decode(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
+                               uint16_t* x16, int32_t* xexp, float* gate_out, int Eall, int H, uint32_t* arrive,
+                               int T, int E, int k, int router, int S, int tile_rows, int shared_slot,
+                               int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                               int32_t* pos, Tile* tiles, int32_t* n_tiles, unsigned long long* distinct_total,
+                               hipStream_t s) {
+#define STRATA_RD(J)                                                                                        \
+  launch_route_decode_jpl<J>(x, wr, bias, logits, x16, xexp, gate_out, Eall, H, arrive, T, E, k, router, S, \
+                             tile_rows, shared_slot, idx, w, counts, offsets, perm, pos, tiles, n_tiles,     \
+                             distinct_total, s)
+  if (E <= 64)
+    STRATA_RD(1);
+  else if (E <= 128)
+    STRATA_RD(2);
+  else if (E <= 256)
+    STRATA_RD(4);
+  else if (E <= 512)
+    STRATA_RD(8);
+  else
+    STRATA_RD(16);
+#undef STRATA_RD
+  return hipGetLastError();
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int router, int S, int tile_rows,

@@ -43,6 +43,10 @@ hipError_t launch_router(const uint16_t*, const uint16_t*, const float*, float*,
 hipError_t launch_route(const float*, int, int, int, int, int, int, int, int32_t*, float*, int32_t*,
                         int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, Tile*, int32_t*,
                         unsigned long long*, hipStream_t);
+bool route_decode_fits(int T, int Eall);
+hipError_t launch_route_decode(const uint16_t*, const uint16_t*, const float*, float*, uint16_t*, int32_t*, float*,
+                               int, int, uint32_t*, int, int, int, int, int, int, int, int32_t*, float*, int32_t*,
+                               int32_t*, int32_t*, int32_t*, Tile*, int32_t*, unsigned long long*, hipStream_t);
 hipError_t launch_expert_gemm(const GemmArgs&, int, bool, bool, int, int, int, hipStream_t);
 hipError_t launch_page_in(const PageBatch&, hipStream_t);
 int decode_log2_splits(int N, int K, int tiles_per_token, int T);
@@ -1166,16 +1170,27 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
   if (capturing && h->timing) return fail(STRATA_E_UNSUPPORTED, "kernel timing cannot be captured");
   if (h->fwd_recorded && !capturing) HIP_CHECK(hipStreamWaitEvent(s, h->ev_fwd_done, 0));
 
-  HIP_CHECK(timed(h, STRATA_K_ROUTER, s, [&]() {
-    return launch_router((const uint16_t*)x, h->d_router_w, h->d_router_bias, ws.logits, ws.x16, ws.xexp,
-                         ws.gate, T, h->E + h->gated, h->E, h->H, s);
-  }));
   const int tile_rows = decode ? (1 << 30) : kPrefillTM;
-  HIP_CHECK(timed(h, STRATA_K_GROUP, s, [&]() {
-    return launch_route(ws.logits, T, h->E, h->k, h->router, h->S, tile_rows, h->budget, ws.idx,
-                        ws.w, ws.rank, ws.hist, ws.counts, ws.offsets,
-                        ws.perm, ws.pos, ws.tiles_dev, ws.ntiles, h->d_distinct, s);
-  }));
+  if (route_decode_fits(T, h->E + h->gated)) {
+    // router and routing in one launch (its last workgroup routes); the
+    // arrival counter is the word after the distinct-expert total
+    HIP_CHECK(timed(h, STRATA_K_ROUTER, s, [&]() {
+      return launch_route_decode((const uint16_t*)x, h->d_router_w, h->d_router_bias, ws.logits, ws.x16, ws.xexp,
+                                 ws.gate, h->E + h->gated, h->H, reinterpret_cast<uint32_t*>(h->d_distinct + 1), T,
+                                 h->E, h->k, h->router, h->S, tile_rows, h->budget, ws.idx, ws.w, ws.counts,
+                                 ws.offsets, ws.perm, ws.pos, ws.tiles_dev, ws.ntiles, h->d_distinct, s);
+    }));
+  } else {
+    HIP_CHECK(timed(h, STRATA_K_ROUTER, s, [&]() {
+      return launch_router((const uint16_t*)x, h->d_router_w, h->d_router_bias, ws.logits, ws.x16, ws.xexp,
+                           ws.gate, T, h->E + h->gated, h->E, h->H, s);
+    }));
+    HIP_CHECK(timed(h, STRATA_K_GROUP, s, [&]() {
+      return launch_route(ws.logits, T, h->E, h->k, h->router, h->S, tile_rows, h->budget, ws.idx,
+                          ws.w, ws.rank, ws.hist, ws.counts, ws.offsets,
+                          ws.perm, ws.pos, ws.tiles_dev, ws.ntiles, h->d_distinct, s);
+    }));
+  }
 
   if (h->budget == h->E) {
     const int ub = decode ? std::min(h->E, TK) + h->S

@@ -328,7 +328,8 @@ strata_status strata_moe_memory(const strata_moe* h, strata_memory_info* out);
  * by HIP events on the forward's stream; strata_moe_timing() waits for them
  * and returns totals per kernel class, and resets them. */
 typedef enum {
-  STRATA_K_ROUTER = 0,   /* router logits                                          */
+  STRATA_K_ROUTER = 0,   /* router logits (T * E <= 1024: and the whole grouping,  */
+                         /* done by the launch's last workgroup)                   */
   STRATA_K_GROUP = 1,    /* top-k, weights, counts, offsets, perm, tile list       */
   STRATA_K_DEC_UP = 2,   /* decode gate+up GEMV + SwiGLU                           */
   STRATA_K_DEC_DOWN = 3, /* decode down GEMV                                       */
