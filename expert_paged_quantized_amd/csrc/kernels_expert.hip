@@ -1064,9 +1064,10 @@ __global__ __launch_bounds__(kPreThreads, 2) void moe_prefill_kernel(GemmArgs p)
   // time: each XCD's workgroups take its items in turn.  With more (a wide
   // expert: its row blocks are the bulk of the bytes) the items go out in
   // list order, which puts the same row block of an expert's consecutive
-  // tiles on one XCD when per_tile is a multiple of 8.
+  // tiles on one XCD when per_tile is a multiple of 8; so do launches with
+  // no more items than workgroups (one item each, whatever the XCD).
   const int G = gridDim.x;
-  const bool by_xcd = G % 8 == 0 && G > 8 && per_tile <= 16;
+  const bool by_xcd = G % 8 == 0 && G > 8 && per_tile <= 16 && n_items > G;
   const int x = blockIdx.x & 7, gx = by_xcd ? G >> 3 : G;
   const int n_local = by_xcd ? ((n_tiles + 7) >> 3) * per_tile : n_items;  // XCD: rounds of 8 tiles
   for (int i = by_xcd ? (blockIdx.x >> 3) : blockIdx.x; i < n_local; i += gx) {
