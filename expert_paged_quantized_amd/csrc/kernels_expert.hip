@@ -485,7 +485,11 @@ __global__ __launch_bounds__(kDecWaves * 64) void moe_decode_kernel(GemmArgs p, 
 // ---------------------------------------------------------------------------
 // weight ring depth: registers at 1024 threads per workgroup are capped at
 // 128 per lane, and every token adds accumulators and activation operands
-constexpr int dot_depth(int tt) { return tt == 1 ? 16 : (tt == 2 ? 12 : 8); }
+// Weight ring depth (K-blocks in flight per wave) by token rows: one row
+// holds 14 blocks, or 16 when every wave's K range is a multiple of 16 (one
+// round then loads each block once; 14 keeps the one-row code within 128
+// registers, which 16 exceeds by a few spilled ones).
+constexpr int dot_depth(int tt, bool d16) { return tt == 1 ? (d16 ? 16 : 14) : (tt == 2 ? 12 : 8); }
 
 // Token rows of a dot-decode unit into registers: thread tid loads the
 // 16-byte pieces tid + j * nthr (j < NPR) of each of the TT rows; rows past
@@ -534,16 +538,20 @@ __device__ __forceinline__ void dot_store_rows(const u32x4 (&v)[TT][NPR], uint32
   }
 }
 
-// Weight ring prologue: slot j holds K-block kb0 + min(j, nkb - 1).
+// Weight ring prologue: slot j holds K-block kb0 + j.  Slots past the wave's
+// K range (never contracted) load the same 16 bytes in every lane instead, one
+// small request rather than a second copy of a 1 KB block: the address is
+// selected, not branched around, so the wait counts stay exact.
 template <int QF, int DEPTH>
 __device__ __forceinline__ void dot_prologue(u32x4 (&wq)[DEPTH], uint32_t (&ws)[DEPTH], const uint8_t* codes,
-                                             const uint8_t* scales, int kb0, int nkb, int sshift) {
+                                             const uint8_t* scales, const uint8_t* codes0, const uint8_t* scales0,
+                                             int kb0, int nkb, int sshift) {
   using SL = ScaleLayout<QF>;
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) {
-    const int kb = min(j, nkb - 1);
-    wq[j] = ld16_nt(codes + (int64_t)kb * kTileCodeBytes);
-    ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kb) >> sshift) * SL::kTileBytes);
+    const bool in = j < nkb;
+    wq[j] = ld16_nt(in ? codes + (int64_t)j * kTileCodeBytes : codes0);
+    ws[j] = SL::load_nt(in ? scales + (int64_t)((kb0 + j) >> sshift) * SL::kTileBytes : scales0);
   }
 }
 
@@ -553,7 +561,8 @@ __device__ __forceinline__ void dot_prologue(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
 // inputs of half lane / 32).
 template <int QF, int TT, int DEPTH>
 __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[DEPTH], const uint8_t* codes,
-                                             const uint8_t* scales, int kb0, int nkb, int sshift,
+                                             const uint8_t* scales, const uint8_t* codes0,
+                                             const uint8_t* scales0, int kb0, int nkb, int sshift,
                                              const uint32_t* xs, int row_u32, const float* xsum, int K,
                                              int lane, float (&acc)[TT]) {
   using SL = ScaleLayout<QF>;
@@ -561,15 +570,16 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
   const uint32_t* xl = xs + (kb0 * 32 + h * 16);  // this lane's 32 inputs of block kb0, row 0
   const float* xsl = xsum + kb0 * 2 + h;
   // One round of DEPTH slots from K-block i; RF: refill each slot with the
-  // K-block DEPTH later (clamped to the last one).  The last round refills
-  // nothing, so a wave whose K range is a multiple of DEPTH loads each of its
-  // blocks exactly once.
+  // K-block DEPTH later (past the K range: the one small request of the
+  // prologue).  The last round refills nothing, so every block of the wave's
+  // K range is loaded exactly once.
   auto round = [&](int i, auto rf) {
     constexpr bool RF = decltype(rf)::value;
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
       const int kbl = i + j;
-      const int kn = min(kbl + DEPTH, nkb - 1);
+      const int kn = kbl + DEPTH;
+      const bool kn_in = kn < nkb;
       if constexpr (QF == Q_INT4) {
         uint32_t m[4][4];
 #pragma unroll
@@ -587,8 +597,8 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
                      "+v"(m[2][2]), "+v"(m[2][3]), "+v"(m[3][0]), "+v"(m[3][1]), "+v"(m[3][2]),
                      "+v"(m[3][3]), "+v"(s), "+v"(b)::"memory");
         if constexpr (RF) {
-          wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
-          ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes);
+          wq[j] = ld16_nt(kn_in ? codes + (int64_t)kn * kTileCodeBytes : codes0);
+          ws[j] = SL::load_nt(kn_in ? scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes : scales0);
         }
         if (kbl < nkb) {
           float xsv[TT];  // sum(x) of the group: read first, used last
@@ -621,8 +631,8 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
         float s0 = e4m3_to_f32(ws[j] & 0xffu), s1 = e4m3_to_f32(ws[j] >> 8);
         asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(s0), "+v"(s1)::"memory");
         if constexpr (RF) {
-          wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
-          ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes);
+          wq[j] = ld16_nt(kn_in ? codes + (int64_t)kn * kTileCodeBytes : codes0);
+          ws[j] = SL::load_nt(kn_in ? scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes : scales0);
         }
         if (kbl < nkb) {
 #pragma unroll
@@ -651,8 +661,8 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
         float scale = __uint_as_float(ws[j] << 23);
         asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(scale)::"memory");
         if constexpr (RF) {
-          wq[j] = ld16_nt(codes + (int64_t)kn * kTileCodeBytes);
-          ws[j] = SL::load_nt(scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes);
+          wq[j] = ld16_nt(kn_in ? codes + (int64_t)kn * kTileCodeBytes : codes0);
+          ws[j] = SL::load_nt(kn_in ? scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes : scales0);
         }
         if (kbl < nkb) {
 #pragma unroll
@@ -682,10 +692,10 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
 // [sw*KB/S, (sw+1)*KB/S)).  Every thread of the workgroup stages the token
 // rows.  The halves of a row are added lane l + lane l+32, then the S
 // partial sums in split order, then the epilogue.
-template <int QF, bool GATE_UP, int TT, int NPR>
+template <int QF, bool GATE_UP, int TT, int NPR, bool D16>
 __device__ __forceinline__ void dot_unit(const GemmArgs& p, const Tile& t, int rt, int S, int sw, uint32_t* xs) {
   using SL = ScaleLayout<QF>;
-  constexpr int DEPTH = dot_depth(TT);
+  constexpr int DEPTH = dot_depth(TT, D16);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = blockDim.x;
   const int K = p.K, KB = K >> 6;
   const int kb0 = sw * KB / S, kb1 = (sw + 1) * KB / S, nkb = kb1 - kb0;
@@ -705,14 +715,17 @@ __device__ __forceinline__ void dot_unit(const GemmArgs& p, const Tile& t, int r
   asm volatile("" ::: "memory");
   u32x4 wq[DEPTH];
   uint32_t ws[DEPTH];
-  dot_prologue<QF, DEPTH>(wq, ws, codes, scales, kb0, nkb, p.sshift);
+  const uint8_t* codes0 = codes - lane * 16;         // the K range's first 16 bytes, every lane
+  const uint8_t* scales0 = scales - SL::lane_off(lane);
+  dot_prologue<QF, DEPTH>(wq, ws, codes, scales, codes0, scales0, kb0, nkb, p.sshift);
   dot_store_rows<QF, TT, NPR>(v, xs, row_u32, xsum, tid, nthr, K);
   __syncthreads();
 
   float acc[TT];
 #pragma unroll
   for (int r = 0; r < TT; ++r) acc[r] = 0.0f;
-  dot_contract<QF, TT, DEPTH>(wq, ws, codes, scales, kb0, nkb, p.sshift, xs, row_u32, xsum, K, lane, acc);
+  dot_contract<QF, TT, DEPTH>(wq, ws, codes, scales, codes0, scales0, kb0, nkb, p.sshift, xs, row_u32, xsum, K,
+                              lane, acc);
 
   // halves: lane l (< 32) adds lane l+32; then the S waves in order
   __syncthreads();  // staging area reused below
@@ -746,7 +759,12 @@ __device__ __forceinline__ void dot_unit(const GemmArgs& p, const Tile& t, int r
   }
 }
 
-template <int QF, bool GATE_UP, int TT, int NPR>
+// TT: the most token rows a tile of the launch can have (1, 2 or 4; the LDS
+// is sized for it).  Each workgroup contracts as many rows as its own tile
+// has, rounded up to 1, 2 or 4: with several tokens most experts still hold
+// one of them, and a 1-row tile then stages, reads and multiplies one row
+// instead of four.  A token's sums do not depend on the rows beside it.
+template <int QF, bool GATE_UP, int TT, int NPR, bool D16>
 __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xs[];
   const int S = blockDim.x >> 6;
@@ -755,7 +773,20 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
   const int n_tiles = p.n_tiles_dev ? p.n_tiles_dev[0] : p.n_tiles;
   if (tile_i >= n_tiles) return;  // the whole workgroup leaves together
   const Tile t = p.tiles[tile_i];
-  dot_unit<QF, GATE_UP, TT, NPR>(p, t, rt, S, threadIdx.x >> 6, xs);
+  const int sw = threadIdx.x >> 6;
+  if constexpr (TT >= 4) {
+    if (t.nrows > 2) {
+      dot_unit<QF, GATE_UP, 4, NPR, D16>(p, t, rt, S, sw, xs);
+      return;
+    }
+  }
+  if constexpr (TT >= 2) {
+    if (t.nrows > 1) {
+      dot_unit<QF, GATE_UP, 2, NPR, D16>(p, t, rt, S, sw, xs);
+      return;
+    }
+  }
+  dot_unit<QF, GATE_UP, 1, NPR, D16>(p, t, rt, S, sw, xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1258,15 +1289,33 @@ int decode_dot_waves(int N, int K, int quant, int tiles_per_token, int T) {
   return S;
 }
 
-template <int QF, bool GATE_UP, int TT>
-static void launch_dot_tt(const GemmArgs& a, int S, int grid, size_t lds, hipStream_t s) {
+template <int QF, bool GATE_UP, int TT, bool D16>
+static void launch_dot_d(const GemmArgs& a, int S, int grid, size_t lds, hipStream_t s) {
   const int npr = (a.K / 8 + 64 * S - 1) / (64 * S);
   if (npr <= 1)
-    launch_k(moe_decode_dot_kernel<QF, GATE_UP, TT, 1>, dim3(grid), dim3(64 * S), lds, s, a);
+    launch_k(moe_decode_dot_kernel<QF, GATE_UP, TT, 1, D16>, dim3(grid), dim3(64 * S), lds, s, a);
   else if (npr <= 2)
-    launch_k(moe_decode_dot_kernel<QF, GATE_UP, TT, 2>, dim3(grid), dim3(64 * S), lds, s, a);
+    launch_k(moe_decode_dot_kernel<QF, GATE_UP, TT, 2, D16>, dim3(grid), dim3(64 * S), lds, s, a);
   else
-    launch_k(moe_decode_dot_kernel<QF, GATE_UP, TT, 4>, dim3(grid), dim3(64 * S), lds, s, a);
+    launch_k(moe_decode_dot_kernel<QF, GATE_UP, TT, 4, D16>, dim3(grid), dim3(64 * S), lds, s, a);
+}
+
+// true when every wave's K range (split sw of S: blocks sw*KB/S .. (sw+1)*KB/S - 1)
+// is a nonzero multiple of 16 K-blocks
+static bool ranges_of_16(int KB, int S) {
+  for (int sw = 0; sw < S; ++sw) {
+    const int n = (sw + 1) * KB / S - sw * KB / S;
+    if (n == 0 || n % 16) return false;
+  }
+  return true;
+}
+
+template <int QF, bool GATE_UP, int TT>
+static void launch_dot_tt(const GemmArgs& a, int S, int grid, size_t lds, hipStream_t s) {
+  if (ranges_of_16(a.K / 64, S))
+    launch_dot_d<QF, GATE_UP, TT, true>(a, S, grid, lds, s);
+  else
+    launch_dot_d<QF, GATE_UP, TT, false>(a, S, grid, lds, s);
 }
 
 template <int QF, bool GATE_UP>
