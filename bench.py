@@ -83,7 +83,7 @@ def parse():
 
 
 KERNEL_SRCS = [os.path.join(ROOT, "expert_paged_quantized_amd", "csrc", f)
-               for f in ("kernels_expert.hip", "kernels_route.hip", "moe_common.h")]
+               for f in ("kernels_expert.hip", "kernels_decode.hip", "kernels_route.hip", "moe_common.h")]
 CALIB_BYTES = 256 << 20                        # plain device copy timed in the same run
 
 # Expert-kernel kinds the profile summaries report, by their mangled-name test.

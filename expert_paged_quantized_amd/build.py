@@ -16,8 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libstrata_moe.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["kernels_route.hip", "kernels_expert.hip", "kernels_probe.hip", "scratch.hip", "residency.cpp",
-           "host_experts.cpp", "runtime.cpp"]
+SOURCES = ["kernels_route.hip", "kernels_expert.hip", "kernels_decode.hip", "kernels_probe.hip", "scratch.hip",
+           "residency.cpp", "host_experts.cpp", "runtime.cpp"]
 ARCH = "gfx950"
 
 

@@ -1122,6 +1122,7 @@ __global__ __launch_bounds__(kPreThreads, 2) void moe_prefill_kernel(GemmArgs p)
   }
 }
 
+#ifndef STRATA_DECODE_UNIT
 // ---------------------------------------------------------------------------
 // Page-in: copies whole records (b.stride bytes each) from the pinned host
 // store, read through its device mapping, into device slots.  The work is cut
@@ -1229,9 +1230,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+#endif  // !STRATA_DECODE_UNIT
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// Dispatch over the quant family and gate+up / down at run time.
+template <template <int, bool> class L, class... A>
+static void by_format(int quant, bool gate_up, A&&... args) {
+  if (quant == Q_INT4) {
+    if (gate_up) L<Q_INT4, true>::run(args...); else L<Q_INT4, false>::run(args...);
+  } else if (quant == Q_NVFP4) {
+    if (gate_up) L<Q_NVFP4, true>::run(args...); else L<Q_NVFP4, false>::run(args...);
+  } else {
+    if (gate_up) L<Q_MXFP4, true>::run(args...); else L<Q_MXFP4, false>::run(args...);
+  }
+}
+
+#ifdef STRATA_DECODE_UNIT
 template <int QF, bool GATE_UP>
 static void launch_decode(const GemmArgs& a, int T, int log2S, int grid, hipStream_t s) {
   const int S = 1 << log2S;
@@ -1332,18 +1348,6 @@ static void launch_dot(const GemmArgs& a, int T, int S, int n_tiles, hipStream_t
     launch_dot_tt<QF, GATE_UP, 4>(a, S, grid, lds, s);
 }
 
-// Dispatch over the quant family and gate+up / down at run time.
-template <template <int, bool> class L, class... A>
-static void by_format(int quant, bool gate_up, A&&... args) {
-  if (quant == Q_INT4) {
-    if (gate_up) L<Q_INT4, true>::run(args...); else L<Q_INT4, false>::run(args...);
-  } else if (quant == Q_NVFP4) {
-    if (gate_up) L<Q_NVFP4, true>::run(args...); else L<Q_NVFP4, false>::run(args...);
-  } else {
-    if (gate_up) L<Q_MXFP4, true>::run(args...); else L<Q_MXFP4, false>::run(args...);
-  }
-}
-
 template <int QF, bool GU>
 struct DotL {
   static void run(const GemmArgs& a, int T, int S, int n_tiles, hipStream_t s) { launch_dot<QF, GU>(a, T, S, n_tiles, s); }
@@ -1354,13 +1358,6 @@ struct DecL {
     launch_decode<QF, GU>(a, T, log2S, grid, s);
   }
 };
-template <int QF, bool GU>
-struct PreL {
-  static void run(const GemmArgs& a, int grid, hipStream_t s) {
-    launch_k(moe_prefill_kernel<QF, GU>, dim3(grid), dim3(kPreThreads), 0, s, a);
-  }
-};
-
 hipError_t launch_decode_dot(const GemmArgs& a, int quant, bool gate_up, int T, int S, int n_tiles,
                              hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
@@ -1368,13 +1365,27 @@ hipError_t launch_decode_dot(const GemmArgs& a, int quant, bool gate_up, int T, 
   return hipGetLastError();
 }
 
+hipError_t launch_decode_mfma(const GemmArgs& a, int quant, bool gate_up, int T, int log2S, int grid,
+                              hipStream_t s) {
+  by_format<DecL>(quant, gate_up, a, T, log2S, grid, s);
+  return hipGetLastError();
+}
+#else   // the main unit: prefill, page-in, combine
+hipError_t launch_decode_mfma(const GemmArgs& a, int quant, bool gate_up, int T, int log2S, int grid,
+                              hipStream_t s);
+
+template <int QF, bool GU>
+struct PreL {
+  static void run(const GemmArgs& a, int grid, hipStream_t s) {
+    launch_k(moe_prefill_kernel<QF, GU>, dim3(grid), dim3(kPreThreads), 0, s, a);
+  }
+};
+
 hipError_t launch_expert_gemm(const GemmArgs& a, int quant, bool gate_up, bool decode, int T, int log2S,
                               int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (decode)
-    by_format<DecL>(quant, gate_up, a, T, log2S, grid, s);
-  else
-    by_format<PreL>(quant, gate_up, a, grid, s);
+  if (decode) return launch_decode_mfma(a, quant, gate_up, T, log2S, grid, s);
+  by_format<PreL>(quant, gate_up, a, grid, s);
   return hipGetLastError();
 }
 
@@ -1387,5 +1398,6 @@ hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, in
            stride, gate, y);
   return hipGetLastError();
 }
+#endif  // STRATA_DECODE_UNIT
 
 }  // namespace strata
