@@ -135,36 +135,47 @@ __device__ __forceinline__ void router_logits_wave(int wave, const uint16_t* __r
     for (int b = 0; b < TE; ++b) acc[a][b] = 0.0f;
   }
   const int C = H >> 9;
-  for (int c = 0; c < C; ++c) {
-    const int off = (c * 64 + lane) * 8;
-    uint4 xv[TT], wv[TE];
+  // Chunks in rounds of up to four (H is a multiple of 512): a round's loads
+  // are all issued before its first multiply waits; the sums still run chunk
+  // by chunk, in order.  Loads past C re-read chunk C - 1 and are not used.
+  constexpr int RC = 4;
+  for (int c0 = 0; c0 < C; c0 += RC) {
+    uint4 xv[RC][TT], wv[RC][TE];
 #pragma unroll
-    for (int a = 0; a < TT; ++a) {
-      const int t = min(t0 + a, T - 1);
-      xv[a] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + off);
-    }
-#pragma unroll
-    for (int b = 0; b < TE; ++b) {
-      const int e = min(e0 + b, E - 1);
-      wv[b] = *reinterpret_cast<const uint4*>(wr + (size_t)e * H + off);
-    }
-    if (copy) {
-#pragma unroll
-      for (int a = 0; a < TT; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) am[a] = amax_bits(am[a], (&xv[a].x)[q]);
-    }
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
+    for (int u = 0; u < RC; ++u) {
+      const int off = (min(c0 + u, C - 1) * 64 + lane) * 8;
 #pragma unroll
       for (int a = 0; a < TT; ++a) {
-        const uint32_t xw = (&xv[a].x)[v >> 1];
-        const float xf = (v & 1) ? bf16_hi(xw) : bf16_lo(xw);
+        const int t = min(t0 + a, T - 1);
+        xv[u][a] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + off);
+      }
 #pragma unroll
-        for (int b = 0; b < TE; ++b) {
-          const uint32_t ww = (&wv[b].x)[v >> 1];
-          const float wf = (v & 1) ? bf16_hi(ww) : bf16_lo(ww);
-          acc[a][b] = __builtin_fmaf(xf, wf, acc[a][b]);
+      for (int b = 0; b < TE; ++b) {
+        const int e = min(e0 + b, E - 1);
+        wv[u][b] = *reinterpret_cast<const uint4*>(wr + (size_t)e * H + off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RC; ++u) {
+      if (c0 + u >= C) break;
+      if (copy) {
+#pragma unroll
+        for (int a = 0; a < TT; ++a)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) am[a] = amax_bits(am[a], (&xv[u][a].x)[q]);
+      }
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+#pragma unroll
+        for (int a = 0; a < TT; ++a) {
+          const uint32_t xw = (&xv[u][a].x)[v >> 1];
+          const float xf = (v & 1) ? bf16_hi(xw) : bf16_lo(xw);
+#pragma unroll
+          for (int b = 0; b < TE; ++b) {
+            const uint32_t ww = (&wv[u][b].x)[v >> 1];
+            const float wf = (v & 1) ? bf16_hi(ww) : bf16_lo(ww);
+            acc[a][b] = __builtin_fmaf(xf, wf, acc[a][b]);
+          }
         }
       }
     }
