@@ -1202,13 +1202,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   // workgroup (t, blockIdx.y) takes column blocks of 1024, gridDim.y apart
   for (int c = blockIdx.y * 1024 + threadIdx.x * 4; c < H; c += gridDim.y * 1024) {
     float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < k; ++j) {
-      const float wj = w[(size_t)t * k + j];
-      const float4 v = o_row(o, (size_t)pos[(size_t)t * k + j] * H + c, ksplit, stride);
-      acc.x = __builtin_fmaf(wj, v.x, acc.x);
-      acc.y = __builtin_fmaf(wj, v.y, acc.y);
-      acc.z = __builtin_fmaf(wj, v.z, acc.z);
-      acc.w = __builtin_fmaf(wj, v.w, acc.w);
+    // experts in rounds of eight: a round's rows are all requested before
+    // the first is added (in the order j = 0, 1, ...; slots past k re-read
+    // the last row and are not added)
+    constexpr int RJ = 8;
+    for (int j0 = 0; j0 < k; j0 += RJ) {
+      float wj[RJ];
+      float4 v[RJ];
+#pragma unroll
+      for (int u = 0; u < RJ; ++u) {
+        const int j = min(j0 + u, k - 1);
+        wj[u] = w[(size_t)t * k + j];
+        v[u] = o_row(o, (size_t)pos[(size_t)t * k + j] * H + c, ksplit, stride);
+      }
+#pragma unroll
+      for (int u = 0; u < RJ; ++u) {
+        if (j0 + u >= k) break;
+        acc.x = __builtin_fmaf(wj[u], v[u].x, acc.x);
+        acc.y = __builtin_fmaf(wj[u], v[u].y, acc.y);
+        acc.z = __builtin_fmaf(wj[u], v[u].z, acc.z);
+        acc.w = __builtin_fmaf(wj[u], v[u].w, acc.w);
+      }
     }
     if (shared_row0 >= 0) {
       const float4 v = o_row(o, (size_t)(shared_row0 + t) * H + c, ksplit, stride);
