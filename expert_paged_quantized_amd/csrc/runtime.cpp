@@ -1264,8 +1264,17 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
       }
     }
     // The expert GEMMs of this forward run on the paged compute stream ps
-    // (after the routing on s; the combine on s waits for them below).
-    hipStream_t ps = h->pstream ? h->pstream : s;
+    // (after the routing on s; the combine on s waits for them below), except
+    // in a decode forward that pages nothing, which computes on s itself: no
+    // page-in of it can share a CU with its kernels, and the fork and the
+    // join would add two cross-queue waits to the token's dependent chain
+    // (Qwen3-shaped layer, LFU: 128 -> 102 us per paged decode token on
+    // average, one box).  A decode forward with pages
+    // keeps the split: its compute beside the page-in workgroups delays them.
+    int n_pages = 0;
+    for (const auto& pw : plan)
+      for (const PlanEntry& p : pw) n_pages += p.paged ? 1 : 0;
+    hipStream_t ps = (h->pstream && !(decode && n_pages == 0)) ? h->pstream : s;
     if (ps != s) {
       HIP_CHECK(hipEventRecord(h->ev_pfork, s));
       HIP_CHECK(hipStreamWaitEvent(ps, h->ev_pfork, 0));
