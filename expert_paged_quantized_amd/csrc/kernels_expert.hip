@@ -538,20 +538,35 @@ __device__ __forceinline__ void dot_store_rows(const u32x4 (&v)[TT][NPR], uint32
   }
 }
 
+// Scale words a wave's ring holds for DEPTH K-blocks.  int4: one register
+// per two consecutive K-blocks.  Lanes l and l + 32 contract the same weight
+// row (l % 32), so both halves of a wave would load the same 32 scale words;
+// instead lanes 0-31 hold K-block 2i's words and lanes 32-63 K-block 2i+1's,
+// and a lane swap (v_permlane32_swap) gives every lane both.  MXFP4 and NVFP4
+// scale bytes differ per lane: one register per K-block.
+constexpr int ring_scales(int qf, int depth) { return qf == Q_INT4 ? depth / 2 : depth; }
+
 // Weight ring prologue: slot j holds K-block kb0 + j.  Slots past the wave's
 // K range (never contracted) load the same 16 bytes in every lane instead, one
 // small request rather than a second copy of a 1 KB block: the address is
 // selected, not branched around, so the wait counts stay exact.
 template <int QF, int DEPTH>
-__device__ __forceinline__ void dot_prologue(u32x4 (&wq)[DEPTH], uint32_t (&ws)[DEPTH], const uint8_t* codes,
-                                             const uint8_t* scales, const uint8_t* codes0, const uint8_t* scales0,
-                                             int kb0, int nkb, int sshift) {
+__device__ __forceinline__ void dot_prologue(u32x4 (&wq)[DEPTH], uint32_t (&ws)[ring_scales(QF, DEPTH)],
+                                             const uint8_t* codes, const uint8_t* scales, const uint8_t* codes0,
+                                             const uint8_t* scales0, int kb0, int nkb, int sshift, int lane) {
   using SL = ScaleLayout<QF>;
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) {
     const bool in = j < nkb;
     wq[j] = ld16_nt(in ? codes + (int64_t)j * kTileCodeBytes : codes0);
-    ws[j] = SL::load_nt(in ? scales + (int64_t)((kb0 + j) >> sshift) * SL::kTileBytes : scales0);
+    if constexpr (QF == Q_INT4) {
+      if (j % 2 == 0) {
+        const int kb = j + (lane >> 5);  // this half's K-block of the pair
+        ws[j / 2] = SL::load_nt(kb < nkb ? scales + (int64_t)((kb0 + kb) >> sshift) * SL::kTileBytes : scales0);
+      }
+    } else {
+      ws[j] = SL::load_nt(in ? scales + (int64_t)((kb0 + j) >> sshift) * SL::kTileBytes : scales0);
+    }
   }
 }
 
@@ -560,7 +575,8 @@ __device__ __forceinline__ void dot_prologue(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
 // contracted.  acc[r] = this lane's partial sum for token r (row lane % 32,
 // inputs of half lane / 32).
 template <int QF, int TT, int DEPTH>
-__device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[DEPTH], const uint8_t* codes,
+__device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[ring_scales(QF, DEPTH)],
+                                             const uint8_t* codes,
                                              const uint8_t* scales, const uint8_t* codes0,
                                              const uint8_t* scales0, int kb0, int nkb, int sshift,
                                              const uint32_t* xs, int row_u32, const float* xsum, int K,
@@ -575,6 +591,7 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
   // K range is loaded exactly once.
   auto round = [&](int i, auto rf) {
     constexpr bool RF = decltype(rf)::value;
+    uint32_t sc_lo = 0, sc_hi = 0;  // int4: the current pair's scale words
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
       const int kbl = i + j;
@@ -590,15 +607,25 @@ __device__ __forceinline__ void dot_contract(u32x4 (&wq)[DEPTH], uint32_t (&ws)[
           m[st][2] = w8 & 0x000F000Fu;  // (k4, k5) * 2^-24
           m[st][3] = w8 & 0x00F000F0u;  // (k6, k7) * 2^-20
         }
-        const f16x2 sbh = bitcast<f16x2>(ws[j]);  // (s', b') in fp16
+        // the pair's words: K-block j (lanes 0-31's) and j + 1 (lanes 32-63's)
+        // in every lane, taken at the even slot, which frees the register
+        if (j % 2 == 0) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(ws[j / 2], ws[j / 2], false, false);
+          sc_lo = sw[0];
+          sc_hi = sw[1];
+        }
+        const f16x2 sbh = bitcast<f16x2>(j % 2 == 0 ? sc_lo : sc_hi);  // (s', b') in fp16
         float s = (float)sbh[0], b = (float)sbh[1];
         asm volatile("" : "+v"(m[0][0]), "+v"(m[0][1]), "+v"(m[0][2]), "+v"(m[0][3]), "+v"(m[1][0]),
                      "+v"(m[1][1]), "+v"(m[1][2]), "+v"(m[1][3]), "+v"(m[2][0]), "+v"(m[2][1]),
                      "+v"(m[2][2]), "+v"(m[2][3]), "+v"(m[3][0]), "+v"(m[3][1]), "+v"(m[3][2]),
-                     "+v"(m[3][3]), "+v"(s), "+v"(b)::"memory");
+                     "+v"(m[3][3]), "+v"(s), "+v"(b), "+v"(sc_hi)::"memory");
         if constexpr (RF) {
           wq[j] = ld16_nt(kn_in ? codes + (int64_t)kn * kTileCodeBytes : codes0);
-          ws[j] = SL::load_nt(kn_in ? scales + (int64_t)((kb0 + kn) >> sshift) * SL::kTileBytes : scales0);
+          if (j % 2 == 0) {
+            const int kh = kn + (lane >> 5);  // this half's K-block of the next pair
+            ws[j / 2] = SL::load_nt(kh < nkb ? scales + (int64_t)((kb0 + kh) >> sshift) * SL::kTileBytes : scales0);
+          }
         }
         if (kbl < nkb) {
           float xsv[TT];  // sum(x) of the group: read first, used last
@@ -696,7 +723,8 @@ template <int QF, bool GATE_UP, int TT, int NPR, bool D16>
 __device__ __forceinline__ void dot_unit(const GemmArgs& p, const Tile& t, int rt, int S, int sw, uint32_t* xs) {
   using SL = ScaleLayout<QF>;
   constexpr int DEPTH = dot_depth(TT, D16);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = blockDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, nthr = blockDim.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = p.K, KB = K >> 6;
   const int kb0 = sw * KB / S, kb1 = (sw + 1) * KB / S, nkb = kb1 - kb0;
   const int row_u32 = K / 2 + 4;                              // staged row: K 16-bit inputs + 16 B pad
@@ -714,10 +742,10 @@ __device__ __forceinline__ void dot_unit(const GemmArgs& p, const Tile& t, int r
   dot_load_rows<TT, NPR>(p, t, tid, nthr, v);
   asm volatile("" ::: "memory");
   u32x4 wq[DEPTH];
-  uint32_t ws[DEPTH];
+  uint32_t ws[ring_scales(QF, DEPTH)];
   const uint8_t* codes0 = codes - lane * 16;         // the K range's first 16 bytes, every lane
   const uint8_t* scales0 = scales - SL::lane_off(lane);
-  dot_prologue<QF, DEPTH>(wq, ws, codes, scales, codes0, scales0, kb0, nkb, p.sshift);
+  dot_prologue<QF, DEPTH>(wq, ws, codes, scales, codes0, scales0, kb0, nkb, p.sshift, lane);
   dot_store_rows<QF, TT, NPR>(v, xs, row_u32, xsum, tid, nthr, K);
   __syncthreads();
 
@@ -773,7 +801,9 @@ __global__ __launch_bounds__(1024) void moe_decode_dot_kernel(GemmArgs p) {
   const int n_tiles = p.n_tiles_dev ? p.n_tiles_dev[0] : p.n_tiles;
   if (tile_i >= n_tiles) return;  // the whole workgroup leaves together
   const Tile t = p.tiles[tile_i];
-  const int sw = threadIdx.x >> 6;
+  // wave-uniform in scalar registers: the K range, its bounds checks and the
+  // ring's branches are then scalar
+  const int sw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (TT >= 4) {
     if (t.nrows > 2) {
       dot_unit<QF, GATE_UP, 4, NPR, D16>(p, t, rt, S, sw, xs);
