@@ -487,8 +487,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void moe_decode_kernel(GemmArgs p, 
 // 128 per lane, and every token adds accumulators and activation operands
 // Weight ring depth (K-blocks in flight per wave) by token rows: one row
 // holds 14 blocks, or 16 when every wave's K range is a multiple of 16 (one
-// round then loads each block once; 14 keeps the one-row code within 128
-// registers, which 16 exceeds by a few spilled ones).
+// round then loads each block once).  At 16 the int4 and MXFP4 code fits the
+// 128 registers of a 1,024-thread launch with no spill (int4 with its paired
+// scale words); NVFP4 at 16 still spills a few registers.
 constexpr int dot_depth(int tt, bool d16) { return tt == 1 ? (d16 ? 16 : 14) : (tt == 2 ? 12 : 8); }
 
 // Token rows of a dot-decode unit into registers: thread tid loads the
