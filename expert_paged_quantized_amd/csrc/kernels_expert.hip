@@ -258,6 +258,41 @@ __device__ __forceinline__ ColExp col_exp(const GemmArgs& p, int expert, int64_t
   }
   return r;
 }
+// The same exponents in two steps, for the prefill epilogue: the expert's
+// weight exponents (and each column's token) can be loaded before the K
+// loop, leaving one dependent load (the token's exponent) for after it.
+// Integer sums, so the split changes no value.
+struct ColExpPre {
+  int wa, wb;  // gate+up: gate and up - h exponents; down: h + down
+};
+template <int QF, bool GATE_UP>
+__device__ __forceinline__ ColExpPre col_exp_pre(const GemmArgs& p, int expert) {
+  ColExpPre r{0, 0};
+  if constexpr (QF != Q_MXFP4) {
+    const int32_t* we = p.wexp + expert * kWexpCount;
+    if constexpr (GATE_UP) {
+      r.wa = we[kWexpGate];
+      r.wb = we[kWexpUp] - we[kWexpH];
+    } else {
+      r.wa = we[kWexpH] + we[kWexpDown];
+    }
+  }
+  return r;
+}
+template <int QF, bool GATE_UP>
+__device__ __forceinline__ ColExp col_exp_post(const GemmArgs& p, const ColExpPre& q, int tok) {
+  ColExp r{0, 0, 0};
+  if constexpr (QF != Q_MXFP4) {
+    const int et = p.xexp[tok];
+    if constexpr (GATE_UP) {
+      r.g = et + q.wa;
+      r.u = q.wb - et;
+    } else {
+      r.o = 2 * et + q.wa;
+    }
+  }
+  return r;
+}
 __device__ __forceinline__ float pow2_scale(float v, int e) { return __builtin_amdgcn_ldexpf(v, e); }
 
 // The stored h element from the gate and up accumulators (gs: NVFP4 matrix
@@ -1055,6 +1090,23 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Epilogue operands, loaded ahead of the K loop (older than every DMA, so
+  // the loop's counted waits cover them): each column's token, the expert's
+  // weight exponents and the NVFP4 matrix scales.  The epilogue then waits
+  // for one dependent load (the tokens' exponents), not for a chain of loads
+  // per row tile and column tile, each behind the h stores before it (the
+  // memory counter counts stores too).
+  int tok[NCT] = {};
+  if constexpr (QF != Q_MXFP4) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int mm = min(ct * 32 + (lane & 31), t.nrows - 1);  // columns past the tile: a valid row
+      tok[ct] = p.tok_of_row[t.row_begin + mm];
+    }
+  }
+  const ColExpPre cpre = col_exp_pre<QF, GATE_UP>(p, t.expert);
+  const float2 gs = matrix_scales<QF>(p, rec);
+
   [&]<int... I>(std::integer_sequence<int, I...>) {
     ((I < KB ? dma(std::integral_constant<int, I>{}, I) : void()), ...);
   }(std::make_integer_sequence<int, S - 1>{});
@@ -1071,7 +1123,9 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
   wait_vm<0>();
 
   // epilogue (NVFP4: times the fp32 matrix scales)
-  const float2 gs = matrix_scales<QF>(p, rec);
+  ColExp ce_ct[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) ce_ct[ct] = col_exp_post<QF, GATE_UP>(p, cpre, tok[ct]);
 #pragma unroll
   for (int r = 0; r < RTW; ++r) {
     const int rt = rt0 + r;
@@ -1081,7 +1135,7 @@ __device__ __forceinline__ void prefill_item(const GemmArgs& p, const Tile& t, i
       const int mm = ct * 32 + (lane & 31);
       if (mm >= t.nrows) continue;
       const int64_t row = t.row_begin + mm;
-      const ColExp ce = col_exp<QF, GATE_UP>(p, t.expert, row);
+      const ColExp& ce = ce_ct[ct];
       if constexpr (GATE_UP) {
         uint16_t* h = reinterpret_cast<uint16_t*>(p.out) + row * p.out_ld + rt * 16;
 #pragma unroll
