@@ -86,12 +86,19 @@ KERNEL_SRCS = [os.path.join(ROOT, "expert_paged_quantized_amd", "csrc", f)
                for f in ("kernels_expert.hip", "kernels_decode.hip", "kernels_route.hip", "moe_common.h")]
 CALIB_BYTES = 256 << 20                        # plain device copy timed in the same run
 
-# Expert-kernel kinds the profile summaries report, by their mangled-name test.
+def _gate_up_arg(name):
+    """The second template argument (gate+up or down) of an expert kernel's
+    demangled name, e.g. 'moe_decode_dot_kernel<1, true, 1, 1, false>'."""
+    args = name[name.find("<") + 1:name.find(">")].split(",")
+    return args[1].strip() if len(args) > 1 else ""
+
+
+# Expert-kernel kinds the profile summaries report, by their demangled name.
 KINDS = {
-    "prefill_gate_up": lambda n: "moe_prefill_kernel" in n and ", true>" in n,
-    "prefill_down": lambda n: "moe_prefill_kernel" in n and ", false>" in n,
-    "decode_gate_up": lambda n: "moe_decode" in n and ", true" in n,
-    "decode_down": lambda n: "moe_decode" in n and ", false" in n,
+    "prefill_gate_up": lambda n: "moe_prefill_kernel" in n and _gate_up_arg(n) == "true",
+    "prefill_down": lambda n: "moe_prefill_kernel" in n and _gate_up_arg(n) == "false",
+    "decode_gate_up": lambda n: "moe_decode" in n and _gate_up_arg(n) == "true",
+    "decode_down": lambda n: "moe_decode" in n and _gate_up_arg(n) == "false",
 }
 
 
