@@ -1265,16 +1265,18 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
     }
     // The expert GEMMs of this forward run on the paged compute stream ps
     // (after the routing on s; the combine on s waits for them below), except
-    // in a decode forward that pages nothing, which computes on s itself: no
-    // page-in of it can share a CU with its kernels, and the fork and the
-    // join would add two cross-queue waits to the token's dependent chain
-    // (Qwen3-shaped layer, LFU: 128 -> 102 us per paged decode token on
-    // average, one box).  A decode forward with pages
-    // keeps the split: its compute beside the page-in workgroups delays them.
+    // in a decode forward, which runs on s itself, its page-in kernels too
+    // (inline_pages), in wave order: nothing of it then runs beside a page-in
+    // workgroup, the page-in spreads over every CU, and the token's dependent
+    // chain has no cross-queue wait (a fork, a join and the waits for the
+    // copy streams cost more than the overlap of the pages with the hit
+    // experts' compute that a decode forward gives up).  With the DMA-engine
+    // pager a decode forward with pages keeps the split.
     int n_pages = 0;
     for (const auto& pw : plan)
       for (const PlanEntry& p : pw) n_pages += p.paged ? 1 : 0;
-    hipStream_t ps = (h->pstream && !(decode && n_pages == 0)) ? h->pstream : s;
+    const bool inline_pages = decode && h->pager == STRATA_PAGER_KERNEL;
+    hipStream_t ps = (h->pstream && !(decode && (n_pages == 0 || inline_pages))) ? h->pstream : s;
     if (ps != s) {
       HIP_CHECK(hipEventRecord(h->ev_pfork, s));
       HIP_CHECK(hipStreamWaitEvent(ps, h->ev_pfork, 0));
@@ -1307,10 +1309,12 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
                    int(g1 - g0) < kPageJobs)
               ++g1;
             if (fault("h2d")) return fail(STRATA_E_HIP, "page-in launch failed (injected fault)");
-            const int c = rr++ % kCopyStreams;
-            used[c] = true;
-            if (pages[g0]->after_wave >= 0)
-              HIP_CHECK(hipStreamWaitEvent(h->copy_streams[c], h->ev_wave_done[pages[g0]->after_wave], 0));
+            // inline: one wave, so no page waits for a wave of this forward
+            const int c = inline_pages ? 0 : rr++ % kCopyStreams;
+            hipStream_t cs = inline_pages ? ps : h->copy_streams[c];
+            if (!inline_pages) used[c] = true;
+            if (pages[g0]->after_wave >= 0 && !inline_pages)
+              HIP_CHECK(hipStreamWaitEvent(cs, h->ev_wave_done[pages[g0]->after_wave], 0));
             PageBatch b;
             b.src = h->host_dev;
             b.stride = int64_t(h->slot_stride);
@@ -1320,7 +1324,7 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
               b.expert[i - g0] = pages[i]->expert;
               b.slot[i - g0] = pages[i]->slot;
             }
-            HIP_CHECK(launch_page_in(b, h->copy_streams[c]));
+            HIP_CHECK(launch_page_in(b, cs));
             g0 = g1;
           }
         } else {
