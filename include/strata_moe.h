@@ -102,9 +102,10 @@ typedef enum {
 
 /* How missing experts travel from the pinned host store into HBM slots.
  * KERNEL: the library's page-in kernel reads the store through its device
- * mapping (64 small workgroups on 16 CUs set aside for paging: two per XCD,
- * the copy streams' CU mask; the layer's expert kernels of paged forwards run
- * on an internal stream masked to the other CUs).  DMA: one
+ * mapping (64 small workgroups; in a prefill on 16 CUs set aside for paging,
+ * two per XCD, the copy streams' CU mask, while the layer's expert kernels of
+ * that forward run on an internal stream masked to the other CUs; in a decode
+ * forward on the caller's stream, before its expert kernels).  DMA: one
  * hipMemcpyAsync per record on the copy streams (the DMA engines; no CU
  * time, but the HIP runtime held the host 5-15 ms inside single copy calls
  * now and then on layers with small records).  AUTO: KERNEL for records of
@@ -236,9 +237,11 @@ typedef struct {
  * x and y must not overlap.  The call enqueues its work on `stream`.  When the
  * budget is smaller than E it waits once for the per-expert token counts to
  * reach the host, decides hits and misses, and pages missing experts from the
- * pinned store into slots (by the engine desc->pager chose) on internal copy
- * streams, and runs the expert kernels on an internal compute stream (ordered
- * after the routing on `stream`, and the combine on `stream` after it); if
+ * pinned store into slots (by the engine desc->pager chose): a prefill pages on
+ * internal copy streams and runs the expert kernels on an internal compute
+ * stream (ordered after the routing on `stream`, and the combine on `stream`
+ * after it); a decode forward (T <= 8) with the page-in kernel pages and
+ * computes on `stream` itself, and one that pages nothing computes there; if
  * more distinct experts are needed than there are slots, the policy's
  * hottest quarter of the slots stays put and the experts stream through the
  * rest in waves of half of it, so one wave's pages land while the previous
