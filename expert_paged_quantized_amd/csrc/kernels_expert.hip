@@ -1386,7 +1386,7 @@ int decode_grid(int N, int log2S, int n_tiles) {
 // 8,192 waves, or, up to 4 splits, while each wave keeps 8 K-blocks and the
 // launch stays within 4,096 waves (small layers: shorter serial K loops).
 int decode_dot_waves(int N, int K, int quant, int tiles_per_token, int T) {
-  if (T > 4) return 0;
+  if (T > kDecodeMaxT) return 0;  // above 4 tokens the tiles hold at most 4 rows
   const int TT = T <= 1 ? 1 : (T <= 2 ? 2 : 4);
   const int KB = K / 64, units = tiles_per_token * (N / 32);
   int S = 1;

@@ -516,6 +516,10 @@ __device__ __forceinline__ void emit_counts_and_tiles(int c, int o, int total, i
     put(i, E, shared_slot, TK + i * tile_rows, min(tile_rows, T - i * tile_rows), 0, nsh);
   if (tile_rows > kPrefillTM) {  // one tile per expert
     if (used) put(nsh + to, e, e, o, c, nsh + to, 1);
+  } else if (tile_rows < 32) {  // decode: tiles of at most tile_rows rows, by expert
+    if (used)
+      for (int j = 0; j < nt; ++j)
+        put(nsh + to + j, e, e, o + j * tile_rows, min(tile_rows, c - j * tile_rows), nsh + to, nt);
   } else {
     // column tiles of each tile: full tiles have tile_rows / 32, the last one
     // ceil(rem / 32); group g = column tiles, g = 4 first

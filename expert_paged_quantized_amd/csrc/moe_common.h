@@ -16,6 +16,10 @@ enum RouterKind : int { R_SOFTMAX = 1, R_SIGMOID = 2 };
 constexpr int kPrefillTM = 128;
 // Largest T that takes the decode (split-K GEMV-style) kernels.
 constexpr int kDecodeMaxT = 8;
+// Rows per tile of a decode forward: one tile per expert up to 4 tokens; above,
+// tiles of at most 4 rows (an expert with more takes two), which the
+// dot-product decode kernel contracts (its 4-row unit).
+constexpr int decode_tile_rows(int T) { return T > 4 ? 4 : (1 << 30); }
 // Weight tile: 32 output rows x 64 inputs; one lane owns 16 bytes of codes.
 constexpr int kTileRows = 32;
 constexpr int kTileK = 64;

@@ -664,7 +664,10 @@ static int prefill_ksplit(int K, int sshift);
 static uint64_t carve(const strata_moe* h, size_t T, uint8_t* base, Workspace* ws) {
   const size_t TK = T * h->k;
   ws->max_rows = TK + (h->S ? T : 0);
-  ws->max_tiles = TK / kPrefillTM + std::min<size_t>(h->E, TK) + (T + kPrefillTM - 1) / kPrefillTM + 4;
+  // prefill tiles, or decode tiles of at most 4 rows (each expert's count
+  // rounded up to 4: at most one more tile per expert than TK / 4)
+  ws->max_tiles = TK / kPrefillTM + std::min<size_t>(h->E, TK) + (T + kPrefillTM - 1) / kPrefillTM + 4 +
+                  std::min<size_t>(T, kDecodeMaxT) * h->k / 4 + 2;
   uint64_t at = 0;
   auto take = [&](auto*& p, size_t bytes) {
     using P = std::remove_reference_t<decltype(p)>;
@@ -990,9 +993,9 @@ static hipError_t run_experts(strata_moe* h, const Workspace& ws, const void* x,
   return hipSuccess;
 }
 
-static void add_tiles(strata_moe* h, int expert, int slot, int row_begin, int count, bool decode,
+static void add_tiles(strata_moe* h, int expert, int slot, int row_begin, int count, int tile_rows,
                       int& n) {
-  const int tr = decode ? count : kPrefillTM;
+  const int tr = std::min(tile_rows, std::max(count, 1));
   const int first = n, nt = (count + tr - 1) / tr;
   for (int r = 0; r < count; r += tr) {
     Tile t;
@@ -1129,8 +1132,9 @@ static strata_status forward_hybrid(strata_moe* h, const Workspace& ws, const vo
   h->rm.forward_hybrid(needed, hits, host, ahead);
   // GPU: the hits and the shared expert, one launch set
   int n = 0;
-  for (const PlanEntry& p : hits) add_tiles(h, p.expert, p.slot, off[p.expert], h->h_counts[p.expert], true, n);
-  if (h->S) add_tiles(h, h->E, h->budget, TK, T, true, n);
+  const int tr = decode_tile_rows(T);
+  for (const PlanEntry& p : hits) add_tiles(h, p.expert, p.slot, off[p.expert], h->h_counts[p.expert], tr, n);
+  if (h->S) add_tiles(h, h->E, h->budget, TK, T, tr, n);
   if ((size_t)n > ws.max_tiles) return fail(STRATA_E_HIP, "tile list overflow");
   if (n > 0)
     HIP_CHECK(hipMemcpyAsync(ws.tiles_host, h->h_tiles, size_t(n) * sizeof(Tile), hipMemcpyHostToDevice, s));
@@ -1170,7 +1174,7 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
   if (capturing && h->timing) return fail(STRATA_E_UNSUPPORTED, "kernel timing cannot be captured");
   if (h->fwd_recorded && !capturing) HIP_CHECK(hipStreamWaitEvent(s, h->ev_fwd_done, 0));
 
-  const int tile_rows = decode ? (1 << 30) : kPrefillTM;
+  const int tile_rows = decode ? decode_tile_rows(T) : kPrefillTM;
   if (route_decode_fits(T, h->E + h->gated)) {
     // router and routing in one launch (its last workgroup routes); the
     // arrival counter is the word after the distinct-expert total
@@ -1193,7 +1197,7 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
   }
 
   if (h->budget == h->E) {
-    const int ub = decode ? std::min(h->E, TK) + h->S
+    const int ub = decode ? (T > 4 ? std::min(h->E, TK) + TK / 4 + h->S * ((T + 3) / 4) : std::min(h->E, TK) + h->S)
                           : TK / kPrefillTM + std::min(h->E, TK) + (h->S ? (T + kPrefillTM - 1) / kPrefillTM : 0);
     HIP_CHECK(run_experts(h, ws, x, ws.tiles_dev, ws.ntiles, ub, decode, T, s));
     h->rm.forwards++;
@@ -1232,11 +1236,11 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
     for (int w = 0; w < nw; ++w) {
       hb[w] = n;
       for (const PlanEntry& p : plan[w])
-        if (!p.paged) add_tiles(h, p.expert, p.slot, off[p.expert], h->h_counts[p.expert], decode, n);
-      if (w == 0 && h->S) add_tiles(h, h->E, h->budget, TK, T, decode, n);
+        if (!p.paged) add_tiles(h, p.expert, p.slot, off[p.expert], h->h_counts[p.expert], tile_rows, n);
+      if (w == 0 && h->S) add_tiles(h, h->E, h->budget, TK, T, tile_rows, n);
       he[w] = n;
       for (const PlanEntry& p : plan[w])
-        if (p.paged) add_tiles(h, p.expert, p.slot, off[p.expert], h->h_counts[p.expert], decode, n);
+        if (p.paged) add_tiles(h, p.expert, p.slot, off[p.expert], h->h_counts[p.expert], tile_rows, n);
       pe[w] = n;
     }
     if ((size_t)n > ws.max_tiles) return fail(STRATA_E_HIP, "tile list overflow");
