@@ -314,7 +314,8 @@ __device__ __forceinline__ float o_elem(float acc, float gsx, const ColExp& ce) 
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel (T <= 8 tokens).  Workgroup = 8 waves = R row tiles (32
+// MFMA decode kernel (T <= 8 tokens; used where the dot-product kernel's
+// staged token rows would not fit its LDS).  Workgroup = 8 waves = R row tiles (32
 // weight rows each) of one expert x S K-splits, R*S = 8.  K is walked in
 // chunks of S*8 K-blocks; in a chunk, wave (r, s) takes the 8 consecutive
 // blocks s*8..s*8+7 of row tile r.  The token rows of a chunk are staged in
@@ -494,7 +495,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void moe_decode_kernel(GemmArgs p, 
 
 
 // ---------------------------------------------------------------------------
-// Dot-product decode kernel (T <= 4 tokens).  At a handful of tokens the
+// Dot-product decode kernel (T <= 8 tokens; above 4 the tiles hold at most 4
+// rows, so a tile never has more than 4).  At a handful of tokens the
 // 32-column MFMA wastes most of its work and its issue time adds to the
 // decode time, so the contraction runs on the VALU dot units instead:
 //   int4:  an AND leaves a code pair as fp16 denormals (q * 2^-24 for the low
