@@ -1313,7 +1313,8 @@ static strata_status forward_impl(strata_moe* h, const Workspace& ws, const void
                    int(g1 - g0) < kPageJobs)
               ++g1;
             if (fault("h2d")) return fail(STRATA_E_HIP, "page-in launch failed (injected fault)");
-            // inline: one wave, so no page waits for a wave of this forward
+            // inline: enqueued on s after every earlier wave's compute, so
+            // a page needs no event to wait for the wave it follows
             const int c = inline_pages ? 0 : rr++ % kCopyStreams;
             hipStream_t cs = inline_pages ? ps : h->copy_streams[c];
             if (!inline_pages) used[c] = true;
