@@ -11,12 +11,13 @@
 // Forward enqueues router -> top-k -> permute, then the expert GEMMs and the
 // combine.  With every expert resident the whole forward stays on the device.
 // With a smaller budget the per-expert counts come back to the host once, the
-// residency manager decides hits, misses and waves, misses are copied from the
-// pinned store into their slots over four copy streams, each wave runs its
-// hit experts while its misses are still in flight, and a wave's pages wait
-// only for the compute of the wave that last read their slots.  After a
-// forward the policy may page experts ahead of need (prefetch); the next
-// forward waits for those pages.
+// residency manager decides hits, misses and waves, and misses are copied from
+// the pinned store into their slots.  A prefill pages on the copy streams
+// (kCopyStreams of them, masked to kPageCUs CUs) while each wave runs its hit
+// experts on the paged compute stream, and a wave's pages wait only for the
+// compute of the wave that last read their slots; a decode forward pages on
+// the caller's stream, in wave order.  After a forward the policy may page
+// experts ahead of need (prefetch); the next forward waits for those pages.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <sched.h>
