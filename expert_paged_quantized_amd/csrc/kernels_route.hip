@@ -352,9 +352,10 @@ __device__ __forceinline__ float load_logit(const float* p) {
     return *p;
 }
 
+// taken_out (optional): bit j of lane l set when expert l + 64 j was picked.
 template <int JPL, bool COHERENT = false>
 __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
-                                           int lane, float& my_v, int& my_e) {
+                                           int lane, float& my_v, int& my_e, uint32_t* taken_out = nullptr) {
   float vals[JPL];
 #pragma unroll
   for (int j = 0; j < JPL; ++j) {
@@ -403,6 +404,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
       my_e = ce;
     }
   }
+  if (taken_out) *taken_out = taken;
 }
 
 // Weights of one token from its selected logits (lanes r < k hold pick r).
@@ -647,9 +649,16 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 constexpr int kSmallT = 16;
 // Small batches with few experts select by counting: T * E^2 comparisons
 // spread over the workgroup's 1024 threads, against k dependent rounds of a
-// one-wave selection.
+// one-wave selection.  (Counting up to E = 1,024 comparisons per thread was
+// slower than the rounds: one token's fused routing launch took 20 instead
+// of 14 us at 512 experts, top-10, and 51 instead of 25 us at 896, top-16.)
 constexpr int kRankCountWork = 65536;  // largest T * E * E
 constexpr int kRankCountSlots = 1024;  // largest T * E
+// One token's grouping in one wave (route_one_token) when its top-k takes at
+// most this many (pick, logit-per-lane) steps: with top-2 of 8 experts it
+// ends ~0.9 us sooner than the workgroup path, with top-8 of 128 ~0.7 us
+// later (the counting selection wins there).
+constexpr int kOneWaveSteps = 4;  // largest k * JPL
 
 // Selection key of a logit of expert e: larger is better.  The fp32 order
 // (with -0 == +0: adding +0 maps -0 to +0) in the high word, the complement
@@ -658,6 +667,75 @@ __device__ __forceinline__ uint64_t select_key(float l, int e) {
   const uint32_t u = __float_as_uint(l + 0.0f);
   const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+}
+
+// One token with one tile per expert (a one-token decode forward): the whole
+// grouping in one wave, with no LDS and no workgroup barrier.  The picks are
+// the one-wave top-k's (value descending, equal values to the lower id).
+// With one token every picked expert holds exactly one row, so a pick's
+// position in the expert-major grouping is the number of picks with a lower
+// id, and counts, offsets, perm, pos and the tile list (the shared expert's
+// tile, then one tile per picked expert by ascending id) follow from the k
+// picks alone; they are the values the workgroup path below computes.
+template <int JPL, bool COHERENT>
+__device__ __forceinline__ void route_one_token(
+    const float* __restrict__ logits, int E, int k, int router, int S, int shared_slot,
+    int32_t* __restrict__ idx, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ pos,
+    Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles, unsigned long long* __restrict__ distinct_total) {
+  const int lane = threadIdx.x & 63;
+  float my_v;
+  int my_e;
+  uint32_t taken;
+  topk_token<JPL, COHERENT>(logits, 0, E, k, lane, my_v, my_e, &taken);
+  const float wt = topk_weight(my_v, k, router, lane);
+  // counts and offsets of experts lane + 64 j: the picks below an id are
+  // those of the earlier 64-expert groups plus this group's lower lanes
+  int below = 0;
+#pragma unroll
+  for (int j = 0; j < JPL; ++j) {
+    const int e = lane + 64 * j;
+    const int c = (taken >> j) & 1;
+    const int inc = wave_inclusive_scan(c);
+    if (e < E) {
+      counts[e] = c;
+      offsets[e] = below + inc - c;
+    }
+    below += __builtin_amdgcn_readlane(inc, 63);
+  }
+  int r = 0;  // pick `lane`'s position: the picks with a lower id
+  for (int j = 0; j < k; ++j) r += __builtin_amdgcn_readlane(my_e, j) < my_e ? 1 : 0;
+  const int nsh = S ? 1 : 0;
+  if (lane < k) {
+    idx[lane] = my_e;
+    w[lane] = wt;
+    perm[r] = 0;
+    pos[lane] = r;
+    Tile tl;
+    tl.expert = my_e;
+    tl.slot = my_e;
+    tl.row_begin = r;
+    tl.nrows = 1;
+    tl.group_first = nsh + r;
+    tl.group_count = 1;
+    tiles[nsh + r] = tl;
+  }
+  if (lane == 0) {
+    offsets[E] = k;
+    if (S) {
+      perm[k] = 0;
+      Tile tl;
+      tl.expert = E;
+      tl.slot = shared_slot;
+      tl.row_begin = k;
+      tl.nrows = 1;
+      tl.group_first = 0;
+      tl.group_count = 1;
+      tiles[0] = tl;
+    }
+    n_tiles[0] = k + nsh;
+    atomicAdd(distinct_total, (unsigned long long)k);
+  }
 }
 
 template <int JPL, bool COHERENT>
@@ -674,6 +752,12 @@ __device__ __forceinline__ void route_small_body(
   __shared__ uint64_t keys[kRankCountSlots];
   __shared__ int wave_tot[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (T == 1 && tile_rows > kPrefillTM && k * JPL <= kOneWaveSteps) {
+    if (wave == 0)
+      route_one_token<JPL, COHERENT>(logits, E, k, router, S, shared_slot, idx, w, counts, offsets, perm, pos,
+                                     tiles, n_tiles, distinct_total);
+    return;
+  }
   for (int e = tid; e < E; e += 1024) mask[e] = 0u;
   // Selection by counting (uniform branch): the expert of slot q = t * E + e
   // takes rank r = the number of its token's keys above its own, and the
