@@ -643,15 +643,17 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 
 // ---------------------------------------------------------------------------
 // Whole routing of a small batch (T <= 16) in one 1024-thread workgroup: top-k
-// (wave w takes token w), then the same masks, offsets, permutation and tile
+// (by counting, or wave w takes token w), then the same masks, offsets, permutation and tile
 // list as the multi-block passes.
 // ---------------------------------------------------------------------------
 constexpr int kSmallT = 16;
 // Small batches with few experts select by counting: T * E^2 comparisons
-// spread over the workgroup's 1024 threads, against k dependent rounds of a
-// one-wave selection.  (Counting up to E = 1,024 comparisons per thread was
-// slower than the rounds: one token's fused routing launch took 20 instead
-// of 14 us at 512 experts, top-10, and 51 instead of 25 us at 896, top-16.)
+// spread over the workgroup's 1024 threads; the others search each token's
+// k-th largest key in one wave (topk_by_threshold).  (Counting up to
+// E = 1,024 comparisons per thread was slower than k rounds of one-wave
+// picks: one token's fused routing launch took 20 instead of 14 us at 512
+// experts, top-10, and 51 instead of 25 us at 896, top-16; the threshold
+// search takes 11 and 17 us there.)
 constexpr int kRankCountWork = 65536;  // largest T * E * E
 constexpr int kRankCountSlots = 1024;  // largest T * E
 // One token's grouping in one wave (route_one_token) when its top-k takes at
@@ -738,6 +740,86 @@ __device__ __forceinline__ void route_one_token(
   }
 }
 
+// Lanes r < k end with the r-th selected (logit, expert) of token t in
+// select_key's order (value descending, -0 == +0, equal values to the lower
+// id), found without k dependent rounds: a bitwise search for the largest
+// fp32 order o that at least k of the token's keys reach (one wave-wide
+// ballot count per bit), and, when more keys sit at o than are still
+// needed, the same search over their ids; the k keys above that threshold
+// are gathered in `lds` (k entries of this wave's own) and each is placed by
+// counting the picks above it.  Slots past E hold order 0 and ids >= E, so
+// they rank below every expert.
+template <int JPL, bool COHERENT>
+__device__ __forceinline__ void topk_by_threshold(const float* __restrict__ logits, int t, int E, int k,
+                                                  int lane, float& my_v, int& my_e, uint64_t* lds) {
+  constexpr int kIdBits = 6 + (JPL >= 2) + (JPL >= 4) + (JPL >= 8) + (JPL >= 16);  // ids < 64 * JPL
+  uint32_t ord[JPL];
+#pragma unroll
+  for (int j = 0; j < JPL; ++j) {
+    const int e = lane + 64 * j;
+    const float v = load_logit<COHERENT>(&logits[(size_t)t * E + min(e, E - 1)]);
+    ord[j] = (e < E) ? (uint32_t)(select_key(v, e) >> 32) : 0u;
+  }
+  uint32_t o = 0;  // count(ord >= o) >= k holds throughout
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = o | (1u << b);
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < JPL; ++j) n += __popcll(__ballot(ord[j] >= c));
+    if (n >= k) o = c;
+  }
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int j = 0; j < JPL; ++j) {
+    n_gt += __popcll(__ballot(ord[j] > o));
+    n_eq += __popcll(__ballot(ord[j] == o));
+  }
+  const int need = k - n_gt;  // 1 .. n_eq keys at o, lowest ids first
+  int x = 64 * JPL - 1;       // the largest id taken at o
+  if (n_eq > need) {
+    x = 0;  // the largest x with fewer than `need` keys at o below it
+    for (int b = kIdBits - 1; b >= 0; --b) {
+      const int c = x | (1 << b);
+      int n = 0;
+#pragma unroll
+      for (int j = 0; j < JPL; ++j) n += __popcll(__ballot(ord[j] == o && lane + 64 * j < c));
+      if (n < need) x = c;
+    }
+  }
+  uint32_t pick = 0;
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < JPL; ++j) {
+    const bool p = ord[j] > o || (ord[j] == o && lane + 64 * j <= x);
+    pick |= (p ? 1u : 0u) << j;
+    cnt += p ? 1 : 0;
+  }
+  int at = wave_inclusive_scan(cnt) - cnt;  // k picks in all
+#pragma unroll
+  for (int j = 0; j < JPL; ++j)
+    if ((pick >> j) & 1u) lds[at++] = ((uint64_t)ord[j] << 32) | (uint32_t)~(uint32_t)(lane + 64 * j);
+  __threadfence_block();
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t key = lane < k ? lds[lane] : 0ull;
+  int r = 0;  // picks above this one
+  for (int j = 0; j < k; ++j) {
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(key >> 32), j);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)key, j);
+    r += (((uint64_t)hi << 32) | lo) > key ? 1 : 0;
+  }
+  if (lane < k) lds[r] = key;
+  __threadfence_block();
+  __builtin_amdgcn_wave_barrier();
+  my_v = 0.0f;
+  my_e = 0;
+  if (lane < k) {
+    const uint64_t q = lds[lane];
+    const uint32_t oq = (uint32_t)(q >> 32);
+    my_v = __uint_as_float((oq & 0x80000000u) ? (oq & 0x7fffffffu) : ~oq);
+    my_e = (int)~(uint32_t)q;
+  }
+}
+
 template <int JPL, bool COHERENT>
 __device__ __forceinline__ void route_small_body(
     const float* __restrict__ logits, int T, int E, int k, int router, int S, int tile_rows,
@@ -809,7 +891,7 @@ __device__ __forceinline__ void route_small_body(
         my_e = sel[wave * k + lane];
       }
     } else {
-      topk_token<JPL, COHERENT>(logits, wave, E, k, lane, my_v, my_e);
+      topk_by_threshold<JPL, COHERENT>(logits, wave, E, k, lane, my_v, my_e, keys + wave * 32);
     }
     const float wt = topk_weight(my_v, k, router, lane);
     if (lane < k) {
