@@ -417,24 +417,6 @@ __device__ __forceinline__ float topk_weight(float my_v, int k, int router, int 
   return z / sum;
 }
 
-// one wave per token, 4 tokens per workgroup
-template <int JPL>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                   int k, int router, int32_t* __restrict__ idx,
-                                                   float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  float my_v;
-  int my_e;
-  topk_token<JPL>(logits, t, E, k, lane, my_v, my_e);
-  const float wt = topk_weight(my_v, k, router, lane);
-  if (lane < k) {
-    idx[(size_t)t * k + lane] = my_e;
-    w[(size_t)t * k + lane] = wt;
-  }
-}
-
 // exclusive scan over up to 1024 values held one per thread of a 1024-thread
 // workgroup; returns the thread's prefix and the total
 // inclusive prefix sum over the wave: row shifts 1, 2, 4, 8 inside each
@@ -817,6 +799,30 @@ __device__ __forceinline__ void topk_by_threshold(const float* __restrict__ logi
     const uint32_t oq = (uint32_t)(q >> 32);
     my_v = __uint_as_float((oq & 0x80000000u) ? (oq & 0x7fffffffu) : ~oq);
     my_e = (int)~(uint32_t)q;
+  }
+}
+
+// Top-k and weights of a long batch: one wave per token, 4 tokens per
+// workgroup; k rounds of one-wave picks when the top-k is short (at most
+// kOneWaveSteps pick x logit-per-lane steps), else the threshold search.
+template <int JPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int k, int router, int32_t* __restrict__ idx,
+                                                   float* __restrict__ w) {
+  __shared__ uint64_t sel[4 * 32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  float my_v;
+  int my_e;
+  if (k * JPL <= kOneWaveSteps)
+    topk_token<JPL>(logits, t, E, k, lane, my_v, my_e);
+  else
+    topk_by_threshold<JPL, false>(logits, t, E, k, lane, my_v, my_e, sel + wave * 32);
+  const float wt = topk_weight(my_v, k, router, lane);
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = my_e;
+    w[(size_t)t * k + lane] = wt;
   }
 }
 
