@@ -635,7 +635,7 @@ constexpr int kSmallT = 16;
 // E = 1,024 comparisons per thread was slower than k rounds of one-wave
 // picks: one token's fused routing launch took 20 instead of 14 us at 512
 // experts, top-10, and 51 instead of 25 us at 896, top-16; the threshold
-// search takes 11 and 17 us there.)
+// search takes 10 and 13 us there.)
 constexpr int kRankCountWork = 65536;  // largest T * E * E
 constexpr int kRankCountSlots = 1024;  // largest T * E
 // One token's grouping in one wave (route_one_token) when its top-k takes at
@@ -724,10 +724,11 @@ __device__ __forceinline__ void route_one_token(
 
 // Lanes r < k end with the r-th selected (logit, expert) of token t in
 // select_key's order (value descending, -0 == +0, equal values to the lower
-// id), found without k dependent rounds: a bitwise search for the largest
-// fp32 order o that at least k of the token's keys reach (one wave-wide
-// ballot count per bit), and, when more keys sit at o than are still
-// needed, the same search over their ids; the k keys above that threshold
+// id), found without k dependent rounds: a bitwise search for an fp32
+// order o that at least k of the token's keys reach (one wave-wide ballot
+// count per bit; the largest such o, unless exactly k reach one on the
+// way), and, when more keys sit at o than are still needed, the same search
+// over their ids; the k keys above that threshold
 // are gathered in `lds` (k entries of this wave's own) and each is placed by
 // counting the picks above it.  Slots past E hold order 0 and ids >= E, so
 // they rank below every expert.
@@ -742,13 +743,18 @@ __device__ __forceinline__ void topk_by_threshold(const float* __restrict__ logi
     const float v = load_logit<COHERENT>(&logits[(size_t)t * E + min(e, E - 1)]);
     ord[j] = (e < E) ? (uint32_t)(select_key(v, e) >> 32) : 0u;
   }
-  uint32_t o = 0;  // count(ord >= o) >= k holds throughout
+  // count(ord >= o) >= k holds throughout; once exactly k keys reach o they
+  // are the top k (the next key lies below o), and the search stops there
+  uint32_t o = 0;
   for (int b = 31; b >= 0; --b) {
     const uint32_t c = o | (1u << b);
     int n = 0;
 #pragma unroll
     for (int j = 0; j < JPL; ++j) n += __popcll(__ballot(ord[j] >= c));
-    if (n >= k) o = c;
+    if (n >= k) {
+      o = c;
+      if (n == k) break;
+    }
   }
   int n_gt = 0, n_eq = 0;
 #pragma unroll
