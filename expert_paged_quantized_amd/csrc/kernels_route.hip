@@ -625,23 +625,15 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 
 // ---------------------------------------------------------------------------
 // Whole routing of a small batch (T <= 16) in one 1024-thread workgroup: top-k
-// (by counting, or wave w takes token w), then the same masks, offsets, permutation and tile
+// (wave w takes token w), then the same masks, offsets, permutation and tile
 // list as the multi-block passes.
 // ---------------------------------------------------------------------------
 constexpr int kSmallT = 16;
-// Small batches with few experts select by counting: T * E^2 comparisons
-// spread over the workgroup's 1024 threads; the others search each token's
-// k-th largest key in one wave (topk_by_threshold).  (Counting up to
-// E = 1,024 comparisons per thread was slower than k rounds of one-wave
-// picks: one token's fused routing launch took 20 instead of 14 us at 512
-// experts, top-10, and 51 instead of 25 us at 896, top-16; the threshold
-// search takes 10 and 13 us there.)
-constexpr int kRankCountWork = 65536;  // largest T * E * E
-constexpr int kRankCountSlots = 1024;  // largest T * E
+// Small batches search each token's k-th largest key in one wave
+// (topk_by_threshold), token t in wave t.
 // One token's grouping in one wave (route_one_token) when its top-k takes at
-// most this many (pick, logit-per-lane) steps: with top-2 of 8 experts it
-// ends ~0.9 us sooner than the workgroup path, with top-8 of 128 ~0.7 us
-// later (the counting selection wins there).
+// most this many (pick, logit-per-lane) steps (top-2 of 8 experts: ~0.9 us
+// sooner than the workgroup path).
 constexpr int kOneWaveSteps = 4;  // largest k * JPL
 
 // Selection key of a logit of expert e: larger is better.  The fp32 order
@@ -842,8 +834,7 @@ __device__ __forceinline__ void route_small_body(
   __shared__ unsigned int mask[kPermMaxE];  // bit = token (T <= 16)
   __shared__ int off[kPermMaxE];
   __shared__ int sel[kSmallT * 32];
-  __shared__ float selv[kSmallT * 32];
-  __shared__ uint64_t keys[kRankCountSlots];
+  __shared__ uint64_t keys[kSmallT * 32];  // threshold search: 32 per token's wave
   __shared__ int wave_tot[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (T == 1 && tile_rows > kPrefillTM && k * JPL <= kOneWaveSteps) {
@@ -853,58 +844,11 @@ __device__ __forceinline__ void route_small_body(
     return;
   }
   for (int e = tid; e < E; e += 1024) mask[e] = 0u;
-  // Selection by counting (uniform branch): the expert of slot q = t * E + e
-  // takes rank r = the number of its token's keys above its own, and the
-  // ranks below k are the picks in order.
-  // The slot's comparisons are split over P = 1024 / (T * E) threads
-  // (a power of two): thread (part, q) counts over keys part * E / P ..
-  // (part + 1) * E / P - 1 and the parts meet in an LDS sum.
-  const bool by_count = T * E <= kRankCountSlots && T * E * E <= kRankCountWork;
-  if (by_count) {
-    const int n = T * E;
-    int P = 1;
-    while (P * 2 * n <= 1024 && P * 2 <= E) P *= 2;
-    const int q = tid % n, part = tid / n, t = q / E, e = q - t * E;
-    const bool live = part < P;
-    uint64_t kq = 0;
-    float lq = 0.0f;
-    if (live) {
-      lq = load_logit<COHERENT>(&logits[(size_t)t * E + e]);
-      kq = select_key(lq, e);
-      if (part == 0) {
-        keys[q] = kq;
-        off[q] = 0;  // rank accumulator (off is rewritten after the scan)
-      }
-    }
-    __syncthreads();
-    if (live) {
-      const uint64_t* kt = keys + t * E;
-      const int j0 = part * E / P, j1 = (part + 1) * E / P;
-      int r = 0;
-      for (int j = j0; j < j1; ++j) r += kt[j] > kq ? 1 : 0;
-      if (r) atomicAdd(&off[q], r);
-    }
-    __syncthreads();
-    if (live && part == 0) {
-      const int r = off[q];
-      if (r < k) {
-        sel[t * k + r] = e;
-        selv[t * k + r] = lq;
-      }
-    }
-  }
   __syncthreads();
   if (wave < T) {
-    float my_v = 0.0f;
-    int my_e = 0;
-    if (by_count) {
-      if (lane < k) {
-        my_v = selv[wave * k + lane];
-        my_e = sel[wave * k + lane];
-      }
-    } else {
-      topk_by_threshold<JPL, COHERENT>(logits, wave, E, k, lane, my_v, my_e, keys + wave * 32);
-    }
+    float my_v;
+    int my_e;
+    topk_by_threshold<JPL, COHERENT>(logits, wave, E, k, lane, my_v, my_e, keys + wave * 32);
     const float wt = topk_weight(my_v, k, router, lane);
     if (lane < k) {
       idx[wave * k + lane] = my_e;
